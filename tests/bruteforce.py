@@ -1,0 +1,67 @@
+"""Pure-Python brute force used to pin the oracle on tiny inputs.
+
+Written independently of ``oracle/`` (plain lists, ``math`` and ``math.fsum``; no
+numpy): the RoPE angle of each pair, the rotation, the score of every key, the
+softmax and the weighted sum are spelled out element by element.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+
+def bf_position(i: int, grid: Sequence[int], offset: Sequence[int]) -> List[int]:
+    # coordinates of token i in a row-major grid, axis 0 slowest
+    n = len(grid)
+    strides = [1] * n
+    for a in range(n - 2, -1, -1):
+        strides[a] = strides[a + 1] * grid[a + 1]
+    return [(i // strides[a]) % grid[a] + offset[a] for a in range(n)]
+
+
+def bf_rope_token(x: List[float], pos: List[int], pairs: Sequence[int], theta: float,
+                  interleaved: bool) -> List[float]:
+    D = len(x)
+    half = D // 2
+    out = list(x)
+    j = 0
+    for axis, npairs in enumerate(pairs):
+        for u in range(npairs):
+            freq = math.pow(theta, -(2.0 * u) / (2.0 * npairs))
+            phi = pos[axis] * freq
+            ia, ib = (2 * j, 2 * j + 1) if interleaved else (j, j + half)
+            a, b = x[ia], x[ib]
+            out[ia] = a * math.cos(phi) - b * math.sin(phi)
+            out[ib] = a * math.sin(phi) + b * math.cos(phi)
+            j += 1
+    return out
+
+
+def bf_rope(x, grid, pairs, offset, theta=10000.0, interleaved=False):
+    """x: nested lists [S][H][D] -> rotated nested lists."""
+    return [[bf_rope_token(list(map(float, x[i][h])), bf_position(i, grid, offset), pairs, theta, interleaved)
+             for h in range(len(x[i]))] for i in range(len(x))]
+
+
+def bf_attention(q, k, v, pk=None, pv=None, scale: Optional[float] = None):
+    """q [Sq][Hq][D], k/v [S][Hkv][D], pk/pv [P][Hkv][D] or None -> o [Sq][Hq][D]."""
+    Sq, Hq, D = len(q), len(q[0]), len(q[0][0])
+    keys = (list(pk) if pk is not None else []) + list(k)
+    vals = (list(pv) if pv is not None else []) + list(v)
+    Hkv = len(keys[0])
+    group = Hq // Hkv
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    out = []
+    for i in range(Sq):
+        row = []
+        for h in range(Hq):
+            g = h // group
+            s = [sc * math.fsum(float(q[i][h][d]) * float(keys[j][g][d]) for d in range(D))
+                 for j in range(len(keys))]
+            m = max(s)
+            w = [math.exp(t - m) for t in s]
+            z = math.fsum(w)
+            row.append([math.fsum(w[j] * float(vals[j][g][d]) for j in range(len(keys))) / z
+                        for d in range(len(vals[0][g]))])
+        out.append(row)
+    return out
