@@ -1,0 +1,222 @@
+"""ctypes binding of libnxattn.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their data
+pointers, sizes, strides and the current HIP stream to the C ABI declared in
+include/nxattn.h, and raises NxattnError on a nonzero status. There is no fallback:
+if the library is not built, or a tensor is not on the GPU, the call fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnxattn.so")
+
+NXATTN_F32 = 0
+NXATTN_BF16 = 1
+MAX_BRANCHES = 8
+
+SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_cfg_combine",
+           "nxattn_status_string", "nxattn_last_error", "nxattn_version")
+
+
+class NxattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"nxattn status {status}: {msg}")
+        self.status = status
+
+
+class RopeDesc(ctypes.Structure):
+    _fields_ = [("n_axes", ctypes.c_int32), ("grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int32 * 3),
+                ("offset", ctypes.c_int32 * 3), ("theta", ctypes.c_double), ("interleaved", ctypes.c_int32)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("seq_q", ctypes.c_int32),
+                ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("q_strides", ctypes.c_int64 * 3), ("kv_strides", ctypes.c_int64 * 3),
+                ("o_strides", ctypes.c_int64 * 3),
+                ("prefix_kv", ctypes.c_void_p * MAX_BRANCHES), ("prefix_len", ctypes.c_int32 * MAX_BRANCHES),
+                ("scale", ctypes.c_float)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libnxattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bidirectional_transformer_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.nxattn_kv_relayout.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, vp]
+    lib.nxattn_kv_relayout.restype = i32
+    lib.nxattn_rope_apply.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), i32,
+                                      ctypes.POINTER(RopeDesc), vp]
+    lib.nxattn_rope_apply.restype = i32
+    lib.nxattn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp]
+    lib.nxattn_fwd.restype = i32
+    lib.nxattn_cfg_combine.argtypes = [vp, vp, vp, i64, ctypes.c_float, i32, vp]
+    lib.nxattn_cfg_combine.restype = i32
+    lib.nxattn_status_string.argtypes = [i32]
+    lib.nxattn_status_string.restype = ctypes.c_char_p
+    lib.nxattn_last_error.argtypes = []
+    lib.nxattn_last_error.restype = ctypes.c_char_p
+    lib.nxattn_version.argtypes = []
+    lib.nxattn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().nxattn_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().nxattn_last_error().decode()
+
+
+def version() -> str:
+    return load().nxattn_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise NxattnError(status, f"{status_string(status)}: {last_error()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return NXATTN_F32
+    if t.dtype == torch.bfloat16:
+        return NXATTN_BF16
+    raise NxattnError(2, f"unsupported tensor dtype {t.dtype}")
+
+
+def _gpu(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise NxattnError(1, "tensors must be on the GPU (HIP device)")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def rope_desc(grid: Sequence[int], pairs: Sequence[int], offset: Sequence[int], theta: float = 10000.0,
+              interleaved: bool = False) -> RopeDesc:
+    d = RopeDesc()
+    d.n_axes = len(grid)
+    for a in range(3):
+        d.grid[a] = int(grid[a]) if a < len(grid) else 1
+        d.pairs[a] = int(pairs[a]) if a < len(pairs) else 0
+        d.offset[a] = int(offset[a]) if a < len(offset) else 0
+    d.theta = float(theta)
+    d.interleaved = 1 if interleaved else 0
+    return d
+
+
+# ---------------------------------------------------------------------------------------
+def nxattn_kv_relayout(src: torch.Tensor, dst: torch.Tensor, direction: int, stream=None) -> None:
+    """dir 0: src replay [L,2,H,S,D] -> dst online [L,2,S,H,D]; dir 1: the inverse."""
+    _gpu(src, dst)
+    if src.dim() != 5 or dst.dim() != 5 or src.shape[1] != 2:
+        raise NxattnError(1, "relayout expects 5-D [L, 2, ., ., D] tensors")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise NxattnError(1, "relayout expects contiguous tensors")
+    if src.dtype != dst.dtype:
+        raise NxattnError(1, "src and dst dtypes differ")
+    L, _, A, B, D = src.shape
+    H, S = (A, B) if direction == 0 else (B, A)
+    if tuple(dst.shape) != (L, 2, B, A, D):
+        raise NxattnError(1, f"dst shape {tuple(dst.shape)} does not match {(L, 2, B, A, D)}")
+    _check(load().nxattn_kv_relayout(src.data_ptr(), dst.data_ptr(), L, H, S, D, _dtype_code(src),
+                                     int(direction), _stream(stream)))
+
+
+def nxattn_rope_apply(x: torch.Tensor, descs: List[RopeDesc], stream=None) -> None:
+    """In-place RoPE on x [B, S, H, D] (strided, D contiguous); one descriptor per branch."""
+    _gpu(x)
+    if x.dim() != 4:
+        raise NxattnError(1, "x must be [B, S, H, D]")
+    B, S, H, D = x.shape
+    if x.stride(3) != 1:
+        raise NxattnError(1, "the head_dim dimension must be contiguous")
+    if len(descs) != B:
+        raise NxattnError(1, "one RopeDesc per batch entry is required")
+    st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    arr = (RopeDesc * max(1, B))(*descs)
+    _check(load().nxattn_rope_apply(x.data_ptr(), B, S, H, D, st, _dtype_code(x), arr, _stream(stream)))
+
+
+def make_fwd_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                  prefix: Sequence[Optional[torch.Tensor]], scale: float = 0.0) -> FwdArgs:
+    B, S, Hq, D = q.shape
+    a = FwdArgs()
+    a.dtype = _dtype_code(q)
+    a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, k.shape[2], D
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    for i in range(3):
+        a.q_strides[i] = q.stride(i)
+        a.kv_strides[i] = k.stride(i)
+        a.o_strides[i] = o.stride(i)
+    for b in range(MAX_BRANCHES):
+        p = prefix[b] if b < len(prefix) else None
+        if p is None or p.numel() == 0:
+            a.prefix_kv[b] = None
+            a.prefix_len[b] = 0
+        else:
+            a.prefix_kv[b] = p.data_ptr()
+            a.prefix_len[b] = p.shape[1]
+    a.scale = float(scale)
+    return a
+
+
+def nxattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+               prefix: Sequence[Optional[torch.Tensor]] = (), scale: float = 0.0, stream=None) -> None:
+    """o = attention(q, [prefix_k ++ k], [prefix_v ++ v]) for every branch.
+
+    q, o [B,S,Hq,D]; k, v [B,S,Hkv,D] (same strides); prefix[b] contiguous [2,P_b,Hkv,D] or None.
+    """
+    _gpu(q, k, v, o, *[p for p in prefix if p is not None])
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise NxattnError(1, "q, k, v, o must be 4-D [B, S, H, D]")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise NxattnError(1, "k and v must have the same shape and strides")
+    if q.shape[0] != k.shape[0] or q.shape[1] != k.shape[1] or q.shape[3] != k.shape[3] or o.shape != q.shape:
+        raise NxattnError(1, "inconsistent q/k/v/o shapes")
+    if len(prefix) not in (0, q.shape[0]):
+        raise NxattnError(1, "prefix must have one entry per batch entry")
+    for p in prefix:
+        if p is not None and (not p.is_contiguous() or p.dim() != 4 or p.shape[0] != 2
+                              or p.shape[2] != k.shape[2] or p.shape[3] != k.shape[3] or p.dtype != q.dtype):
+            raise NxattnError(1, "prefix entries must be contiguous [2, P, Hkv, D] of q's dtype")
+    for t in (k, v, o):
+        if t.dtype != q.dtype:
+            raise NxattnError(1, "q, k, v, o dtypes differ")
+    a = make_fwd_args(q, k, v, o, prefix, scale)
+    _check(load().nxattn_fwd(ctypes.byref(a), _stream(stream)))
+
+
+def nxattn_cfg_combine(cond: torch.Tensor, uncond: torch.Tensor, out: torch.Tensor, guidance: float,
+                       stream=None) -> None:
+    """out = uncond + guidance * (cond - uncond) over contiguous tensors of equal size."""
+    _gpu(cond, uncond, out)
+    if not (cond.is_contiguous() and uncond.is_contiguous() and out.is_contiguous()):
+        raise NxattnError(1, "cfg tensors must be contiguous")
+    if cond.numel() != uncond.numel() or cond.numel() != out.numel():
+        raise NxattnError(1, "cfg tensors differ in size")
+    if cond.dtype != uncond.dtype or cond.dtype != out.dtype:
+        raise NxattnError(1, "cfg dtypes differ")
+    _check(load().nxattn_cfg_combine(cond.data_ptr(), uncond.data_ptr(), out.data_ptr(), cond.numel(),
+                                     float(guidance), _dtype_code(cond), _stream(stream)))

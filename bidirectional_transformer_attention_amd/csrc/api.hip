@@ -1,0 +1,118 @@
+// Host side of the nxattn C ABI: error reporting, status strings and the validation
+// and dispatch of nxattn_fwd (the relayout, RoPE and CFG entry points live beside
+// their kernels).
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "nx_internal.h"
+
+namespace nx {
+
+static thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(NXATTN_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return NXATTN_OK;
+}
+
+// Byte extent of a strided [n0, n1, n2, inner] view (0 if empty).
+static int64_t extent_bytes(const int64_t st[3], int64_t n0, int64_t n1, int64_t n2, int64_t inner, int64_t es) {
+  if (n0 <= 0 || n1 <= 0 || n2 <= 0 || inner <= 0) return 0;
+  return ((n0 - 1) * st[0] + (n1 - 1) * st[1] + (n2 - 1) * st[2] + inner) * es;
+}
+
+}  // namespace nx
+
+using namespace nx;
+
+extern "C" const char* nxattn_status_string(int status) {
+  switch (status) {
+    case NXATTN_OK: return "ok";
+    case NXATTN_ERR_INVALID: return "invalid argument";
+    case NXATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NXATTN_ERR_ALIGN: return "misaligned pointer or stride";
+    case NXATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* nxattn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* nxattn_version(void) { return "0.1.0"; }
+
+extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
+  clear_error();
+  if (!a) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: args is NULL");
+  if (a->dtype != NXATTN_F32 && a->dtype != NXATTN_BF16)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: dtype %d is not F32 or BF16", a->dtype);
+  if (a->batch < 0 || a->seq_q < 0 || a->heads_q <= 0 || a->heads_kv <= 0 || a->head_dim <= 0)
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd: bad sizes batch=%d seq_q=%d heads_q=%d heads_kv=%d head_dim=%d",
+                a->batch, a->seq_q, a->heads_q, a->heads_kv, a->head_dim);
+  if (a->batch > NXATTN_MAX_BRANCHES)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: batch %d > %d", a->batch, NXATTN_MAX_BRANCHES);
+  if (a->heads_q % a->heads_kv != 0)
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd: heads_q %d is not a multiple of heads_kv %d", a->heads_q, a->heads_kv);
+  if (a->heads_q > 4096) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: heads_q %d > 4096", a->heads_q);
+  if (a->dtype == NXATTN_BF16 && a->head_dim != 128)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: bf16 supports head_dim 128, got %d", a->head_dim);
+  if (a->dtype == NXATTN_F32 && a->head_dim != 64 && a->head_dim != 72)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: f32 supports head_dim 64 or 72, got %d", a->head_dim);
+  if (!(a->scale == a->scale) || std::isinf(a->scale)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: scale is not finite");
+  for (int b = 0; b < a->batch; ++b) {
+    if (a->prefix_len[b] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: prefix_len[%d] < 0", b);
+    if ((a->prefix_len[b] > 0) != (a->prefix_kv[b] != nullptr))
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: prefix_kv[%d] must be non-NULL iff prefix_len[%d] > 0", b, b);
+    if ((int64_t)a->prefix_len[b] + a->seq_q > INT32_MAX)
+      return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: prefix_len[%d] + seq_q overflows int32", b);
+  }
+  if (a->batch == 0 || a->seq_q == 0) return NXATTN_OK;
+  if (!a->q || !a->k || !a->v || !a->o) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
+  const int64_t es = esize(a->dtype);
+  const int64_t* sts[3] = {a->q_strides, a->kv_strides, a->o_strides};
+  for (int t = 0; t < 3; ++t)
+    for (int i = 0; i < 3; ++i) {
+      if (sts[t][i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: negative stride");
+      if ((sts[t][i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: stride %lld is not a multiple of 16 bytes", (long long)sts[t][i]);
+    }
+  const void* ptrs[4] = {a->q, a->k, a->v, a->o};
+  for (auto p : ptrs)
+    if (!aligned16(p)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: q/k/v/o must be 16-byte aligned");
+  for (int b = 0; b < a->batch; ++b)
+    if (a->prefix_kv[b] && !aligned16(a->prefix_kv[b])) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: prefix_kv[%d] misaligned", b);
+  // the output must not overlap any input
+  const int64_t D = a->head_dim;
+  const int64_t ob = extent_bytes(a->o_strides, a->batch, a->seq_q, a->heads_q, D, es);
+  const int64_t qb = extent_bytes(a->q_strides, a->batch, a->seq_q, a->heads_q, D, es);
+  const int64_t kb = extent_bytes(a->kv_strides, a->batch, a->seq_q, a->heads_kv, D, es);
+  if (overlaps(a->o, ob, a->q, qb) || overlaps(a->o, ob, a->k, kb) || overlaps(a->o, ob, a->v, kb))
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd: o overlaps q, k or v");
+  for (int b = 0; b < a->batch; ++b)
+    if (a->prefix_kv[b] && overlaps(a->o, ob, a->prefix_kv[b], 2LL * a->prefix_len[b] * a->heads_kv * D * es))
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: o overlaps prefix_kv[%d]", b);
+
+  FwdProblem p;
+  p.dtype = a->dtype; p.batch = a->batch; p.seq_q = a->seq_q; p.heads_q = a->heads_q;
+  p.heads_kv = a->heads_kv; p.head_dim = a->head_dim;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o;
+  for (int i = 0; i < 3; ++i) { p.qs[i] = a->q_strides[i]; p.ks[i] = a->kv_strides[i]; p.os[i] = a->o_strides[i]; }
+  for (int b = 0; b < NXATTN_MAX_BRANCHES; ++b) {
+    p.prefix[b] = b < a->batch ? a->prefix_kv[b] : nullptr;
+    p.plen[b] = b < a->batch ? a->prefix_len[b] : 0;
+  }
+  p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+  return a->dtype == NXATTN_BF16 ? launch_fwd_bf16(p, stream) : launch_fwd_f32(p, stream);
+}

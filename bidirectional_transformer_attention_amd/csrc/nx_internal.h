@@ -1,0 +1,60 @@
+// Internal helpers shared by the nxattn HIP sources (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cstdio>
+#include <cstdarg>
+
+#include "../../include/nxattn.h"
+
+namespace nx {
+
+// ---- error reporting (thread-local detail string) ----------------------------------
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t esize(int dtype) { return dtype == NXATTN_F32 ? 4 : 2; }
+
+// true if [a, a+na) and [b, b+nb) (bytes) overlap
+inline bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// ---- device-side element types ------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = static_cast<__bf16>(lo);
+  r[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---- launchers implemented per kernel file -------------------------------------------
+struct FwdProblem {
+  int dtype, batch, seq_q, heads_q, heads_kv, head_dim;
+  const void* q; const void* k; const void* v; void* o;
+  int64_t qs[3], ks[3], os[3];
+  const void* prefix[NXATTN_MAX_BRANCHES];
+  int32_t plen[NXATTN_MAX_BRANCHES];
+  float scale;
+};
+int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
+int launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
+
+}  // namespace nx

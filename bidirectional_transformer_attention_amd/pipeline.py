@@ -1,0 +1,73 @@
+"""One attention step of a DiT / ViT layer, chained from the four C-ABI calls.
+
+    relayout (replay -> online, when the prefix arrives in the replay layout)
+    -> RoPE on own q and own k (every branch, its own offsets)
+    -> fused attention over [prefix ++ own] for all branches in one launch
+    -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
+
+Only tensor allocation and argument marshalling happen here; every step runs in the HIP
+library. The prefix of branch b is passed as one layer slice [2, P_b, Hkv, D] of the
+online cache (NeoPP page, "KV file layout").
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import binding as nx
+from .synth import Inputs, Workload
+
+
+class AttentionStep:
+    def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda"):
+        self.wl = wl
+        dev = torch.device(device)
+        self.q = inp.q.to(dev)
+        self.k = inp.k.to(dev)
+        self.v = inp.v.to(dev)
+        self.B, self.S, self.Hq, self.D = self.q.shape
+        self.Hkv = self.k.shape[2]
+        # prefix as stored (replay [1,2,H,P,D] or online [2,P,H,D]) and the online buffers
+        self.prefix_src: List[Optional[torch.Tensor]] = []
+        self.prefix_online: List[Optional[torch.Tensor]] = []
+        for p in inp.prefix:
+            if p is None:
+                self.prefix_src.append(None)
+                self.prefix_online.append(None)
+            elif wl.prefix_layout == "replay":
+                src = p.to(dev).unsqueeze(0).contiguous()                 # [1, 2, H, P, D]
+                self.prefix_src.append(src)
+                self.prefix_online.append(torch.empty((2, src.shape[3], src.shape[2], src.shape[4]),
+                                                      dtype=src.dtype, device=dev))
+            else:
+                on = p.to(dev).contiguous()                               # [2, P, H, D]
+                self.prefix_src.append(None)
+                self.prefix_online.append(on)
+        self.descs = [nx.rope_desc(wl.grid, wl.pairs, wl.offsets[b], wl.theta) for b in range(self.B)]
+        self.o = torch.empty_like(self.q)
+        self.use_cfg = self.B == 2 and wl.guidance > 1.0
+        self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
+
+    def relayout(self) -> None:
+        for src, dst in zip(self.prefix_src, self.prefix_online):
+            if src is not None:
+                nx.nxattn_kv_relayout(src, dst.unsqueeze(0), 0)
+
+    def rope(self) -> None:
+        nx.nxattn_rope_apply(self.q, self.descs)
+        nx.nxattn_rope_apply(self.k, self.descs)
+
+    def attention(self) -> None:
+        nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online)
+
+    def cfg(self) -> None:
+        if self.use_cfg:
+            nx.nxattn_cfg_combine(self.o[0], self.o[1], self.out, self.wl.guidance)
+
+    def __call__(self) -> torch.Tensor:
+        self.relayout()
+        self.rope()
+        self.attention()
+        self.cfg()
+        return self.out if self.use_cfg else self.o

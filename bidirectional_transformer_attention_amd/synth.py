@@ -87,6 +87,15 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+def bench_workload(name: str) -> Workload:
+    """The timed configuration of a workload: its prefix arrives in the replay layout
+    [2, H, P, D] (as the KV-replay path loads it), so every step also relays it."""
+    wl = WORKLOADS[name]
+    if any(p > 0 for p in wl.prefix_len) and wl.prefix_layout != "replay":
+        wl = dataclasses.replace(wl, name=wl.name + "+replay", prefix_layout="replay")
+    return wl
+
+
 def seed_of(cid: int, layer: int, branch: int, tensor: int) -> int:
     return 1_000_000 * cid + 1000 * layer + 10 * branch + tensor
 

@@ -1,0 +1,155 @@
+/*
+ * nxattn — non-causal (bidirectional) grouped-query attention over a conditioning
+ * KV prefix plus the model's own tokens, with RoPE at explicit position offsets,
+ * for AMD Instinct MI355X (gfx950). C ABI: plain pointers, sizes and a HIP stream.
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are owned by the caller; the library allocates no device memory,
+ *    keeps no state except a thread-local error message, and never synchronises:
+ *    work is enqueued on `stream` (NULL = the default stream) and the call returns.
+ *  - Every argument is validated on the host before anything is enqueued; on error
+ *    nothing is launched and the return value is a nonzero nxattn_status. The detail
+ *    of the last failing call on this thread is in nxattn_last_error().
+ *  - Zero-size problems return NXATTN_OK without launching.
+ *  - Element types: NXATTN_F32 (IEEE binary32) or NXATTN_BF16 (bfloat16, stored as
+ *    16-bit words). Every float -> bf16 conversion rounds to nearest even.
+ *  - Strides are in elements; the innermost (head_dim) dimension is contiguous.
+ *  - Base pointers must be 16-byte aligned and every stride must keep rows 16-byte
+ *    aligned (NXATTN_ERR_ALIGN otherwise).
+ */
+#ifndef NXATTN_H
+#define NXATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NXATTN_OK = 0,
+  NXATTN_ERR_INVALID = 1,      /* NULL pointer, negative size, inconsistent shape   */
+  NXATTN_ERR_UNSUPPORTED = 2,  /* valid but outside the supported set (dtype, D, …)  */
+  NXATTN_ERR_ALIGN = 3,        /* pointer or stride breaks the 16-byte rule          */
+  NXATTN_ERR_HIP = 4           /* the HIP runtime reported an error at launch        */
+} nxattn_status;
+
+typedef enum { NXATTN_F32 = 0, NXATTN_BF16 = 1 } nxattn_dtype;
+
+#define NXATTN_MAX_BRANCHES 8
+
+/*
+ * KV relayout between the replay-file layout and the online layout.
+ * Defined by the NeoPP page ("NeoPP: LightLLM integration and KV replay"), section
+ * "KV file layout": the online cache is [layers, 2, seq, kv_heads, head_dim], replay
+ * files hold [layers, 2, kv_heads, seq, head_dim], and converting between them
+ * exchanges dimensions 2 and 3 (index 0 of the size-2 dimension is K, 1 is V).
+ *
+ *   dir 0: src replay [L,2,H,S,D]  -> dst online [L,2,S,H,D]
+ *   dir 1: src online [L,2,S,H,D]  -> dst replay [L,2,H,S,D]
+ *
+ * Both buffers are contiguous device memory of L*2*H*S*D elements of `dtype`; they
+ * must not overlap (NXATTN_ERR_INVALID). The copy is bit-exact.
+ */
+int nxattn_kv_relayout(const void* src, void* dst, int64_t layers, int64_t kv_heads, int64_t seq,
+                       int64_t head_dim, int dtype, int dir, hipStream_t stream);
+
+/*
+ * Rotary position embedding descriptor of one branch (batch entry).
+ * KLiteInfer page, section "架构" (architecture): RoPE, 2-D RoPE (vision) and MRoPE
+ * operators; NeoPP page, intro and "KV file layout": position offsets are supplied
+ * with the KV cache and never inferred from tensor sizes.
+ *
+ * Own token s in [0, seq) is unravelled row-major over grid[0..n_axes) (axis 0
+ * slowest); the position on axis k is its coordinate plus offset[k]. The head_dim/2
+ * rotary pairs are split into contiguous sections, pairs[k] of them for axis k in
+ * axis order (sum == head_dim/2). Pair j with local index u in section k rotates by
+ * angle pos_k * theta^(-2u / (2*pairs[k])):
+ *   a' = a cos - b sin,  b' = a sin + b cos,
+ * with (a, b) = (x[j], x[j + head_dim/2]) (interleaved == 0) or (x[2j], x[2j+1]).
+ */
+typedef struct {
+  int32_t n_axes;        /* 1, 2 or 3                                   */
+  int32_t grid[3];       /* grid extents; product == seq                */
+  int32_t pairs[3];      /* rotary pairs per axis; sum == head_dim / 2  */
+  int32_t offset[3];     /* position offset per axis (>= 0)             */
+  double theta;          /* frequency base (> 1), 10000 in the configs  */
+  int32_t interleaved;   /* 0 = half-split pairs, 1 = adjacent pairs    */
+} nxattn_rope_desc;
+
+/*
+ * In-place RoPE on x[b, s, h, :] for b < batch, s < seq, h < heads.
+ * strides = {stride_b, stride_s, stride_h} in elements; the head_dim elements of a
+ * row are contiguous. rope points to `batch` host descriptors (one per branch, so the
+ * two CFG branches may use different offsets); batch <= NXATTN_MAX_BRANCHES.
+ * The rotation is computed in fp32 from an fp64 angle; bf16 results are rounded to
+ * nearest even. Supported: head_dim even, 8 <= head_dim <= 256, dtype F32 or BF16.
+ */
+int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                      const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
+                      hipStream_t stream);
+
+/*
+ * Fused non-causal attention over [prefix ++ own] for every branch of a CFG batch.
+ * KLiteInfer page, section "架构": bidirectional attention is scores GEMM, softmax,
+ * output GEMM (here fused, the score matrix never leaves the chip); NeoPP page:
+ * the DiT attends to the injected conditioning KV (one branch per CFG side).
+ *
+ * For branch b, q head h (kv head g = h / (heads_q / heads_kv)), own query i:
+ *   keys j in [0, P_b + seq_q): K_j = prefix K row j for j < P_b, else own k row j-P_b
+ *   (same for V); s_j = scale * <q_i, K_j>; o = sum_j softmax(s)_j V_j.
+ * q, k and v must already be rotated (nxattn_rope_apply); prefix keys are used as
+ * stored. Layouts (element strides {b, s, h}, head_dim contiguous):
+ *   q [batch, seq_q, heads_q, D]     k, v [batch, seq_q, heads_kv, D]
+ *   o [batch, seq_q, heads_q, D]     (written, must not overlap the inputs)
+ *   prefix_kv[b]: one layer slice of the online cache, contiguous [2, P_b, heads_kv, D]
+ *                 (K at offset 0, V at offset P_b*heads_kv*D); NULL iff P_b == 0.
+ * scale <= 0 selects 1/sqrt(head_dim). Accumulation is fp32; P is rounded to bf16
+ * before the P*V product on the bf16 path; the output is rounded to nearest even.
+ * Supported: BF16 with head_dim 128; F32 with head_dim 64 or 72 (true fp32 MFMA, no
+ * reduced-precision inputs); heads_q % heads_kv == 0; batch <= 8; seq_q >= 1.
+ */
+typedef struct {
+  int32_t dtype;
+  int32_t batch;       /* CFG branches                                  */
+  int32_t seq_q;       /* own tokens (queries and own keys/values)      */
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_strides[3];
+  int64_t kv_strides[3];
+  int64_t o_strides[3];
+  const void* prefix_kv[NXATTN_MAX_BRANCHES];
+  int32_t prefix_len[NXATTN_MAX_BRANCHES];
+  float scale;
+} nxattn_fwd_args;
+
+int nxattn_fwd(const nxattn_fwd_args* args, hipStream_t stream);
+
+/*
+ * Classifier-free guidance: out = uncond + guidance * (cond - uncond) over n elements.
+ * LingBot-Video page, "Key Parameters": guidance_scale, guidance active above 1.0;
+ * NeoPP page: the two KV branches (cond, uncond). The combination is evaluated in
+ * fp32 as fma(guidance, cond - uncond, uncond). out may alias cond or uncond exactly
+ * (any other overlap is NXATTN_ERR_INVALID).
+ */
+int nxattn_cfg_combine(const void* cond, const void* uncond, void* out, int64_t n, float guidance,
+                       int dtype, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* nxattn_status_string(int status);
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* nxattn_last_error(void);
+/* Library version, e.g. "0.1.0". */
+const char* nxattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NXATTN_H */

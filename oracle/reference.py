@@ -98,17 +98,23 @@ def rope_angles(pos: np.ndarray, pairs: Sequence[int], theta: float = 10000.0) -
 
 
 def rope(x: np.ndarray, grid: Sequence[int], pairs: Sequence[int], offset: Sequence[int],
-         theta: float = 10000.0, interleaved: bool = False) -> np.ndarray:
+         theta: float = 10000.0, interleaved: bool = False, rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Rotate x [S, H, D] (one branch) by the positions of its tokens; returns float64.
 
     Half-split pairs (a, b) = (j, j + D/2), or interleaved (2j, 2j+1):
     a' = a cos(phi) - b sin(phi), b' = a sin(phi) + b cos(phi).
+    With ``rows``, x holds only those tokens ([len(rows), H, D]) of the grid.
     """
     x = _f64(x)
     S, H, D = x.shape
     if 2 * int(sum(pairs)) != D:
         raise ValueError("sum of pairs must be head_dim / 2")
-    phi = rope_angles(positions(grid, offset), pairs, theta)          # [S, D/2]
+    pos = positions(grid, offset)
+    if rows is not None:
+        pos = pos[np.asarray(rows)]
+    if pos.shape[0] != S:
+        raise ValueError("x has a different number of tokens than the grid (or rows)")
+    phi = rope_angles(pos, pairs, theta)                               # [S, D/2]
     c = np.cos(phi)[:, None, :]
     s = np.sin(phi)[:, None, :]
     if interleaved:

@@ -1,0 +1,90 @@
+"""Shared test helpers: oracle evaluation of a workload step and the error metric."""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+from bidirectional_transformer_attention_amd.synth import Inputs, Workload
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a CPU/GPU tensor (fp32 or bf16) to float64."""
+    return t.detach().to("cpu").to(torch.float32).numpy().astype(np.float64)
+
+
+def online_prefix(wl: Workload, p: Optional[torch.Tensor]) -> Optional[np.ndarray]:
+    """Prefix of one branch as float64 [2, P, H, D] (online layout), via the oracle relayout."""
+    if p is None:
+        return None
+    a = f64(p)
+    if wl.prefix_layout == "replay":
+        a = oracle.relayout(a[None], 0)[0]
+    return a
+
+
+def oracle_rope(wl: Workload, x: torch.Tensor, b: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    xb = x[b] if rows is None else x[b][torch.from_numpy(np.asarray(rows))]
+    return oracle.rope(f64(xb), wl.grid, wl.pairs, wl.offsets[b], wl.theta, rows=rows)
+
+
+def oracle_attention(wl: Workload, inp: Inputs, rows: Optional[Dict[int, np.ndarray]] = None,
+                     q_rot: Optional[Sequence[np.ndarray]] = None,
+                     k_rot: Optional[Sequence[np.ndarray]] = None) -> Dict[int, np.ndarray]:
+    """Per branch b: attention output [R, Hq, D] (float64) of the whole step before CFG.
+
+    RoPE is applied by the oracle unless already-rotated q/k are given (used to isolate
+    the fused kernel from the RoPE kernel's bf16 rounding).
+    """
+    out = {}
+    for b in range(wl.branches):
+        r = None if rows is None else rows[b]
+        if q_rot is not None:
+            q = q_rot[b] if r is None else q_rot[b][r]
+        else:
+            q = oracle_rope(wl, inp.q, b, r)
+        k = k_rot[b] if k_rot is not None else oracle_rope(wl, inp.k, b)
+        pre = online_prefix(wl, inp.prefix[b])
+        pk = pre[0] if pre is not None else None
+        pv = pre[1] if pre is not None else None
+        # q holds only the selected rows; every key row is used
+        out[b] = oracle.attention(q, k, f64(inp.v[b]), pk, pv) if r is None else \
+            _attention_rows(q, k, f64(inp.v[b]), pk, pv)
+    return out
+
+
+def _attention_rows(q_rows, k, v, pk, pv):
+    # q_rows [R, Hq, D] are queries only; keys/values are all P + S rows
+    return oracle.attention(q_rows, k, v, pk, pv, rows=np.arange(q_rows.shape[0]))
+
+
+def slice_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |g_i - r_i| / max(|r_i|, rms(r)) over one (branch, head) slice."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    den = np.maximum(np.abs(ref), rms)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den)) if ref.size else 0.0
+
+
+def attention_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Worst slice error over heads of arrays shaped [R, H, D]."""
+    return max(slice_err(got[:, h, :], ref[:, h, :]) for h in range(ref.shape[1]))
+
+
+def sample_rows(S: int, count: int, seed: int, extra: Sequence[int] = ()) -> np.ndarray:
+    """Seeded query rows: first, last, 32/64 tile edges and random rows."""
+    rng = np.random.default_rng(seed)
+    base = {0, S - 1}
+    for e in (31, 32, 63, 64, 127, 128, S // 2, S - 32, S - 33):
+        if 0 <= e < S:
+            base.add(e)
+    base.update(int(x) for x in extra if 0 <= x < S)
+    rest = rng.choice(S, size=min(S, count), replace=False)
+    base.update(int(x) for x in rest)
+    return np.array(sorted(base), dtype=np.int64)

@@ -1,0 +1,377 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Bars: bit-exact for the relayout and for index selection; max slice error
+max|g-r| / max(|r|, rms(r)) <= 1e-4 (fp32) / 2e-2 (bf16) for attention; RoPE and CFG
+within one bf16 rounding (or fp32 rounding error) of the exact value.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bidirectional_transformer_attention_amd as nx
+from bidirectional_transformer_attention_amd import synth
+from bidirectional_transformer_attention_amd.pipeline import AttentionStep
+from helpers import TOL, attention_err, f64, oracle_attention, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def note(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    nx.load()
+
+
+def bf(x):
+    return x.to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------- relayout
+@pytest.mark.parametrize("shape,dtype", [((1, 2, 8, 1024, 128), torch.bfloat16), ((1, 2, 8, 128, 128), torch.bfloat16),
+                                         ((3, 2, 5, 37, 72), torch.float32), ((2, 2, 3, 7, 4), torch.bfloat16),
+                                         ((1, 2, 12, 256, 128), torch.bfloat16), ((2, 2, 1, 1, 8), torch.float32)])
+def test_relayout_bitwise(shape, dtype):
+    note(f"relayout {shape} {dtype}")
+    src = synth.random_tensor(shape, 11, dtype)
+    L, _, H, S, D = shape
+    d_src = src.to(DEV)
+    d_dst = torch.empty((L, 2, S, H, D), dtype=dtype, device=DEV)
+    nx.nxattn_kv_relayout(d_src, d_dst, 0)
+    back = torch.empty_like(d_src)
+    nx.nxattn_kv_relayout(d_dst, back, 1)
+    torch.cuda.synchronize()
+    ints = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    exp = oracle.relayout(src.view(ints).numpy(), 0)
+    assert np.array_equal(d_dst.cpu().view(ints).numpy(), exp)
+    assert torch.equal(back.cpu().view(ints), src.view(ints))
+
+
+# ---------------------------------------------------------------------------- rope
+ROPE_CASES = [
+    ("tiny_f32", None), ("vit_f32", None), ("dit1k_bf16", 8), ("video_bf16", 4),
+]
+
+
+def rope_check(wl, x_cpu, out_gpu, tol):
+    for b in range(x_cpu.shape[0]):
+        ref = oracle.rope(f64(x_cpu[b]), wl.grid, wl.pairs, wl.offsets[b], wl.theta)
+        err = attention_err(f64(out_gpu[b]), ref)
+        assert err <= tol, err
+
+
+@pytest.mark.parametrize("name,heads", ROPE_CASES)
+def test_rope_matches_oracle(name, heads):
+    wl = synth.WORKLOADS[name]
+    H = heads or wl.heads_q
+    note(f"rope {name} H={H}")
+    x = synth.random_tensor((wl.branches, wl.seq, H, wl.head_dim), 21, wl.torch_dtype)
+    d = x.to(DEV)
+    nx.nxattn_rope_apply(d, [nx.rope_desc(wl.grid, wl.pairs, wl.offsets[b]) for b in range(wl.branches)])
+    torch.cuda.synchronize()
+    # bf16: one rounding of the exact value (2^-9 relative) plus fp32 arithmetic
+    rope_check(wl, x, d.cpu(), 2.0 ** -8 if wl.dtype == "bf16" else 2e-6)
+
+
+def test_rope_strided_interleaved_and_per_branch_offsets():
+    note("rope strided / interleaved")
+    base = synth.random_tensor((2, 48, 6, 64), 22, torch.float32)
+    d = base.to(DEV)
+    view = d[:, :, 1:5, :]                       # strided heads
+    descs = [nx.rope_desc((6, 8), (16, 16), (3, 5), interleaved=True),
+             nx.rope_desc((6, 8), (16, 16), (100, 7), interleaved=True)]
+    nx.nxattn_rope_apply(view, descs)
+    torch.cuda.synchronize()
+    out = d.cpu()
+    assert torch.equal(out[:, :, 0], base[:, :, 0]) and torch.equal(out[:, :, 5], base[:, :, 5])
+    for b, off in enumerate(((3, 5), (100, 7))):
+        ref = oracle.rope(f64(base[b, :, 1:5]), (6, 8), (16, 16), off, interleaved=True)
+        assert np.max(np.abs(f64(out[b, :, 1:5]) - ref)) <= 2e-6 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_rope_integer_positions_exact():
+    # pairs (1, 0): the result is (cos phi, sin phi); the GPU must match the oracle at the
+    # expected integer position, not at +-1 (u = 0 has a 1-radian step per position)
+    note("rope integer positions")
+    wl = synth.WORKLOADS["video_bf16"]
+    S, D = wl.seq, wl.head_dim
+    x = torch.zeros((1, S, 1, D), dtype=torch.float32)
+    x[..., : D // 2] = 1.0
+    d = x.to(DEV)
+    nx.nxattn_rope_apply(d, [nx.rope_desc(wl.grid, wl.pairs, (5, 7, 11))])
+    torch.cuda.synchronize()
+    got = f64(d.cpu()[0, :, 0])
+    pos = oracle.positions(wl.grid, (5, 7, 11))
+    j0 = [0, wl.pairs[0], wl.pairs[0] + wl.pairs[1]]     # u = 0 pair of each axis
+    for ax in range(3):
+        for delta in (-1, 1):
+            wrong = np.cos(pos[:, ax] + delta)
+            right = np.cos(pos[:, ax])
+            g = got[:, j0[ax]]
+            assert np.all(np.abs(g - right) < 1e-5)
+            assert np.all(np.abs(g - right) < np.abs(g - wrong) + 1e-12)
+
+
+# ---------------------------------------------------------------------------- cfg
+@pytest.mark.parametrize("n,dtype", [(4096 * 32 * 128, torch.bfloat16), (1000003, torch.bfloat16),
+                                     (77, torch.float32), (3900 * 16 * 72, torch.float32)])
+def test_cfg_matches_oracle(n, dtype):
+    note(f"cfg n={n} {dtype}")
+    c = synth.random_tensor((n,), 31, dtype)
+    u = synth.random_tensor((n,), 32, dtype)
+    dc, du = c.to(DEV), u.to(DEV)
+    out = torch.empty_like(dc)
+    for s in (4.0, 6.0):
+        nx.nxattn_cfg_combine(dc, du, out, s)
+        torch.cuda.synchronize()
+        ref = oracle.cfg_combine(f64(c), f64(u), s)
+        got = f64(out.cpu())
+        # fp32 fma of exact-widened inputs, then one rounding to the output type
+        rel = 2.0 ** -8 if dtype == torch.bfloat16 else 2e-6
+        assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * (np.abs(f64(c)) + np.abs(f64(u))) * (1 + s))
+    nx.nxattn_cfg_combine(dc, du, out, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), u)                      # s = 0 gives uncond bitwise
+    alias = dc.clone()
+    nx.nxattn_cfg_combine(alias, du, alias, 4.0)          # out aliases cond
+    nx.nxattn_cfg_combine(dc, du, out, 4.0)
+    torch.cuda.synchronize()
+    assert torch.equal(alias, out)
+
+
+# ---------------------------------------------------------------------------- attention
+def run_fwd(q, k, v, prefix, scale=0.0):
+    o = torch.empty_like(q)
+    nx.nxattn_fwd(q, k, v, o, prefix, scale)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def fwd_case(dtype, B, S, Hq, Hkv, D, plens, seed, scale_v=1.0):
+    note(f"fwd {dtype} B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} P={plens} seed={seed}")
+    q = synth.random_tensor((B, S, Hq, D), seed, dtype, scale_v)
+    k = synth.random_tensor((B, S, Hkv, D), seed + 1, dtype, scale_v)
+    v = synth.random_tensor((B, S, Hkv, D), seed + 2, dtype, scale_v)
+    pre = [synth.random_tensor((2, p, Hkv, D), seed + 3 + b, dtype, scale_v) if p else None
+           for b, p in enumerate(plens)]
+    o = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), [p.to(DEV) if p is not None else None for p in pre])
+    tol = TOL["bf16" if dtype == torch.bfloat16 else "f32"]
+    for b in range(B):
+        ref = oracle.attention(f64(q[b]), f64(k[b]), f64(v[b]),
+                               f64(pre[b][0]) if pre[b] is not None else None,
+                               f64(pre[b][1]) if pre[b] is not None else None)
+        err = attention_err(f64(o[b]), ref)
+        assert err <= tol, (b, err)
+    return o
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,P", [
+    (1, 300, 8, 2, (37,)),        # ragged Sq, prefix straddling a key tile, G = 4
+    (2, 129, 4, 4, (64, 0)),      # G = 1, one branch without prefix
+    (2, 65, 6, 2, (1, 130)),      # G = 3: query blocks cross heads inside a workgroup
+    (1, 1, 8, 1, (0,)),           # a single query and a single key
+    (1, 1, 16, 2, (200,)),        # one own token, long prefix
+    (1, 33, 16, 2, (31,)),        # G = 8
+    (3, 70, 2, 1, (5, 0, 64)),
+])
+def test_fwd_bf16_reduced(B, S, Hq, Hkv, P):
+    fwd_case(torch.bfloat16, B, S, Hq, Hkv, 128, P, 1000 + S)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,P", [
+    (1, 64, 2, 2, 64, (32,)),
+    (1, 300, 4, 2, 72, (0,)),
+    (2, 97, 3, 3, 72, (13, 64)),
+    (1, 1, 2, 1, 64, (0,)),
+    (1, 5, 4, 4, 72, (70,)),
+])
+def test_fwd_f32_reduced(B, S, Hq, Hkv, D, P):
+    fwd_case(torch.float32, B, S, Hq, Hkv, D, P, 2000 + S)
+
+
+def test_fwd_single_key_returns_v():
+    # Skv = 1: the only weight is 1, so o = v (bf16: exactly after rounding; fp32: the
+    # normalisation p / l may move the last bit)
+    for dtype, D in ((torch.bfloat16, 128), (torch.float32, 72)):
+        note(f"fwd single key {dtype}")
+        q = synth.random_tensor((2, 1, 4, D), 41, dtype)
+        k = synth.random_tensor((2, 1, 2, D), 42, dtype)
+        v = synth.random_tensor((2, 1, 2, D), 43, dtype)
+        o = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), [])
+        exp = v.repeat_interleave(2, dim=2)
+        if dtype == torch.bfloat16:
+            assert torch.equal(o, exp)
+        else:
+            assert torch.allclose(o, exp, rtol=4e-7, atol=0)
+
+
+def test_fwd_constant_v_and_zero_q():
+    note("fwd constant V / zero q")
+    D, S, P = 128, 150, 70
+    row = synth.random_tensor((D,), 44, torch.bfloat16)
+    v = row.expand(1, S, 2, D).contiguous()
+    pre = torch.stack([synth.random_tensor((P, 2, D), 45, torch.bfloat16), row.expand(P, 2, D)], 0).contiguous()
+    q = synth.random_tensor((1, S, 4, D), 46, torch.bfloat16)
+    k = synth.random_tensor((1, S, 2, D), 47, torch.bfloat16)
+    o = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), [pre.to(DEV)])
+    # the weights sum to one: the output is that row, up to the bf16 rounding of P and O
+    assert np.max(np.abs(f64(o) - f64(row))) <= 2.0 ** -7 * np.max(np.abs(f64(row)))
+    oz = run_fwd(torch.zeros_like(q).to(DEV), k.to(DEV), synth.random_tensor((1, S, 2, D), 48, torch.bfloat16).to(DEV),
+                 [pre.to(DEV)])
+    assert np.all(np.isfinite(f64(oz)))
+
+
+def test_fwd_bit_exact_selection():
+    """Each query selects exactly one key (others underflow to weight 0); V rows encode
+    (key mod 256, key // 256, branch, kv head) so the output must decode bit for bit to
+    the expected key of the expected branch and kv head: pins prefix ++ own, the GQA
+    mapping and the branch indexing."""
+    D, B, S, Hq, Hkv = 128, 2, 200, 8, 2
+    plens = (70, 135)
+    rng = np.random.default_rng(7)
+    for dtype in (torch.bfloat16,):
+        note(f"fwd bit-exact selection {dtype}")
+        q = torch.zeros((B, S, Hq, D))
+        k = torch.zeros((B, S, Hkv, D))
+        v = torch.full((B, S, Hkv, D), 0.5)          # non-selected rows: must get weight 0
+        pre = [torch.stack([torch.zeros((p, Hkv, D)), torch.full((p, Hkv, D), 0.5)], 0) for p in plens]
+        expect = np.zeros((B, S, Hq), dtype=np.int64)
+        for b in range(B):
+            Skv = plens[b] + S
+            for g in range(Hkv):
+                # active keys: tile edges, the prefix/own boundary, the tail, random others
+                cand = {0, 63, 64, 65, plens[b] - 1, plens[b], Skv - 1, Skv - 2, 127, 128}
+                cand.update(int(x) for x in rng.choice(Skv, 60, replace=False))
+                active = sorted(c for c in cand if 0 <= c < Skv)[:D]
+                for dim, j in enumerate(active):
+                    kv_k = torch.zeros(D)
+                    kv_k[dim] = 48.0
+                    code = torch.zeros(D)
+                    code[0], code[1], code[2], code[3] = j % 256, j // 256, b, g
+                    if j < plens[b]:
+                        pre[b][0, j, g] = kv_k
+                        pre[b][1, j, g] = code
+                    else:
+                        k[b, j - plens[b], g] = kv_k
+                        v[b, j - plens[b], g] = code
+                for hl in range(Hq // Hkv):
+                    h = g * (Hq // Hkv) + hl
+                    pick = rng.integers(0, len(active), S)
+                    for i in range(S):
+                        q[b, i, h, pick[i]] = 48.0
+                        expect[b, i, h] = active[pick[i]]
+        o = run_fwd(bf(q).to(DEV), bf(k).to(DEV), bf(v).to(DEV), [bf(p).to(DEV) for p in pre])
+        got = f64(o)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                exp_rows = np.stack([expect[b, :, h] % 256, expect[b, :, h] // 256,
+                                     np.full(S, b), np.full(S, g)], 1).astype(np.float64)
+                assert np.array_equal(got[b, :, h, :4], exp_rows), (b, h)
+
+
+def test_fwd_deterministic():
+    note("fwd determinism")
+    q = synth.random_tensor((2, 257, 8, 128), 51, torch.bfloat16).to(DEV)
+    k = synth.random_tensor((2, 257, 2, 128), 52, torch.bfloat16).to(DEV)
+    v = synth.random_tensor((2, 257, 2, 128), 53, torch.bfloat16).to(DEV)
+    pre = [synth.random_tensor((2, 99, 2, 128), 54, torch.bfloat16).to(DEV), None]
+    a = run_fwd(q, k, v, pre)
+    b = run_fwd(q, k, v, pre)
+    assert torch.equal(a, b)
+
+
+def test_fwd_key_permutation_invariance():
+    note("fwd key permutation")
+    S, P, D = 190, 66, 128
+    q = synth.random_tensor((1, S, 4, D), 61, torch.bfloat16)
+    k = synth.random_tensor((1, S, 1, D), 62, torch.bfloat16)
+    v = synth.random_tensor((1, S, 1, D), 63, torch.bfloat16)
+    pre = synth.random_tensor((2, P, 1, D), 64, torch.bfloat16)
+    K = torch.cat([pre[0], k[0]], 0)
+    V = torch.cat([pre[1], v[0]], 0)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(S + P))
+    K2, V2 = K[perm], V[perm]
+    o1 = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), [pre.to(DEV)])
+    o2 = run_fwd(q.to(DEV), K2[P:][None].contiguous().to(DEV), V2[P:][None].contiguous().to(DEV),
+                 [torch.stack([K2[:P], V2[:P]], 0).contiguous().to(DEV)])
+    assert attention_err(f64(o1[0]), f64(o2[0])) <= TOL["bf16"]
+
+
+def test_fwd_strided_views():
+    note("fwd strided q/k/v/o views")
+    D = 128
+    qkv = synth.random_tensor((2, 100, 8 + 2 + 2, D), 71, torch.bfloat16).to(DEV)   # fused projection
+    q, k, v = qkv[:, :, :8], qkv[:, :, 8:10], qkv[:, :, 10:12]
+    obuf = torch.zeros((2, 100, 9, D), dtype=torch.bfloat16, device=DEV)
+    o = obuf[:, :, 1:9]
+    nx.nxattn_fwd(q, k, v, o, [])
+    torch.cuda.synchronize()
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    for b in range(2):
+        ref = oracle.attention(f64(qc[b]), f64(kc[b]), f64(vc[b]))
+        assert attention_err(f64(o.cpu()[b]), ref) <= TOL["bf16"]
+    assert torch.count_nonzero(obuf[:, :, 0]) == 0
+
+
+# ---------------------------------------------------------------------------- whole workloads
+def step_case(name, rows_per_branch, seed_rows):
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
+    note(f"step {name} (sampled rows {rows_per_branch})")
+    inp = synth.make_inputs(wl)
+    step = AttentionStep(wl, inp)
+    out = step()
+    torch.cuda.synchronize()
+    o_gpu = step.o.cpu()
+    rows = {b: sample_rows(wl.seq, rows_per_branch, seed_rows + b) for b in range(wl.branches)}
+    # isolate the fused kernel: oracle attention over the GPU's own rotated q and k
+    qg, kg = step.q.cpu(), step.k.cpu()
+    ref_iso = oracle_attention(wl, inp, rows, [f64(qg[b]) for b in range(wl.branches)],
+                               [f64(kg[b]) for b in range(wl.branches)])
+    # the whole step against the oracle's own RoPE
+    ref = oracle_attention(wl, inp, rows)
+    tol = TOL[wl.dtype]
+    for b in range(wl.branches):
+        g = f64(o_gpu[b][rows[b]])
+        assert attention_err(g, ref_iso[b]) <= tol
+        assert attention_err(g, ref[b]) <= tol
+    if step.use_cfg:
+        r = rows[0]
+        both = sorted(set(rows[0]).intersection(rows[1]))
+        c = oracle.cfg_combine(ref[0][np.searchsorted(r, both)], ref[1][np.searchsorted(rows[1], both)], wl.guidance)
+        got = f64(out.cpu()[both])
+        # guidance amplifies the branch errors by up to (1 + 2s)
+        assert attention_err(got, c) <= tol * (1 + 2 * wl.guidance)
+    return wl
+
+
+def test_step_tiny_f32_full():
+    step_case("tiny_f32", 64, 1)
+
+
+def test_step_vit_f32_one_layer_sampled():
+    step_case("vit_f32", 300, 2)
+
+
+def test_step_dit1k_bf16_sampled():
+    step_case("dit1k_bf16", 96, 3)
+
+
+def test_step_bench_configuration_sampled():
+    # exactly what bench.py times: dit1k with the prefix delivered in the replay layout
+    step_case("dit1k_bf16+replay", 64, 6)
+
+
+def test_step_dit2k_bf16_sampled():
+    step_case("dit2k_bf16", 24, 4)
+
+
+def test_step_video_bf16_sampled():
+    step_case("video_bf16", 24, 5)
