@@ -25,6 +25,8 @@
 // row (K: chunk ^ (row & 15), V: chunk ^ 4*(row & 3)) so the row-parallel K reads and
 // the 4-row transposing V reads are free of bank conflicts. 64 KB per workgroup.
 // MFMA-bound: 4*Sq*Skv*Hq*D flops per launch.
+#include <type_traits>
+
 #include "nx_internal.h"
 
 namespace nx {
@@ -59,74 +61,135 @@ __device__ __forceinline__ int remap_xcd(int i, int n) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// LDS placement of 16-byte chunk `chunk` of tile row `row`
 __device__ __forceinline__ int kslot(int row, int chunk) { return chunk ^ (row & 15); }
 __device__ __forceinline__ int vslot(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barriers that also fence the instruction scheduler: nothing (not even pure
+// ALU work) may move across, so each half-iteration's work stays in its slot.
+__device__ __forceinline__ void barrier_only() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_dma_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// LDS map: [K buffer 0][K buffer 1][V buffer 0][V buffer 1], TILEB bytes each.
+constexpr int KOFF0 = 0, VOFF0 = 2 * TILEB;
+
 struct Wave {
-  // per-wave state of one 32-row query block
   bf16x8 qf[8];       // Q^T operand, k-step ks: Q[row][16ks + 8hh .. +7]
-  f32x16 o[4];        // O^T accumulators, d-block db: rows d = 32db + ..., lane = query
+  f32x16 o[4];        // O^T accumulators, d-block db (lane = query, registers = d)
   f32x16 s[2];        // S^T accumulators of the tile being scored (2 key blocks of 32)
   bf16x8 p[4];        // P^T operand of the tile being accumulated, step (kb, half)
   float m, l;
+  // lane parts of the LDS byte addresses: K fragment of k-step ks at kbase + (32ks ^ kx),
+  // V^T fragment of d-block db at vbase + (64db ^ vy)
+  int kbase, kx, vbase, vy;
 };
 
-// S^T = K_tile Q^T for the tile in LDS buffer kbuf.
-__device__ __forceinline__ void gemm_s(Wave& w, const lds_u8* kbuf, int n, int hh) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = kb * 32 + n;
-    const lds_u8* rowp = kbuf + r * ROWB;
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 kv = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(rowp + 16 * kslot(r, 2 * ks + hh));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), w.qf[ks], acc, 0, 0, 0);
-    }
-    w.s[kb] = acc;
+__device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* smem, int byte) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((const lds_u8*)smem + byte);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* smem, int byte) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)((const lds_u8*)smem + byte));
+}
+
+// Scheduling-group helpers (compile-time sequences for __builtin_amdgcn_sched_group_barrier):
+// step i reads two transposed halves (P V steps, i < 16) or one b128 (score steps).
+template <int I, int N>
+__device__ __forceinline__ void sched_reads() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x100, I < 16 ? 2 : 1, 0);
+    sched_reads<I + 1, N>();
+  }
+}
+template <int I, int N, int DIST>
+__device__ __forceinline__ void sched_steps() {
+  if constexpr (I < N) {
+    if constexpr (I + DIST < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DIST < 16 ? 2 : 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    sched_steps<I + 1, N, DIST>();
   }
 }
 
-// O^T += V_tile^T P^T for the tile in LDS buffer vbuf.
-__device__ __forceinline__ void gemm_pv(Wave& w, const lds_u8* vbuf, int lane) {
-  const int q = lane >> 4, j = lane & 15;
-  const int hq = q >> 1;                 // lane half of the reading group
-  const int rsub = j >> 2;               // row within the 4-row group this lane addresses
-  const int csub = 4 * (j & 3);          // first column this lane addresses
+// One GEMM phase of a wave: O^T += V_t^T P_t^T (16 MFMAs) and, if `score`, S^T =
+// K_{t+1} Q^T (16 MFMAs). Fragments are read from LDS three MFMAs ahead so the
+// matrix core never waits on LDS latency; consecutive MFMAs target different
+// accumulators. VPAR / KPAR select the V and K buffers (compile-time LDS offsets).
+template <int VPAR, int KPAR, bool SCORE>
+__device__ __forceinline__ void gemm_phase(Wave& w, const uint8_t* smem) {
+  constexpr int VB = VOFF0 + VPAR * TILEB, KB = KOFF0 + KPAR * TILEB;
+  constexpr int DIST = 3;
+  constexpr int nsteps = SCORE ? 32 : 16;
+  // step i < 16: PV, (kbhs = i / 4, db = i % 4); step i >= 16: S, (ks = (i-16)/2, kb = (i-16)%2)
+  auto read = [&](int i) -> bf16x8 {
+    if (i < 16) {
+      const int kbhs = i >> 2, db = i & 3;
+      const int rbase = (kbhs >> 1) * 32 + (kbhs & 1) * 16;   // kb*32 + 16*hs
+      const int off = w.vbase + ((64 * db) ^ w.vy);
+      const bf16x4 a = lds_read_tr(smem, VB + rbase * ROWB + off);
+      const bf16x4 b = lds_read_tr(smem, VB + (rbase + 8) * ROWB + off);
+      return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const int j = i - 16, ks = j >> 1, kb = j & 1;
+    return as_bf16x8(lds_read_b128(smem, KB + kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
+  };
+  bf16x8 ring[DIST + 1];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < DIST; ++i) ring[i] = read(i);
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const int r0 = kb * 32 + 16 * hs + 4 * hq + rsub;   // rows of elements 0..3
-      const int r1 = r0 + 8;                              // rows of elements 4..7
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int col = 32 * db + 16 * (q & 1) + csub;
-        const lds_u8* a0 = vbuf + r0 * ROWB + 16 * vslot(r0, col >> 3) + 2 * (col & 7);
-        const lds_u8* a1 = vbuf + r1 * ROWB + 16 * vslot(r1, col >> 3) + 2 * (col & 7);
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a0);
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a1);
-        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, w.p[2 * kb + hs], w.o[db], 0, 0, 0);
+  for (int i = 0; i < 32; ++i) {
+    if (i < nsteps) {
+      if (i + DIST < nsteps) ring[(i + DIST) % (DIST + 1)] = read(i + DIST);
+      const bf16x8 f = ring[i % (DIST + 1)];
+      if (i < 16) {
+        const int kbhs = i >> 2, db = i & 3;
+        w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.p[kbhs], w.o[db], 0, 0, 0);
+      } else {
+        const int j = i - 16, ks = j >> 1, kb = j & 1;
+        if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], f32x16{}, 0, 0, 0);
+        else w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], w.s[kb], 0, 0, 0);
       }
+    }
+  }
+  // keep the issue order: the first DIST fragments' reads, then per step the reads of
+  // step i+DIST followed by MFMA i
+  sched_reads<0, DIST>();
+  sched_steps<0, nsteps, DIST>();
+}
+
+// S^T only (prologue).
+template <int KPAR>
+__device__ __forceinline__ void gemm_s_only(Wave& w, const uint8_t* smem) {
+  constexpr int KB = KOFF0 + KPAR * TILEB;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 f = as_bf16x8(lds_read_b128(smem, KB + kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
+      if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], f32x16{}, 0, 0, 0);
+      else w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], w.s[kb], 0, 0, 0);
     }
 }
 
 // Online softmax of w.s (tile with `valid` keys, < BN only for the last tile) -> w.p.
 __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
   if (valid < BN) {
+    // key of register i in block kb is kb*32 + 8(i/4) + 4hh + (i%4): compare the
+    // compile-time part against valid - 4hh
+    const int lim = valid - 4 * hh;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (key >= valid) w.s[kb][i] = -__builtin_inff();
-      }
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) w.s[kb][i] = -__builtin_inff();
   }
   float t0 = __builtin_fmaxf(w.s[0][0], w.s[0][1]);
   float t1 = __builtin_fmaxf(w.s[1][0], w.s[1][1]);
@@ -172,17 +235,11 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
   w.l += l0 + l1;
 }
 
-__global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILEB];   // K0 K1 V0 V1
-  lds_u8* lds = (lds_u8*)smem;
-  lds_u8* kbufs[2] = {lds, lds + TILEB};
-  lds_u8* vbufs[2] = {lds + 2 * TILEB, lds + 3 * TILEB};
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+// The per-wave program. Group A (waves 0-3) and group B (waves 4-7) run it half a tile
+// apart; both execute the same sequence of workgroup barriers.
+template <bool GROUP_A>
+__device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
-  const bool grpA = wave < 4;
-
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
   const int b = wg / (a.heads_kv * a.wg_per_group);
   const int rem = wg % (a.heads_kv * a.wg_per_group);
@@ -207,95 +264,93 @@ __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
   w.m = -__builtin_inff();
   w.l = 0.f;
+  // lane parts of the LDS read addresses. K: row n, chunk 2ks+hh at slot
+  // (2ks+hh) ^ (n & 15), i.e. byte n*ROWB + 16*(hh ^ (n&1)) + (32ks ^ 16*(n & 14)).
+  // V (transposing read): row r = 4*(q>>1) + rsub, column col = 32db + 16(q&1) + csub,
+  // chunk col>>3 = 4db + e at slot (4db + e) ^ 4rsub, i.e. byte
+  // r*ROWB + 16e + 2*(csub&7) + (64db ^ 64rsub).
+  w.kbase = n * ROWB + 16 * (hh ^ (n & 1));
+  w.kx = 16 * (n & 14);
+  {
+    const int q = lane >> 4, j = lane & 15;
+    const int rsub = j >> 2, csub = 4 * (j & 3);
+    const int r = 4 * (q >> 1) + rsub;                 // row within a 16-row step (+ 8 for elements 4..7)
+    const int e = 2 * (q & 1) + (csub >> 3);
+    w.vbase = r * ROWB + 16 * e + 2 * (csub & 7);
+    w.vy = 64 * rsub;
+  }
 
-  // Tile loads: thread -> two 16-byte chunks of K and two of V (row = it / 16, chunk = it % 16).
+  // DMA tile loads (global_load_lds, 1 KB = 4 rows per instruction). With NW waves
+  // taking part, wave slot ws fills rows (64/NW)*ws .. ; lane -> (row, LDS slot), and it
+  // fetches the global chunk that the swizzle places in that slot.
   const uint16_t* kprefix = a.prefix[b] ? a.prefix[b] + (int64_t)g * D : nullptr;
   const int64_t pstride = (int64_t)a.heads_kv * D;
   const uint16_t* kown = a.k + b * a.ks0 + (int64_t)g * a.ks2;
   const uint16_t* vown = a.v + b * a.ks0 + (int64_t)g * a.ks2;
-  auto row_ptrs = [&](int j, const uint16_t*& kr, const uint16_t*& vr) {
-    j = j < Skv ? j : Skv - 1;
-    if (j < P) {
-      kr = kprefix + (int64_t)j * pstride;
-      vr = kr + (int64_t)P * pstride;
-    } else {
-      kr = kown + (int64_t)(j - P) * a.ks1;
-      vr = vown + (int64_t)(j - P) * a.ks1;
-    }
-  };
-  u32x4 stg_k[2], stg_v[2];
-  auto load_k = [&](int t) {
+  const int64_t ks1 = a.ks1;
+  auto dma_tile = [&](int t, bool isv, int dst, int ws, auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    constexpr int ROWS = BN / NW;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + i * THREADS;
-      const uint16_t *kr, *vr;
-      row_ptrs(t * BN + (it >> 4), kr, vr);
-      stg_k[i] = *reinterpret_cast<const u32x4*>(kr + 8 * (it & 15));
+    for (int i = 0; i < ROWS / 4; ++i) {
+      const int r = ROWS * ws + 4 * i + (lane >> 4);
+      const int slot = lane & 15;
+      const int chunk = isv ? (slot ^ ((r & 3) << 2)) : (slot ^ (r & 15));
+      int j = t * BN + r;
+      j = j < Skv ? j : Skv - 1;
+      const uint16_t* src;
+      if (j < P) src = (isv ? kprefix + (int64_t)P * pstride : kprefix) + (int64_t)j * pstride;
+      else src = (isv ? vown : kown) + (int64_t)(j - P) * ks1;
+      __builtin_amdgcn_global_load_lds(src + 8 * chunk,
+                                       (__attribute__((address_space(3))) void*)((lds_u8*)smem + dst + (ROWS * ws + 4 * i) * ROWB),
+                                       16, 0, 0);
     }
   };
-  auto load_v = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + i * THREADS;
-      const uint16_t *kr, *vr;
-      row_ptrs(t * BN + (it >> 4), kr, vr);
-      stg_v[i] = *reinterpret_cast<const u32x4*>(vr + 8 * (it & 15));
-    }
-  };
-  auto store_k = [&](lds_u8* buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + i * THREADS, r = it >> 4, ch = it & 15;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(buf + r * ROWB + 16 * kslot(r, ch)) = stg_k[i];
-    }
-  };
-  auto store_v = [&](lds_u8* buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + i * THREADS, r = it >> 4, ch = it & 15;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(buf + r * ROWB + 16 * vslot(r, ch)) = stg_v[i];
-    }
-  };
+  using All = std::integral_constant<int, 8>;
+  using Half = std::integral_constant<int, 4>;
 
   // ---- prologue: K_0, V_0, K_1 resident; both groups score tile 0; group A also
   // ---- runs its softmax, so that A leads B by half a tile from here on.
-  load_k(0);
-  load_v(0);
-  store_k(kbufs[0]);
-  store_v(vbufs[0]);
-  if (T > 1) {
-    load_k(1);
-    store_k(kbufs[1]);
-  }
-  barrier_lds();
-  gemm_s(w, kbufs[0], n, hh);
-  if (grpA) softmax(w, c, Skv < BN ? Skv : BN, hh);
+  dma_tile(0, false, KOFF0, wave, All{});
+  dma_tile(0, true, VOFF0, wave, All{});
+  if (T > 1) dma_tile(1, false, KOFF0 + TILEB, wave, All{});
+  wait_dma_barrier();
+  gemm_s_only<0>(w, smem);
+  if (GROUP_A) softmax(w, c, Skv < BN ? Skv : BN, hh);
   barrier_only();
 
-  for (int t = 0; t < T; ++t) {
+  // iteration t: slot 2t (A multiplies, B normalises), slot 2t+1 (swapped)
+  auto iteration = [&](int t, auto par) {
+    constexpr int PAR = decltype(par)::value;        // t & 1
     const bool more = t + 1 < T;
-    const int valid_next = Skv - (t + 1) * BN;
-    // slot 2t: loads for tile t+2 (K) / t+1 (V) go out; A multiplies, B normalises.
-    if (t + 2 < T) load_k(t + 2);
-    if (more) load_v(t + 1);
-    if (grpA) {
-      gemm_pv(w, vbufs[t & 1], lane);
-      if (more) gemm_s(w, kbufs[(t + 1) & 1], n, hh);
+    // opaque per iteration: keeps the compiler from hoisting the per-fragment address
+    // arithmetic out of the loop (which would pin a dozen more registers)
+    asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
+    // The last iteration also scores a stale K buffer (never used afterwards): one code
+    // path keeps the register allocation of S and P straight.
+    if (GROUP_A) {
+      gemm_phase<PAR, PAR ^ 1, true>(w, smem);
+      barrier_only();
+      if (more) softmax(w, c, Skv - (t + 1) * BN < BN ? Skv - (t + 1) * BN : BN, hh);
     } else {
+      // group B fetches the next tiles while it normalises (it reads no LDS in this
+      // slot, so the DMA has a whole slot to land before B's own next LDS read):
+      // K_{t+2} -> K buffer t&1, V_{t+1} -> V buffer (t+1)&1; both were last read in
+      // the previous iteration.
+      if (t + 2 < T) dma_tile(t + 2, false, KOFF0 + PAR * TILEB, wave - 4, Half{});
+      if (more) dma_tile(t + 1, true, VOFF0 + (PAR ^ 1) * TILEB, wave - 4, Half{});
       softmax(w, c, Skv - t * BN < BN ? Skv - t * BN : BN, hh);
+      barrier_only();
+      gemm_phase<PAR, PAR ^ 1, true>(w, smem);
     }
-    barrier_only();
-    // slot 2t+1: A normalises tile t+1, B multiplies; staged tiles land in LDS.
-    if (grpA) {
-      if (more) softmax(w, c, valid_next < BN ? valid_next : BN, hh);
-    } else {
-      gemm_pv(w, vbufs[t & 1], lane);
-      if (more) gemm_s(w, kbufs[(t + 1) & 1], n, hh);
-    }
-    if (t + 2 < T) store_k(kbufs[t & 1]);
-    if (more) store_v(vbufs[(t + 1) & 1]);
-    barrier_lds();
+    wait_dma_barrier();
+  };
+  int t = 0;
+  for (; t + 1 < T; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{});
+    iteration(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < T) iteration(t, std::integral_constant<int, 0>{});
 
   // ---- epilogue: total row sum (both lane halves), normalise, round, store
   {
@@ -314,6 +369,14 @@ __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
           u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
                 pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
     }
+}
+
+__global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];   // K0 K1 V0 V1
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave < 4) wave_program<true>(a, smem, lane, wave);
+  else wave_program<false>(a, smem, lane, wave);
 }
 
 }  // namespace bf16k

@@ -34,7 +34,8 @@ def oracle_rope(wl: Workload, x: torch.Tensor, b: int, rows: Optional[np.ndarray
 
 def oracle_attention(wl: Workload, inp: Inputs, rows: Optional[Dict[int, np.ndarray]] = None,
                      q_rot: Optional[Sequence[np.ndarray]] = None,
-                     k_rot: Optional[Sequence[np.ndarray]] = None) -> Dict[int, np.ndarray]:
+                     k_rot: Optional[Sequence[np.ndarray]] = None,
+                     q_rot_rows_only: bool = False) -> Dict[int, np.ndarray]:
     """Per branch b: attention output [R, Hq, D] (float64) of the whole step before CFG.
 
     RoPE is applied by the oracle unless already-rotated q/k are given (used to isolate
@@ -44,7 +45,7 @@ def oracle_attention(wl: Workload, inp: Inputs, rows: Optional[Dict[int, np.ndar
     for b in range(wl.branches):
         r = None if rows is None else rows[b]
         if q_rot is not None:
-            q = q_rot[b] if r is None else q_rot[b][r]
+            q = q_rot[b] if (r is None or q_rot_rows_only) else q_rot[b][r]
         else:
             q = oracle_rope(wl, inp.q, b, r)
         k = k_rot[b] if k_rot is not None else oracle_rope(wl, inp.k, b)

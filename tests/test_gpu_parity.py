@@ -14,7 +14,7 @@ import oracle
 import bidirectional_transformer_attention_amd as nx
 from bidirectional_transformer_attention_amd import synth
 from bidirectional_transformer_attention_amd.pipeline import AttentionStep
-from helpers import TOL, attention_err, f64, oracle_attention, sample_rows
+from helpers import TOL, attention_err, f64, oracle_attention, oracle_rope, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -335,13 +335,25 @@ def step_case(name, rows_per_branch, seed_rows):
     qg, kg = step.q.cpu(), step.k.cpu()
     ref_iso = oracle_attention(wl, inp, rows, [f64(qg[b]) for b in range(wl.branches)],
                                [f64(kg[b]) for b in range(wl.branches)])
-    # the whole step against the oracle's own RoPE
+    # the whole step against the oracle's own RoPE. The bf16 path stores the rotated q
+    # and k in bf16 (one rounding each, as any bf16 pipeline does), which by itself moves
+    # the exact attention output; that share of the error is measured with the oracle
+    # alone (its own RoPE outputs rounded to bf16) and added to the kernel's bar.
     ref = oracle_attention(wl, inp, rows)
     tol = TOL[wl.dtype]
+    if wl.dtype == "bf16":
+        rnd = lambda a: \
+            torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
+        q_r = [rnd(oracle_rope(wl, inp.q, b, rows[b])) for b in range(wl.branches)]
+        k_r = [rnd(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)]
+        ref_r = oracle_attention(wl, inp, rows, q_r, k_r, q_rot_rows_only=True)
+        rope_share = max(attention_err(ref_r[b], ref[b]) for b in range(wl.branches))
+    else:
+        rope_share = 0.0
     for b in range(wl.branches):
         g = f64(o_gpu[b][rows[b]])
         assert attention_err(g, ref_iso[b]) <= tol
-        assert attention_err(g, ref[b]) <= tol
+        assert attention_err(g, ref[b]) <= tol + rope_share, (attention_err(g, ref[b]), rope_share)
     if step.use_cfg:
         r = rows[0]
         both = sorted(set(rows[0]).intersection(rows[1]))
