@@ -88,6 +88,9 @@ def main() -> int:
     ap.add_argument("--workload", default="dit1k_bf16")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="after timing, relayout one buffer of this many MB (a plain copy of known size "
+                         "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -158,6 +161,15 @@ def main() -> int:
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name else None),
             "kernel": "nx::bf16k::fwd_bf16_kernel" if wl.dtype == "bf16" else "nx::f32k::fwd_f32_kernel",
             "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_ms[0], 4)}
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 2
+        src = torch.empty((1, 2, 8, n // (2 * 8 * 128), 128), dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty((1, 2, src.shape[3], 8, 128), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        nx.nxattn_kv_relayout(src, dst, 0)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

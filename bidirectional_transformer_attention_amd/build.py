@@ -33,9 +33,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -45,20 +45,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = True, out: str = OUT, build_dir: str = BUILD_DIR,
+          extra=()) -> str:
+    """Compile every csrc/*.hip for gfx950 and link `out`; `extra` adds hipcc flags
+    (for instance -D tuning macros)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, build_dir, tuple(extra)), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT} from {len(srcs)} sources")
-    return OUT
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":

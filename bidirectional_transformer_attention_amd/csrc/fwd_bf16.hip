@@ -309,6 +309,37 @@ __device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int l
   using All = std::integral_constant<int, 8>;
   using Half = std::integral_constant<int, 4>;
 
+  // Steady-state tile loads (4 waves, 16 rows each, tile wholly inside the prefix or
+  // wholly inside the own keys): a wave-uniform row base in scalar registers plus a
+  // per-lane 32-bit byte offset fixed for the whole loop. Lane (rl = lane/16, slot =
+  // lane%16) of instruction i fills row 16ws + 4i + rl, whose K swizzle is
+  // slot ^ (4i + rl) and whose V swizzle is slot ^ 4rl.
+  const int rl = lane >> 4, lslot = lane & 15;
+  const uint32_t rp_pre = (uint32_t)(rl * pstride * 2), rp_own = (uint32_t)(rl * ks1 * 2);
+  uint32_t ck[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ck[i] = 16u * (uint32_t)(lslot ^ (4 * i + rl));
+  const uint32_t cv = 16u * (uint32_t)(lslot ^ (rl << 2));
+  auto dma_tile_half = [&](int t, bool isv, int dst, int ws) {
+    const int j0 = t * BN;
+    if (j0 + BN <= P || (j0 >= P && j0 + BN <= Skv)) {
+      const bool pre = j0 + BN <= P;
+      const int64_t rs = pre ? pstride : ks1;   // row stride, elements
+      const uint16_t* tb = pre ? (isv ? kprefix + (int64_t)P * pstride : kprefix) + (int64_t)(j0 + 16 * ws) * pstride
+                               : (isv ? vown : kown) + (int64_t)(j0 - P + 16 * ws) * ks1;
+      const uint32_t rp = pre ? rp_pre : rp_own;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(tb + 4 * i * rs) + (rp + (isv ? cv : ck[i]));
+        __builtin_amdgcn_global_load_lds(src,
+                                         (__attribute__((address_space(3))) void*)((lds_u8*)smem + dst + (16 * ws + 4 * i) * ROWB),
+                                         16, 0, 0);
+      }
+    } else {
+      dma_tile(t, isv, dst, ws, Half{});
+    }
+  };
+
   // ---- prologue: K_0, V_0, K_1 resident; both groups score tile 0; group A also
   // ---- runs its softmax, so that A leads B by half a tile from here on.
   dma_tile(0, false, KOFF0, wave, All{});
@@ -330,15 +361,15 @@ __device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int l
     // path keeps the register allocation of S and P straight.
     if (GROUP_A) {
       gemm_phase<PAR, PAR ^ 1, true>(w, smem);
+      // group A fetches the next tiles after its last LDS read of the slot (its next LDS
+      // read is two slots away, so the compiler's wait for the direct loads costs
+      // nothing): K_{t+2} -> K buffer t&1, V_{t+1} -> V buffer (t+1)&1, both last read
+      // in the previous iteration; they land before the barrier that ends slot 2t+1.
+      if (t + 2 < T) dma_tile_half(t + 2, false, KOFF0 + PAR * TILEB, wave);
+      if (more) dma_tile_half(t + 1, true, VOFF0 + (PAR ^ 1) * TILEB, wave);
       barrier_only();
       if (more) softmax(w, c, Skv - (t + 1) * BN < BN ? Skv - (t + 1) * BN : BN, hh);
     } else {
-      // group B fetches the next tiles while it normalises (it reads no LDS in this
-      // slot, so the DMA has a whole slot to land before B's own next LDS read):
-      // K_{t+2} -> K buffer t&1, V_{t+1} -> V buffer (t+1)&1; both were last read in
-      // the previous iteration.
-      if (t + 2 < T) dma_tile(t + 2, false, KOFF0 + PAR * TILEB, wave - 4, Half{});
-      if (more) dma_tile(t + 1, true, VOFF0 + (PAR ^ 1) * TILEB, wave - 4, Half{});
       softmax(w, c, Skv - t * BN < BN ? Skv - t * BN : BN, hh);
       barrier_only();
       gemm_phase<PAR, PAR ^ 1, true>(w, smem);

@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <cstdarg>
 
-#include "../../include/nxattn.h"
+#include "nxattn.h"
 
 namespace nx {
 
