@@ -62,7 +62,7 @@ def cpu_baseline(wl, rows_per_branch: int):
         cores = 1
     inp = synth.make_inputs(wl)
     f64 = lambda t: t.to(torch.float32).numpy().astype(np.float64)  # noqa: E731
-    rows = np.arange(min(rows_per_branch, wl.seq))
+    rows = np.arange(wl.seq if rows_per_branch <= 0 else min(rows_per_branch, wl.seq))
     t0 = time.perf_counter()
     flops = 0.0
     for b in range(wl.branches):
@@ -86,7 +86,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit1k_bf16")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows per branch for the CPU oracle timing (0: all, i.e. one whole step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after timing, relayout one buffer of this many MB (a plain copy of known size "
