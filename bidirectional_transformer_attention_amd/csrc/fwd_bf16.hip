@@ -19,7 +19,21 @@
 // Ping-pong. Waves 0-3 and 4-7 (one of each per SIMD) run the same program half a
 // tile apart: while one group issues the MFMAs of tile t (scores of t+1 and P V of t),
 // the other group runs the exp2/max/sum of its softmax, so matrix cores and VALU of a
-// SIMD overlap. Each half-iteration ends at a workgroup barrier.
+// SIMD overlap. Each half-iteration ends at a workgroup barrier, and the wave that
+// issues MFMAs in a half-iteration runs at the higher s_setprio level (the issue
+// arbiter otherwise favours the older wave, which starves the second group's GEMM).
+//
+// Tile loads. Direct-to-LDS loads (global_load_lds_dwordx4) issued by waves 0-3 and
+// interleaved with their score MFMAs: a wave-uniform row base plus a fixed per-lane
+// offset for tiles wholly inside the prefix or the own keys; the tile straddling the
+// prefix end is processed last and, with the ragged last tile, uses per-lane clamped
+// addresses. K and V buffers are distinct LDS objects, so the compiler does not make
+// the score reads of one K buffer wait for loads into the other.
+//
+// Work order. Workgroups enumerate (kv head, branch, query blocks) kv-head-major and
+// are remapped so that each XCD runs a contiguous range: the workgroups that stream
+// the same K/V share an L2, and every XCD gets a mix of CFG branches (whose key
+// counts differ).
 //
 // LDS: K and V double-buffered, 64 rows x 256 B each, 16-byte chunks XOR-swizzled per
 // row (K: chunk ^ (row & 15), V: chunk ^ 4*(row & 3)) so the row-parallel K reads and
@@ -72,6 +86,25 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+// s_setprio around a barrier: the wave that issues MFMAs in the coming slot gets
+// priority over its SIMD partner's softmax VALU (the issue arbiter would otherwise
+// favour the older wave).
+template <int BEFORE, int AFTER>
+__device__ __forceinline__ void barrier_prio() {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (BEFORE >= 0) asm volatile("s_setprio %0" :: "n"(BEFORE));
+  asm volatile("s_barrier" ::: "memory");
+  if constexpr (AFTER >= 0) asm volatile("s_setprio %0" :: "n"(AFTER));
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int BEFORE, int AFTER>
+__device__ __forceinline__ void wait_dma_barrier_prio() {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (BEFORE >= 0) asm volatile("s_setprio %0" :: "n"(BEFORE));
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (AFTER >= 0) asm volatile("s_setprio %0" :: "n"(AFTER));
+  __builtin_amdgcn_sched_barrier(0);
+}
 __device__ __forceinline__ void wait_dma_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -80,8 +113,27 @@ __device__ __forceinline__ void wait_dma_barrier() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// LDS map: [K buffer 0][K buffer 1][V buffer 0][V buffer 1], TILEB bytes each.
-constexpr int KOFF0 = 0, VOFF0 = 2 * TILEB;
+// LDS: K and V tiles, double-buffered, as four distinct objects (TILEB bytes each), so
+// the compiler can tell a direct-to-LDS load into one buffer from a read of another and
+// does not serialise them.
+__shared__ __attribute__((aligned(1024))) uint8_t lds_k0[TILEB];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_k1[TILEB];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_v0[TILEB];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_v1[TILEB];
+template <int PAR> __device__ __forceinline__ uint8_t* kbuf() { return PAR ? lds_k1 : lds_k0; }
+template <int PAR> __device__ __forceinline__ uint8_t* vbuf() { return PAR ? lds_v1 : lds_v0; }
+
+// Direct-to-LDS tile load plan of a wave for one iteration: K tile t+2 and V tile t+1,
+// each wholly inside the prefix or wholly inside the own keys. Instruction i (0-3: K,
+// 4-7: V) moves rows 16ws + 4(i%4) .. +3: global address = row base (wave-uniform) +
+// lane offset; LDS address = the buffer + the same rows.
+struct DmaPlan {
+  const uint8_t* kb; const uint8_t* vb;   // byte address of row 16ws of the K / V tile
+  int64_t krs, vrs;                       // 4-row step in bytes
+  uint32_t krp, vrp;                      // lane row offset (rl * row stride) in bytes
+  uint32_t ck[4], cv;                     // lane chunk offsets (swizzled) in bytes
+  int ws;
+};
 
 struct Wave {
   bf16x8 qf[8];       // Q^T operand, k-step ks: Q[row][16ks + 8hh .. +7]
@@ -110,12 +162,13 @@ __device__ __forceinline__ void sched_reads() {
     sched_reads<I + 1, N>();
   }
 }
-template <int I, int N, int DIST>
+template <int I, int N, int DIST, bool DMA>
 __device__ __forceinline__ void sched_steps() {
   if constexpr (I < N) {
     if constexpr (I + DIST < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DIST < 16 ? 2 : 1, 0);
+    if constexpr (DMA && I >= 16 && ((I - 16) & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    sched_steps<I + 1, N, DIST>();
+    sched_steps<I + 1, N, DIST, DMA>();
   }
 }
 
@@ -123,9 +176,10 @@ __device__ __forceinline__ void sched_steps() {
 // K_{t+1} Q^T (16 MFMAs). Fragments are read from LDS three MFMAs ahead so the
 // matrix core never waits on LDS latency; consecutive MFMAs target different
 // accumulators. VPAR / KPAR select the V and K buffers (compile-time LDS offsets).
-template <int VPAR, int KPAR, bool SCORE>
-__device__ __forceinline__ void gemm_phase(Wave& w, const uint8_t* smem) {
-  constexpr int VB = VOFF0 + VPAR * TILEB, KB = KOFF0 + KPAR * TILEB;
+template <int VPAR, int KPAR, bool SCORE, bool DMA = false>
+__device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullptr) {
+  const uint8_t* vsm = vbuf<VPAR>();
+  const uint8_t* ksm = kbuf<KPAR>();
   constexpr int DIST = 3;
   constexpr int nsteps = SCORE ? 32 : 16;
   // step i < 16: PV, (kbhs = i / 4, db = i % 4); step i >= 16: S, (ks = (i-16)/2, kb = (i-16)%2)
@@ -134,12 +188,23 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const uint8_t* smem) {
       const int kbhs = i >> 2, db = i & 3;
       const int rbase = (kbhs >> 1) * 32 + (kbhs & 1) * 16;   // kb*32 + 16*hs
       const int off = w.vbase + ((64 * db) ^ w.vy);
-      const bf16x4 a = lds_read_tr(smem, VB + rbase * ROWB + off);
-      const bf16x4 b = lds_read_tr(smem, VB + (rbase + 8) * ROWB + off);
+      const bf16x4 a = lds_read_tr(vsm, rbase * ROWB + off);
+      const bf16x4 b = lds_read_tr(vsm, (rbase + 8) * ROWB + off);
       return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     const int j = i - 16, ks = j >> 1, kb = j & 1;
-    return as_bf16x8(lds_read_b128(smem, KB + kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
+    return as_bf16x8(lds_read_b128(ksm, kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
+  };
+  // DMA instruction d (after the last V read of the phase, so every later LDS read of
+  // the phase is of the other K buffer): K_{t+2} into K buffer KPAR^1, V_{t+1} into V
+  // buffer VPAR^1, both last read in the previous iteration
+  auto dma = [&](int d) {
+    const int i = d & 3;
+    const bool isv = d >= 4;
+    const uint8_t* src = isv ? plan->vb + i * plan->vrs + (plan->vrp + plan->cv)
+                             : plan->kb + i * plan->krs + (plan->krp + plan->ck[i]);
+    uint8_t* dst = (isv ? vbuf<VPAR ^ 1>() : kbuf<KPAR ^ 1>()) + (16 * plan->ws + 4 * i) * ROWB;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_u8*)dst, 16, 0, 0);
   };
   bf16x8 ring[DIST + 1];
 #pragma unroll
@@ -148,6 +213,9 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const uint8_t* smem) {
   for (int i = 0; i < 32; ++i) {
     if (i < nsteps) {
       if (i + DIST < nsteps) ring[(i + DIST) % (DIST + 1)] = read(i + DIST);
+      if constexpr (DMA) {
+        if (i >= 16 && ((i - 16) & 1) == 0) dma((i - 16) >> 1);
+      }
       const bf16x8 f = ring[i % (DIST + 1)];
       if (i < 16) {
         const int kbhs = i >> 2, db = i & 3;
@@ -162,18 +230,18 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const uint8_t* smem) {
   // keep the issue order: the first DIST fragments' reads, then per step the reads of
   // step i+DIST followed by MFMA i
   sched_reads<0, DIST>();
-  sched_steps<0, nsteps, DIST>();
+  sched_steps<0, nsteps, DIST, DMA>();
 }
 
 // S^T only (prologue).
 template <int KPAR>
-__device__ __forceinline__ void gemm_s_only(Wave& w, const uint8_t* smem) {
-  constexpr int KB = KOFF0 + KPAR * TILEB;
+__device__ __forceinline__ void gemm_s_only(Wave& w) {
+  const uint8_t* ksm = kbuf<KPAR>();
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 f = as_bf16x8(lds_read_b128(smem, KB + kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
+      const bf16x8 f = as_bf16x8(lds_read_b128(ksm, kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
       if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], f32x16{}, 0, 0, 0);
       else w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], w.s[kb], 0, 0, 0);
     }
@@ -238,13 +306,14 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
 // The per-wave program. Group A (waves 0-3) and group B (waves 4-7) run it half a tile
 // apart; both execute the same sequence of workgroup barriers.
 template <bool GROUP_A>
-__device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int lane, int wave) {
+__device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
-  const int b = wg / (a.heads_kv * a.wg_per_group);
-  const int rem = wg % (a.heads_kv * a.wg_per_group);
-  const int g = rem / a.wg_per_group;
-  const int qb = (rem % a.wg_per_group) * WAVES + wave;
+  // (kv head, branch) groups in kv-head-major order: each XCD's contiguous share mixes
+  // the CFG branches, whose key counts differ
+  const int grp = wg / a.wg_per_group;
+  const int g = grp / a.batch, b = grp % a.batch;
+  const int qb = (wg % a.wg_per_group) * WAVES + wave;
   const bool active = qb < a.nqb;
   const int hq = g * a.group + (active ? qb / a.nchunks : 0);
   const int tok = (active ? qb % a.nchunks : 0) * 32 + n;
@@ -288,7 +357,7 @@ __device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int l
   const uint16_t* kown = a.k + b * a.ks0 + (int64_t)g * a.ks2;
   const uint16_t* vown = a.v + b * a.ks0 + (int64_t)g * a.ks2;
   const int64_t ks1 = a.ks1;
-  auto dma_tile = [&](int t, bool isv, int dst, int ws, auto nw) {
+  auto dma_tile = [&](int t, bool isv, uint8_t* dst, int ws, auto nw) {
     constexpr int NW = decltype(nw)::value;
     constexpr int ROWS = BN / NW;
 #pragma unroll
@@ -302,16 +371,25 @@ __device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int l
       if (j < P) src = (isv ? kprefix + (int64_t)P * pstride : kprefix) + (int64_t)j * pstride;
       else src = (isv ? vown : kown) + (int64_t)(j - P) * ks1;
       __builtin_amdgcn_global_load_lds(src + 8 * chunk,
-                                       (__attribute__((address_space(3))) void*)((lds_u8*)smem + dst + (ROWS * ws + 4 * i) * ROWB),
+                                       (__attribute__((address_space(3))) void*)((lds_u8*)dst + (ROWS * ws + 4 * i) * ROWB),
                                        16, 0, 0);
     }
   };
   using All = std::integral_constant<int, 8>;
   using Half = std::integral_constant<int, 4>;
 
-  // Steady-state tile loads (4 waves, 16 rows each, tile wholly inside the prefix or
-  // wholly inside the own keys): a wave-uniform row base in scalar registers plus a
-  // per-lane 32-bit byte offset fixed for the whole loop. Lane (rl = lane/16, slot =
+  // Key tiles are processed in natural order, except that a tile straddling the end of
+  // the prefix (when it is not also the last tile) moves to the end: the online softmax
+  // does not depend on the order. Positions [0, nwhole) then hold only whole tiles,
+  // wholly inside the prefix or wholly inside the own keys.
+  const int sb = (P % BN != 0 && P / BN < T - 1) ? P / BN : -1;
+  auto tile_at = [&](int pos) { return (sb < 0 || pos < sb) ? pos : (pos < T - 1 ? pos + 1 : sb); };
+  auto valid_at = [&](int pos) { const int r = Skv - tile_at(pos) * BN; return r < BN ? r : BN; };
+  const bool last_whole = (T - 1) * BN >= P && T * BN <= Skv;
+  const int nwhole = T - (sb >= 0 ? 1 : 0) - (last_whole ? 0 : 1);
+
+  // Steady-state loads of whole tiles (4 waves x 16 rows): a wave-uniform row base in
+  // scalar registers plus a per-lane 32-bit byte offset. Lane (rl = lane/16, slot =
   // lane%16) of instruction i fills row 16ws + 4i + rl, whose K swizzle is
   // slot ^ (4i + rl) and whose V swizzle is slot ^ 4rl.
   const int rl = lane >> 4, lslot = lane & 15;
@@ -320,69 +398,94 @@ __device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int l
 #pragma unroll
   for (int i = 0; i < 4; ++i) ck[i] = 16u * (uint32_t)(lslot ^ (4 * i + rl));
   const uint32_t cv = 16u * (uint32_t)(lslot ^ (rl << 2));
-  auto dma_tile_half = [&](int t, bool isv, int dst, int ws) {
-    const int j0 = t * BN;
-    if (j0 + BN <= P || (j0 >= P && j0 + BN <= Skv)) {
-      const bool pre = j0 + BN <= P;
-      const int64_t rs = pre ? pstride : ks1;   // row stride, elements
-      const uint16_t* tb = pre ? (isv ? kprefix + (int64_t)P * pstride : kprefix) + (int64_t)(j0 + 16 * ws) * pstride
-                               : (isv ? vown : kown) + (int64_t)(j0 - P + 16 * ws) * ks1;
-      const uint32_t rp = pre ? rp_pre : rp_own;
+  auto plan_of = [&](int t) {
+    DmaPlan pl;
+    const int jk = tile_at(t + 2) * BN + 16 * wave, jv = tile_at(t + 1) * BN + 16 * wave;
+    const bool kpre = jk < P, vpre = jv < P;
+    pl.kb = reinterpret_cast<const uint8_t*>(kpre ? kprefix + (int64_t)jk * pstride : kown + (int64_t)(jk - P) * ks1);
+    pl.vb = reinterpret_cast<const uint8_t*>(vpre ? kprefix + (int64_t)(P + jv) * pstride : vown + (int64_t)(jv - P) * ks1);
+    pl.krs = 8 * (kpre ? pstride : ks1);
+    pl.vrs = 8 * (vpre ? pstride : ks1);
+    pl.krp = kpre ? rp_pre : rp_own;
+    pl.vrp = vpre ? rp_pre : rp_own;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(tb + 4 * i * rs) + (rp + (isv ? cv : ck[i]));
-        __builtin_amdgcn_global_load_lds(src,
-                                         (__attribute__((address_space(3))) void*)((lds_u8*)smem + dst + (16 * ws + 4 * i) * ROWB),
-                                         16, 0, 0);
-      }
-    } else {
-      dma_tile(t, isv, dst, ws, Half{});
-    }
+    for (int i = 0; i < 4; ++i) pl.ck[i] = ck[i];
+    pl.cv = cv;
+    pl.ws = wave;
+    return pl;
   };
 
-  // ---- prologue: K_0, V_0, K_1 resident; both groups score tile 0; group A also
-  // ---- runs its softmax, so that A leads B by half a tile from here on.
-  dma_tile(0, false, KOFF0, wave, All{});
-  dma_tile(0, true, VOFF0, wave, All{});
-  if (T > 1) dma_tile(1, false, KOFF0 + TILEB, wave, All{});
+  // ---- prologue: the first K tile, V tile and second K tile resident; both groups
+  // ---- score position 0; group A also runs its softmax, so that A leads B by half a
+  // ---- tile from here on.
+  dma_tile(tile_at(0), false, kbuf<0>(), wave, All{});
+  dma_tile(tile_at(0), true, vbuf<0>(), wave, All{});
+  if (T > 1) dma_tile(tile_at(1), false, kbuf<1>(), wave, All{});
   wait_dma_barrier();
-  gemm_s_only<0>(w, smem);
-  if (GROUP_A) softmax(w, c, Skv < BN ? Skv : BN, hh);
-  barrier_only();
+  gemm_s_only<0>(w);
+  if (GROUP_A) softmax(w, c, valid_at(0), hh);
+  if (GROUP_A) barrier_prio<-1, 2>();
+  else barrier_only();
 
-  // iteration t: slot 2t (A multiplies, B normalises), slot 2t+1 (swapped)
-  auto iteration = [&](int t, auto par) {
+  // Iteration t: slot 2t (A multiplies, B normalises), slot 2t+1 (swapped). Each GEMM
+  // phase accumulates P V of position t and scores position t+1 (the last iteration
+  // scores a stale K buffer that is never used: one code path keeps the register
+  // allocation of S and P straight). The multiplying wave holds the higher priority.
+  // Group A fetches K of position t+2 into K buffer t&1 and V of position t+1 into V
+  // buffer (t+1)&1, both last read in the previous iteration; the loads land before
+  // the barrier that ends slot 2t+1. FAST: both are whole tiles, and the loads are
+  // interleaved with the score MFMAs (after the phase's last V read).
+  auto iter_a = [&](int t, auto par, auto fast) {
     constexpr int PAR = decltype(par)::value;        // t & 1
-    const bool more = t + 1 < T;
+    constexpr bool FAST = decltype(fast)::value;
     // opaque per iteration: keeps the compiler from hoisting the per-fragment address
     // arithmetic out of the loop (which would pin a dozen more registers)
     asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
-    // The last iteration also scores a stale K buffer (never used afterwards): one code
-    // path keeps the register allocation of S and P straight.
-    if (GROUP_A) {
-      gemm_phase<PAR, PAR ^ 1, true>(w, smem);
-      // group A fetches the next tiles after its last LDS read of the slot (its next LDS
-      // read is two slots away, so the compiler's wait for the direct loads costs
-      // nothing): K_{t+2} -> K buffer t&1, V_{t+1} -> V buffer (t+1)&1, both last read
-      // in the previous iteration; they land before the barrier that ends slot 2t+1.
-      if (t + 2 < T) dma_tile_half(t + 2, false, KOFF0 + PAR * TILEB, wave);
-      if (more) dma_tile_half(t + 1, true, VOFF0 + (PAR ^ 1) * TILEB, wave);
-      barrier_only();
-      if (more) softmax(w, c, Skv - (t + 1) * BN < BN ? Skv - (t + 1) * BN : BN, hh);
+    if constexpr (FAST) {
+      const DmaPlan pl = plan_of(t);
+      gemm_phase<PAR, PAR ^ 1, true, true>(w, &pl);
     } else {
-      softmax(w, c, Skv - t * BN < BN ? Skv - t * BN : BN, hh);
-      barrier_only();
-      gemm_phase<PAR, PAR ^ 1, true>(w, smem);
+      gemm_phase<PAR, PAR ^ 1, true>(w);
+      if (t + 2 < T) dma_tile(tile_at(t + 2), false, kbuf<PAR>(), wave, Half{});
+      if (t + 1 < T) dma_tile(tile_at(t + 1), true, vbuf<PAR ^ 1>(), wave, Half{});
     }
-    wait_dma_barrier();
+    barrier_prio<0, -1>();
+    if (t + 1 < T) softmax(w, c, valid_at(t + 1), hh);
+    wait_dma_barrier_prio<-1, 2>();
   };
+  auto iter_b = [&](int t, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
+    softmax(w, c, valid_at(t), hh);
+    barrier_prio<-1, 2>();
+    gemm_phase<PAR, PAR ^ 1, true>(w);
+    wait_dma_barrier_prio<0, -1>();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using Fast = std::true_type;
+  using Slow = std::false_type;
   int t = 0;
-  for (; t + 1 < T; t += 2) {
-    iteration(t, std::integral_constant<int, 0>{});
-    iteration(t + 1, std::integral_constant<int, 1>{});
+  if (GROUP_A) {
+    const int nfast = nwhole - 2;
+    for (; t + 1 < nfast; t += 2) {
+      iter_a(t, P0{}, Fast{});
+      iter_a(t + 1, P1{}, Fast{});
+    }
+    for (; t + 1 < T; t += 2) {
+      iter_a(t, P0{}, Slow{});
+      iter_a(t + 1, P1{}, Slow{});
+    }
+    if (t < T) iter_a(t, P0{}, Slow{});
+  } else {
+    for (; t + 1 < T; t += 2) {
+      iter_b(t, P0{});
+      iter_b(t + 1, P1{});
+    }
+    if (t < T) iter_b(t, P0{});
   }
-  if (t < T) iteration(t, std::integral_constant<int, 0>{});
 
+  if (GROUP_A) asm volatile("s_setprio 0");
   // ---- epilogue: total row sum (both lane halves), normalise, round, store
   {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(w.l), __float_as_int(w.l), false, false);
@@ -403,11 +506,10 @@ __device__ __forceinline__ void wave_program(const Args& a, uint8_t* smem, int l
 }
 
 __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];   // K0 K1 V0 V1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true>(a, smem, lane, wave);
-  else wave_program<false>(a, smem, lane, wave);
+  if (wave < 4) wave_program<true>(a, lane, wave);
+  else wave_program<false>(a, lane, wave);
 }
 
 }  // namespace bf16k

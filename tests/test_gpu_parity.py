@@ -180,6 +180,8 @@ def fwd_case(dtype, B, S, Hq, Hkv, D, plens, seed, scale_v=1.0):
     (1, 1, 16, 2, (200,)),        # one own token, long prefix
     (1, 33, 16, 2, (31,)),        # G = 8
     (3, 70, 2, 1, (5, 0, 64)),
+    (2, 640, 8, 2, (128, 200)),   # whole prefix tiles, then a straddling one (processed last)
+    (2, 200, 4, 2, (300, 7)),     # prefix longer than the own tokens; ragged last tile
 ])
 def test_fwd_bf16_reduced(B, S, Hq, Hkv, P):
     fwd_case(torch.bfloat16, B, S, Hq, Hkv, 128, P, 1000 + S)
@@ -319,6 +321,21 @@ def test_fwd_strided_views():
         ref = oracle.attention(f64(qc[b]), f64(kc[b]), f64(vc[b]))
         assert attention_err(f64(o.cpu()[b]), ref) <= TOL["bf16"]
     assert torch.count_nonzero(obuf[:, :, 0]) == 0
+
+
+def test_fwd_strided_own_keys_with_prefix():
+    # own q/k/v are views of a fused projection (k row stride (Hq + 2 Hkv) D), the prefix
+    # is a contiguous [2, P, Hkv, D] slice (row stride Hkv D): whole own tiles and whole
+    # prefix tiles are loaded with different row strides; P = 130 straddles a tile
+    note("fwd strided own keys + prefix of another stride")
+    D, S, Hq, Hkv, P = 128, 600, 8, 2, 130
+    qkv = synth.random_tensor((1, S, Hq + 2 * Hkv, D), 81, torch.bfloat16).to(DEV)
+    q, k, v = qkv[:, :, :Hq], qkv[:, :, Hq:Hq + Hkv], qkv[:, :, Hq + Hkv:]
+    pre = synth.random_tensor((2, P, Hkv, D), 82, torch.bfloat16)
+    o = run_fwd(q, k, v, [pre.to(DEV)])
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    ref = oracle.attention(f64(qc[0]), f64(kc[0]), f64(vc[0]), f64(pre[0]), f64(pre[1]))
+    assert attention_err(f64(o[0]), ref) <= TOL["bf16"]
 
 
 # ---------------------------------------------------------------------------- whole workloads
