@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit1k_bf16]
 
 One step = one pass of the whole path over one synthetic batch, inputs resident in HBM:
-prefix relayout (replay -> online layout), RoPE on own q and k of both CFG branches,
-the fused attention launch over [prefix ++ own] for both branches, CFG combine.
+prefix relayout (replay -> online layout), RoPE on own k (and q) of both CFG branches,
+the fused attention launch over [prefix ++ own] for both branches (on the bf16 path it
+rotates q as it loads it), CFG combine.
 Prints one JSON line. ``value`` is attention TFLOP/s (4*Sq*Skv*Hq*D summed over the
 branches, divided by the step time). ``roofline`` is measured on the fused attention
 kernel with HIP events recorded on the stream it runs on; ``cpu_baseline`` times the
@@ -185,7 +186,8 @@ def main() -> int:
                    "head_dim": wl.head_dim, "rope_offsets": [list(o) for o in wl.offsets],
                    "guidance": wl.guidance, "prefix_layout_in": "replay [2,H,P,D] relaid each step"
                    if wl.prefix_layout == "replay" else "online [2,P,H,D]",
-                   "step": "relayout + rope(q,k) + fused attention + cfg",
+                   "step": ("relayout + rope(k) + fused attention (q rotated on load) + cfg" if step.fuse_q_rope
+                            else "relayout + rope(q,k) + fused attention + cfg"),
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},
         "roofline": roof,
         "cpu_baseline": cpu,

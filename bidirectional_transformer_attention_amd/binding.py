@@ -42,7 +42,7 @@ class FwdArgs(ctypes.Structure):
                 ("q_strides", ctypes.c_int64 * 3), ("kv_strides", ctypes.c_int64 * 3),
                 ("o_strides", ctypes.c_int64 * 3),
                 ("prefix_kv", ctypes.c_void_p * MAX_BRANCHES), ("prefix_len", ctypes.c_int32 * MAX_BRANCHES),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("q_rope", ctypes.POINTER(RopeDesc))]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -160,7 +160,10 @@ def nxattn_rope_apply(x: torch.Tensor, descs: List[RopeDesc], stream=None) -> No
 
 
 def make_fwd_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                  prefix: Sequence[Optional[torch.Tensor]], scale: float = 0.0) -> FwdArgs:
+                  prefix: Sequence[Optional[torch.Tensor]], scale: float = 0.0,
+                  q_rope: Optional[Sequence[RopeDesc]] = None) -> FwdArgs:
+    """FwdArgs for the tensors; q_rope (one RopeDesc per batch entry) is kept alive on
+    the returned object for as long as it is in use."""
     B, S, Hq, D = q.shape
     a = FwdArgs()
     a.dtype = _dtype_code(q)
@@ -179,14 +182,21 @@ def make_fwd_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
             a.prefix_kv[b] = p.data_ptr()
             a.prefix_len[b] = p.shape[1]
     a.scale = float(scale)
+    if q_rope is not None:
+        arr = (RopeDesc * len(q_rope))(*q_rope)
+        a._q_rope_keep = arr
+        a.q_rope = ctypes.cast(arr, ctypes.POINTER(RopeDesc))
     return a
 
 
 def nxattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-               prefix: Sequence[Optional[torch.Tensor]] = (), scale: float = 0.0, stream=None) -> None:
+               prefix: Sequence[Optional[torch.Tensor]] = (), scale: float = 0.0, stream=None,
+               q_rope: Optional[Sequence[RopeDesc]] = None) -> None:
     """o = attention(q, [prefix_k ++ k], [prefix_v ++ v]) for every branch.
 
     q, o [B,S,Hq,D]; k, v [B,S,Hkv,D] (same strides); prefix[b] contiguous [2,P_b,Hkv,D] or None.
+    q_rope: None (q already rotated) or one RopeDesc per batch entry, to rotate q on load
+    (bf16 only); q itself is left unchanged.
     """
     _gpu(q, k, v, o, *[p for p in prefix if p is not None])
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
@@ -204,7 +214,9 @@ def nxattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
     for t in (k, v, o):
         if t.dtype != q.dtype:
             raise NxattnError(1, "q, k, v, o dtypes differ")
-    a = make_fwd_args(q, k, v, o, prefix, scale)
+    if q_rope is not None and len(q_rope) != q.shape[0]:
+        raise NxattnError(1, "q_rope must have one descriptor per batch entry")
+    a = make_fwd_args(q, k, v, o, prefix, scale, q_rope)
     _check(load().nxattn_fwd(ctypes.byref(a), _stream(stream)))
 
 

@@ -79,7 +79,15 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
     if ((int64_t)a->prefix_len[b] + a->seq_q > INT32_MAX)
       return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: prefix_len[%d] + seq_q overflows int32", b);
   }
+  if (a->q_rope && a->dtype != NXATTN_BF16)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: q_rope is supported for BF16 only");
   if (a->batch == 0 || a->seq_q == 0) return NXATTN_OK;
+  if (a->q_rope)
+    for (int b = 0; b < a->batch; ++b) {
+      const int st = check_rope_desc(a->q_rope[b], a->seq_q, a->head_dim, "nxattn_fwd (q_rope)");
+      if (st != NXATTN_OK) return st;
+
+    }
   if (!a->q || !a->k || !a->v || !a->o) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
   const int64_t es = esize(a->dtype);
   const int64_t* sts[3] = {a->q_strides, a->kv_strides, a->o_strides};
@@ -114,5 +122,18 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
     p.plen[b] = b < a->batch ? a->prefix_len[b] : 0;
   }
   p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+  p.rope_q = a->q_rope != nullptr;
+  std::memset(p.rq, 0, sizeof(p.rq));
+  for (int b = 0; p.rope_q && b < a->batch; ++b) {
+    const nxattn_rope_desc& d = a->q_rope[b];
+    RopeQ& r = p.rq[b];
+    r.n_axes = d.n_axes; r.interleaved = d.interleaved;
+    r.log2_theta = (float)std::log2(d.theta);
+    for (int ax = 0; ax < 3; ++ax) {
+      r.grid[ax] = ax < d.n_axes ? d.grid[ax] : 1;
+      r.pairs[ax] = ax < d.n_axes ? d.pairs[ax] : 0;
+      r.offset[ax] = ax < d.n_axes ? d.offset[ax] : 0;
+    }
+  }
   return a->dtype == NXATTN_BF16 ? launch_fwd_bf16(p, stream) : launch_fwd_f32(p, stream);
 }

@@ -67,6 +67,8 @@ struct Args {
   int32_t plen[NXATTN_MAX_BRANCHES];
   int32_t batch, seq, heads_q, heads_kv, group, nchunks, nqb, wg_per_group, total_wg;
   float c;  // scale * log2(e)
+  int32_t rope_q;
+  RopeQ rq[NXATTN_MAX_BRANCHES];
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -257,6 +259,73 @@ __device__ __forceinline__ void gemm_s_only(Wave& w) {
     }
 }
 
+// RoPE of this lane's q values on load (same convention as the RoPE kernel: pair j of
+// axis k with local index u turns by pos_k * theta^(-u / pairs_k); pairs (j, j + 64)
+// or, interleaved, (2j, 2j + 1)). Lane l first evaluates pair l's step in revolutions
+// per position (with its axis in the two low mantissa bits, a 2^-21 relative change);
+// every lane then fetches its pairs' entries with ds_bpermute. The turn pos * step is
+// reduced to [0, 1) in fp32 before the hardware sin/cos; results are rounded to bf16
+// (RNE). Lane data: qf[ks][e] = q[16 ks + 8 hh + e].
+__device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, int lane) {
+  const int hh = lane >> 5;
+  int c0 = tok, c1 = 0, c2 = 0;
+  if (r.n_axes == 2) {
+    c0 = tok / r.grid[1];
+    c1 = tok - c0 * r.grid[1];
+  } else if (r.n_axes == 3) {
+    const int hw = r.grid[1] * r.grid[2];
+    c0 = tok / hw;
+    const int rem = tok - c0 * hw;
+    c1 = rem / r.grid[2];
+    c2 = rem - c1 * r.grid[2];
+  }
+  const float p0 = (float)(c0 + r.offset[0]), p1 = (float)(c1 + r.offset[1]), p2 = (float)(c2 + r.offset[2]);
+  uint32_t entry;
+  {
+    // axis of pair j = lane as 0/1 weights (a blend keeps the choice in registers)
+    const int j = lane, n0 = r.pairs[0], n1 = r.pairs[1], n2 = r.pairs[2];
+    const int i0 = j < n0, i1 = (1 - i0) & (j < n0 + n1), i2 = 1 - i0 - i1;
+    const int u = j - i1 * n0 - i2 * (n0 + n1);
+    const int n = i0 * n0 + i1 * n1 + i2 * n2;
+    const float step = __builtin_amdgcn_exp2f(-(float)u * r.log2_theta / (float)(n > 0 ? n : 1)) * 0.15915494309189535f;
+    entry = (__float_as_uint(step) & ~3u) | (uint32_t)(i1 + 2 * i2);
+  }
+  auto turn = [&](int j, float& sn, float& cs) {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * j, (int)entry);
+    const uint32_t ax = v & 3u;
+    const float step = __uint_as_float(v & ~3u);
+    const float w1 = (float)(ax == 1u), w2 = (float)(ax == 2u), w0 = 1.f - w1 - w2;
+    const float pos = w0 * p0 + w1 * p1 + w2 * p2;
+    const float rev = pos * step;
+    const float f = rev - __builtin_floorf(rev);
+    sn = __builtin_amdgcn_sinf(f);
+    cs = __builtin_amdgcn_cosf(f);
+  };
+  if (!r.interleaved) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sn, cs;
+        turn(16 * ks + 8 * hh + e, sn, cs);
+        const float xa = (float)qf[ks][e], xb = (float)qf[ks + 4][e];
+        qf[ks][e] = (__bf16)(xa * cs - xb * sn);
+        qf[ks + 4][e] = (__bf16)(xa * sn + xb * cs);
+      }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float sn, cs;
+        turn((16 * ks + 8 * hh + e) >> 1, sn, cs);
+        const float xa = (float)qf[ks][e], xb = (float)qf[ks][e + 1];
+        qf[ks][e] = (__bf16)(xa * cs - xb * sn);
+        qf[ks][e + 1] = (__bf16)(xa * sn + xb * cs);
+      }
+  }
+}
+
 // Online softmax of w.s (tile with `valid` keys, < BN only for the last tile) -> w.p.
 __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
   if (valid < BN) {
@@ -433,6 +502,8 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   dma_tile(tile_at(0), false, kbuf<0>(), wave, All{});
   dma_tile(tile_at(0), true, vbuf<0>(), wave, All{});
   if (T > 1) dma_tile(tile_at(1), false, kbuf<1>(), wave, All{});
+  // q's RoPE (if requested) while the first tiles are in flight
+  if (a.rope_q) rotate_q(w.qf, a.rq[b], tokc, lane);
   wait_dma_barrier();
   gemm_s_only<0>(w);
   if (GROUP_A) softmax(w, c, valid_at(0), hh);
@@ -544,6 +615,8 @@ int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   if (total > INT32_MAX / 2) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: problem too large");
   a.nqb = (int)nqb; a.wg_per_group = (int)wpg; a.total_wg = (int)total;
   a.c = p.scale * LOG2E;
+  a.rope_q = p.rope_q;
+  for (int b = 0; b < NXATTN_MAX_BRANCHES; ++b) a.rq[b] = p.rq[b];
   fwd_bf16_kernel<<<a.total_wg, THREADS, 0, stream>>>(a);
   return check_launch("nxattn_fwd(bf16)");
 }

@@ -45,6 +45,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// ---- RoPE descriptors ---------------------------------------------------------------------
+// Checks one nxattn_rope_desc against seq and head_dim (fail() with `who` on error).
+int check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim, const char* who);
+
+// RoPE of q applied on load by the fused attention kernel (axes beyond n_axes have grid
+// 1, pairs 0, offset 0)
+struct RopeQ {
+  int32_t n_axes, interleaved;
+  int32_t grid[3], pairs[3], offset[3];
+  float log2_theta;
+};
+
 // ---- launchers implemented per kernel file -------------------------------------------
 struct FwdProblem {
   int dtype, batch, seq_q, heads_q, heads_kv, head_dim;
@@ -53,6 +65,8 @@ struct FwdProblem {
   const void* prefix[NXATTN_MAX_BRANCHES];
   int32_t plen[NXATTN_MAX_BRANCHES];
   float scale;
+  int32_t rope_q;                       // rotate q on load with rq[b]
+  RopeQ rq[NXATTN_MAX_BRANCHES];
 };
 int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
 int launch_fwd_f32(const FwdProblem& p, hipStream_t stream);

@@ -130,6 +130,21 @@ __global__ __launch_bounds__(256) void rope_kernel(T* x, int64_t seq, int64_t he
 
 using namespace nx;
 
+int nx::check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim, const char* who) {
+  if (d.n_axes < 1 || d.n_axes > 3) return fail(NXATTN_ERR_INVALID, "%s: n_axes %d not in 1..3", who, d.n_axes);
+  int64_t prod = 1, psum = 0;
+  for (int a = 0; a < d.n_axes; ++a) {
+    if (d.grid[a] < 1 || d.pairs[a] < 1) return fail(NXATTN_ERR_INVALID, "%s: grid and pairs must be >= 1", who);
+    prod *= d.grid[a];
+    psum += d.pairs[a];
+  }
+  if (prod != seq) return fail(NXATTN_ERR_INVALID, "%s: grid product %lld != seq %lld", who, (long long)prod, (long long)seq);
+  if (2 * psum != head_dim) return fail(NXATTN_ERR_INVALID, "%s: 2*sum(pairs) %lld != head_dim", who, (long long)(2 * psum));
+  if (!(d.theta > 1.0) || std::isinf(d.theta)) return fail(NXATTN_ERR_INVALID, "%s: theta must be finite and > 1", who);
+  if (d.interleaved != 0 && d.interleaved != 1) return fail(NXATTN_ERR_INVALID, "%s: interleaved must be 0 or 1", who);
+  return NXATTN_OK;
+}
+
 extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                                  const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
                                  hipStream_t stream) {
@@ -147,17 +162,8 @@ extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t he
   memset(&args, 0, sizeof(args));
   for (int64_t b = 0; b < batch; ++b) {
     const nxattn_rope_desc& d = rope[b];
-    if (d.n_axes < 1 || d.n_axes > 3) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: n_axes %d not in 1..3", d.n_axes);
-    int64_t prod = 1, psum = 0;
-    for (int a = 0; a < d.n_axes; ++a) {
-      if (d.grid[a] < 1 || d.pairs[a] < 1) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: grid and pairs must be >= 1");
-      prod *= d.grid[a];
-      psum += d.pairs[a];
-    }
-    if (prod != seq) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: grid product %lld != seq %lld", (long long)prod, (long long)seq);
-    if (2 * psum != head_dim) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: 2*sum(pairs) %lld != head_dim", (long long)(2 * psum));
-    if (!(d.theta > 1.0) || std::isinf(d.theta)) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: theta must be finite and > 1");
-    if (d.interleaved != 0 && d.interleaved != 1) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: interleaved must be 0 or 1");
+    const int st = check_rope_desc(d, seq, head_dim, "nxattn_rope_apply");
+    if (st != NXATTN_OK) return st;
     RopeBranch& r = args.br[b];
     r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.log2_theta = std::log2(d.theta);
     for (int a = 0; a < 3; ++a) {

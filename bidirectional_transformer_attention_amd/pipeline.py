@@ -1,7 +1,8 @@
 """One attention step of a DiT / ViT layer, chained from the four C-ABI calls.
 
     relayout (replay -> online, when the prefix arrives in the replay layout)
-    -> RoPE on own q and own k (every branch, its own offsets)
+    -> RoPE on own k, and on own q unless the attention kernel rotates q as it loads it
+       (the bf16 path; every branch with its own offsets)
     -> fused attention over [prefix ++ own] for all branches in one launch
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
 
@@ -20,8 +21,10 @@ from .synth import Inputs, Workload
 
 
 class AttentionStep:
-    def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda"):
+    def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None):
         self.wl = wl
+        # bf16: q is rotated inside the attention kernel (no separate pass over q)
+        self.fuse_q_rope = (wl.dtype == "bf16") if fuse_q_rope is None else bool(fuse_q_rope)
         dev = torch.device(device)
         self.q = inp.q.to(dev)
         self.k = inp.k.to(dev)
@@ -55,11 +58,13 @@ class AttentionStep:
                 nx.nxattn_kv_relayout(src, dst.unsqueeze(0), 0)
 
     def rope(self) -> None:
-        nx.nxattn_rope_apply(self.q, self.descs)
+        if not self.fuse_q_rope:
+            nx.nxattn_rope_apply(self.q, self.descs)
         nx.nxattn_rope_apply(self.k, self.descs)
 
     def attention(self) -> None:
-        nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online)
+        nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online,
+                      q_rope=self.descs if self.fuse_q_rope else None)
 
     def cfg(self) -> None:
         if self.use_cfg:

@@ -99,8 +99,9 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * For branch b, q head h (kv head g = h / (heads_q / heads_kv)), own query i:
  *   keys j in [0, P_b + seq_q): K_j = prefix K row j for j < P_b, else own k row j-P_b
  *   (same for V); s_j = scale * <q_i, K_j>; o = sum_j softmax(s)_j V_j.
- * q, k and v must already be rotated (nxattn_rope_apply); prefix keys are used as
- * stored. Layouts (element strides {b, s, h}, head_dim contiguous):
+ * k must already be rotated (nxattn_rope_apply); q too, unless q_rope is given (see
+ * below); prefix keys are used as stored. Layouts (element strides {b, s, h},
+ * head_dim contiguous):
  *   q [batch, seq_q, heads_q, D]     k, v [batch, seq_q, heads_kv, D]
  *   o [batch, seq_q, heads_q, D]     (written, must not overlap the inputs)
  *   prefix_kv[b]: one layer slice of the online cache, contiguous [2, P_b, heads_kv, D]
@@ -109,6 +110,15 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * before the P*V product on the bf16 path; the output is rounded to nearest even.
  * Supported: BF16 with head_dim 128; F32 with head_dim 64 or 72 (true fp32 MFMA, no
  * reduced-precision inputs); heads_q % heads_kv == 0; batch <= 8; seq_q >= 1.
+ *
+ * q_rope (optional, host memory, `batch` descriptors; NULL: q is used as stored):
+ * rotate q on load with the RoPE of nxattn_rope_apply (same descriptor meaning and
+ * checks, grid product == seq_q), inside the attention kernel, so that no separate
+ * pass over q is needed; the q buffer is not modified. The angle is evaluated in fp32
+ * (absolute error about 1e-4 rad at positions near 1000, far below the bf16 rounding
+ * of the rotated value, which is rounded to nearest even as a stored q would be).
+ * BF16 only: F32 with q_rope returns NXATTN_ERR_UNSUPPORTED (rotate with
+ * nxattn_rope_apply, whose fp64 angles keep the fp32 path exact to 1e-4).
  */
 typedef struct {
   int32_t dtype;
@@ -127,6 +137,7 @@ typedef struct {
   const void* prefix_kv[NXATTN_MAX_BRANCHES];
   int32_t prefix_len[NXATTN_MAX_BRANCHES];
   float scale;
+  const nxattn_rope_desc* q_rope;   /* NULL, or batch descriptors (see above)        */
 } nxattn_fwd_args;
 
 int nxattn_fwd(const nxattn_fwd_args* args, hipStream_t stream);

@@ -107,6 +107,30 @@ def test_fwd_rejects(lib, kw, code):
     assert nx.last_error() != ""
 
 
+def _with_q_rope(a, descs):
+    arr = (binding.RopeDesc * len(descs))(*descs)
+    a._keep = arr
+    a.q_rope = ctypes.cast(arr, ctypes.POINTER(binding.RopeDesc))
+    return a
+
+
+@pytest.mark.parametrize("kw,descs,code", [
+    # f32 cannot rotate q on load
+    (dict(dtype=0, head_dim=64), [binding.rope_desc((64,), (32,), (0,))] * 2, UNSUPPORTED),
+    # grid product must equal seq_q (64)
+    (dict(), [binding.rope_desc((8, 4), (32, 32), (0, 0))] * 2, INVALID),
+    # 2 * sum(pairs) must equal head_dim (128)
+    (dict(), [binding.rope_desc((8, 8), (16, 16), (0, 0))] * 2, INVALID),
+    # theta must exceed 1
+    (dict(), [binding.rope_desc((64,), (64,), (0,), theta=0.5)] * 2, INVALID),
+    # a valid q_rope does not skip the other checks (o overlaps q: nothing launches)
+    (dict(o=FAKE), [binding.rope_desc((8, 8), (32, 32), (4, 4))] * 2, INVALID),
+])
+def test_fwd_q_rope_rejects(lib, kw, descs, code):
+    assert call_fwd(lib, _with_q_rope(fwd_args(**kw), descs)) == code
+    assert nx.last_error() != ""
+
+
 def test_fwd_null_args(lib):
     assert lib.nxattn_fwd(None, None) == INVALID
 

@@ -338,6 +338,41 @@ def test_fwd_strided_own_keys_with_prefix():
     assert attention_err(f64(o[0]), ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("grid,pairs,offsets,P,inter", [
+    ((12, 20), (32, 32), ((7, 3), (512, 512)), (70, 0), False),      # 2-D, ragged, two branches
+    ((240,), (64,), ((32,), (0,)), (0, 33), True),                    # 1-D interleaved
+    ((3, 5, 8), (22, 21, 21), ((0, 0, 0), (5, 6, 7)), (16, 64), False),  # 3-D sections
+])
+def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter):
+    # q rotated inside the kernel == oracle RoPE of q, then attention (k pre-rotated by
+    # the oracle and rounded to bf16); q itself stays unchanged
+    S, Hq, Hkv, D = int(np.prod(grid)), 8, 2, 128
+    note(f"fwd q_rope grid={grid} pairs={pairs} offsets={offsets} P={P} interleaved={inter}")
+    q = synth.random_tensor((2, S, Hq, D), 91, torch.bfloat16)
+    k = synth.random_tensor((2, S, Hkv, D), 92, torch.bfloat16)
+    v = synth.random_tensor((2, S, Hkv, D), 93, torch.bfloat16)
+    pre = [synth.random_tensor((2, p, Hkv, D), 94 + b, torch.bfloat16) if p else None for b, p in enumerate(P)]
+    rnd = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    k_rot = torch.stack([rnd(oracle.rope(f64(k[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter))
+                         for b in range(2)])
+    descs = [nx.rope_desc(grid, pairs, offsets[b], 10000.0, inter) for b in range(2)]
+    qd = q.to(DEV)
+    o = torch.empty_like(qd)
+    nx.nxattn_fwd(qd, k_rot.to(DEV), v.to(DEV), o, [p.to(DEV) if p is not None else None for p in pre],
+                  q_rope=descs)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.cpu(), q)
+    for b in range(2):
+        q_ex = oracle.rope(f64(q[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter)
+        pk = f64(pre[b][0]) if pre[b] is not None else None
+        pv = f64(pre[b][1]) if pre[b] is not None else None
+        ref = oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv)
+        # the kernel rounds rotated q to bf16: that rounding alone, measured with the oracle
+        share = attention_err(oracle.attention(f64(rnd(q_ex)), f64(k_rot[b]), f64(v[b]), pk, pv), ref)
+        err = attention_err(f64(o.cpu()[b]), ref)
+        assert err <= TOL["bf16"] + share, (b, err, share)
+
+
 # ---------------------------------------------------------------------------- whole workloads
 def step_case(name, rows_per_branch, seed_rows):
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
@@ -348,16 +383,13 @@ def step_case(name, rows_per_branch, seed_rows):
     torch.cuda.synchronize()
     o_gpu = step.o.cpu()
     rows = {b: sample_rows(wl.seq, rows_per_branch, seed_rows + b) for b in range(wl.branches)}
-    # isolate the fused kernel: oracle attention over the GPU's own rotated q and k
-    qg, kg = step.q.cpu(), step.k.cpu()
-    ref_iso = oracle_attention(wl, inp, rows, [f64(qg[b]) for b in range(wl.branches)],
-                               [f64(kg[b]) for b in range(wl.branches)])
-    # the whole step against the oracle's own RoPE. The bf16 path stores the rotated q
-    # and k in bf16 (one rounding each, as any bf16 pipeline does), which by itself moves
+    # the whole step against the oracle's own RoPE. The bf16 path rounds the rotated q
+    # and k to bf16 (one rounding each, as any bf16 pipeline does), which by itself moves
     # the exact attention output; that share of the error is measured with the oracle
     # alone (its own RoPE outputs rounded to bf16) and added to the kernel's bar.
     ref = oracle_attention(wl, inp, rows)
     tol = TOL[wl.dtype]
+    qg, kg = step.q.cpu(), step.k.cpu()
     if wl.dtype == "bf16":
         rnd = lambda a: \
             torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
@@ -367,6 +399,15 @@ def step_case(name, rows_per_branch, seed_rows):
         rope_share = max(attention_err(ref_r[b], ref[b]) for b in range(wl.branches))
     else:
         rope_share = 0.0
+    # isolate the fused kernel: oracle attention over the GPU's own rotated k and q (q
+    # rotated on load inside the kernel is stood in for by the oracle's rotation rounded
+    # to bf16, the rounding the kernel applies)
+    if step.fuse_q_rope:
+        ref_iso = oracle_attention(wl, inp, rows, q_r, [f64(kg[b]) for b in range(wl.branches)],
+                                   q_rot_rows_only=True)
+    else:
+        ref_iso = oracle_attention(wl, inp, rows, [f64(qg[b]) for b in range(wl.branches)],
+                                   [f64(kg[b]) for b in range(wl.branches)])
     for b in range(wl.branches):
         g = f64(o_gpu[b][rows[b]])
         assert attention_err(g, ref_iso[b]) <= tol
