@@ -147,6 +147,7 @@ struct Wave {
   f32x16 s[2];        // S^T accumulators of the tile being scored (2 key blocks of 32)
   bf16x8 p[4];        // P^T operand of the tile being accumulated, step (kb, half)
   float m, l;
+  float thr;          // (m + RESCALE_T) / c: the raw row max above which m moves
   // lane parts of the LDS byte addresses: K fragment of k-step ks at kbase + (32ks ^ kx),
   // V^T fragment of d-block db at vbase + (64db ^ vy)
   int kbase, kx, vbase, vy;
@@ -350,10 +351,9 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
     tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
   }
-  const float cand = tmax * c;
-  const bool grow = cand > w.m + RESCALE_T;
+  const bool grow = tmax > w.thr;
   if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float mnew = grow ? cand : w.m;
+    const float mnew = grow ? tmax * c : w.m;
     const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
     w.l *= alpha;
 #pragma unroll
@@ -361,6 +361,7 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
     w.m = mnew;
+    w.thr = (mnew + RESCALE_T) / c;
   }
   const float nm = -w.m;
   float l0 = 0.f, l1 = 0.f;
@@ -411,6 +412,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
   w.m = -__builtin_inff();
+  w.thr = -__builtin_inff();
   w.l = 0.f;
   // lane parts of the LDS read addresses. K: row n, chunk 2ks+hh at slot
   // (2ks+hh) ^ (n & 15), i.e. byte n*ROWB + 16*(hh ^ (n&1)) + (32ks ^ 16*(n & 14)).
