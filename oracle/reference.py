@@ -77,12 +77,16 @@ def positions(grid: Sequence[int], offset: Sequence[int]) -> np.ndarray:
 # ---------------------------------------------------------------------------------
 # RoPE (KLiteInfer "架构": RoPE, 2-D RoPE, MRoPE operators)
 # ---------------------------------------------------------------------------------
-def rope_angles(pos: np.ndarray, pairs: Sequence[int], theta: float = 10000.0) -> np.ndarray:
+def rope_angles(pos: np.ndarray, pairs: Sequence[int], theta: float = 10000.0,
+                global_freq: bool = False) -> np.ndarray:
     """Rotation angle [S, D/2] of every (token, rotary pair).
 
-    Pairs are split into contiguous sections, one per axis in axis order. Pair j of
-    axis k with local index u rotates by pos[:, k] * theta ** (-2u / d_k), where
-    d_k = 2 * pairs[k].
+    Pairs are split into contiguous sections, one per axis in axis order. By default
+    each section has its own frequency ladder: pair j of axis k with local index u
+    rotates by pos[:, k] * theta ** (-2u / d_k), where d_k = 2 * pairs[k]. With
+    ``global_freq`` there is one ladder over all D/2 pairs, as in the MRoPE of the
+    KLiteInfer page's ERNIE decoder (section "架构"): pair j rotates by
+    pos[:, k] * theta ** (-2j / D) and the sections only choose the axis k.
     """
     S = pos.shape[0]
     half = int(sum(pairs))
@@ -91,14 +95,18 @@ def rope_angles(pos: np.ndarray, pairs: Sequence[int], theta: float = 10000.0) -
     for k, pk in enumerate(pairs):
         d_k = 2 * int(pk)
         for u in range(int(pk)):
-            inv_freq = float(theta) ** (-2.0 * u / d_k)
+            if global_freq:
+                inv_freq = float(theta) ** (-2.0 * j / (2 * half))
+            else:
+                inv_freq = float(theta) ** (-2.0 * u / d_k)
             ang[:, j] = pos[:, k].astype(np.float64) * inv_freq
             j += 1
     return ang
 
 
 def rope(x: np.ndarray, grid: Sequence[int], pairs: Sequence[int], offset: Sequence[int],
-         theta: float = 10000.0, interleaved: bool = False, rows: Optional[np.ndarray] = None) -> np.ndarray:
+         theta: float = 10000.0, interleaved: bool = False, rows: Optional[np.ndarray] = None,
+         global_freq: bool = False) -> np.ndarray:
     """Rotate x [S, H, D] (one branch) by the positions of its tokens; returns float64.
 
     Half-split pairs (a, b) = (j, j + D/2), or interleaved (2j, 2j+1):
@@ -114,7 +122,7 @@ def rope(x: np.ndarray, grid: Sequence[int], pairs: Sequence[int], offset: Seque
         pos = pos[np.asarray(rows)]
     if pos.shape[0] != S:
         raise ValueError("x has a different number of tokens than the grid (or rows)")
-    phi = rope_angles(pos, pairs, theta)                               # [S, D/2]
+    phi = rope_angles(pos, pairs, theta, global_freq)                  # [S, D/2]
     c = np.cos(phi)[:, None, :]
     s = np.sin(phi)[:, None, :]
     if interleaved:

@@ -20,14 +20,18 @@ def bf_position(i: int, grid: Sequence[int], offset: Sequence[int]) -> List[int]
 
 
 def bf_rope_token(x: List[float], pos: List[int], pairs: Sequence[int], theta: float,
-                  interleaved: bool) -> List[float]:
+                  interleaved: bool, global_freq: bool = False) -> List[float]:
     D = len(x)
     half = D // 2
     out = list(x)
     j = 0
     for axis, npairs in enumerate(pairs):
         for u in range(npairs):
-            freq = math.pow(theta, -(2.0 * u) / (2.0 * npairs))
+            if global_freq:
+                # one ladder over every pair of the head; the section picks the axis
+                freq = math.pow(theta, -(2.0 * j) / D)
+            else:
+                freq = math.pow(theta, -(2.0 * u) / (2.0 * npairs))
             phi = pos[axis] * freq
             ia, ib = (2 * j, 2 * j + 1) if interleaved else (j, j + half)
             a, b = x[ia], x[ib]
@@ -37,9 +41,10 @@ def bf_rope_token(x: List[float], pos: List[int], pairs: Sequence[int], theta: f
     return out
 
 
-def bf_rope(x, grid, pairs, offset, theta=10000.0, interleaved=False):
+def bf_rope(x, grid, pairs, offset, theta=10000.0, interleaved=False, global_freq=False):
     """x: nested lists [S][H][D] -> rotated nested lists."""
-    return [[bf_rope_token(list(map(float, x[i][h])), bf_position(i, grid, offset), pairs, theta, interleaved)
+    return [[bf_rope_token(list(map(float, x[i][h])), bf_position(i, grid, offset), pairs, theta, interleaved,
+                           global_freq)
              for h in range(len(x[i]))] for i in range(len(x))]
 
 

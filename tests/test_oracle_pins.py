@@ -62,6 +62,31 @@ def test_rope_matches_bruteforce(grid, pairs, offset, D, inter):
     assert _maxrel(got, exp) <= 1e-13
 
 
+@pytest.mark.parametrize("grid,pairs,offset,D,inter", ROPE_CASES[2:])
+def test_rope_global_freq_matches_bruteforce(grid, pairs, offset, D, inter):
+    S = int(np.prod(grid))
+    x = _rand(S, 3, D)
+    got = oracle.rope(x, grid, pairs, offset, 10000.0, inter, global_freq=True)
+    exp = np.array(bf_rope(x.tolist(), grid, pairs, offset, 10000.0, inter, global_freq=True))
+    assert _maxrel(got, exp) <= 1e-13
+
+
+def test_rope_global_freq_reductions():
+    # one axis: the global ladder and the per-axis ladder are the same ladder
+    x = _rand(10, 2, 16)
+    assert np.array_equal(oracle.rope(x, (10,), (8,), (3,), global_freq=True), oracle.rope(x, (10,), (8,), (3,)))
+    # every axis at the same position p: plain 1-D RoPE over the head at position p
+    # (the text-token case of an MRoPE decoder)
+    y = _rand(1, 2, 16)
+    for p in (0, 5, 77):
+        got = oracle.rope(y, (1, 1, 1), (2, 3, 3), (p, p, p), global_freq=True)
+        exp = oracle.rope(y, (1,), (8,), (p,))
+        assert np.max(np.abs(got - exp)) <= 1e-15
+    # the two ladders differ for a multi-axis split (the mode is not a no-op)
+    z = _rand(6, 1, 16)
+    assert not np.allclose(oracle.rope(z, (2, 3), (4, 4), (1, 2), global_freq=True), oracle.rope(z, (2, 3), (4, 4), (1, 2)))
+
+
 ATTN_CASES = [
     # Sq, P, Hq, Hkv, D
     (5, 0, 2, 2, 8),
