@@ -32,7 +32,8 @@ class NxattnError(RuntimeError):
 
 class RopeDesc(ctypes.Structure):
     _fields_ = [("n_axes", ctypes.c_int32), ("grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int32 * 3),
-                ("offset", ctypes.c_int32 * 3), ("theta", ctypes.c_double), ("interleaved", ctypes.c_int32)]
+                ("offset", ctypes.c_int32 * 3), ("theta", ctypes.c_double), ("interleaved", ctypes.c_int32),
+                ("global_freq", ctypes.c_int32)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -114,7 +115,7 @@ def _stream(stream) -> int:
 
 
 def rope_desc(grid: Sequence[int], pairs: Sequence[int], offset: Sequence[int], theta: float = 10000.0,
-              interleaved: bool = False) -> RopeDesc:
+              interleaved: bool = False, global_freq: bool = False) -> RopeDesc:
     d = RopeDesc()
     d.n_axes = len(grid)
     for a in range(3):
@@ -123,6 +124,7 @@ def rope_desc(grid: Sequence[int], pairs: Sequence[int], offset: Sequence[int], 
         d.offset[a] = int(offset[a]) if a < len(offset) else 0
     d.theta = float(theta)
     d.interleaved = 1 if interleaved else 0
+    d.global_freq = 1 if global_freq else 0
     return d
 
 

@@ -127,7 +127,7 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   for (int b = 0; p.rope_q && b < a->batch; ++b) {
     const nxattn_rope_desc& d = a->q_rope[b];
     RopeQ& r = p.rq[b];
-    r.n_axes = d.n_axes; r.interleaved = d.interleaved;
+    r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.global_freq = d.global_freq;
     r.log2_theta = (float)std::log2(d.theta);
     for (int ax = 0; ax < 3; ++ax) {
       r.grid[ax] = ax < d.n_axes ? d.grid[ax] : 1;

@@ -261,7 +261,8 @@ __device__ __forceinline__ void gemm_s_only(Wave& w) {
 }
 
 // RoPE of this lane's q values on load (same convention as the RoPE kernel: pair j of
-// axis k with local index u turns by pos_k * theta^(-u / pairs_k); pairs (j, j + 64)
+// axis k with local index u turns by pos_k * theta^(-u / pairs_k), or with the global
+// ladder by pos_k * theta^(-j / 64); pairs (j, j + 64)
 // or, interleaved, (2j, 2j + 1)). Lane l first evaluates pair l's step in revolutions
 // per position (with its axis in the two low mantissa bits, a 2^-21 relative change);
 // every lane then fetches its pairs' entries with ds_bpermute. The turn pos * step is
@@ -286,8 +287,10 @@ __device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, in
     // axis of pair j = lane as 0/1 weights (a blend keeps the choice in registers)
     const int j = lane, n0 = r.pairs[0], n1 = r.pairs[1], n2 = r.pairs[2];
     const int i0 = j < n0, i1 = (1 - i0) & (j < n0 + n1), i2 = 1 - i0 - i1;
-    const int u = j - i1 * n0 - i2 * (n0 + n1);
-    const int n = i0 * n0 + i1 * n1 + i2 * n2;
+    // per-section ladder (local index u over the section's n pairs) or one ladder over
+    // all pairs (index j over n0 + n1 + n2)
+    const int u = r.global_freq ? j : j - i1 * n0 - i2 * (n0 + n1);
+    const int n = r.global_freq ? n0 + n1 + n2 : i0 * n0 + i1 * n1 + i2 * n2;
     const float step = __builtin_amdgcn_exp2f(-(float)u * r.log2_theta / (float)(n > 0 ? n : 1)) * 0.15915494309189535f;
     entry = (__float_as_uint(step) & ~3u) | (uint32_t)(i1 + 2 * i2);
   }

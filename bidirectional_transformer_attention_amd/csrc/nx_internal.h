@@ -52,7 +52,7 @@ int check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim, co
 // RoPE of q applied on load by the fused attention kernel (axes beyond n_axes have grid
 // 1, pairs 0, offset 0)
 struct RopeQ {
-  int32_t n_axes, interleaved;
+  int32_t n_axes, interleaved, global_freq;
   int32_t grid[3], pairs[3], offset[3];
   float log2_theta;
 };

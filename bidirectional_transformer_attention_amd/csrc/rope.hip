@@ -19,7 +19,7 @@ constexpr int ROPE_TOK = 4;          // tokens per workgroup
 constexpr int ROPE_MAX_HALF = 128;   // head_dim / 2 limit
 
 struct RopeBranch {
-  int32_t n_axes, interleaved;
+  int32_t n_axes, interleaved, global_freq;
   int32_t grid[3], pairs[3], offset[3];
   double log2_theta;
 };
@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void rope_kernel(T* x, int64_t seq, int64_t he
     int axis = 0, u = j;
     while (axis < br.n_axes - 1 && u >= br.pairs[axis]) { u -= br.pairs[axis]; ++axis; }
     const double pos = (double)(coord[axis] + br.offset[axis]);
-    const double inv_freq = exp2(br.log2_theta * (-2.0 * (double)u / (2.0 * (double)br.pairs[axis])));
+    // per-section ladder theta^(-2u / (2 pairs_k)), or one ladder theta^(-2j / D)
+    const double inv_freq = br.global_freq ? exp2(br.log2_theta * (-2.0 * (double)j / (double)D))
+                                           : exp2(br.log2_theta * (-2.0 * (double)u / (2.0 * (double)br.pairs[axis])));
     double sv, cv;
     sincos(pos * inv_freq, &sv, &cv);
     cs[tk][j] = (float)cv;
@@ -142,6 +144,7 @@ int nx::check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim
   if (2 * psum != head_dim) return fail(NXATTN_ERR_INVALID, "%s: 2*sum(pairs) %lld != head_dim", who, (long long)(2 * psum));
   if (!(d.theta > 1.0) || std::isinf(d.theta)) return fail(NXATTN_ERR_INVALID, "%s: theta must be finite and > 1", who);
   if (d.interleaved != 0 && d.interleaved != 1) return fail(NXATTN_ERR_INVALID, "%s: interleaved must be 0 or 1", who);
+  if (d.global_freq != 0 && d.global_freq != 1) return fail(NXATTN_ERR_INVALID, "%s: global_freq must be 0 or 1", who);
   return NXATTN_OK;
 }
 
@@ -165,7 +168,8 @@ extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t he
     const int st = check_rope_desc(d, seq, head_dim, "nxattn_rope_apply");
     if (st != NXATTN_OK) return st;
     RopeBranch& r = args.br[b];
-    r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.log2_theta = std::log2(d.theta);
+    r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.global_freq = d.global_freq;
+    r.log2_theta = std::log2(d.theta);
     for (int a = 0; a < 3; ++a) {
       r.grid[a] = a < d.n_axes ? d.grid[a] : 1;
       r.pairs[a] = a < d.n_axes ? d.pairs[a] : 0;

@@ -65,7 +65,10 @@ int nxattn_kv_relayout(const void* src, void* dst, int64_t layers, int64_t kv_he
  * slowest); the position on axis k is its coordinate plus offset[k]. The head_dim/2
  * rotary pairs are split into contiguous sections, pairs[k] of them for axis k in
  * axis order (sum == head_dim/2). Pair j with local index u in section k rotates by
- * angle pos_k * theta^(-2u / (2*pairs[k])):
+ * angle pos_k * theta^(-2u / (2*pairs[k])) (global_freq == 0: a frequency ladder per
+ * section), or by pos_k * theta^(-2j / head_dim) (global_freq == 1: one ladder over
+ * all pairs, the sections only choose the axis; the MRoPE of the KLiteInfer page's
+ * ERNIE decoder):
  *   a' = a cos - b sin,  b' = a sin + b cos,
  * with (a, b) = (x[j], x[j + head_dim/2]) (interleaved == 0) or (x[2j], x[2j+1]).
  */
@@ -76,6 +79,7 @@ typedef struct {
   int32_t offset[3];     /* position offset per axis (>= 0)             */
   double theta;          /* frequency base (> 1), 10000 in the configs  */
   int32_t interleaved;   /* 0 = half-split pairs, 1 = adjacent pairs    */
+  int32_t global_freq;   /* 0 = ladder per axis section, 1 = one ladder */
 } nxattn_rope_desc;
 
 /*

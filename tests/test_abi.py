@@ -107,6 +107,12 @@ def test_fwd_rejects(lib, kw, code):
     assert nx.last_error() != ""
 
 
+def _bad_global_freq():
+    d = binding.rope_desc((64,), (64,), (0,))
+    d.global_freq = 2
+    return d
+
+
 def _with_q_rope(a, descs):
     arr = (binding.RopeDesc * len(descs))(*descs)
     a._keep = arr
@@ -123,6 +129,8 @@ def _with_q_rope(a, descs):
     (dict(), [binding.rope_desc((8, 8), (16, 16), (0, 0))] * 2, INVALID),
     # theta must exceed 1
     (dict(), [binding.rope_desc((64,), (64,), (0,), theta=0.5)] * 2, INVALID),
+    # global_freq is 0 or 1
+    (dict(), [_bad_global_freq()] * 2, INVALID),
     # a valid q_rope does not skip the other checks (o overlaps q: nothing launches)
     (dict(o=FAKE), [binding.rope_desc((8, 8), (32, 32), (4, 4))] * 2, INVALID),
 ])

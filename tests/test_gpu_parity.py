@@ -96,6 +96,24 @@ def test_rope_strided_interleaved_and_per_branch_offsets():
         assert np.max(np.abs(f64(out[b, :, 1:5]) - ref)) <= 2e-6 * max(1.0, np.max(np.abs(ref)))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rope_global_frequency_ladder(dtype):
+    # one theta ladder over all pairs, the sections choose the axis (3-D MRoPE)
+    note(f"rope global ladder {dtype}")
+    grid, pairs, D = (4, 6, 10), (22, 21, 21), 128
+    S = int(np.prod(grid))
+    x = synth.random_tensor((2, S, 3, D), 23, dtype)
+    d = x.to(DEV)
+    offs = ((0, 0, 0), (12, 12, 12))
+    nx.nxattn_rope_apply(d, [nx.rope_desc(grid, pairs, offs[b], global_freq=True) for b in range(2)])
+    torch.cuda.synchronize()
+    out = d.cpu()
+    tol = 2.0 ** -8 if dtype == torch.bfloat16 else 2e-6
+    for b in range(2):
+        ref = oracle.rope(f64(x[b]), grid, pairs, offs[b], global_freq=True)
+        assert np.max(np.abs(f64(out[b]) - ref) / np.maximum(1.0, np.abs(ref))) <= tol
+
+
 def test_rope_integer_positions_exact():
     # pairs (1, 0): the result is (cos phi, sin phi); the GPU must match the oracle at the
     # expected integer position, not at +-1 (u = 0 has a 1-radian step per position)
@@ -338,12 +356,13 @@ def test_fwd_strided_own_keys_with_prefix():
     assert attention_err(f64(o[0]), ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("grid,pairs,offsets,P,inter", [
-    ((12, 20), (32, 32), ((7, 3), (512, 512)), (70, 0), False),      # 2-D, ragged, two branches
-    ((240,), (64,), ((32,), (0,)), (0, 33), True),                    # 1-D interleaved
-    ((3, 5, 8), (22, 21, 21), ((0, 0, 0), (5, 6, 7)), (16, 64), False),  # 3-D sections
+@pytest.mark.parametrize("grid,pairs,offsets,P,inter,gf", [
+    ((12, 20), (32, 32), ((7, 3), (512, 512)), (70, 0), False, False),      # 2-D, ragged, two branches
+    ((240,), (64,), ((32,), (0,)), (0, 33), True, False),                    # 1-D interleaved
+    ((3, 5, 8), (22, 21, 21), ((0, 0, 0), (5, 6, 7)), (16, 64), False, False),  # 3-D sections
+    ((3, 5, 8), (16, 24, 24), ((2, 0, 0), (9, 9, 9)), (0, 40), False, True),    # 3-D, one global ladder
 ])
-def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter):
+def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter, gf):
     # q rotated inside the kernel == oracle RoPE of q, then attention (k pre-rotated by
     # the oracle and rounded to bf16); q itself stays unchanged
     S, Hq, Hkv, D = int(np.prod(grid)), 8, 2, 128
@@ -353,9 +372,9 @@ def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter):
     v = synth.random_tensor((2, S, Hkv, D), 93, torch.bfloat16)
     pre = [synth.random_tensor((2, p, Hkv, D), 94 + b, torch.bfloat16) if p else None for b, p in enumerate(P)]
     rnd = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
-    k_rot = torch.stack([rnd(oracle.rope(f64(k[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter))
-                         for b in range(2)])
-    descs = [nx.rope_desc(grid, pairs, offsets[b], 10000.0, inter) for b in range(2)]
+    k_rot = torch.stack([rnd(oracle.rope(f64(k[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter,
+                                         global_freq=gf)) for b in range(2)])
+    descs = [nx.rope_desc(grid, pairs, offsets[b], 10000.0, inter, gf) for b in range(2)]
     qd = q.to(DEV)
     o = torch.empty_like(qd)
     nx.nxattn_fwd(qd, k_rot.to(DEV), v.to(DEV), o, [p.to(DEV) if p is not None else None for p in pre],
@@ -363,7 +382,7 @@ def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter):
     torch.cuda.synchronize()
     assert torch.equal(qd.cpu(), q)
     for b in range(2):
-        q_ex = oracle.rope(f64(q[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter)
+        q_ex = oracle.rope(f64(q[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter, global_freq=gf)
         pk = f64(pre[b][0]) if pre[b] is not None else None
         pv = f64(pre[b][1]) if pre[b] is not None else None
         ref = oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv)
