@@ -15,5 +15,7 @@ from .reference import (  # noqa: F401
     rope,
     attention,
     attention_weights,
+    attention_lse,
+    merge_partials,
     cfg_combine,
 )

@@ -205,6 +205,61 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def attention_lse(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                  prefix_k: Optional[np.ndarray] = None, prefix_v: Optional[np.ndarray] = None,
+                  scale: Optional[float] = None, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Log-sum-exp of the scaled scores, [Hq, R] (natural log), of one branch.
+
+    lse_i = log sum_j exp(s_ij) over the same keys as ``attention`` (prefix rows then own
+    rows), with s_ij = scale * <q_i, K_j>; evaluated as m + log sum_j exp(s_ij - m),
+    m = max_j s_ij. It is the softmax normaliser of the KLiteInfer "架构" attention: the
+    weights are exp(s_ij - lse_i).
+    """
+    q = _f64(q)
+    Sq, Hq, D = q.shape
+    K, _ = _keys_values(k, v, prefix_k, prefix_v)
+    Hkv = K.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("heads_q must be a multiple of heads_kv")
+    G = Hq // Hkv
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    r = np.arange(Sq) if rows is None else np.asarray(rows)
+    out = np.zeros((Hq, len(r)), dtype=np.float64)
+    for h in range(Hq):
+        s = sc * (q[r, h, :] @ K[:, h // G, :].T)                   # [R, Skv]
+        m = s.max(axis=1)
+        out[h, :] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
+def merge_partials(parts_o: Sequence[np.ndarray], parts_lse: Sequence[np.ndarray]):
+    """Combine attention results over disjoint key sets into the result over their union.
+
+    parts_o[p] [R, Hq, D] is the attention output over key set p alone and parts_lse[p]
+    [Hq, R] its log-sum-exp (-inf for an empty set). Softmax over the union has the
+    normaliser exp(lse) = sum_p exp(lse_p), and each part's normalised output enters with
+    weight exp(lse_p - lse), so
+        lse = log sum_p exp(lse_p),   o = sum_p exp(lse_p - lse) * o_p.
+    This is the rescaling step of the online softmax (the softmax between the two GEMMs of
+    the KLiteInfer "架构" attention) applied to whole key blocks; it is what a key range
+    split across workgroups, or across devices (the NeoPP replay's sequence-parallel
+    degree), needs. Returns (o [R, Hq, D], lse [Hq, R]).
+    """
+    if len(parts_o) == 0 or len(parts_o) != len(parts_lse):
+        raise ValueError("need one lse per part and at least one part")
+    L = np.stack([_f64(x) for x in parts_lse])                       # [n, Hq, R]
+    m = L.max(axis=0)                                                 # [Hq, R]
+    if not np.all(np.isfinite(m)):
+        raise ValueError("every row needs at least one non-empty part")
+    e = np.exp(L - m[None])                                           # exp(-inf) = 0
+    lse = m + np.log(e.sum(axis=0))
+    wts = np.exp(L - lse[None])                                       # [n, Hq, R]
+    o = np.zeros(_f64(parts_o[0]).shape, dtype=np.float64)
+    for p, op in enumerate(parts_o):
+        o += wts[p].T[:, :, None] * _f64(op)
+    return o, lse
+
+
 # ---------------------------------------------------------------------------------
 # Classifier-free guidance ("Key Parameters": guidance_scale, active above 1.0)
 # ---------------------------------------------------------------------------------

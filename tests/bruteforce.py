@@ -70,3 +70,20 @@ def bf_attention(q, k, v, pk=None, pv=None, scale: Optional[float] = None):
                         for d in range(len(vals[0][g]))])
         out.append(row)
     return out
+
+
+def bf_lse(q, k, pk=None, scale: Optional[float] = None):
+    """q [Sq][Hq][D], k [S][Hkv][D], pk [P][Hkv][D] or None -> [Hq][Sq] of log sum_j exp(s_j)."""
+    Sq, Hq, D = len(q), len(q[0]), len(q[0][0])
+    keys = (list(pk) if pk is not None else []) + list(k)
+    group = Hq // len(keys[0])
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    out = [[0.0] * Sq for _ in range(Hq)]
+    for h in range(Hq):
+        g = h // group
+        for i in range(Sq):
+            s = [sc * math.fsum(float(q[i][h][d]) * float(keys[j][g][d]) for d in range(D))
+                 for j in range(len(keys))]
+            m = max(s)
+            out[h][i] = m + math.log(math.fsum(math.exp(t - m) for t in s))
+    return out

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from bruteforce import bf_attention, bf_position, bf_rope
+from bruteforce import bf_attention, bf_lse, bf_position, bf_rope
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 RNG = np.random.default_rng(1234)
@@ -109,6 +109,84 @@ def test_attention_matches_bruteforce(Sq, P, Hq, Hkv, D):
     exp = np.array(bf_attention(q.tolist(), k.tolist(), v.tolist(),
                                 pk.tolist() if P else None, pv.tolist() if P else None))
     assert _maxrel(got, exp) <= 1e-13
+
+
+@pytest.mark.parametrize("Sq,P,Hq,Hkv,D", ATTN_CASES)
+def test_lse_matches_bruteforce(Sq, P, Hq, Hkv, D):
+    q = _rand(Sq, Hq, D)
+    k = _rand(Sq, Hkv, D)
+    pk = _rand(P, Hkv, D) if P else None
+    got = oracle.attention_lse(q, k, k, pk, pk)
+    exp = np.array(bf_lse(q.tolist(), k.tolist(), pk.tolist() if P else None))
+    assert got.shape == (Hq, Sq)
+    assert np.max(np.abs(got - exp)) <= 1e-12
+
+
+def test_lse_closed_forms():
+    D = 8
+    q = _rand(3, 2, D)
+    k1 = _rand(1, 1, D)
+    # one key: the log-sum-exp is that key's scaled score
+    s = (q[:, :, :] @ k1[0, 0]) / math.sqrt(D)                        # [3, 2]
+    assert np.max(np.abs(oracle.attention_lse(q, k1, k1) - s.T)) <= 1e-14
+    # q = 0: every score is 0, so lse = log(number of keys) (prefix and own both count)
+    z = np.zeros((4, 2, D))
+    assert np.max(np.abs(oracle.attention_lse(z, _rand(4, 1, D), _rand(4, 1, D), _rand(5, 1, D), _rand(5, 1, D))
+                      - math.log(9))) <= 1e-14
+    # n copies of one key: lse = s + log n
+    k5 = np.repeat(k1, 5, axis=0)
+    assert np.max(np.abs(oracle.attention_lse(q, k5, k5) - (s.T + math.log(5)))) <= 1e-13
+    # the softmax weights are exp(s - lse)
+    q2, k2 = _rand(6, 4, D), _rand(6, 2, D)
+    pk2 = _rand(3, 2, D)
+    wts = oracle.attention_weights(q2, k2, k2, pk2, pk2)               # [R, Hq, Skv]
+    keys = np.concatenate([pk2, k2], 0)
+    for h in range(4):
+        sc = q2[:, h, :] @ keys[:, h // 2, :].T / math.sqrt(D)
+        lse = oracle.attention_lse(q2, k2, k2, pk2, pk2)[h]
+        assert np.max(np.abs(np.exp(sc - lse[:, None]) - wts[:, h, :])) <= 1e-14
+
+
+@pytest.mark.parametrize("cuts", [(4,), (3, 9), (1, 6, 10), (5, 6, 7, 8)])
+def test_merge_of_key_splits_matches_bruteforce(cuts):
+    # disjoint contiguous ranges of [prefix ++ own], one of them straddling the prefix end
+    Sq, P, Hq, Hkv, D = 5, 6, 4, 2, 8
+    q, k, v = _rand(Sq, Hq, D), _rand(Sq, Hkv, D), _rand(Sq, Hkv, D)
+    pk, pv = _rand(P, Hkv, D), _rand(P, Hkv, D)
+    K, V = np.concatenate([pk, k], 0), np.concatenate([pv, v], 0)
+    bounds = (0,) + cuts + (P + Sq,)
+    po, pl = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        po.append(oracle.attention(q, K[a:b], V[a:b]))
+        pl.append(oracle.attention_lse(q, K[a:b], V[a:b]))
+    o, lse = oracle.merge_partials(po, pl)
+    exp_o = np.array(bf_attention(q.tolist(), k.tolist(), v.tolist(), pk.tolist(), pv.tolist()))
+    exp_l = np.array(bf_lse(q.tolist(), k.tolist(), pk.tolist()))
+    assert _maxrel(o, exp_o) <= 1e-13
+    assert np.max(np.abs(lse - exp_l)) <= 1e-12
+    # the parts may come in any order
+    o2, lse2 = oracle.merge_partials(po[::-1], pl[::-1])
+    assert _maxrel(o2, o) <= 1e-14 and np.max(np.abs(lse2 - lse)) <= 1e-14
+
+
+def test_merge_special_cases():
+    q, k, v = _rand(4, 2, 8), _rand(7, 1, 8), _rand(7, 1, 8)
+    o, l = oracle.attention(q, k, v), oracle.attention_lse(q, k, v)
+    # one part is returned unchanged
+    o1, l1 = oracle.merge_partials([o], [l])
+    assert _maxrel(o1, o) <= 1e-15 and np.max(np.abs(l1 - l)) <= 1e-15
+    # an empty part (lse = -inf, output 0) changes nothing
+    o2, l2 = oracle.merge_partials([np.zeros_like(o), o], [np.full_like(l, -np.inf), l])
+    assert _maxrel(o2, o) <= 1e-15 and np.max(np.abs(l2 - l)) <= 1e-15
+    # two halves with equal lse: plain average, lse + log 2
+    oa, ob = _rand(4, 2, 8), _rand(4, 2, 8)
+    om, lm = oracle.merge_partials([oa, ob], [l, l])
+    assert _maxrel(om, 0.5 * (oa + ob)) <= 1e-15 and np.max(np.abs(lm - (l + math.log(2)))) <= 1e-14
+    # a part far below the other carries (almost) no weight
+    om, lm = oracle.merge_partials([oa, ob], [l, l - 800.0])
+    assert _maxrel(om, oa) <= 1e-15
+    with pytest.raises(ValueError):
+        oracle.merge_partials([oa], [np.full_like(l, -np.inf)])
 
 
 def test_rope_then_attention_matches_bruteforce():
