@@ -236,7 +236,7 @@ def merge_partials(parts_o: Sequence[np.ndarray], parts_lse: Sequence[np.ndarray
     """Combine attention results over disjoint key sets into the result over their union.
 
     parts_o[p] [R, Hq, D] is the attention output over key set p alone and parts_lse[p]
-    [Hq, R] its log-sum-exp (-inf for an empty set). Softmax over the union has the
+    [Hq, R] its log-sum-exp (-inf for an empty set, whose output values are then ignored). Softmax over the union has the
     normaliser exp(lse) = sum_p exp(lse_p), and each part's normalised output enters with
     weight exp(lse_p - lse), so
         lse = log sum_p exp(lse_p),   o = sum_p exp(lse_p - lse) * o_p.
@@ -256,7 +256,9 @@ def merge_partials(parts_o: Sequence[np.ndarray], parts_lse: Sequence[np.ndarray
     wts = np.exp(L - lse[None])                                       # [n, Hq, R]
     o = np.zeros(_f64(parts_o[0]).shape, dtype=np.float64)
     for p, op in enumerate(parts_o):
-        o += wts[p].T[:, :, None] * _f64(op)
+        # an empty key set has no output (0/0): its term is absent from the sum
+        term = wts[p].T[:, :, None] * _f64(op)
+        o += np.where(np.isneginf(L[p]).T[:, :, None], 0.0, term)
     return o, lse
 
 

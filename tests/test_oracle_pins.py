@@ -178,6 +178,9 @@ def test_merge_special_cases():
     # an empty part (lse = -inf, output 0) changes nothing
     o2, l2 = oracle.merge_partials([np.zeros_like(o), o], [np.full_like(l, -np.inf), l])
     assert _maxrel(o2, o) <= 1e-15 and np.max(np.abs(l2 - l)) <= 1e-15
+    # ... whatever its output holds (an empty set's output is 0/0)
+    o3, _ = oracle.merge_partials([np.full_like(o, np.nan), o], [np.full_like(l, -np.inf), l])
+    assert _maxrel(o3, o) <= 1e-15
     # two halves with equal lse: plain average, lse + log 2
     oa, ob = _rand(4, 2, 8), _rand(4, 2, 8)
     om, lm = oracle.merge_partials([oa, ob], [l, l])
