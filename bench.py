@@ -141,13 +141,14 @@ def main() -> int:
     if wl.branches >= 1 and wl.dtype == "bf16":
         q0, k0, v0, o0 = step.q[:1], step.k[:1], step.v[:1], step.o[:1]
         pre0 = step.prefix_online[:1]
+        split_kw = dict(num_splits=step.splits, workspace=step.workspace)
         for _ in range(3):
-            nx.nxattn_fwd(q0, k0, v0, o0, pre0)
+            nx.nxattn_fwd(q0, k0, v0, o0, pre0, **split_kw)
         h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 20
         h0.record(stream)
         for _ in range(reps):
-            nx.nxattn_fwd(q0, k0, v0, o0, pre0)
+            nx.nxattn_fwd(q0, k0, v0, o0, pre0, **split_kw)
         h1.record(stream)
         torch.cuda.synchronize()
         hms = h0.elapsed_time(h1) / reps
@@ -156,12 +157,16 @@ def main() -> int:
                     "ms": round(hms, 4), "tflops": round(hfl / hms / 1e9, 1),
                     "pct_peak": round(100 * hfl / hms / 1e9 / PEAK[wl.dtype], 2)}
 
+    # with key splits the timed attention phase is the split kernel plus the merge kernel
+    # (both on this stream); rocprofv3 separates the two
     achieved = flops_step / (fwd_avg * 1e-3) / 1e12
     rec = traffic_record()
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[wl.dtype], "unit": "TFLOP/s",
             "frac": round(achieved / PEAK[wl.dtype], 4),
-            "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name else None),
-            "kernel": "nx::bf16k::fwd_bf16_kernel" if wl.dtype == "bf16" else "nx::f32k::fwd_f32_kernel",
+            "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
+                        else None),
+            "kernel": ("nx::bf16k::fwd_bf16_kernel" if wl.dtype == "bf16" else "nx::f32k::fwd_f32_kernel")
+            + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),
             "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_ms[0], 4)}
 
     if args.copy_calibration > 0:
@@ -186,8 +191,10 @@ def main() -> int:
                    "head_dim": wl.head_dim, "rope_offsets": [list(o) for o in wl.offsets],
                    "guidance": wl.guidance, "prefix_layout_in": "replay [2,H,P,D] relaid each step"
                    if wl.prefix_layout == "replay" else "online [2,P,H,D]",
-                   "step": ("relayout + rope(k) + fused attention (q rotated on load) + cfg" if step.fuse_q_rope
-                            else "relayout + rope(q,k) + fused attention + cfg"),
+                   "splits": step.splits,
+                   "step": ("relayout + rope(k) + fused attention (q rotated on load)" if step.fuse_q_rope
+                            else "relayout + rope(q,k) + fused attention")
+                   + (f" over {step.splits} key ranges + merge" if step.splits > 1 else "") + " + cfg",
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},
         "roofline": roof,
         "cpu_baseline": cpu,

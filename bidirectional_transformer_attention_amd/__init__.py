@@ -9,7 +9,9 @@ four calls into one attention step of a DiT layer.
 from .binding import (  # noqa: F401
     NxattnError,
     RopeDesc,
+    fwd_workspace_bytes,
     load,
+    nxattn_attn_merge,
     nxattn_cfg_combine,
     nxattn_fwd,
     nxattn_kv_relayout,

@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libnxattn.so")
 NXATTN_F32 = 0
 NXATTN_BF16 = 1
 MAX_BRANCHES = 8
+MAX_SPLITS = 16
 
-SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_cfg_combine",
-           "nxattn_status_string", "nxattn_last_error", "nxattn_version")
+SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_fwd_workspace_size",
+           "nxattn_attn_merge", "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error",
+           "nxattn_version")
 
 
 class NxattnError(RuntimeError):
@@ -43,7 +45,9 @@ class FwdArgs(ctypes.Structure):
                 ("q_strides", ctypes.c_int64 * 3), ("kv_strides", ctypes.c_int64 * 3),
                 ("o_strides", ctypes.c_int64 * 3),
                 ("prefix_kv", ctypes.c_void_p * MAX_BRANCHES), ("prefix_len", ctypes.c_int32 * MAX_BRANCHES),
-                ("scale", ctypes.c_float), ("q_rope", ctypes.POINTER(RopeDesc))]
+                ("scale", ctypes.c_float), ("q_rope", ctypes.POINTER(RopeDesc)),
+                ("lse", ctypes.c_void_p), ("prefix_only", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -65,6 +69,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nxattn_rope_apply.restype = i32
     lib.nxattn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp]
     lib.nxattn_fwd.restype = i32
+    lib.nxattn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_int64)]
+    lib.nxattn_fwd_workspace_size.restype = i32
+    lib.nxattn_attn_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32, i64, i64, i64, i64,
+                                      ctypes.POINTER(ctypes.c_int64), i32, vp, ctypes.POINTER(ctypes.c_int64), vp,
+                                      vp]
+    lib.nxattn_attn_merge.restype = i32
     lib.nxattn_cfg_combine.argtypes = [vp, vp, vp, i64, ctypes.c_float, i32, vp]
     lib.nxattn_cfg_combine.restype = i32
     lib.nxattn_status_string.argtypes = [i32]
@@ -161,19 +171,25 @@ def nxattn_rope_apply(x: torch.Tensor, descs: List[RopeDesc], stream=None) -> No
     _check(load().nxattn_rope_apply(x.data_ptr(), B, S, H, D, st, _dtype_code(x), arr, _stream(stream)))
 
 
-def make_fwd_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+def make_fwd_args(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: torch.Tensor,
                   prefix: Sequence[Optional[torch.Tensor]], scale: float = 0.0,
-                  q_rope: Optional[Sequence[RopeDesc]] = None) -> FwdArgs:
+                  q_rope: Optional[Sequence[RopeDesc]] = None, lse: Optional[torch.Tensor] = None,
+                  prefix_only: bool = False, num_splits: int = 0,
+                  workspace: Optional[torch.Tensor] = None) -> FwdArgs:
     """FwdArgs for the tensors; q_rope (one RopeDesc per batch entry) is kept alive on
-    the returned object for as long as it is in use."""
+    the returned object for as long as it is in use. k and v may be None with
+    prefix_only (heads_kv then comes from the first prefix)."""
     B, S, Hq, D = q.shape
     a = FwdArgs()
     a.dtype = _dtype_code(q)
-    a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, k.shape[2], D
-    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    hkv = k.shape[2] if k is not None else next(p.shape[2] for p in prefix if p is not None)
+    a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, hkv, D
+    a.q, a.o = q.data_ptr(), o.data_ptr()
+    a.k = k.data_ptr() if k is not None else None
+    a.v = v.data_ptr() if v is not None else None
     for i in range(3):
         a.q_strides[i] = q.stride(i)
-        a.kv_strides[i] = k.stride(i)
+        a.kv_strides[i] = k.stride(i) if k is not None else 0
         a.o_strides[i] = o.stride(i)
     for b in range(MAX_BRANCHES):
         p = prefix[b] if b < len(prefix) else None
@@ -188,38 +204,107 @@ def make_fwd_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
         arr = (RopeDesc * len(q_rope))(*q_rope)
         a._q_rope_keep = arr
         a.q_rope = ctypes.cast(arr, ctypes.POINTER(RopeDesc))
+    a.lse = lse.data_ptr() if lse is not None else None
+    a.prefix_only = 1 if prefix_only else 0
+    a.num_splits = int(num_splits)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     return a
 
 
-def nxattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+def fwd_workspace_bytes(batch: int, seq_q: int, heads_q: int, head_dim: int, num_splits: int) -> int:
+    """Bytes of workspace nxattn_fwd needs for num_splits key ranges (0 if <= 1)."""
+    a = FwdArgs()
+    a.batch, a.seq_q, a.heads_q, a.head_dim, a.num_splits = batch, seq_q, heads_q, head_dim, num_splits
+    n = ctypes.c_int64(0)
+    _check(load().nxattn_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+def nxattn_fwd(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: torch.Tensor,
                prefix: Sequence[Optional[torch.Tensor]] = (), scale: float = 0.0, stream=None,
-               q_rope: Optional[Sequence[RopeDesc]] = None) -> None:
+               q_rope: Optional[Sequence[RopeDesc]] = None, lse: Optional[torch.Tensor] = None,
+               prefix_only: bool = False, num_splits: int = 0,
+               workspace: Optional[torch.Tensor] = None) -> None:
     """o = attention(q, [prefix_k ++ k], [prefix_v ++ v]) for every branch.
 
     q, o [B,S,Hq,D]; k, v [B,S,Hkv,D] (same strides); prefix[b] contiguous [2,P_b,Hkv,D] or None.
     q_rope: None (q already rotated) or one RopeDesc per batch entry, to rotate q on load
     (bf16 only); q itself is left unchanged.
+    lse: None or a contiguous fp32 [B, Hq, S] output for the log-sum-exp of the scores.
+    prefix_only: the keys are the prefix rows alone (k and v may then be None).
+    num_splits > 1: split every branch's keys into that many ranges merged by a second
+    kernel; workspace is a device tensor of at least fwd_workspace_bytes() bytes (one is
+    allocated with torch when None).
     """
-    _gpu(q, k, v, o, *[p for p in prefix if p is not None])
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+    own = [t for t in (k, v) if t is not None]
+    _gpu(q, o, *own, lse, workspace, *[p for p in prefix if p is not None])
+    if not prefix_only and len(own) != 2:
+        raise NxattnError(1, "k and v are required unless prefix_only")
+    if q.dim() != 4 or o.dim() != 4 or any(t.dim() != 4 for t in own):
         raise NxattnError(1, "q, k, v, o must be 4-D [B, S, H, D]")
-    if k.shape != v.shape or k.stride() != v.stride():
+    if len(own) == 2 and (k.shape != v.shape or k.stride() != v.stride()):
         raise NxattnError(1, "k and v must have the same shape and strides")
-    if q.shape[0] != k.shape[0] or q.shape[1] != k.shape[1] or q.shape[3] != k.shape[3] or o.shape != q.shape:
+    if len(own) == 1:
+        raise NxattnError(1, "give both k and v, or neither")
+    if o.shape != q.shape or any(q.shape[0] != t.shape[0] or q.shape[1] != t.shape[1] or q.shape[3] != t.shape[3]
+                                 for t in own):
         raise NxattnError(1, "inconsistent q/k/v/o shapes")
+    if prefix_only and (len(prefix) != q.shape[0] or any(p is None for p in prefix)):
+        raise NxattnError(1, "prefix_only needs one prefix per batch entry")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1])):
+        raise NxattnError(1, "lse must be a contiguous float32 [B, Hq, S] tensor")
     if len(prefix) not in (0, q.shape[0]):
         raise NxattnError(1, "prefix must have one entry per batch entry")
-    for p in prefix:
-        if p is not None and (not p.is_contiguous() or p.dim() != 4 or p.shape[0] != 2
-                              or p.shape[2] != k.shape[2] or p.shape[3] != k.shape[3] or p.dtype != q.dtype):
+    given = [p for p in prefix if p is not None]
+    hkv = k.shape[2] if k is not None else (given[0].shape[2] if given and given[0].dim() == 4 else -1)
+    for p in given:
+        if (not p.is_contiguous() or p.dim() != 4 or p.shape[0] != 2
+                or p.shape[2] != hkv or p.shape[3] != q.shape[3] or p.dtype != q.dtype):
             raise NxattnError(1, "prefix entries must be contiguous [2, P, Hkv, D] of q's dtype")
-    for t in (k, v, o):
+    for t in (*own, o):
         if t.dtype != q.dtype:
             raise NxattnError(1, "q, k, v, o dtypes differ")
     if q_rope is not None and len(q_rope) != q.shape[0]:
         raise NxattnError(1, "q_rope must have one descriptor per batch entry")
-    a = make_fwd_args(q, k, v, o, prefix, scale, q_rope)
+    if num_splits > 1 and workspace is None:
+        n = fwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3], num_splits)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    a = make_fwd_args(q, k, v, o, prefix, scale, q_rope, lse, prefix_only, num_splits, workspace)
     _check(load().nxattn_fwd(ctypes.byref(a), _stream(stream)))
+
+
+def nxattn_attn_merge(parts_o: Sequence[torch.Tensor], parts_lse: Sequence[torch.Tensor], o: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Merge attention results over disjoint key sets (o and lse of each part).
+
+    parts_o[p] [B,S,H,D] (all with the same strides and o's dtype), parts_lse[p] contiguous
+    fp32 [B,H,S]; o [B,S,H,D] may be exactly one of the parts; lse (optional) [B,H,S] fp32
+    may be exactly one of parts_lse.
+    """
+    _gpu(o, lse, *parts_o, *parts_lse)
+    n = len(parts_o)
+    if n != len(parts_lse) or n == 0:
+        raise NxattnError(1, "one lse per part and at least one part are required")
+    if o.dim() != 4:
+        raise NxattnError(1, "o must be [B, S, H, D]")
+    B, S, H, D = o.shape
+    for t in parts_o:
+        if t.shape != o.shape or t.stride() != parts_o[0].stride() or t.dtype != o.dtype:
+            raise NxattnError(1, "parts must share o's shape and dtype and one set of strides")
+    for t in (*parts_lse, *([lse] if lse is not None else [])):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, H, S):
+            raise NxattnError(1, "lse tensors must be contiguous float32 [B, H, S]")
+    if o.stride(3) != 1 or parts_o[0].stride(3) != 1:
+        raise NxattnError(1, "the head_dim dimension must be contiguous")
+    po = (ctypes.c_void_p * n)(*[t.data_ptr() for t in parts_o])
+    pl = (ctypes.c_void_p * n)(*[t.data_ptr() for t in parts_lse])
+    pst = (ctypes.c_int64 * 3)(*parts_o[0].stride()[:3])
+    ost = (ctypes.c_int64 * 3)(*o.stride()[:3])
+    _check(load().nxattn_attn_merge(po, pl, n, B, S, H, D, pst, _dtype_code(o), o.data_ptr(), ost,
+                                    lse.data_ptr() if lse is not None else None, _stream(stream)))
 
 
 def nxattn_cfg_combine(cond: torch.Tensor, uncond: torch.Tensor, out: torch.Tensor, guidance: float,

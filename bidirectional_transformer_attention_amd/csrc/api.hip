@@ -35,6 +35,21 @@ static int64_t extent_bytes(const int64_t st[3], int64_t n0, int64_t n1, int64_t
   return ((n0 - 1) * st[0] + (n1 - 1) * st[1] + (n2 - 1) * st[2] + inner) * es;
 }
 
+// Workspace of a split-key nxattn_fwd: fp32 partial outputs, then (256-byte aligned)
+// their log-sum-exp. Returns false if the sizes are out of range.
+struct SplitLayout { int64_t o_bytes, lse_offset, total; };
+static bool split_layout(int64_t ns, int64_t batch, int64_t seq, int64_t heads, int64_t d, SplitLayout* L) {
+  if (ns < 0 || batch < 0 || seq < 0 || heads < 0 || d < 0) return false;
+  if (ns <= 1) { *L = SplitLayout{0, 0, 0}; return true; }
+  const double approx = (double)ns * batch * seq * heads * (d + 1) * 4.0;
+  if (approx > 4.0e18) return false;
+  const int64_t rows = ns * batch * seq * heads;
+  L->o_bytes = rows * d * 4;
+  L->lse_offset = (L->o_bytes + 255) / 256 * 256;
+  L->total = L->lse_offset + rows * 4 + 256;
+  return true;
+}
+
 }  // namespace nx
 
 using namespace nx;
@@ -54,6 +69,19 @@ extern "C" const char* nxattn_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" const char* nxattn_version(void) { return "0.1.0"; }
 
+extern "C" int nxattn_fwd_workspace_size(const nxattn_fwd_args* a, int64_t* bytes) {
+  clear_error();
+  if (!a || !bytes) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_workspace_size: NULL argument");
+  if (a->num_splits < 0 || a->num_splits > NXATTN_MAX_SPLITS)
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_workspace_size: num_splits %d not in [0, %d]", a->num_splits,
+                NXATTN_MAX_SPLITS);
+  SplitLayout L;
+  if (!split_layout(a->num_splits, a->batch, a->seq_q, a->heads_q, a->head_dim, &L))
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_workspace_size: bad sizes");
+  *bytes = L.total;
+  return NXATTN_OK;
+}
+
 extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   clear_error();
   if (!a) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: args is NULL");
@@ -72,8 +100,14 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   if (a->dtype == NXATTN_F32 && a->head_dim != 64 && a->head_dim != 72)
     return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: f32 supports head_dim 64 or 72, got %d", a->head_dim);
   if (!(a->scale == a->scale) || std::isinf(a->scale)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: scale is not finite");
+  if (a->prefix_only != 0 && a->prefix_only != 1)
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd: prefix_only must be 0 or 1, got %d", a->prefix_only);
+  if (a->num_splits < 0 || a->num_splits > NXATTN_MAX_SPLITS)
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd: num_splits %d not in [0, %d]", a->num_splits, NXATTN_MAX_SPLITS);
   for (int b = 0; b < a->batch; ++b) {
     if (a->prefix_len[b] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: prefix_len[%d] < 0", b);
+    if (a->prefix_only && a->prefix_len[b] == 0)
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: prefix_only needs prefix_len[%d] >= 1", b);
     if ((a->prefix_len[b] > 0) != (a->prefix_kv[b] != nullptr))
       return fail(NXATTN_ERR_INVALID, "nxattn_fwd: prefix_kv[%d] must be non-NULL iff prefix_len[%d] > 0", b, b);
     if ((int64_t)a->prefix_len[b] + a->seq_q > INT32_MAX)
@@ -88,29 +122,54 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
       if (st != NXATTN_OK) return st;
 
     }
-  if (!a->q || !a->k || !a->v || !a->o) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
+  // own k and v are not read with prefix_only
+  const bool own = !a->prefix_only;
+  if (!a->q || !a->o || (own && (!a->k || !a->v))) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
   const int64_t es = esize(a->dtype);
   const int64_t* sts[3] = {a->q_strides, a->kv_strides, a->o_strides};
   for (int t = 0; t < 3; ++t)
     for (int i = 0; i < 3; ++i) {
+      if (t == 1 && !own) continue;
       if (sts[t][i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: negative stride");
       if ((sts[t][i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: stride %lld is not a multiple of 16 bytes", (long long)sts[t][i]);
     }
-  const void* ptrs[4] = {a->q, a->k, a->v, a->o};
-  for (auto p : ptrs)
-    if (!aligned16(p)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: q/k/v/o must be 16-byte aligned");
+  if (!aligned16(a->q) || !aligned16(a->o) || (own && (!aligned16(a->k) || !aligned16(a->v))))
+    return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: q/k/v/o must be 16-byte aligned");
   for (int b = 0; b < a->batch; ++b)
     if (a->prefix_kv[b] && !aligned16(a->prefix_kv[b])) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: prefix_kv[%d] misaligned", b);
-  // the output must not overlap any input
+  if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u))
+    return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: lse is not 4-byte aligned");
+  // outputs (o, lse, workspace) must not overlap any input or each other
   const int64_t D = a->head_dim;
   const int64_t ob = extent_bytes(a->o_strides, a->batch, a->seq_q, a->heads_q, D, es);
   const int64_t qb = extent_bytes(a->q_strides, a->batch, a->seq_q, a->heads_q, D, es);
-  const int64_t kb = extent_bytes(a->kv_strides, a->batch, a->seq_q, a->heads_kv, D, es);
-  if (overlaps(a->o, ob, a->q, qb) || overlaps(a->o, ob, a->k, kb) || overlaps(a->o, ob, a->v, kb))
-    return fail(NXATTN_ERR_INVALID, "nxattn_fwd: o overlaps q, k or v");
-  for (int b = 0; b < a->batch; ++b)
-    if (a->prefix_kv[b] && overlaps(a->o, ob, a->prefix_kv[b], 2LL * a->prefix_len[b] * a->heads_kv * D * es))
-      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: o overlaps prefix_kv[%d]", b);
+  const int64_t kb = own ? extent_bytes(a->kv_strides, a->batch, a->seq_q, a->heads_kv, D, es) : 0;
+  const int64_t lb = a->lse ? (int64_t)a->batch * a->heads_q * a->seq_q * 4 : 0;
+  const int ns = a->num_splits > 1 ? a->num_splits : 1;
+  SplitLayout L;
+  if (!split_layout(ns, a->batch, a->seq_q, a->heads_q, D, &L)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: bad sizes");
+  if (ns > 1) {
+    if (!a->workspace) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: num_splits > 1 needs a workspace");
+    if (!aligned16(a->workspace)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: workspace is not 16-byte aligned");
+    if (a->workspace_bytes < L.total)
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: workspace_bytes %lld < %lld needed for %d splits",
+                  (long long)a->workspace_bytes, (long long)L.total, ns);
+  }
+  const int64_t wb = ns > 1 ? L.total : 0;
+  struct Span { const void* p; int64_t n; const char* name; };
+  const Span outs[3] = {{a->o, ob, "o"}, {a->lse, lb, "lse"}, {a->workspace, wb, "workspace"}};
+  for (int i = 0; i < 3; ++i) {
+    const Span& x = outs[i];
+    if (!x.p || x.n == 0) continue;
+    if (overlaps(x.p, x.n, a->q, qb) || overlaps(x.p, x.n, a->k, kb) || overlaps(x.p, x.n, a->v, kb))
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: %s overlaps q, k or v", x.name);
+    for (int b = 0; b < a->batch; ++b)
+      if (a->prefix_kv[b] && overlaps(x.p, x.n, a->prefix_kv[b], 2LL * a->prefix_len[b] * a->heads_kv * D * es))
+        return fail(NXATTN_ERR_INVALID, "nxattn_fwd: %s overlaps prefix_kv[%d]", x.name, b);
+    for (int j = 0; j < i; ++j)
+      if (outs[j].p && overlaps(x.p, x.n, outs[j].p, outs[j].n))
+        return fail(NXATTN_ERR_INVALID, "nxattn_fwd: %s overlaps %s", x.name, outs[j].name);
+  }
 
   FwdProblem p;
   p.dtype = a->dtype; p.batch = a->batch; p.seq_q = a->seq_q; p.heads_q = a->heads_q;
@@ -135,5 +194,37 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
       r.offset[ax] = ax < d.n_axes ? d.offset[ax] : 0;
     }
   }
-  return a->dtype == NXATTN_BF16 ? launch_fwd_bf16(p, stream) : launch_fwd_f32(p, stream);
+  // key ranges: `per` whole tiles each, per = ceil(max tiles / splits)
+  int64_t tmax = 0;
+  int32_t tiles[NXATTN_MAX_BRANCHES] = {0};
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t skv = (int64_t)a->prefix_len[b] + (own ? a->seq_q : 0);
+    tiles[b] = (int32_t)((skv + KEY_TILE - 1) / KEY_TILE);
+    if (tiles[b] > tmax) tmax = tiles[b];
+  }
+  p.lse = ns > 1 ? nullptr : a->lse;
+  p.prefix_only = a->prefix_only;
+  p.nsplit = ns;
+  p.per = (int32_t)((tmax + ns - 1) / ns);
+  p.part_o = ns > 1 ? static_cast<float*>(a->workspace) : nullptr;
+  p.part_lse = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + L.lse_offset) : nullptr;
+  const int st = a->dtype == NXATTN_BF16 ? launch_fwd_bf16(p, stream) : launch_fwd_f32(p, stream);
+  if (st != NXATTN_OK || ns == 1) return st;
+
+  // merge the key ranges of each branch into o (and lse)
+  MergeProblem m;
+  std::memset(&m, 0, sizeof(m));
+  const int64_t part_rows = (int64_t)a->batch * a->seq_q * a->heads_q;
+  for (int s = 0; s < ns; ++s) {
+    m.po[s] = p.part_o + s * part_rows * D;
+    m.pl[s] = p.part_lse + s * part_rows;
+  }
+  m.per_branch = 1;
+  for (int b = 0; b < a->batch; ++b) m.nparts[b] = (tiles[b] + p.per - 1) / p.per;
+  m.in_dtype = NXATTN_F32; m.out_dtype = a->dtype;
+  m.batch = a->batch; m.seq = a->seq_q; m.heads = a->heads_q; m.head_dim = D;
+  m.is[0] = (int64_t)a->seq_q * a->heads_q * D; m.is[1] = (int64_t)a->heads_q * D; m.is[2] = D;
+  for (int i = 0; i < 3; ++i) m.os[i] = a->o_strides[i];
+  m.o = a->o; m.lse = a->lse;
+  return launch_merge(m, stream);
 }

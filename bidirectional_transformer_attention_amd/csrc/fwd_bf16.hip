@@ -8,7 +8,9 @@
 // Work split. A workgroup of 8 waves serves one (branch, kv head) and 8 query blocks of
 // 32 rows; query blocks enumerate (q head within the GQA group, 32-token chunk), so all
 // 8 waves read the same K/V tiles from LDS (one tile load feeds G heads). Keys are
-// walked in tiles of 64 over the virtual sequence [prefix ++ own].
+// walked in tiles of 64 over the virtual sequence [prefix ++ own], or over one range of
+// whole tiles of it when the keys are split across workgroups (each range then writes a
+// normalised fp32 partial and its log-sum-exp, combined by the merge kernel).
 //
 // Per wave: S^T = K Q^T lives in the 32x32 accumulator layout (lane = query row, 16
 // registers = keys), so row max / row sum are in-lane plus one permlane32 swap; the
@@ -48,12 +50,13 @@ namespace nx {
 namespace bf16k {
 
 constexpr int D = 128;
-constexpr int BN = 64;            // keys per tile
+constexpr int BN = KEY_TILE;      // keys per tile (64)
 constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
 constexpr int ROWB = D * 2;       // bytes per K/V row
 constexpr int TILEB = BN * ROWB;  // bytes per K or V tile (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_T = 8.0f; // running max moves only when it grows by > 2^8
 // raw buffer descriptors for the tile loads: no stride, bounds check effectively off
 // (every steady-state tile lies inside its tensor), 32-bit data format
@@ -69,6 +72,10 @@ struct Args {
   float c;  // scale * log2(e)
   int32_t rope_q;
   RopeQ rq[NXATTN_MAX_BRANCHES];
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int32_t nsplit, per, prefix_only;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -392,18 +399,23 @@ template <bool GROUP_A>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
-  // (kv head, branch) groups in kv-head-major order: each XCD's contiguous share mixes
-  // the CFG branches, whose key counts differ
+  // (kv head, branch, key range) groups in kv-head-major order: each XCD's contiguous
+  // share mixes the CFG branches, whose key counts differ
   const int grp = wg / a.wg_per_group;
-  const int g = grp / a.batch, b = grp % a.batch;
+  const int split = grp % a.nsplit, gb = grp / a.nsplit;
+  const int g = gb / a.batch, b = gb % a.batch;
   const int qb = (wg % a.wg_per_group) * WAVES + wave;
   const bool active = qb < a.nqb;
   const int hq = g * a.group + (active ? qb / a.nchunks : 0);
   const int tok = (active ? qb % a.nchunks : 0) * 32 + n;
   const int tokc = tok < a.seq ? tok : a.seq - 1;
+  // this work item's keys: tiles [t0, t0 + T) of the virtual sequence, keys below kend
   const int P = a.plen[b];
-  const int Skv = P + a.seq;
-  const int T = (Skv + BN - 1) / BN;
+  const int Skv = P + (a.prefix_only ? 0 : a.seq);
+  const int t0 = split * a.per;
+  const int T = min(a.per, (Skv + BN - 1) / BN - t0);
+  if (T <= 0) return;   // empty key range (uniform over the workgroup, before any barrier)
+  const int kend = min((t0 + T) * BN, Skv);
   const float c = a.c;
 
   Wave w;
@@ -450,7 +462,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
       const int slot = lane & 15;
       const int chunk = isv ? (slot ^ ((r & 3) << 2)) : (slot ^ (r & 15));
       int j = t * BN + r;
-      j = j < Skv ? j : Skv - 1;
+      j = j < kend ? j : kend - 1;
       const uint16_t* src;
       if (j < P) src = (isv ? kprefix + (int64_t)P * pstride : kprefix) + (int64_t)j * pstride;
       else src = (isv ? vown : kown) + (int64_t)(j - P) * ks1;
@@ -463,13 +475,17 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   using Half = std::integral_constant<int, 4>;
 
   // Key tiles are processed in natural order, except that a tile straddling the end of
-  // the prefix (when it is not also the last tile) moves to the end: the online softmax
-  // does not depend on the order. Positions [0, nwhole) then hold only whole tiles,
-  // wholly inside the prefix or wholly inside the own keys.
-  const int sb = (P % BN != 0 && P / BN < T - 1) ? P / BN : -1;
-  auto tile_at = [&](int pos) { return (sb < 0 || pos < sb) ? pos : (pos < T - 1 ? pos + 1 : sb); };
-  auto valid_at = [&](int pos) { const int r = Skv - tile_at(pos) * BN; return r < BN ? r : BN; };
-  const bool last_whole = (T - 1) * BN >= P && T * BN <= Skv;
+  // the prefix (when it is not also the range's last tile) moves to the end: the online
+  // softmax does not depend on the order. Positions [0, nwhole) then hold only whole
+  // tiles, wholly inside the prefix or wholly inside the own keys.
+  const int tl = t0 + T - 1;
+  const int sb = (P % BN != 0 && P / BN >= t0 && P / BN < tl) ? P / BN : -1;
+  auto tile_at = [&](int pos) {
+    const int t = t0 + pos;
+    return (sb < 0 || t < sb) ? t : (pos < T - 1 ? t + 1 : sb);
+  };
+  auto valid_at = [&](int pos) { const int r = kend - tile_at(pos) * BN; return r < BN ? r : BN; };
+  const bool last_whole = (tl + 1) * BN <= kend && (tl * BN >= P || (tl + 1) * BN <= P);
   const int nwhole = T - (sb >= 0 ? 1 : 0) - (last_whole ? 0 : 1);
 
   // Steady-state loads of whole tiles (4 waves x 16 rows): a wave-uniform row base in
@@ -581,6 +597,24 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   }
   if (!active || tok >= a.seq) return;
   const float inv = 1.0f / w.l;
+  // log-sum-exp of the scaled scores: sum_j exp2(c s_j - m) = l, so in natural log
+  // lse = ln2 * (m + log2 l)  (l >= 1: the key that set m contributes 1)
+  const float lse = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
+  if (a.nsplit > 1) {
+    // normalised fp32 partial of this key range, and its log-sum-exp
+    const int64_t row = ((int64_t)split * a.batch + b) * a.seq + tok;
+    float* prow = a.part_o + (row * a.heads_q + hq) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * hh;
+        *reinterpret_cast<f32x4*>(prow + d) = f32x4{w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv,
+                                                    w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv};
+      }
+    if (hh == 0) a.part_lse[(((int64_t)split * a.batch + b) * a.heads_q + hq) * a.seq + tok] = lse;
+    return;
+  }
   uint16_t* orow = a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -591,6 +625,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
           u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
                 pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
     }
+  if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = lse;
 }
 
 __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
@@ -616,12 +651,18 @@ int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   a.nchunks = (p.seq_q + 31) / 32;
   const int64_t nqb = (int64_t)a.group * a.nchunks;
   const int64_t wpg = (nqb + WAVES - 1) / WAVES;
-  const int64_t total = wpg * p.heads_kv * p.batch;
+  const int64_t total = wpg * p.heads_kv * p.batch * p.nsplit;
   if (total > INT32_MAX / 2) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: problem too large");
   a.nqb = (int)nqb; a.wg_per_group = (int)wpg; a.total_wg = (int)total;
   a.c = p.scale * LOG2E;
   a.rope_q = p.rope_q;
   for (int b = 0; b < NXATTN_MAX_BRANCHES; ++b) a.rq[b] = p.rq[b];
+  a.lse = p.lse; a.part_o = p.part_o; a.part_lse = p.part_lse;
+  a.nsplit = p.nsplit; a.per = p.per; a.prefix_only = p.prefix_only;
+  if (p.prefix_only) {  // own keys are never read: keep valid (unused) base pointers
+    a.k = a.q; a.v = a.q;
+    a.ks0 = a.ks1 = a.ks2 = 0;
+  }
   fwd_bf16_kernel<<<a.total_wg, THREADS, 0, stream>>>(a);
   return check_launch("nxattn_fwd(bf16)");
 }

@@ -5,7 +5,9 @@
 // Work split: a workgroup (4 waves) serves one (branch, kv head) and 4 query blocks of
 // 32 rows; query blocks enumerate (q head in the group, 32-token chunk), so every wave
 // of a workgroup reads the same K/V tiles. Keys are walked in tiles of 64 over the
-// virtual sequence [prefix ++ own] (the concatenation is only index arithmetic).
+// virtual sequence [prefix ++ own] (the concatenation is only index arithmetic), or
+// over one key range of it when the keys are split (each range then writes a normalised
+// fp32 partial and its log-sum-exp for the merge kernel).
 // Each wave keeps S^T = K Q^T in the MFMA accumulator layout (lane = query, registers
 // = keys), so the running max and sum are per lane; the P^T accumulator registers feed
 // the P V MFMA directly as its B operand (no shuffle). K and V tiles are staged through
@@ -18,9 +20,10 @@ namespace nx {
 namespace f32k {
 
 constexpr int WAVES = 4;
-constexpr int BN = 64;          // keys per tile
+constexpr int BN = KEY_TILE;    // keys per tile (64)
 constexpr int VSTR = 72;        // V row stride in LDS (floats)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_T = 8.0f;   // running max moves only when it grows by > 2^8
 
 struct Args {
@@ -30,6 +33,10 @@ struct Args {
   int32_t plen[NXATTN_MAX_BRANCHES];
   int32_t batch, seq, heads_q, heads_kv, group, nchunks, nqb, wg_per_group, total_wg;
   float c;  // scale * log2(e)
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int32_t nsplit, per, prefix_only;
 };
 
 __device__ __forceinline__ int remap_xcd(int i, int n) {
@@ -52,17 +59,23 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int w = remap_xcd(blockIdx.x, a.total_wg);
-  const int b = w / (a.heads_kv * a.wg_per_group);
-  const int rem = w % (a.heads_kv * a.wg_per_group);
-  const int g = rem / a.wg_per_group;
-  const int qb = (rem % a.wg_per_group) * WAVES + wave;
+  // (branch, kv head, key range) groups of wg_per_group workgroups
+  const int grp = w / a.wg_per_group;
+  const int split = grp % a.nsplit, bg = grp / a.nsplit;
+  const int b = bg / a.heads_kv, g = bg % a.heads_kv;
+  const int rem = w % a.wg_per_group;
+  const int qb = rem * WAVES + wave;
   const bool active = qb < a.nqb;
   const int hq = g * a.group + (active ? qb / a.nchunks : 0);
   const int tok = (active ? qb % a.nchunks : 0) * 32 + n;
   const int tokc = tok < a.seq ? tok : a.seq - 1;
+  // this work item's keys: tiles [t0, t0 + T) of the virtual sequence, keys below kend
   const int P = a.plen[b];
-  const int Skv = P + a.seq;
-  const int T = (Skv + BN - 1) / BN;
+  const int Skv = P + (a.prefix_only ? 0 : a.seq);
+  const int t0 = split * a.per;
+  const int T = min(a.per, (Skv + BN - 1) / BN - t0);
+  if (T <= 0) return;   // empty key range (uniform over the workgroup, before any barrier)
+  const int kend = min((t0 + T) * BN, Skv);
 
   // Q^T operand: k-step s holds Q[tok][hq][2s + hh]
   float qv[D / 2];
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
 
   // tile loader: thread -> (row, 16-byte chunk) items of K and V
   auto key_rows = [&](int j, const float*& kr, const float*& vr) {
-    j = j < Skv ? j : Skv - 1;
+    j = j < kend ? j : kend - 1;
     if (j < P) {
       const float* base = a.prefix[b] + ((int64_t)j * a.heads_kv + g) * D;
       kr = base;
@@ -117,13 +130,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
   float m = -__builtin_inff(), l = 0.f;
 
-  gload(0);
+  gload(t0);
   lstore(0);
   __syncthreads();
 
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < T) gload(t + 1);
+  for (int t = t0; t < t0 + T; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t0 + T) gload(t + 1);
     const float* kb_ = Ks[buf];
     const float* vb_ = Vs[buf];
 
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * st], qv[st], s[kb], 0, 0, 0);
     }
     // mask keys past the end (only the last tile can have them)
-    const int valid = Skv - t * BN;
+    const int valid = kend - t * BN;
     if (valid < BN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vb_[key * VSTR + d], s[kb][i], acc_o[db], 0, 0, 0);
         }
     }
-    if (t + 1 < T) lstore(buf ^ 1);
+    if (t + 1 < t0 + T) lstore(buf ^ 1);
     __syncthreads();
   }
 
@@ -201,7 +214,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   }
   if (!active || tok >= a.seq) return;
   const float inv = 1.0f / l;
-  float* orow = a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2;
+  // log-sum-exp: sum_j exp2(c s_j - m) = l, so lse = ln2 * (m + log2 l)  (l >= 1)
+  const float lse = LN2 * (m + __builtin_amdgcn_logf(l));
+  float* orow;
+  if (a.nsplit > 1) {
+    orow = a.part_o + ((((int64_t)split * a.batch + b) * a.seq + tok) * a.heads_q + hq) * D;
+    if (hh == 0) a.part_lse[(((int64_t)split * a.batch + b) * a.heads_q + hq) * a.seq + tok] = lse;
+  } else {
+    orow = a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2;
+    if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = lse;
+  }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -229,10 +251,16 @@ int launch_fwd_f32(const FwdProblem& p, hipStream_t stream) {
   a.nchunks = (p.seq_q + 31) / 32;
   const int64_t nqb = (int64_t)a.group * a.nchunks;
   const int64_t wpg = (nqb + WAVES - 1) / WAVES;
-  const int64_t total = wpg * p.heads_kv * p.batch;
+  const int64_t total = wpg * p.heads_kv * p.batch * p.nsplit;
   if (total > INT32_MAX / 2) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: problem too large");
   a.nqb = (int)nqb; a.wg_per_group = (int)wpg; a.total_wg = (int)total;
   a.c = p.scale * LOG2E;
+  a.lse = p.lse; a.part_o = p.part_o; a.part_lse = p.part_lse;
+  a.nsplit = p.nsplit; a.per = p.per; a.prefix_only = p.prefix_only;
+  if (p.prefix_only) {  // own keys are never read: keep valid (unused) base pointers
+    a.k = a.q; a.v = a.q;
+    a.ks0 = a.ks1 = a.ks2 = 0;
+  }
   if (p.head_dim == 64)
     fwd_f32_kernel<64><<<a.total_wg, 256, 0, stream>>>(a);
   else

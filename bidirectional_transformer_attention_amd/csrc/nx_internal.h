@@ -67,8 +67,34 @@ struct FwdProblem {
   float scale;
   int32_t rope_q;                       // rotate q on load with rq[b]
   RopeQ rq[NXATTN_MAX_BRANCHES];
+  float* lse;                           // one pass: [batch, heads_q, seq_q] or NULL
+  int32_t prefix_only;                  // keys = prefix rows only
+  // Key ranges: work item `split` of a branch covers tiles [split*per, split*per + per)
+  // (clipped to the branch; empty ranges do nothing). nsplit == 1: per >= every
+  // branch's tile count and the kernel writes o (and lse) directly; nsplit > 1: it
+  // writes normalised fp32 partials part_o [nsplit, batch, seq_q, heads_q, D] and their
+  // log-sum-exp part_lse [nsplit, batch, heads_q, seq_q] for a merge pass.
+  int32_t nsplit, per;
+  float* part_o;
+  float* part_lse;
 };
+constexpr int KEY_TILE = 64;            // keys per tile in both attention kernels
 int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
 int launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
+
+// Merge of per-part attention results (see nxattn_attn_merge). Part p of batch entry b
+// is used for p < nparts[b] (per_branch) or p < n_all.
+struct MergeProblem {
+  const void* po[NXATTN_MAX_SPLITS];
+  const float* pl[NXATTN_MAX_SPLITS];
+  int32_t n_all, per_branch;
+  int32_t nparts[NXATTN_MAX_BRANCHES];
+  int in_dtype, out_dtype;
+  int64_t batch, seq, heads, head_dim;
+  int64_t is[3], os[3];
+  void* o;
+  float* lse;
+};
+int launch_merge(const MergeProblem& m, hipStream_t stream);
 
 }  // namespace nx

@@ -3,7 +3,8 @@
     relayout (replay -> online, when the prefix arrives in the replay layout)
     -> RoPE on own k, and on own q unless the attention kernel rotates q as it loads it
        (the bf16 path; every branch with its own offsets)
-    -> fused attention over [prefix ++ own] for all branches in one launch
+    -> fused attention over [prefix ++ own] for all branches in one launch (or, with
+       key splits, one launch over key ranges plus one merge launch)
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
 
 Only tensor allocation and argument marshalling happen here; every step runs in the HIP
@@ -21,8 +22,10 @@ from .synth import Inputs, Workload
 
 
 class AttentionStep:
-    def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None):
+    def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None,
+                 splits: Optional[int] = None):
         self.wl = wl
+        self.splits = wl.splits if splits is None else int(splits)
         # bf16: q is rotated inside the attention kernel (no separate pass over q)
         self.fuse_q_rope = (wl.dtype == "bf16") if fuse_q_rope is None else bool(fuse_q_rope)
         dev = torch.device(device)
@@ -49,6 +52,11 @@ class AttentionStep:
                 self.prefix_online.append(on)
         self.descs = [nx.rope_desc(wl.grid, wl.pairs, wl.offsets[b], wl.theta) for b in range(self.B)]
         self.o = torch.empty_like(self.q)
+        # workspace of the key-range partials, allocated once outside the step
+        self.workspace = None
+        if self.splits > 1:
+            n = nx.fwd_workspace_bytes(self.B, self.S, self.Hq, self.D, self.splits)
+            self.workspace = torch.empty(n, dtype=torch.uint8, device=dev)
         self.use_cfg = self.B == 2 and wl.guidance > 1.0
         self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
 
@@ -64,7 +72,8 @@ class AttentionStep:
 
     def attention(self) -> None:
         nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online,
-                      q_rope=self.descs if self.fuse_q_rope else None)
+                      q_rope=self.descs if self.fuse_q_rope else None,
+                      num_splits=self.splits, workspace=self.workspace)
 
     def cfg(self) -> None:
         if self.use_cfg:

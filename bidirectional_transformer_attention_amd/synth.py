@@ -22,6 +22,13 @@ checkpoints):
 * ``video_bf16`` video DiT step: 21 latent frames x 30x52 patches (32760 tokens),
                  3-D RoPE (t,h,w), 12 heads, D 128, prefixes of 256, guidance 6.0
                  (LingBot-Video page, "Key Parameters": multiples of 16, 4n+1 frames).
+* ``longctx_bf16`` a short query against a long conditioning prefix: 32x32 latent
+                 grid (1024 tokens) with 2-D RoPE offset by 16384, 32 q / 8 kv heads,
+                 D 128, prefixes of 16384 (cond) and 256 (uncond) tokens, guidance
+                 4.0. Not one of the pages' measured shapes: it stands for a DiT
+                 conditioned on a long injected KV cache (NeoPP page, intro), where one
+                 workgroup per query block leaves most of the GPU idle; the step splits
+                 the keys into 4 ranges.
 
 Seeds: ``1_000_000*c + 1000*layer + 10*branch + t`` with t = 0 q, 1 own k, 2 own v,
 3 prefix k, 4 prefix v; values drawn in fp32 on the CPU with ``torch.Generator`` and
@@ -55,6 +62,7 @@ class Workload:
     guidance: float = 1.0
     prefix_layout: str = "online"  # "online" [2,P,H,D] or "replay" [2,H,P,D]
     theta: float = 10000.0
+    splits: int = 0               # key ranges per branch in the attention call (0: one pass)
 
     @property
     def seq(self) -> int:
@@ -84,6 +92,8 @@ WORKLOADS: Dict[str, Workload] = {
                            (1024, 128), 32, 8, 128, guidance=4.0, prefix_layout="replay"),
     "video_bf16": Workload("video_bf16", 5, "bf16", 2, (21, 30, 52), (22, 21, 21), ((0, 0, 0), (0, 0, 0)),
                            (256, 256), 12, 12, 128, guidance=6.0),
+    "longctx_bf16": Workload("longctx_bf16", 6, "bf16", 2, (32, 32), (32, 32), ((16384, 16384), (16384, 16384)),
+                             (16384, 256), 32, 8, 128, guidance=4.0, splits=4),
 }
 
 

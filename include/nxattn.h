@@ -38,6 +38,7 @@ typedef enum {
 typedef enum { NXATTN_F32 = 0, NXATTN_BF16 = 1 } nxattn_dtype;
 
 #define NXATTN_MAX_BRANCHES 8
+#define NXATTN_MAX_SPLITS 16
 
 /*
  * KV relayout between the replay-file layout and the online layout.
@@ -123,6 +124,32 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * of the rotated value, which is rounded to nearest even as a stored q would be).
  * BF16 only: F32 with q_rope returns NXATTN_ERR_UNSUPPORTED (rotate with
  * nxattn_rope_apply, whose fp64 angles keep the fp32 path exact to 1e-4).
+ *
+ * The fields after q_rope are off when zero (a zero-initialised struct keeps the
+ * behaviour above). They are the softmax normaliser of the same attention (KLiteInfer
+ * page, "架构": the softmax between the two GEMMs) and the block form of its online
+ * rescale, which a key range split over workgroups, or over devices (the NeoPP
+ * replay's sequence-parallel degree), needs.
+ *
+ * lse (optional, device, fp32 [batch, heads_q, seq_q] contiguous, 4-byte aligned):
+ *   lse[b, h, i] = log sum_j exp(s_j), natural log, over the keys of query (b, h, i),
+ *   s_j including the scale; then softmax(s)_j = exp(s_j - lse). Must not overlap o or
+ *   any input. With it, results over disjoint key sets combine with nxattn_attn_merge.
+ * prefix_only (0 or 1): 1 = the keys are the prefix rows alone (every prefix_len[b] >= 1;
+ *   k, v and kv_strides are not read and may be NULL / zero). Attention over the own
+ *   keys alone is a call with no prefix; the two merge into the full result.
+ * num_splits (0 or 1: one pass; 2 .. NXATTN_MAX_SPLITS): every branch's key range is
+ *   cut into ranges of `per` whole 64-key tiles, per = ceil(max_b tiles_b / num_splits),
+ *   so branch b uses ceil(tiles_b / per) <= num_splits ranges. Each range runs in its
+ *   own workgroups, which write an fp32 partial output and log-sum-exp into the
+ *   workspace; a second kernel on the same stream merges them (the arithmetic of
+ *   nxattn_attn_merge) into o, and into lse if given. For problems with too few
+ *   workgroups to fill the GPU (batch * heads_kv * ceil(heads_q/heads_kv *
+ *   ceil(seq_q/32) / 8) well under 256 for BF16, a short query against a long prefix)
+ *   or with branches of very different key counts.
+ * workspace, workspace_bytes: with num_splits > 1, 16-byte aligned device memory of at
+ *   least nxattn_fwd_workspace_size() bytes, overlapping nothing else; its contents on
+ *   entry do not matter and it is busy until the merge kernel has run on `stream`.
  */
 typedef struct {
   int32_t dtype;
@@ -142,9 +169,48 @@ typedef struct {
   int32_t prefix_len[NXATTN_MAX_BRANCHES];
   float scale;
   const nxattn_rope_desc* q_rope;   /* NULL, or batch descriptors (see above)        */
+  float* lse;                       /* NULL, or [batch, heads_q, seq_q] fp32 output  */
+  int32_t prefix_only;              /* 1: keys = prefix rows only                     */
+  int32_t num_splits;               /* 0/1: one pass; 2..NXATTN_MAX_SPLITS key ranges */
+  void* workspace;                  /* num_splits > 1: caller's device scratch        */
+  int64_t workspace_bytes;
 } nxattn_fwd_args;
 
 int nxattn_fwd(const nxattn_fwd_args* args, hipStream_t stream);
+
+/*
+ * Workspace bytes that nxattn_fwd needs for args->num_splits (0 when num_splits <= 1):
+ * num_splits * batch * seq_q * heads_q * (head_dim + 1) * 4 plus 256 bytes of alignment.
+ * Checks only the sizes it reads (NXATTN_ERR_INVALID if negative or out of range).
+ */
+int nxattn_fwd_workspace_size(const nxattn_fwd_args* args, int64_t* bytes);
+
+/*
+ * Merge attention results over disjoint key sets into the result over their union:
+ *   lse = log sum_p exp(lse_p),   o = sum_p exp(lse_p - lse) * o_p.
+ * The softmax of the KLiteInfer page's "架构" attention over a union of key blocks is
+ * the weighted sum of the blocks' normalised outputs (the online-softmax rescale); the
+ * NeoPP replay splits work over a sequence-parallel degree, whose key blocks combine
+ * this way. Typical use: nxattn_fwd with lse over the own keys (no prefix) and again
+ * with prefix_only over each prefix block, then one merge.
+ *
+ * part_o:   host array of n_parts device pointers, each [batch, seq, heads, head_dim]
+ *           of `dtype` with part_strides (elements {b, s, h}; head_dim contiguous).
+ * part_lse: host array of n_parts device pointers, each fp32 [batch, heads, seq]
+ *           contiguous; -inf marks an empty part (its o_p is then not used). Every row
+ *           needs one finite lse_p; a row with none gets NaN.
+ * o:        output [batch, seq, heads, head_dim] of `dtype` with o_strides; it may be
+ *           exactly one of the parts (same pointer and strides: in-place accumulation).
+ * lse:      NULL, or fp32 [batch, heads, seq] contiguous output; it may be exactly one
+ *           of part_lse. Any other overlap between outputs and inputs is
+ *           NXATTN_ERR_INVALID.
+ * Arithmetic in fp32; bf16 output rounded to nearest even. 1 <= n_parts <=
+ * NXATTN_MAX_SPLITS; head_dim a multiple of 8, at most 256; dtype F32 or BF16.
+ */
+int nxattn_attn_merge(const void* const* part_o, const float* const* part_lse, int32_t n_parts,
+                      int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                      const int64_t part_strides[3], int dtype, void* o, const int64_t o_strides[3],
+                      float* lse, hipStream_t stream);
 
 /*
  * Classifier-free guidance: out = uncond + guidance * (cond - uncond) over n elements.

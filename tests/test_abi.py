@@ -139,6 +139,82 @@ def test_fwd_q_rope_rejects(lib, kw, descs, code):
     assert nx.last_error() != ""
 
 
+GB = 1 << 30
+WS = FAKE + 8 * GB          # a workspace / lse address clear of q, k, v and o
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(lse=FAKE + 8 * GB + 2), ALIGN, "lse"),
+    (dict(lse=FAKE), INVALID, "lse overlaps q"),
+    (dict(lse=FAKE + (1 << 32) + 64), INVALID, "lse overlaps o"),
+    (dict(prefix_only=2), INVALID, "prefix_only"),
+    (dict(prefix_only=1), INVALID, "prefix_len"),                     # no prefix at all
+    (dict(prefix_only=1, prefix_len=(8, 8), prefix_kv=(FAKE + 2 * GB, FAKE + 3 * GB), k=None, v=None,
+          o=FAKE), INVALID, "o overlaps q"),                             # k/v NULL accepted, next check fires
+    (dict(num_splits=17), INVALID, "num_splits"),
+    (dict(num_splits=-1), INVALID, "num_splits"),
+    (dict(num_splits=4), INVALID, "workspace"),                         # no workspace
+    (dict(num_splits=4, workspace=WS + 8, workspace_bytes=1 << 30), ALIGN, "workspace"),
+    (dict(num_splits=4, workspace=WS, workspace_bytes=1024), INVALID, "workspace_bytes"),
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=1 << 30), INVALID, "workspace overlaps q"),
+    (dict(num_splits=4, workspace=WS, workspace_bytes=1 << 30, lse=WS + 4096), INVALID, "overlaps lse"),
+])
+def test_fwd_lse_split_rejects(lib, kw, code, msg):
+    assert call_fwd(lib, fwd_args(**kw)) == code
+    assert msg in nx.last_error()
+
+
+def test_fwd_workspace_size(lib):
+    n = ctypes.c_int64(-1)
+    for ns in (0, 1):
+        assert lib.nxattn_fwd_workspace_size(ctypes.byref(fwd_args(num_splits=ns)), ctypes.byref(n)) == OK
+        assert n.value == 0
+    assert lib.nxattn_fwd_workspace_size(ctypes.byref(fwd_args(num_splits=4)), ctypes.byref(n)) == OK
+    rows = 4 * 2 * 64 * 8
+    assert rows * (128 + 1) * 4 <= n.value <= rows * (128 + 1) * 4 + 512
+    assert binding.fwd_workspace_bytes(2, 64, 8, 128, 4) == n.value
+    assert lib.nxattn_fwd_workspace_size(ctypes.byref(fwd_args(num_splits=17)), ctypes.byref(n)) == INVALID
+    assert lib.nxattn_fwd_workspace_size(None, ctypes.byref(n)) == INVALID
+
+
+def merge_call(lib, po, pl, n=None, B=2, S=64, H=8, D=128, pst=None, dtype=1, o=FAKE + 16 * GB, ost=None,
+               lse=None):
+    n = len(po) if n is None else n
+    st = (S * H * D, H * D, D)
+    P = (ctypes.c_void_p * max(1, len(po)))(*po)
+    L = (ctypes.c_void_p * max(1, len(pl)))(*pl)
+    return lib.nxattn_attn_merge(P, L, n, B, S, H, D, (ctypes.c_int64 * 3)(*(pst or st)), dtype, o,
+                                 (ctypes.c_int64 * 3)(*(ost or st)), lse, None)
+
+
+def test_merge_rejects(lib):
+    po = [FAKE, FAKE + GB]
+    pl = [FAKE + 2 * GB, FAKE + 3 * GB]
+    assert merge_call(lib, po, pl, dtype=5) == UNSUPPORTED
+    assert merge_call(lib, po, pl, n=0) == INVALID
+    assert merge_call(lib, po * 9, pl * 9) == INVALID                 # 18 parts
+    assert merge_call(lib, po, pl, D=12) == UNSUPPORTED
+    assert merge_call(lib, po, pl, D=264) == UNSUPPORTED
+    assert merge_call(lib, po, pl, B=-1) == INVALID
+    assert merge_call(lib, [FAKE, None], pl) == INVALID
+    assert merge_call(lib, [FAKE + 8, FAKE + GB], pl) == ALIGN
+    assert merge_call(lib, po, [FAKE + 2 * GB + 2, FAKE + 3 * GB]) == ALIGN
+    assert merge_call(lib, po, pl, o=FAKE + 16 * GB + 8) == ALIGN
+    assert merge_call(lib, po, pl, lse=FAKE + 17 * GB + 1) == ALIGN
+    assert merge_call(lib, po, pl, pst=(64 * 8 * 128, 8 * 128 + 4, 128)) == ALIGN
+    # overlaps: o partly over a part, o exactly a part but with other strides, o over an
+    # lse, lse partly over a part's lse, lse over a part's output, lse over o
+    assert merge_call(lib, po, pl, o=FAKE + 256) == INVALID
+    assert merge_call(lib, po, pl, o=FAKE, ost=(64 * 8 * 256, 8 * 256, 256)) == INVALID
+    assert merge_call(lib, po, pl, o=FAKE + 2 * GB) == INVALID
+    assert merge_call(lib, po, pl, lse=FAKE + 2 * GB + 64) == INVALID
+    assert merge_call(lib, po, pl, lse=FAKE + GB + 64) == INVALID
+    assert merge_call(lib, po, pl, lse=FAKE + 16 * GB + 64) == INVALID
+    assert "overlaps" in nx.last_error()
+    # empty problems return before anything else is looked at
+    assert merge_call(lib, po, pl, S=0) == OK
+
+
 def test_fwd_null_args(lib):
     assert lib.nxattn_fwd(None, None) == INVALID
 

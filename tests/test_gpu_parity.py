@@ -453,6 +453,13 @@ def test_step_dit1k_bf16_sampled():
     step_case("dit1k_bf16", 96, 3)
 
 
+def test_step_longctx_split_keys_sampled():
+    # a short query against a long prefix, keys split into ranges and merged, in the
+    # launch configuration the benchmark times
+    wl = step_case("longctx_bf16+replay", 48, 6)
+    assert wl.splits > 1
+
+
 def test_step_bench_configuration_sampled():
     # exactly what bench.py times: dit1k with the prefix delivered in the replay layout
     step_case("dit1k_bf16+replay", 64, 6)
