@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--workload", default="dit1k_bf16")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="query rows per branch for the CPU oracle timing (0: all, i.e. one whole step)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="key ranges per branch in the attention call (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after timing, relayout one buffer of this many MB (a plain copy of known size "
@@ -109,7 +111,7 @@ def main() -> int:
     wl = synth.bench_workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    step = AttentionStep(wl, synth.make_inputs(wl), "cuda:0")
+    step = AttentionStep(wl, synth.make_inputs(wl), "cuda:0", splits=args.splits)
     flops_step = wl.flops()
 
     for _ in range(args.warmup):

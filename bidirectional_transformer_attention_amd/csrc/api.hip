@@ -1,6 +1,7 @@
 // Host side of the nxattn C ABI: error reporting, status strings and the validation
 // and dispatch of nxattn_fwd (the relayout, RoPE and CFG entry points live beside
 // their kernels).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -145,7 +146,7 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   const int64_t qb = extent_bytes(a->q_strides, a->batch, a->seq_q, a->heads_q, D, es);
   const int64_t kb = own ? extent_bytes(a->kv_strides, a->batch, a->seq_q, a->heads_kv, D, es) : 0;
   const int64_t lb = a->lse ? (int64_t)a->batch * a->heads_q * a->seq_q * 4 : 0;
-  const int ns = a->num_splits > 1 ? a->num_splits : 1;
+  int ns = a->num_splits > 1 ? a->num_splits : 1;
   SplitLayout L;
   if (!split_layout(ns, a->batch, a->seq_q, a->heads_q, D, &L)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: bad sizes");
   if (ns > 1) {
@@ -194,18 +195,36 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
       r.offset[ax] = ax < d.n_axes ? d.offset[ax] : 0;
     }
   }
-  // key ranges: `per` whole tiles each, per = ceil(max tiles / splits)
-  int64_t tmax = 0;
+  // Key ranges of `per` whole tiles. The range length is at least ceil(max tiles /
+  // num_splits) and at least the tile work per resident workgroup slot of the GPU
+  // (sum over branches of tiles * workgroups per range, over the workgroups the GPU
+  // holds at once): ranges no shorter than a fair share leave no slot idle while one
+  // runs, and a branch shorter than a range stays whole (no partial, no merge). With
+  // per >= every branch's tiles the call is one pass.
+  int64_t tmax = 0, tsum = 0;
   int32_t tiles[NXATTN_MAX_BRANCHES] = {0};
   for (int b = 0; b < a->batch; ++b) {
     const int64_t skv = (int64_t)a->prefix_len[b] + (own ? a->seq_q : 0);
     tiles[b] = (int32_t)((skv + KEY_TILE - 1) / KEY_TILE);
     if (tiles[b] > tmax) tmax = tiles[b];
+    tsum += tiles[b];
   }
-  p.lse = ns > 1 ? nullptr : a->lse;
   p.prefix_only = a->prefix_only;
+  int64_t per = tmax;
+  if (ns > 1) {
+    const FwdShape sh = a->dtype == NXATTN_BF16 ? fwd_shape_bf16(p) : fwd_shape_f32(p);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return fail(NXATTN_ERR_HIP, "nxattn_fwd: cannot query the device's compute units");
+    const int64_t slots = (int64_t)cus * sh.resident_per_cu;
+    const int64_t fair = (sh.wgs_per_range * tsum + slots - 1) / slots;
+    per = std::max<int64_t>((tmax + ns - 1) / ns, fair);
+    if (per >= tmax) { per = tmax; ns = 1; }
+    else ns = (int)((tmax + per - 1) / per);
+  }
+  p.lse = a->lse;
   p.nsplit = ns;
-  p.per = (int32_t)((tmax + ns - 1) / ns);
+  p.per = (int32_t)per;
   p.part_o = ns > 1 ? static_cast<float*>(a->workspace) : nullptr;
   p.part_lse = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + L.lse_offset) : nullptr;
   const int st = a->dtype == NXATTN_BF16 ? launch_fwd_bf16(p, stream) : launch_fwd_f32(p, stream);

@@ -413,8 +413,11 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   const int P = a.plen[b];
   const int Skv = P + (a.prefix_only ? 0 : a.seq);
   const int t0 = split * a.per;
-  const int T = min(a.per, (Skv + BN - 1) / BN - t0);
+  const int Tall = (Skv + BN - 1) / BN;
+  const int T = min(a.per, Tall - t0);
   if (T <= 0) return;   // empty key range (uniform over the workgroup, before any barrier)
+  // a branch whose keys fit in one range writes its result directly, without a merge
+  const bool partial = a.nsplit > 1 && Tall > a.per;
   const int kend = min((t0 + T) * BN, Skv);
   const float c = a.c;
 
@@ -600,7 +603,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   // log-sum-exp of the scaled scores: sum_j exp2(c s_j - m) = l, so in natural log
   // lse = ln2 * (m + log2 l)  (l >= 1: the key that set m contributes 1)
   const float lse = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
-  if (a.nsplit > 1) {
+  if (partial) {
     // normalised fp32 partial of this key range, and its log-sum-exp
     const int64_t row = ((int64_t)split * a.batch + b) * a.seq + tok;
     float* prow = a.part_o + (row * a.heads_q + hq) * D;
@@ -636,6 +639,18 @@ __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
 }
 
 }  // namespace bf16k
+
+FwdShape fwd_shape_bf16(const FwdProblem& p) {
+  using namespace bf16k;
+  static int per_cu = -1;   // resident workgroups per CU (registers and LDS bound it)
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel, THREADS, 0) != hipSuccess || n < 1) n = 1;
+    per_cu = n;
+  }
+  const int64_t nqb = (int64_t)(p.heads_q / p.heads_kv) * ((p.seq_q + 31) / 32);
+  return FwdShape{(nqb + WAVES - 1) / WAVES * p.heads_kv, per_cu};
+}
 
 int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   using namespace bf16k;

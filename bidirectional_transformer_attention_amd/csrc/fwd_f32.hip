@@ -73,8 +73,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   const int P = a.plen[b];
   const int Skv = P + (a.prefix_only ? 0 : a.seq);
   const int t0 = split * a.per;
-  const int T = min(a.per, (Skv + BN - 1) / BN - t0);
+  const int Tall = (Skv + BN - 1) / BN;
+  const int T = min(a.per, Tall - t0);
   if (T <= 0) return;   // empty key range (uniform over the workgroup, before any barrier)
+  // a branch whose keys fit in one range writes its result directly, without a merge
+  const bool partial = a.nsplit > 1 && Tall > a.per;
   const int kend = min((t0 + T) * BN, Skv);
 
   // Q^T operand: k-step s holds Q[tok][hq][2s + hh]
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   // log-sum-exp: sum_j exp2(c s_j - m) = l, so lse = ln2 * (m + log2 l)  (l >= 1)
   const float lse = LN2 * (m + __builtin_amdgcn_logf(l));
   float* orow;
-  if (a.nsplit > 1) {
+  if (partial) {
     orow = a.part_o + ((((int64_t)split * a.batch + b) * a.seq + tok) * a.heads_q + hq) * D;
     if (hh == 0) a.part_lse[(((int64_t)split * a.batch + b) * a.heads_q + hq) * a.seq + tok] = lse;
   } else {
@@ -236,6 +239,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
 }
 
 }  // namespace f32k
+
+FwdShape fwd_shape_f32(const FwdProblem& p) {
+  using namespace f32k;
+  static int per_cu[2] = {-1, -1};   // resident workgroups per CU, D = 64 / 72
+  const int i = p.head_dim == 64 ? 0 : 1;
+  if (per_cu[i] < 0) {
+    int n = 0;
+    const hipError_t e = i == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<64>, 256, 0)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<72>, 256, 0);
+    per_cu[i] = (e != hipSuccess || n < 1) ? 1 : n;
+  }
+  const int64_t nqb = (int64_t)(p.heads_q / p.heads_kv) * ((p.seq_q + 31) / 32);
+  return FwdShape{(nqb + WAVES - 1) / WAVES * p.heads_kv, per_cu[i]};
+}
 
 int launch_fwd_f32(const FwdProblem& p, hipStream_t stream) {
   using namespace f32k;

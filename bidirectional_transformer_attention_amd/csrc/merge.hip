@@ -72,6 +72,7 @@ __global__ __launch_bounds__(THREADS) void merge_kernel(Args a) {
   if (a.per_branch) {
 #pragma unroll
     for (int i = 0; i < NXATTN_MAX_BRANCHES; ++i) n = (uint32_t)i == b ? a.nparts[i] : n;
+    if (n <= 1) return;                         // written directly by the attention kernel
   }
   const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq + s;
   float lv[NXATTN_MAX_SPLITS];

@@ -70,20 +70,27 @@ struct FwdProblem {
   float* lse;                           // one pass: [batch, heads_q, seq_q] or NULL
   int32_t prefix_only;                  // keys = prefix rows only
   // Key ranges: work item `split` of a branch covers tiles [split*per, split*per + per)
-  // (clipped to the branch; empty ranges do nothing). nsplit == 1: per >= every
-  // branch's tile count and the kernel writes o (and lse) directly; nsplit > 1: it
-  // writes normalised fp32 partials part_o [nsplit, batch, seq_q, heads_q, D] and their
-  // log-sum-exp part_lse [nsplit, batch, heads_q, seq_q] for a merge pass.
+  // (clipped to the branch; empty ranges do nothing). A branch with at most `per` tiles
+  // (every branch when nsplit == 1) is one range and its o (and lse) are written
+  // directly; the ranges of a longer branch write normalised fp32 partials part_o
+  // [nsplit, batch, seq_q, heads_q, D] and their log-sum-exp part_lse
+  // [nsplit, batch, heads_q, seq_q] for the merge pass.
   int32_t nsplit, per;
   float* part_o;
   float* part_lse;
 };
 constexpr int KEY_TILE = 64;            // keys per tile in both attention kernels
+// Launch shape of an attention kernel for a problem: workgroups per key range of one
+// branch (all kv heads and query blocks) and workgroups resident per CU.
+struct FwdShape { int64_t wgs_per_range; int resident_per_cu; };
+FwdShape fwd_shape_bf16(const FwdProblem& p);
+FwdShape fwd_shape_f32(const FwdProblem& p);
 int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream);
 int launch_fwd_f32(const FwdProblem& p, hipStream_t stream);
 
 // Merge of per-part attention results (see nxattn_attn_merge). Part p of batch entry b
-// is used for p < nparts[b] (per_branch) or p < n_all.
+// is used for p < nparts[b] (per_branch; rows of a batch entry with one part were
+// written directly and are skipped) or p < n_all.
 struct MergeProblem {
   const void* po[NXATTN_MAX_SPLITS];
   const float* pl[NXATTN_MAX_SPLITS];

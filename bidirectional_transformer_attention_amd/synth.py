@@ -28,7 +28,7 @@ checkpoints):
                  4.0. Not one of the pages' measured shapes: it stands for a DiT
                  conditioned on a long injected KV cache (NeoPP page, intro), where one
                  workgroup per query block leaves most of the GPU idle; the step splits
-                 the keys into 4 ranges.
+                 the keys into 2 ranges.
 
 Seeds: ``1_000_000*c + 1000*layer + 10*branch + t`` with t = 0 q, 1 own k, 2 own v,
 3 prefix k, 4 prefix v; values drawn in fp32 on the CPU with ``torch.Generator`` and
@@ -93,7 +93,7 @@ WORKLOADS: Dict[str, Workload] = {
     "video_bf16": Workload("video_bf16", 5, "bf16", 2, (21, 30, 52), (22, 21, 21), ((0, 0, 0), (0, 0, 0)),
                            (256, 256), 12, 12, 128, guidance=6.0),
     "longctx_bf16": Workload("longctx_bf16", 6, "bf16", 2, (32, 32), (32, 32), ((16384, 16384), (16384, 16384)),
-                             (16384, 256), 32, 8, 128, guidance=4.0, splits=4),
+                             (16384, 256), 32, 8, 128, guidance=4.0, splits=2),
 }
 
 

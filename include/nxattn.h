@@ -138,15 +138,18 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * prefix_only (0 or 1): 1 = the keys are the prefix rows alone (every prefix_len[b] >= 1;
  *   k, v and kv_strides are not read and may be NULL / zero). Attention over the own
  *   keys alone is a call with no prefix; the two merge into the full result.
- * num_splits (0 or 1: one pass; 2 .. NXATTN_MAX_SPLITS): every branch's key range is
- *   cut into ranges of `per` whole 64-key tiles, per = ceil(max_b tiles_b / num_splits),
- *   so branch b uses ceil(tiles_b / per) <= num_splits ranges. Each range runs in its
- *   own workgroups, which write an fp32 partial output and log-sum-exp into the
- *   workspace; a second kernel on the same stream merges them (the arithmetic of
- *   nxattn_attn_merge) into o, and into lse if given. For problems with too few
- *   workgroups to fill the GPU (batch * heads_kv * ceil(heads_q/heads_kv *
- *   ceil(seq_q/32) / 8) well under 256 for BF16, a short query against a long prefix)
- *   or with branches of very different key counts.
+ * num_splits (0 or 1: one pass; 2 .. NXATTN_MAX_SPLITS): the most key ranges a branch
+ *   may be cut into. Ranges are `per` whole 64-key tiles long, with
+ *     per = max(ceil(max_b tiles_b / num_splits), ceil(W * sum_b tiles_b / slots)),
+ *   W the workgroups one key range of one branch takes (all kv heads and query blocks)
+ *   and slots the workgroups the GPU holds at once: no range is shorter than a fair
+ *   share of the whole problem's work per slot. A branch of at most `per` tiles runs as
+ *   one range and writes o (and lse) directly; if that holds for every branch the call
+ *   is one pass. The ranges of a longer branch write fp32 partial outputs and
+ *   log-sum-exps into the workspace, and a second kernel on the same stream merges them
+ *   (the arithmetic of nxattn_attn_merge) into o, and into lse if given. For problems
+ *   with too few workgroups to fill the GPU (a short query against a long prefix) or
+ *   with branches of very different key counts.
  * workspace, workspace_bytes: with num_splits > 1, 16-byte aligned device memory of at
  *   least nxattn_fwd_workspace_size() bytes, overlapping nothing else; its contents on
  *   entry do not matter and it is busy until the merge kernel has run on `stream`.

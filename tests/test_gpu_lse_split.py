@@ -145,6 +145,21 @@ def test_fwd_split_keys(dtype, B, S, Hq, Hkv, D, P, ns):
     assert torch.equal(o.cpu(), o2.cpu())
 
 
+def test_split_request_on_a_full_problem_is_one_pass():
+    # a problem that already fills the GPU: the ranges would be shorter than a fair
+    # share, so the call runs as one pass and matches the plain call bit for bit
+    note("fwd split request on a full-size problem")
+    B, S, Hq, Hkv, D, P = 2, 4096, 32, 8, 128, (512, 128)
+    q, k, v, pre = make_case(torch.bfloat16, B, S, Hq, Hkv, D, P, 3250)
+    dq, dk, dv = dev(q, k, v)
+    dp = dev(*pre)
+    o1, o2 = torch.empty_like(dq), torch.empty_like(dq)
+    nx.nxattn_fwd(dq, dk, dv, o1, dp)
+    nx.nxattn_fwd(dq, dk, dv, o2, dp, num_splits=8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2.cpu())
+
+
 def test_fwd_split_with_q_rope_and_prefix_only():
     # every option at once: q rotated on load, keys = prefix only, split ranges, lse
     note("fwd split + q_rope + prefix_only")
