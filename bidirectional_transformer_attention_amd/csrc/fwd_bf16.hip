@@ -13,8 +13,11 @@
 // normalised fp32 partial and its log-sum-exp, combined by the merge kernel).
 //
 // Per wave: S^T = K Q^T lives in the 32x32 accumulator layout (lane = query row, 16
-// registers = keys), so row max / row sum are in-lane plus one permlane32 swap; the
-// accumulator registers, rounded to bf16, are directly the B operand (P^T) of
+// registers = keys), so row max / row sum are in-lane plus one permlane32 swap. When q
+// is rotated on load it is also multiplied by scale*log2(e) before its one rounding to
+// bf16, and the score accumulators start at -m (the running row max): the MFMAs then
+// deliver the exponent c s - m itself and the softmax needs no per-score FMA. The
+// weights, rounded to bf16 in the accumulator layout, are directly the B operand (P^T) of
 // O^T += V^T P^T. The V^T operand comes from row-major V in LDS through the gfx950
 // transposing read ds_read_b64_tr_b16, so K and V are both stored row-major.
 //
@@ -154,7 +157,9 @@ struct Wave {
   f32x16 s[2];        // S^T accumulators of the tile being scored (2 key blocks of 32)
   bf16x8 p[4];        // P^T operand of the tile being accumulated, step (kb, half)
   float m, l;
-  float thr;          // (m + RESCALE_T) / c: the raw row max above which m moves
+  float thr;          // FOLD: row max of the shifted scores above which m moves (-inf
+                      // before the first tile); else (m + RESCALE_T) / c on raw scores
+  f32x16 negm;        // FOLD: -m in every register, the score accumulators' start value
   // lane parts of the LDS byte addresses: K fragment of k-step ks at kbase + (32ks ^ kx),
   // V^T fragment of d-block db at vbase + (64db ^ vy)
   int kbase, kx, vbase, vy;
@@ -190,7 +195,7 @@ __device__ __forceinline__ void sched_steps() {
 // K_{t+1} Q^T (16 MFMAs). Fragments are read from LDS three MFMAs ahead so the
 // matrix core never waits on LDS latency; consecutive MFMAs target different
 // accumulators. VPAR / KPAR select the V and K buffers (compile-time LDS offsets).
-template <int VPAR, int KPAR, bool SCORE, bool DMA = false>
+template <int VPAR, int KPAR, bool SCORE, bool FOLD, bool DMA = false>
 __device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullptr) {
   const uint8_t* vsm = vbuf<VPAR>();
   const uint8_t* ksm = kbuf<KPAR>();
@@ -242,7 +247,7 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullpt
         w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.p[kbhs], w.o[db], 0, 0, 0);
       } else {
         const int j = i - 16, ks = j >> 1, kb = j & 1;
-        if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], f32x16{}, 0, 0, 0);
+        if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], FOLD ? w.negm : f32x16{}, 0, 0, 0);
         else w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], w.s[kb], 0, 0, 0);
       }
     }
@@ -254,7 +259,7 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullpt
 }
 
 // S^T only (prologue).
-template <int KPAR>
+template <int KPAR, bool FOLD>
 __device__ __forceinline__ void gemm_s_only(Wave& w) {
   const uint8_t* ksm = kbuf<KPAR>();
 #pragma unroll
@@ -262,7 +267,7 @@ __device__ __forceinline__ void gemm_s_only(Wave& w) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 f = as_bf16x8(lds_read_b128(ksm, kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
-      if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], f32x16{}, 0, 0, 0);
+      if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], FOLD ? w.negm : f32x16{}, 0, 0, 0);
       else w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], w.s[kb], 0, 0, 0);
     }
 }
@@ -275,7 +280,7 @@ __device__ __forceinline__ void gemm_s_only(Wave& w) {
 // every lane then fetches its pairs' entries with ds_bpermute. The turn pos * step is
 // reduced to [0, 1) in fp32 before the hardware sin/cos; results are rounded to bf16
 // (RNE). Lane data: qf[ks][e] = q[16 ks + 8 hh + e].
-__device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, int lane) {
+__device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, int lane, float sc) {
   const int hh = lane >> 5;
   int c0 = tok, c1 = 0, c2 = 0;
   if (r.n_axes == 2) {
@@ -320,8 +325,8 @@ __device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, in
         float sn, cs;
         turn(16 * ks + 8 * hh + e, sn, cs);
         const float xa = (float)qf[ks][e], xb = (float)qf[ks + 4][e];
-        qf[ks][e] = (__bf16)(xa * cs - xb * sn);
-        qf[ks + 4][e] = (__bf16)(xa * sn + xb * cs);
+        qf[ks][e] = (__bf16)((xa * cs - xb * sn) * sc);
+        qf[ks + 4][e] = (__bf16)((xa * sn + xb * cs) * sc);
       }
   } else {
 #pragma unroll
@@ -331,15 +336,18 @@ __device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, in
         float sn, cs;
         turn((16 * ks + 8 * hh + e) >> 1, sn, cs);
         const float xa = (float)qf[ks][e], xb = (float)qf[ks][e + 1];
-        qf[ks][e] = (__bf16)(xa * cs - xb * sn);
-        qf[ks][e + 1] = (__bf16)(xa * sn + xb * cs);
+        qf[ks][e] = (__bf16)((xa * cs - xb * sn) * sc);
+        qf[ks][e + 1] = (__bf16)((xa * sn + xb * cs) * sc);
       }
   }
 }
 
 // Online softmax of w.s (tile with `valid` keys, < BN only for the last tile) -> w.p.
+// FOLD: w.s already holds c s - m (q pre-scaled, accumulators started at -m).
+template <bool MASK, bool FOLD>
 __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
-  if (valid < BN) {
+  // MASK = false: the tile is known to be whole (no per-key compare/select is compiled)
+  if (MASK && valid < BN) {
     // key of register i in block kb is kb*32 + 8(i/4) + 4hh + (i%4): compare the
     // compile-time part against valid - 4hh
     const int lim = valid - 4 * hh;
@@ -362,16 +370,38 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
     tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
   }
   const bool grow = tmax > w.thr;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float mnew = grow ? tmax * c : w.m;
-    const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
-    w.l *= alpha;
+  if constexpr (FOLD) {
+    // the scores arrive as c s - m: a row moves its max by d = tmax, and this tile's
+    // scores by -d
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float d = grow ? tmax : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      w.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
-    w.m = mnew;
-    w.thr = (mnew + RESCALE_T) / c;
+        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+      w.m += d;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        w.negm[i] = -w.m;
+        w.s[0][i] -= d;
+        w.s[1][i] -= d;
+      }
+      w.thr = RESCALE_T;
+    }
+  } else {
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? tmax * c : w.m;
+      const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
+      w.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+      w.m = mnew;
+      w.thr = (mnew + RESCALE_T) / c;
+    }
   }
   const float nm = -w.m;
   float l0 = 0.f, l1 = 0.f;
@@ -382,8 +412,10 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       u32x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e], c, nm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e + 1], c, nm));
+        const float p0 = FOLD ? __builtin_amdgcn_exp2f(w.s[kb][8 * hs + 2 * e])
+                              : __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e], c, nm));
+        const float p1 = FOLD ? __builtin_amdgcn_exp2f(w.s[kb][8 * hs + 2 * e + 1])
+                              : __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e + 1], c, nm));
         l0 += p0;
         l1 += p1;
         pk[e] = pack_bf16x2(p0, p1);
@@ -395,7 +427,7 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
 
 // The per-wave program. Group A (waves 0-3) and group B (waves 4-7) run it half a tile
 // apart; both execute the same sequence of workgroup barriers.
-template <bool GROUP_A>
+template <bool GROUP_A, bool FOLD>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
@@ -429,8 +461,12 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   }
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
-  w.m = -__builtin_inff();
+  // FOLD: m starts at 0 (the accumulators start at -m = 0) and the first tile always
+  // moves it to its row max
+  w.m = FOLD ? 0.f : -__builtin_inff();
   w.thr = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w.negm[i] = 0.f;
   w.l = 0.f;
   // lane parts of the LDS read addresses. K: row n, chunk 2ks+hh at slot
   // (2ks+hh) ^ (n & 15), i.e. byte n*ROWB + 16*(hh ^ (n&1)) + (32ks ^ 16*(n & 14)).
@@ -527,10 +563,11 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   dma_tile(tile_at(0), true, vbuf<0>(), wave, All{});
   if (T > 1) dma_tile(tile_at(1), false, kbuf<1>(), wave, All{});
   // q's RoPE (if requested) while the first tiles are in flight
-  if (a.rope_q) rotate_q(w.qf, a.rq[b], tokc, lane);
+  if (FOLD) rotate_q(w.qf, a.rq[b], tokc, lane, c);
+  else if (a.rope_q) rotate_q(w.qf, a.rq[b], tokc, lane, 1.0f);
   wait_dma_barrier();
-  gemm_s_only<0>(w);
-  if (GROUP_A) softmax(w, c, valid_at(0), hh);
+  gemm_s_only<0, FOLD>(w);
+  if (GROUP_A) softmax<true, FOLD>(w, c, valid_at(0), hh);
   if (GROUP_A) barrier_prio<-1, 2>();
   else barrier_only();
 
@@ -550,28 +587,32 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
     if constexpr (FAST) {
       const DmaPlan pl = plan_of(t);
-      gemm_phase<PAR, PAR ^ 1, true, true>(w, &pl);
+      gemm_phase<PAR, PAR ^ 1, true, FOLD, true>(w, &pl);
     } else {
-      gemm_phase<PAR, PAR ^ 1, true>(w);
+      gemm_phase<PAR, PAR ^ 1, true, FOLD>(w);
       if (t + 2 < T) dma_tile(tile_at(t + 2), false, kbuf<PAR>(), wave, Half{});
       if (t + 1 < T) dma_tile(tile_at(t + 1), true, vbuf<PAR ^ 1>(), wave, Half{});
     }
     barrier_prio<0, -1>();
-    if (t + 1 < T) softmax(w, c, valid_at(t + 1), hh);
+    // a fast iteration's next position is a whole tile
+    if (t + 1 < T) softmax<!FAST, FOLD>(w, c, valid_at(t + 1), hh);
     wait_dma_barrier_prio<-1, 2>();
   };
-  auto iter_b = [&](int t, auto par) {
+  // MASK: the position may be the range's last, possibly ragged, tile
+  auto iter_b = [&](int t, auto par, auto mask) {
     constexpr int PAR = decltype(par)::value;
     asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
-    softmax(w, c, valid_at(t), hh);
+    softmax<decltype(mask)::value, FOLD>(w, c, valid_at(t), hh);
     barrier_prio<-1, 2>();
-    gemm_phase<PAR, PAR ^ 1, true>(w);
+    gemm_phase<PAR, PAR ^ 1, true, FOLD>(w);
     wait_dma_barrier_prio<0, -1>();
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using Fast = std::true_type;
   using Slow = std::false_type;
+  using Mask = std::true_type;
+  using NoMask = std::false_type;
   int t = 0;
   if (GROUP_A) {
     const int nfast = nwhole - 2;
@@ -585,11 +626,17 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     }
     if (t < T) iter_a(t, P0{}, Slow{});
   } else {
-    for (; t + 1 < T; t += 2) {
-      iter_b(t, P0{});
-      iter_b(t + 1, P1{});
+    // positions [0, nwhole) are whole tiles; a ragged tile can sit at T - 2 when the
+    // straddling tile is moved to T - 1
+    for (; t + 1 < nwhole; t += 2) {
+      iter_b(t, P0{}, NoMask{});
+      iter_b(t + 1, P1{}, NoMask{});
     }
-    if (t < T) iter_b(t, P0{});
+    for (; t + 1 < T; t += 2) {
+      iter_b(t, P0{}, Mask{});
+      iter_b(t + 1, P1{}, Mask{});
+    }
+    if (t < T) iter_b(t, P0{}, Mask{});
   }
 
   if (GROUP_A) asm volatile("s_setprio 0");
@@ -631,11 +678,12 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = lse;
 }
 
+template <bool FOLD>
 __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true>(a, lane, wave);
-  else wave_program<false>(a, lane, wave);
+  if (wave < 4) wave_program<true, FOLD>(a, lane, wave);
+  else wave_program<false, FOLD>(a, lane, wave);
 }
 
 }  // namespace bf16k
@@ -645,7 +693,7 @@ FwdShape fwd_shape_bf16(const FwdProblem& p) {
   static int per_cu = -1;   // resident workgroups per CU (registers and LDS bound it)
   if (per_cu < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel, THREADS, 0) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<false>, THREADS, 0) != hipSuccess || n < 1) n = 1;
     per_cu = n;
   }
   const int64_t nqb = (int64_t)(p.heads_q / p.heads_kv) * ((p.seq_q + 31) / 32);
@@ -678,7 +726,8 @@ int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
     a.k = a.q; a.v = a.q;
     a.ks0 = a.ks1 = a.ks2 = 0;
   }
-  fwd_bf16_kernel<<<a.total_wg, THREADS, 0, stream>>>(a);
+  if (a.rope_q) fwd_bf16_kernel<true><<<a.total_wg, THREADS, 0, stream>>>(a);
+  else fwd_bf16_kernel<false><<<a.total_wg, THREADS, 0, stream>>>(a);
   return check_launch("nxattn_fwd(bf16)");
 }
 

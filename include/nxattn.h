@@ -121,7 +121,10 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * checks, grid product == seq_q), inside the attention kernel, so that no separate
  * pass over q is needed; the q buffer is not modified. The angle is evaluated in fp32
  * (absolute error about 1e-4 rad at positions near 1000, far below the bf16 rounding
- * of the rotated value, which is rounded to nearest even as a stored q would be).
+ * of the rotated value). The rotated value is multiplied by scale * log2(e) (the units
+ * of the kernel's base-2 softmax) and rounded once to bf16, nearest even: the q used
+ * is that rounding divided by scale * log2(e), as close to the rotated q as a stored
+ * bf16 q would be, but rounded at a different point.
  * BF16 only: F32 with q_rope returns NXATTN_ERR_UNSUPPORTED (rotate with
  * nxattn_rope_apply, whose fp64 angles keep the fp32 path exact to 1e-4).
  *

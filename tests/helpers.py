@@ -16,6 +16,17 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 TOL_LSE = 1e-3
 
 
+def fused_q(q_rot: np.ndarray, head_dim: int, scale: float = 0.0) -> np.ndarray:
+    """The q that the bf16 kernel uses when it rotates q on load, given the exact rotated
+    q: the rotated value times c = scale*log2(e) (fp32, as the library forms it), rounded
+    once to bf16 (nearest even), divided back by c. The rounding point is the library's
+    documented one; everything else comes from the oracle."""
+    sc = np.float32(scale) if scale > 0 else np.float32(1.0) / np.sqrt(np.float32(head_dim))
+    c = float(np.float32(sc * np.float32(1.4426950408889634)))
+    r = torch.from_numpy(np.asarray(q_rot, dtype=np.float64) * c).to(torch.float32).to(torch.bfloat16)
+    return r.to(torch.float64).numpy() / c
+
+
 def f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a CPU/GPU tensor (fp32 or bf16) to float64."""
     return t.detach().to("cpu").to(torch.float32).numpy().astype(np.float64)

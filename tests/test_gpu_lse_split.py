@@ -14,7 +14,7 @@ import torch
 import oracle
 import bidirectional_transformer_attention_amd as nx
 from bidirectional_transformer_attention_amd import synth
-from helpers import TOL, TOL_LSE, attention_err, f64
+from helpers import TOL, TOL_LSE, attention_err, f64, fused_q
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -166,14 +166,14 @@ def test_fwd_split_with_q_rope_and_prefix_only():
     B, S, Hq, Hkv, D, P = 2, 96, 8, 2, 128, (700, 65)
     q, k, v, pre = make_case(torch.bfloat16, B, S, Hq, Hkv, D, P, 3300)
     descs = [nx.rope_desc((8, 12), (32, 32), (P[b], P[b])) for b in range(B)]
-    q_rot = torch.stack([torch.from_numpy(oracle.rope(f64(q[b]), (8, 12), (32, 32), (P[b], P[b])))
-                         .to(torch.float32).to(torch.bfloat16) for b in range(B)])
+    q_rot = torch.stack([torch.from_numpy(fused_q(oracle.rope(f64(q[b]), (8, 12), (32, 32), (P[b], P[b])), D))
+                         for b in range(B)])
     dq, = dev(q)
     o = torch.empty_like(dq)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
     nx.nxattn_fwd(dq, None, None, o, dev(*pre), q_rope=descs, lse=lse, prefix_only=True, num_splits=6)
     torch.cuda.synchronize()
-    # the isolation reference: the oracle's rotation rounded to bf16, as the kernel rounds it
+    # the isolation reference: the oracle's rotation, rounded at the kernel's documented point
     check(o.cpu(), lse.cpu(), q_rot, k, v, pre, torch.bfloat16, prefix_only=True)
 
 

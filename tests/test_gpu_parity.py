@@ -14,7 +14,7 @@ import oracle
 import bidirectional_transformer_attention_amd as nx
 from bidirectional_transformer_attention_amd import synth
 from bidirectional_transformer_attention_amd.pipeline import AttentionStep
-from helpers import TOL, attention_err, f64, oracle_attention, oracle_rope, sample_rows
+from helpers import TOL, attention_err, f64, fused_q, oracle_attention, oracle_rope, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -386,8 +386,9 @@ def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter, gf):
         pk = f64(pre[b][0]) if pre[b] is not None else None
         pv = f64(pre[b][1]) if pre[b] is not None else None
         ref = oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv)
-        # the kernel rounds rotated q to bf16: that rounding alone, measured with the oracle
-        share = attention_err(oracle.attention(f64(rnd(q_ex)), f64(k_rot[b]), f64(v[b]), pk, pv), ref)
+        # the kernel rounds the rotated (and scaled) q to bf16: that rounding alone,
+        # measured with the oracle
+        share = attention_err(oracle.attention(fused_q(q_ex, D), f64(k_rot[b]), f64(v[b]), pk, pv), ref)
         err = attention_err(f64(o.cpu()[b]), ref)
         assert err <= TOL["bf16"] + share, (b, err, share)
 
@@ -412,7 +413,10 @@ def step_case(name, rows_per_branch, seed_rows):
     if wl.dtype == "bf16":
         rnd = lambda a: \
             torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
-        q_r = [rnd(oracle_rope(wl, inp.q, b, rows[b])) for b in range(wl.branches)]
+        # q rotated on load is rounded after scaling by scale*log2(e) (the kernel's
+        # documented rounding point); a stored q is rounded as it is
+        rq = (lambda a: fused_q(a, wl.head_dim)) if step.fuse_q_rope else rnd
+        q_r = [rq(oracle_rope(wl, inp.q, b, rows[b])) for b in range(wl.branches)]
         k_r = [rnd(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)]
         ref_r = oracle_attention(wl, inp, rows, q_r, k_r, q_rot_rows_only=True)
         rope_share = max(attention_err(ref_r[b], ref[b]) for b in range(wl.branches))
