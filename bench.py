@@ -167,7 +167,8 @@ def main() -> int:
             "frac": round(achieved / PEAK[wl.dtype], 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
                         else None),
-            "kernel": ("nx::bf16k::fwd_bf16_kernel" if wl.dtype == "bf16" else "nx::f32k::fwd_f32_kernel")
+            "kernel": ((f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
+                       if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),
             "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_ms[0], 4)}
 
