@@ -48,8 +48,29 @@ def traffic_record():
     return rec
 
 
-def cpu_baseline(wl, rows_per_branch: int):
-    """Time the CPU fp64 oracle on the first rows of every branch (full keys)."""
+def time_call(fn, stream, reps: int = 20) -> float:
+    """Average GPU milliseconds of fn() (which enqueues work on `stream`): HIP events around
+    reps calls that were all enqueued behind a spin kernel, so the GPU runs them back to back
+    and the host's per-call submission time is not counted."""
+    import torch
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(4_000_000)      # about 2 ms of spinning while the calls are enqueued
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(wl, rows_per_branch: int, threads: int = 0):
+    """Time the CPU fp64 oracle on the first rows of every branch (full keys); threads > 0
+    limits the BLAS thread pool to that many threads."""
+    import contextlib
+
     import numpy as np
     import torch
 
@@ -57,10 +78,17 @@ def cpu_baseline(wl, rows_per_branch: int):
     from bidirectional_transformer_attention_amd import synth
 
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = threadpool_limits(limits=threads) if threads > 0 else contextlib.nullcontext()
+        with limit:
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        limit, cores = contextlib.nullcontext(), 1
+    with limit:
+        return _cpu_baseline(wl, rows_per_branch, cores, np, torch, oracle, synth)
+
+
+def _cpu_baseline(wl, rows_per_branch, cores, np, torch, oracle, synth):
     inp = synth.make_inputs(wl)
     f64 = lambda t: t.to(torch.float32).numpy().astype(np.float64)  # noqa: E731
     rows = np.arange(wl.seq if rows_per_branch <= 0 else min(rows_per_branch, wl.seq))
@@ -92,6 +120,8 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=None,
                     help="key ranges per branch in the attention call (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-1thread-rows", type=int, default=-1,
+                    help="query rows per branch for the 1-thread CPU oracle timing (-1: seq/16, 0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after timing, relayout one buffer of this many MB (a plain copy of known size "
                          "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -163,6 +193,23 @@ def main() -> int:
     # (both on this stream); rocprofv3 separates the two
     achieved = flops_step / (fwd_avg * 1e-3) / 1e12
     rec = traffic_record()
+
+    # the side calls of the step, each timed alone, against the 8 TB/s HBM peak
+    es = 2 if wl.dtype == "bf16" else 4
+    side = {}
+    nbytes = {
+        "relayout": sum(2 * 2 * p * wl.heads_kv * wl.head_dim * es for p in wl.prefix_len)
+        if wl.prefix_layout == "replay" else 0,
+        "rope": 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
+        "cfg": 3 * step.q[0].numel() * es if step.use_cfg else 0,
+    }
+    for name, fn in (("relayout", step.relayout), ("rope", step.rope), ("cfg", step.cfg)):
+        if nbytes[name] == 0:
+            continue
+        ms = time_call(fn, stream)
+        gbs = nbytes[name] / (ms * 1e-3) / 1e9
+        side[name] = {"us": round(1000 * ms, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
+                      "frac_of_hbm": round(gbs / HBM_PEAK, 4)}
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[wl.dtype], "unit": "TFLOP/s",
             "frac": round(achieved / PEAK[wl.dtype], 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
@@ -181,9 +228,12 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_rows)
+        r1 = max(32, wl.seq // 16) if args.cpu_1thread_rows < 0 else args.cpu_1thread_rows
+        if r1 > 0:
+            cpu1 = cpu_baseline(wl, r1, threads=1)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -201,6 +251,8 @@ def main() -> int:
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
+        "side_calls": side,
         "headline_cond_branch": headline,
     }
     print(json.dumps(out))
