@@ -87,3 +87,41 @@ def bf_lse(q, k, pk=None, scale: Optional[float] = None):
             m = max(s)
             out[h][i] = m + math.log(math.fsum(math.exp(t - m) for t in s))
     return out
+
+
+def bf_e4m3_value(code: int) -> float:
+    """Value of one E4M3 code by its field definition (None for NaN)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 7
+    if e == 0xF and m == 7:
+        return None
+    if e == 0:
+        return s * math.ldexp(m, -9)
+    return s * math.ldexp(8 + m, e - 10)
+
+
+def bf_e4m3_encode(x: float) -> int:
+    """Nearest finite E4M3 code by scanning every code (ties: even code); beyond the
+    largest finite value, the largest; NaN -> 0x7F."""
+    if x != x:
+        return 0x7F
+    best, bd = None, None
+    for c in range(0x7F):
+        v = bf_e4m3_value(c)
+        d = abs(abs(x) - v)
+        if bd is None or d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    if math.copysign(1.0, x) < 0:
+        best |= 0x80
+    return best
+
+
+def bf_fp8_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e, by search (0 for amax = 0)."""
+    if amax == 0.0:
+        return 0
+    for e in range(-160, 160):
+        if amax <= math.ldexp(448.0, e):
+            return e
+    raise ValueError(amax)
