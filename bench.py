@@ -24,7 +24,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s and % of MI355X MFMA peak, 4096x(4096+512) GQA bf16"
-PEAK = {"bf16": 2516.6, "f32": 157.3}          # TFLOP/s, dense MFMA, MI355X published
+PEAK = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}   # TFLOP/s, dense MFMA, MI355X published
+# the fp8 score GEMM does half the flops on the fp8 unit and half (P.V) on the bf16 unit:
+# at both peaks a step would take F/2/fp8 + F/2/bf16, i.e. an effective peak of
+PEAK_FP8QK = 2.0 / (1.0 / PEAK["fp8"] + 1.0 / PEAK["bf16"])
 HBM_PEAK = 8000.0                               # GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_dit1k_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "bidirectional_transformer_attention_amd", "csrc", "fwd_bf16.hip")
@@ -101,7 +104,14 @@ def _cpu_baseline(wl, rows_per_branch, cores, np, torch, oracle, synth):
         pre = None if p is None else f64(p)
         if pre is not None and wl.prefix_layout == "replay":
             pre = oracle.relayout(pre[None], 0)[0]
-        oracle.attention(q, k, f64(inp.v[b]), None if pre is None else pre[0], None if pre is None else pre[1])
+        pk = None if pre is None else pre[0]
+        if wl.qk_fp8:
+            # the fp8 score GEMM's inputs: q, k and the prefix K through E4M3 and back
+            from oracle import fp8 as ofp8
+            q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None]))[0]
+            k = ofp8.dequantize_fp8(*ofp8.quantize_fp8(k[None]))[0]
+            pk = None if pk is None else ofp8.dequantize_fp8(*ofp8.quantize_fp8(pk[None]))[0]
+        oracle.attention(q, k, f64(inp.v[b]), pk, None if pre is None else pre[1])
         flops += 4.0 * len(rows) * (wl.prefix_len[b] + wl.seq) * wl.heads_q * wl.head_dim
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
@@ -156,6 +166,7 @@ def main() -> int:
     for i in range(args.steps):
         step.relayout()
         step.rope()
+        step.quantize()
         ev[i][0].record(stream)
         step.attention()
         ev[i][1].record(stream)
@@ -170,7 +181,7 @@ def main() -> int:
 
     # the headline shape alone: the cond branch, 4096 x (4096 + 512), as a batch-1 launch
     headline = None
-    if wl.branches >= 1 and wl.dtype == "bf16":
+    if wl.branches >= 1 and wl.dtype == "bf16" and not wl.qk_fp8:
         q0, k0, v0, o0 = step.q[:1], step.k[:1], step.v[:1], step.o[:1]
         pre0 = step.prefix_online[:1]
         split_kw = dict(num_splits=step.splits, workspace=step.workspace)
@@ -192,6 +203,7 @@ def main() -> int:
     # with key splits the timed attention phase is the split kernel plus the merge kernel
     # (both on this stream); rocprofv3 separates the two
     achieved = flops_step / (fwd_avg * 1e-3) / 1e12
+    peak = PEAK_FP8QK if wl.qk_fp8 else PEAK[wl.dtype]
     rec = traffic_record()
 
     # the side calls of the step, each timed alone, against the 8 TB/s HBM peak
@@ -202,19 +214,25 @@ def main() -> int:
         if wl.prefix_layout == "replay" else 0,
         "rope": 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
         "cfg": 3 * step.q[0].numel() * es if step.use_cfg else 0,
+        # reads q, k and the prefix K twice (maximum, then codes), writes one byte per element
+        "quantize": (2 * es + 1) * (step.q.numel() + step.k.numel()
+                                    + sum(p[0].numel() for p in step.prefix_online if p is not None))
+        if wl.qk_fp8 else 0,
     }
-    for name, fn in (("relayout", step.relayout), ("rope", step.rope), ("cfg", step.cfg)):
+    for name, fn in (("relayout", step.relayout), ("rope", step.rope), ("quantize", step.quantize),
+                     ("cfg", step.cfg)):
         if nbytes[name] == 0:
             continue
         ms = time_call(fn, stream)
         gbs = nbytes[name] / (ms * 1e-3) / 1e9
         side[name] = {"us": round(1000 * ms, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
                       "frac_of_hbm": round(gbs / HBM_PEAK, 4)}
-    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[wl.dtype], "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK[wl.dtype], 4),
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
-                        else None),
-            "kernel": ((f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
+                        and not wl.qk_fp8 else None),
+            "kernel": ("nx::fp8k::fwd_fp8_kernel" if wl.qk_fp8 else
+                       (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
                        if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),
             "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_ms[0], 4)}
@@ -238,7 +256,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded N(0,1), shapes of the workload)",
+        "vs_baseline": None, "dtype": "fp8e4m3 QK / bf16 PV" if wl.qk_fp8 else wl.dtype, "data": "synthetic (seeded N(0,1), shapes of the workload)",
         "config": {"workload": wl.name, "branches": wl.branches, "seq_q": wl.seq, "grid": list(wl.grid),
                    "prefix_len": list(wl.prefix_len), "heads_q": wl.heads_q, "heads_kv": wl.heads_kv,
                    "head_dim": wl.head_dim, "rope_offsets": [list(o) for o in wl.offsets],
@@ -246,7 +264,8 @@ def main() -> int:
                    if wl.prefix_layout == "replay" else "online [2,P,H,D]",
                    "splits": step.splits,
                    "step": ("relayout + rope(k) + fused attention (q rotated on load)" if step.fuse_q_rope
-                            else "relayout + rope(q,k) + fused attention")
+                            else "relayout + rope(q,k) + fp8 quantize(q, k, prefix k) + fused attention with fp8 QK"
+                            if wl.qk_fp8 else "relayout + rope(q,k) + fused attention")
                    + (f" over {step.splits} key ranges + merge" if step.splits > 1 else "") + " + cfg",
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},
         "roofline": roof,

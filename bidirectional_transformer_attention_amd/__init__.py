@@ -14,6 +14,9 @@ from .binding import (  # noqa: F401
     nxattn_attn_merge,
     nxattn_cfg_combine,
     nxattn_fwd,
+    nxattn_fwd_fp8,
+    nxattn_quantize_fp8,
+    quantize_fp8_workspace_bytes,
     nxattn_kv_relayout,
     nxattn_rope_apply,
     rope_desc,

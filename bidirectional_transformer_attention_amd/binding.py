@@ -22,8 +22,8 @@ MAX_BRANCHES = 8
 MAX_SPLITS = 16
 
 SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_fwd_workspace_size",
-           "nxattn_attn_merge", "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error",
-           "nxattn_version")
+           "nxattn_attn_merge", "nxattn_quantize_fp8_workspace_size", "nxattn_quantize_fp8", "nxattn_fwd_fp8",
+           "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error", "nxattn_version")
 
 
 class NxattnError(RuntimeError):
@@ -48,6 +48,17 @@ class FwdArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("q_rope", ctypes.POINTER(RopeDesc)),
                 ("lse", ctypes.c_void_p), ("prefix_only", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
+
+
+class FwdFp8Args(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_q", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q8", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("q_exp", ctypes.c_void_p),
+                ("k_exp", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
+                ("prefix_k8", ctypes.c_void_p * MAX_BRANCHES), ("prefix_v", ctypes.c_void_p * MAX_BRANCHES),
+                ("prefix_len", ctypes.c_int32 * MAX_BRANCHES), ("prefix_k_exp", ctypes.c_void_p),
+                ("scale", ctypes.c_float), ("lse", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -75,6 +86,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_int64), i32, vp, ctypes.POINTER(ctypes.c_int64), vp,
                                       vp]
     lib.nxattn_attn_merge.restype = i32
+    lib.nxattn_quantize_fp8_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.nxattn_quantize_fp8_workspace_size.restype = i32
+    lib.nxattn_quantize_fp8.argtypes = [vp, i32, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), vp, vp, vp,
+                                        i64, vp]
+    lib.nxattn_quantize_fp8.restype = i32
+    lib.nxattn_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), vp]
+    lib.nxattn_fwd_fp8.restype = i32
     lib.nxattn_cfg_combine.argtypes = [vp, vp, vp, i64, ctypes.c_float, i32, vp]
     lib.nxattn_cfg_combine.restype = i32
     lib.nxattn_status_string.argtypes = [i32]
@@ -319,3 +337,88 @@ def nxattn_cfg_combine(cond: torch.Tensor, uncond: torch.Tensor, out: torch.Tens
         raise NxattnError(1, "cfg dtypes differ")
     _check(load().nxattn_cfg_combine(cond.data_ptr(), uncond.data_ptr(), out.data_ptr(), cond.numel(),
                                      float(guidance), _dtype_code(cond), _stream(stream)))
+
+
+def quantize_fp8_workspace_bytes(batch: int, seq: int, heads: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(load().nxattn_quantize_fp8_workspace_size(batch, seq, heads, ctypes.byref(n)))
+    return int(n.value)
+
+
+def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, exps: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """E4M3 codes (uint8, contiguous [B,S,H,D]) and per-(b,h) exponents (int8 [B,H]) of x
+    [B,S,H,D] (bf16 or f32, strided, D contiguous); outputs and the workspace are
+    allocated with torch when not given. Returns (codes, exps)."""
+    _gpu(x, codes, exps, workspace)
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise NxattnError(1, "x must be [B, S, H, D] with D contiguous")
+    B, S, H, D = x.shape
+    if codes is None:
+        codes = torch.empty((B, S, H, D), dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty((B, H), dtype=torch.int8, device=x.device)
+    if codes.dtype != torch.uint8 or tuple(codes.shape) != (B, S, H, D) or not codes.is_contiguous():
+        raise NxattnError(1, "codes must be a contiguous uint8 [B, S, H, D] tensor")
+    if exps.dtype != torch.int8 or tuple(exps.shape) != (B, H) or not exps.is_contiguous():
+        raise NxattnError(1, "exps must be a contiguous int8 [B, H] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(4, quantize_fp8_workspace_bytes(B, S, H)), dtype=torch.uint8, device=x.device)
+    st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    _check(load().nxattn_quantize_fp8(x.data_ptr(), _dtype_code(x), B, S, H, D, st, codes.data_ptr(), exps.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+    return codes, exps
+
+
+def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_exp: torch.Tensor, v: torch.Tensor,
+                   o: torch.Tensor, prefix_k8: Sequence[Optional[torch.Tensor]] = (),
+                   prefix_v: Sequence[Optional[torch.Tensor]] = (), prefix_k_exp: Optional[torch.Tensor] = None,
+                   scale: float = 0.0, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Attention with the fp8 score GEMM: q8 [B,S,Hq,128], k8 [B,S,Hkv,128] uint8 codes
+    (contiguous), q_exp [B,Hq], k_exp [B,Hkv] int8; v [B,S,Hkv,128] and o [B,S,Hq,128] bf16;
+    prefix_k8[b] uint8 [P_b,Hkv,128] and prefix_v[b] bf16 [P_b,Hkv,128] contiguous (or None),
+    prefix_k_exp int8 [B,Hkv]."""
+    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, *[t for t in prefix_k8 if t is not None],
+         *[t for t in prefix_v if t is not None])
+    B, S, Hq, D = q8.shape
+    Hkv = k8.shape[2]
+    for t in (q8, k8):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 4:
+            raise NxattnError(1, "q8 and k8 must be contiguous uint8 [B, S, H, D] tensors")
+    if tuple(k8.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D) or tuple(o.shape) != (B, S, Hq, D):
+        raise NxattnError(1, "inconsistent q8/k8/v/o shapes")
+    if v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 or v.stride(3) != 1 or o.stride(3) != 1:
+        raise NxattnError(1, "v and o must be bf16 with head_dim contiguous")
+    for t, shp in ((q_exp, (B, Hq)), (k_exp, (B, Hkv))):
+        if t.dtype != torch.int8 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise NxattnError(1, "exponents must be contiguous int8 [B, H] tensors")
+    if len(prefix_k8) not in (0, B) or len(prefix_v) != len(prefix_k8):
+        raise NxattnError(1, "prefix_k8 and prefix_v need one entry per batch entry")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, S)):
+        raise NxattnError(1, "lse must be a contiguous float32 [B, Hq, S] tensor")
+    a = FwdFp8Args()
+    a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, Hkv, D
+    a.q8, a.k8, a.q_exp, a.k_exp = q8.data_ptr(), k8.data_ptr(), q_exp.data_ptr(), k_exp.data_ptr()
+    a.v, a.o = v.data_ptr(), o.data_ptr()
+    for i in range(3):
+        a.v_strides[i] = v.stride(i)
+        a.o_strides[i] = o.stride(i)
+    for b in range(MAX_BRANCHES):
+        pk = prefix_k8[b] if b < len(prefix_k8) else None
+        pv = prefix_v[b] if b < len(prefix_v) else None
+        if pk is None or pk.numel() == 0:
+            a.prefix_k8[b] = None
+            a.prefix_v[b] = None
+            a.prefix_len[b] = 0
+            continue
+        if (pk.dtype != torch.uint8 or not pk.is_contiguous() or pv is None or pv.dtype != torch.bfloat16
+                or not pv.is_contiguous() or pk.shape != pv.shape or pk.dim() != 3 or pk.shape[1:] != (Hkv, D)):
+            raise NxattnError(1, "prefix entries must be contiguous [P, Hkv, 128] (uint8 codes, bf16 values)")
+        a.prefix_k8[b] = pk.data_ptr()
+        a.prefix_v[b] = pv.data_ptr()
+        a.prefix_len[b] = pk.shape[0]
+    a.prefix_k_exp = prefix_k_exp.data_ptr() if prefix_k_exp is not None else None
+    a.scale = float(scale)
+    a.lse = lse.data_ptr() if lse is not None else None
+    _check(load().nxattn_fwd_fp8(ctypes.byref(a), _stream(stream)))

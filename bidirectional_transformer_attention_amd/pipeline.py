@@ -6,6 +6,8 @@
     -> fused attention over [prefix ++ own] for all branches in one launch (or, with
        key splits, one launch over key ranges plus one merge launch)
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
+With the fp8 score GEMM (``qk_fp8`` workloads) q is rotated by the RoPE kernel too, and q,
+own k and each prefix K are quantized to E4M3 before the attention call.
 
 Only tensor allocation and argument marshalling happen here; every step runs in the HIP
 library. The prefix of branch b is passed as one layer slice [2, P_b, Hkv, D] of the
@@ -27,7 +29,9 @@ class AttentionStep:
         self.wl = wl
         self.splits = wl.splits if splits is None else int(splits)
         # bf16: q is rotated inside the attention kernel (no separate pass over q)
-        self.fuse_q_rope = (wl.dtype == "bf16") if fuse_q_rope is None else bool(fuse_q_rope)
+        self.fuse_q_rope = (wl.dtype == "bf16" and not wl.qk_fp8) if fuse_q_rope is None else bool(fuse_q_rope)
+        if wl.qk_fp8 and self.fuse_q_rope:
+            raise ValueError("the fp8 score GEMM takes q already rotated and quantized")
         dev = torch.device(device)
         self.q = inp.q.to(dev)
         self.k = inp.k.to(dev)
@@ -57,6 +61,18 @@ class AttentionStep:
         if self.splits > 1:
             n = nx.fwd_workspace_bytes(self.B, self.S, self.Hq, self.D, self.splits)
             self.workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+        if wl.qk_fp8:
+            # E4M3 codes, exponents and the quantizer's workspace, allocated once
+            self.q8 = torch.empty(self.q.shape, dtype=torch.uint8, device=dev)
+            self.k8 = torch.empty(self.k.shape, dtype=torch.uint8, device=dev)
+            self.qe = torch.empty((self.B, self.Hq), dtype=torch.int8, device=dev)
+            self.ke = torch.empty((self.B, self.Hkv), dtype=torch.int8, device=dev)
+            self.pke = torch.zeros((self.B, self.Hkv), dtype=torch.int8, device=dev)
+            self.pk8 = [None if p is None else torch.empty((1, p.shape[1], self.Hkv, self.D), dtype=torch.uint8,
+                                                           device=dev) for p in self.prefix_online]
+            plen = max([p.shape[1] for p in self.prefix_online if p is not None] + [1])
+            n = max(nx.quantize_fp8_workspace_bytes(self.B, self.S, self.Hq), nx.quantize_fp8_workspace_bytes(1, plen, self.Hkv))
+            self.qws = torch.empty(max(4, n), dtype=torch.uint8, device=dev)
         self.use_cfg = self.B == 2 and wl.guidance > 1.0
         self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
 
@@ -70,7 +86,23 @@ class AttentionStep:
             nx.nxattn_rope_apply(self.q, self.descs)
         nx.nxattn_rope_apply(self.k, self.descs)
 
+    def quantize(self) -> None:
+        """E4M3 codes of the rotated q and k and of each prefix K (fp8 workloads only)."""
+        if not self.wl.qk_fp8:
+            return
+        nx.nxattn_quantize_fp8(self.q, self.q8, self.qe, self.qws)
+        nx.nxattn_quantize_fp8(self.k, self.k8, self.ke, self.qws)
+        for b, p in enumerate(self.prefix_online):
+            if p is not None:
+                nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)
+
     def attention(self) -> None:
+        if self.wl.qk_fp8:
+            nx.nxattn_fwd_fp8(self.q8, self.k8, self.qe, self.ke, self.v, self.o,
+                              [None if p is None else p[0] for p in self.pk8],
+                              [None if p is None else p[1] for p in self.prefix_online],
+                              self.pke if any(p is not None for p in self.prefix_online) else None)
+            return
         nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online,
                       q_rope=self.descs if self.fuse_q_rope else None,
                       num_splits=self.splits, workspace=self.workspace)
@@ -82,6 +114,7 @@ class AttentionStep:
     def __call__(self) -> torch.Tensor:
         self.relayout()
         self.rope()
+        self.quantize()
         self.attention()
         self.cfg()
         return self.out if self.use_cfg else self.o

@@ -29,6 +29,9 @@ checkpoints):
                  conditioned on a long injected KV cache (NeoPP page, intro), where one
                  workgroup per query block leaves most of the GPU idle; the step splits
                  the keys into 2 ranges.
+* ``dit1k_fp8qk``, ``dit2k_fp8qk`` the 1K and 2K DiT steps (same shapes and seeds) with
+                 q and k quantized each step to FP8 E4M3 for the score GEMM (the pages
+                 name fp8 DiT variants, NeoPP "Run the replay examples").
 
 Seeds: ``1_000_000*c + 1000*layer + 10*branch + t`` with t = 0 q, 1 own k, 2 own v,
 3 prefix k, 4 prefix v; values drawn in fp32 on the CPU with ``torch.Generator`` and
@@ -63,6 +66,7 @@ class Workload:
     prefix_layout: str = "online"  # "online" [2,P,H,D] or "replay" [2,H,P,D]
     theta: float = 10000.0
     splits: int = 0               # key ranges per branch in the attention call (0: one pass)
+    qk_fp8: bool = False          # q and k quantized to E4M3 for the score GEMM (bf16 tensors in)
 
     @property
     def seq(self) -> int:
@@ -95,6 +99,10 @@ WORKLOADS: Dict[str, Workload] = {
     "longctx_bf16": Workload("longctx_bf16", 6, "bf16", 2, (32, 32), (32, 32), ((16384, 16384), (16384, 16384)),
                              (16384, 256), 32, 8, 128, guidance=4.0, splits=2),
 }
+# the DiT steps with the fp8 score GEMM: same shapes and seeds, q and k quantized each step
+for _n in ("dit1k_bf16", "dit2k_bf16"):
+    _w = WORKLOADS[_n]
+    WORKLOADS[_n.replace("bf16", "fp8qk")] = dataclasses.replace(_w, name=_n.replace("bf16", "fp8qk"), qk_fp8=True)
 
 
 def bench_workload(name: str) -> Workload:

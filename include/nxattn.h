@@ -219,6 +219,72 @@ int nxattn_attn_merge(const void* const* part_o, const float* const* part_lse, i
                       float* lse, hipStream_t stream);
 
 /*
+ * FP8 score GEMM. The pages name fp8 variants of the DiT (NeoPP page, "Run the
+ * replay examples") without a recipe; the one here: q and k (own and prefix keys) are OCP
+ * FP8 E4M3 codes with one power-of-two scale 2^e per (branch, head); the scores are the
+ * dot products of the decoded codes times both scales (exact inside the fp8 MFMA, whose
+ * E8M0 scale operands carry 2^e); softmax, P (bf16) and the P*V product with bf16 V are
+ * those of nxattn_fwd.
+ *
+ * E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is subnormal
+ * (m/8 * 2^-6); S.1111.111 is NaN; the largest finite magnitude is 448.
+ *
+ * nxattn_quantize_fp8: x [batch, seq, heads, head_dim] of dtype (F32 or BF16; strides
+ * {b, s, h} in elements, multiples of 16 bytes; head_dim contiguous, a multiple of 8, at
+ * most 1024; heads <= 4096) ->
+ *   exps  int8 [batch, heads]: e = the smallest integer with max|x[b, :, h, :]| <= 448 * 2^e,
+ *         0 for an all-zero slice, at least -127 (the E8M0 range);
+ *   codes uint8 [batch, seq, heads, head_dim] contiguous: the nearest E4M3 value of
+ *         x * 2^-e (an exact scaling), ties to the even code; the sign of a value that
+ *         rounds to zero is kept; NaN -> 0x7F.
+ * workspace: device memory of nxattn_quantize_fp8_workspace_size() bytes (batch * heads *
+ * 4: one running maximum per slice; its contents on entry do not matter); x, codes, exps
+ * and workspace must not overlap (NXATTN_ERR_INVALID). Four launches on
+ * `stream`; bit-exact by construction.
+ */
+int nxattn_quantize_fp8_workspace_size(int64_t batch, int64_t seq, int64_t heads, int64_t* bytes);
+int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                        const int64_t strides[3], uint8_t* codes, int8_t* exps, void* workspace,
+                        int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Attention of nxattn_fwd with the fp8 score GEMM above (head_dim 128, heads_q % heads_kv
+ * == 0, batch <= 8). For branch b, q head h (kv head g = h / (heads_q / heads_kv)):
+ *   keys j < P_b: prefix row j (codes prefix_k8[b], exponent prefix_k_exp[b, g]; value
+ *   prefix_v[b]), else own row j - P_b (codes k8, exponent k_exp[b, g]; value v);
+ *   s_j = scale * 2^(q_exp[b, h] + e_j) * <dec(q8), dec(k8_j)>, o = softmax(s) . V.
+ * Layouts: q8 [batch, seq_q, heads_q, 128] and k8 [batch, seq_q, heads_kv, 128] contiguous
+ * E4M3 (as nxattn_quantize_fp8 writes them); v, o bf16 with element strides {b, s, h};
+ * prefix_k8[b] E4M3 [P_b, heads_kv, 128] contiguous; prefix_v[b] bf16 [P_b, heads_kv, 128]
+ * contiguous (the V half of one layer slice of the online cache); exponents int8 in
+ * device memory. lse as in nxattn_fwd. Outputs must not overlap inputs. scale <= 0 selects
+ * 1/sqrt(128).
+ */
+typedef struct {
+  int32_t batch;
+  int32_t seq_q;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;                                   /* 128 */
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const int8_t* q_exp;                                /* [batch, heads_q]  */
+  const int8_t* k_exp;                                /* [batch, heads_kv] */
+  const void* v;
+  void* o;
+  int64_t v_strides[3];
+  int64_t o_strides[3];
+  const uint8_t* prefix_k8[NXATTN_MAX_BRANCHES];      /* NULL iff prefix_len[b] == 0 */
+  const void* prefix_v[NXATTN_MAX_BRANCHES];          /* NULL iff prefix_len[b] == 0 */
+  int32_t prefix_len[NXATTN_MAX_BRANCHES];
+  const int8_t* prefix_k_exp;                         /* [batch, heads_kv]; needed if any prefix */
+  float scale;
+  float* lse;                                         /* NULL, or [batch, heads_q, seq_q] fp32 */
+} nxattn_fwd_fp8_args;
+
+int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* args, hipStream_t stream);
+
+/*
  * Classifier-free guidance: out = uncond + guidance * (cond - uncond) over n elements.
  * LingBot-Video page, "Key Parameters": guidance_scale, guidance active above 1.0;
  * NeoPP page: the two KV branches (cond, uncond). The combination is evaluated in

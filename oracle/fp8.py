@@ -62,12 +62,14 @@ def e4m3_encode(x) -> np.ndarray:
 
 def fp8_exponent(amax: float) -> int:
     """The scale exponent of a slice with largest magnitude amax: the smallest integer e
-    with amax <= 448 * 2^e (so every scaled value fits the finite range); 0 for amax = 0."""
+    with amax <= 448 * 2^e (so every scaled value fits the finite range); 0 for amax = 0.
+    The scale 2^e is consumed as an E8M0 value (2^(v - 127), v in 0..254), so e is held at
+    -127 or above (a slice below 448 * 2^-127 keeps e = -127 and still fits)."""
     a = float(amax)
     if a == 0.0:
         return 0
     m, E = math.frexp(a)            # a = m * 2^E, 0.5 <= m < 1; 448 = 0.875 * 2^9
-    return E - 9 + (1 if m > 0.875 else 0)
+    return max(-127, E - 9 + (1 if m > 0.875 else 0))
 
 
 def quantize_fp8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -14,6 +14,16 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 # (relative error ~ Skv * 2^-24 at worst) plus the fp32 scores; a shift of the lse by
 # d scales the implied softmax normaliser by e^d, so 1e-3 is a 0.1 % normaliser error
 TOL_LSE = 1e-3
+# ... plus a part relative to |lse|: the scores themselves carry fp32 accumulation error
+# (about D * 2^-24 of the sum of |q_d k_d| over the head dimension), which grows with
+# their magnitude; large-magnitude scores (keys 100x the queries' scale) reach |lse| ~ 300
+TOL_LSE_REL = 1e-4
+
+
+def lse_err_ok(got, ref) -> bool:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return bool(np.all(np.abs(got - ref) <= TOL_LSE + TOL_LSE_REL * np.abs(ref)))
 
 
 def fused_q(q_rot: np.ndarray, head_dim: int, scale: float = 0.0) -> np.ndarray:

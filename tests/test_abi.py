@@ -31,7 +31,7 @@ def binding_build():
 
 def declared_symbols():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(nxattn_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(nxattn_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_declares_the_four_calls():
@@ -213,6 +213,68 @@ def test_merge_rejects(lib):
     assert "overlaps" in nx.last_error()
     # empty problems return before anything else is looked at
     assert merge_call(lib, po, pl, S=0) == OK
+
+
+def test_quantize_fp8_rejects(lib):
+    f = lib.nxattn_quantize_fp8
+    st = (ctypes.c_int64 * 3)(64 * 4 * 128, 4 * 128, 128)
+    X, C, E, W = FAKE, FAKE + GB, FAKE + 2 * GB, FAKE + 3 * GB
+    ok = dict(x=X, dtype=1, B=2, S=64, H=4, D=128, st=st, c=C, e=E, w=W, wb=1 << 20)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["dtype"], a["B"], a["S"], a["H"], a["D"], a["st"], a["c"], a["e"], a["w"], a["wb"], None)
+    assert call(dtype=7) == UNSUPPORTED
+    assert call(D=12) == UNSUPPORTED
+    assert call(H=5000) == UNSUPPORTED
+    assert call(B=-1) == INVALID
+    assert call(x=None) == INVALID
+    assert call(x=X + 8) == ALIGN
+    assert call(c=C + 4) == ALIGN
+    assert call(wb=4) == INVALID                                 # workspace too small (32 needed)
+    assert call(c=X + 64) == INVALID                             # codes overlap x
+    assert call(e=C + 100) == INVALID                            # exps overlap codes
+    assert call(S=0) == OK
+    n = ctypes.c_int64(-1)
+    assert lib.nxattn_quantize_fp8_workspace_size(2, 64, 4, ctypes.byref(n)) == OK and n.value == 2 * 4 * 4
+    assert lib.nxattn_quantize_fp8_workspace_size(-1, 64, 4, ctypes.byref(n)) == INVALID
+
+
+def fp8_args(**kw):
+    a = binding.FwdFp8Args()
+    a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = 2, 64, 8, 2, 128
+    a.q8, a.k8, a.v = FAKE, FAKE + GB, FAKE + 2 * GB
+    a.q_exp, a.k_exp = FAKE + 3 * GB, FAKE + 3 * GB + 4096
+    a.o = FAKE + 4 * GB
+    for i, s in enumerate((64 * 2 * 128, 2 * 128, 128)):
+        a.v_strides[i] = s
+    for i, s in enumerate((64 * 8 * 128, 8 * 128, 128)):
+        a.o_strides[i] = s
+    for key, val in kw.items():
+        if key in ("prefix_len", "prefix_k8", "prefix_v", "v_strides", "o_strides"):
+            for i, x in enumerate(val):
+                getattr(a, key)[i] = x
+        else:
+            setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), UNSUPPORTED),
+    (dict(batch=9), UNSUPPORTED),
+    (dict(heads_q=6, heads_kv=4), INVALID),
+    (dict(q8=None), INVALID),
+    (dict(q_exp=None), INVALID),
+    (dict(q8=FAKE + 8), ALIGN),
+    (dict(v_strides=(64 * 2 * 128, 2 * 128 + 4, 128)), ALIGN),
+    (dict(prefix_len=(5, 0)), INVALID),                                   # P > 0 needs pointers
+    (dict(prefix_len=(5, 0), prefix_k8=(FAKE + 5 * GB, None)), INVALID),  # ... both of them
+    (dict(prefix_len=(5, 0), prefix_k8=(FAKE + 5 * GB, None), prefix_v=(FAKE + 6 * GB, None)), INVALID),  # exps
+    (dict(o=FAKE + GB), INVALID),                                         # o overlaps k8
+    (dict(scale=float("inf")), INVALID),
+])
+def test_fwd_fp8_rejects(lib, kw, code):
+    assert lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(**kw)), None) == code
+    assert nx.last_error() != ""
 
 
 def test_fwd_null_args(lib):

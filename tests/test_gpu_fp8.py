@@ -1,0 +1,117 @@
+"""GPU parity of the FP8 path: the E4M3 quantization bit for bit against the oracle, and
+the attention with the fp8 score GEMM against the oracle's attention of the dequantized
+q and k (the recipe's definition), within the bf16 gate (P and P.V are the bf16 path's)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+import bidirectional_transformer_attention_amd as nx
+from bidirectional_transformer_attention_amd import synth
+from helpers import TOL, attention_err, f64, lse_err_ok
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def note(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    nx.load()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(2, 300, 5, 128), (1, 17, 3, 72), (3, 1, 2, 8)])
+def test_quantize_bitexact(dtype, shape):
+    note(f"quantize fp8 {dtype} {shape}")
+    B, S, H, D = shape
+    x = synth.random_tensor(shape, 4000 + S, torch.float32)
+    mult = torch.tensor([1.0, 300.0, 1e-3, 0.0, 7.0][:H] + [1.0] * max(0, H - 5))
+    x = (x * mult[None, None, :, None]).to(dtype)              # head 3 (if any): all zero
+    if H > 2:
+        x[0, 0, 2, 0] = torch.tensor(448.0 * 2.0 ** -10, dtype=dtype)   # an exact 448 * 2^e amax
+    codes, exps = nx.nxattn_quantize_fp8(x.to(DEV))
+    torch.cuda.synchronize()
+    rc, re = ofp8.quantize_fp8(f64(x))
+    assert np.array_equal(exps.cpu().numpy(), re)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_strided_and_tiny():
+    note("quantize fp8 strided view, fp32 subnormal slice")
+    base = synth.random_tensor((2, 40, 6, 64), 4100, torch.float32)
+    base[:, :, 3, :] *= 1e-39                                   # fp32 subnormals: e clamps at -127
+    x = base.to(DEV)[:, :, 1:5, :]
+    codes, exps = nx.nxattn_quantize_fp8(x)
+    torch.cuda.synchronize()
+    rc, re = ofp8.quantize_fp8(f64(base[:, :, 1:5, :]))
+    assert np.array_equal(exps.cpu().numpy(), re) and np.array_equal(codes.cpu().numpy(), rc)
+    assert int(re[:, 2].min()) == -127
+
+
+def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True):
+    D = 128
+    note(f"fwd fp8 B={B} S={S} Hq={Hq} Hkv={Hkv} P={P} prefix x{pre_mult} seed={seed}")
+    q = synth.random_tensor((B, S, Hq, D), seed, torch.bfloat16)
+    k = synth.random_tensor((B, S, Hkv, D), seed + 1, torch.bfloat16)
+    v = synth.random_tensor((B, S, Hkv, D), seed + 2, torch.bfloat16)
+    pk = [(synth.random_tensor((p, Hkv, D), seed + 3 + b, torch.float32) * pre_mult).to(torch.bfloat16) if p else None
+          for b, p in enumerate(P)]
+    pv = [synth.random_tensor((p, Hkv, D), seed + 13 + b, torch.bfloat16) if p else None for b, p in enumerate(P)]
+    q8, qe = nx.nxattn_quantize_fp8(q.to(DEV))
+    k8, ke = nx.nxattn_quantize_fp8(k.to(DEV))
+    pk8, pke = [], torch.zeros((B, Hkv), dtype=torch.int8, device=DEV)
+    for b in range(B):
+        if pk[b] is None:
+            pk8.append(None)
+            continue
+        c, e = nx.nxattn_quantize_fp8(pk[b].to(DEV)[None])
+        pk8.append(c[0])
+        pke[b] = e[0]
+    o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+    ls = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV) if lse else None
+    nx.nxattn_fwd_fp8(q8, k8, qe, ke, v.to(DEV), o, pk8, [t.to(DEV) if t is not None else None for t in pv],
+                      pke if any(P) else None, lse=ls)
+    torch.cuda.synchronize()
+    # the reference dequantizes the oracle's own codes (equal to the GPU's: checked here too)
+    rq, rqe = ofp8.quantize_fp8(f64(q))
+    rk, rke = ofp8.quantize_fp8(f64(k))
+    assert np.array_equal(q8.cpu().numpy(), rq) and np.array_equal(k8.cpu().numpy(), rk)
+    dq, dk = ofp8.dequantize_fp8(rq, rqe), ofp8.dequantize_fp8(rk, rke)
+    for b in range(B):
+        dpk = None
+        if pk[b] is not None:
+            c, e = ofp8.quantize_fp8(f64(pk[b])[None])
+            dpk = ofp8.dequantize_fp8(c, e)[0]
+        args = (dq[b], dk[b], f64(v[b]), dpk, f64(pv[b]) if pv[b] is not None else None)
+        ref = oracle.attention(*args)
+        err = attention_err(f64(o.cpu()[b]), ref)
+        assert err <= TOL["bf16"], (b, err)
+        if lse:
+            rl = oracle.attention_lse(*args)
+            assert lse_err_ok(f64(ls.cpu()[b]), rl), (b, float(np.max(np.abs(f64(ls.cpu()[b]) - rl))))
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,P", [
+    (2, 300, 8, 2, (37, 0)),      # ragged Sq, straddling prefix, a branch without prefix
+    (1, 1, 8, 1, (200,)),         # one own token, long prefix
+    (2, 640, 8, 2, (128, 200)),   # whole prefix tiles, then a straddling one
+    (3, 70, 2, 1, (5, 0, 64)),
+    (2, 200, 4, 2, (300, 7)),     # prefix longer than the own tokens; ragged last tile
+    (1, 129, 4, 4, (0,)),         # G = 1, no prefix
+])
+def test_fwd_fp8_reduced(B, S, Hq, Hkv, P):
+    fp8_case(B, S, Hq, Hkv, P, 4200 + S)
+
+
+def test_fwd_fp8_prefix_scale_differs():
+    # prefix keys 100x larger than own keys: their exponents differ by ~7, so the tile that
+    # straddles the prefix end mixes two E8M0 row scales
+    fp8_case(2, 160, 8, 2, (100, 30), 4300, pre_mult=100.0)

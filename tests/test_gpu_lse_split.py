@@ -2,7 +2,7 @@
 of attention over disjoint key sets, through the C ABI, against the CPU fp64 oracle.
 
 Bars: the attention gate (max slice error 1e-4 fp32 / 2e-2 bf16) for outputs; the
-log-sum-exp within TOL_LSE (absolute, natural log) of the oracle's; the merge alone
+log-sum-exp within 1e-3 + 1e-4*|lse| (natural log) of the oracle's; the merge alone
 within its fp32 arithmetic plus one output rounding.
 """
 import sys
@@ -14,7 +14,7 @@ import torch
 import oracle
 import bidirectional_transformer_attention_amd as nx
 from bidirectional_transformer_attention_amd import synth
-from helpers import TOL, TOL_LSE, attention_err, f64, fused_q
+from helpers import TOL, attention_err, f64, fused_q, lse_err_ok
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -58,7 +58,7 @@ def check(o, lse, q, k, v, pre, dtype, prefix_only=False):
         assert err <= tol, (b, err)
         if lse is not None:
             lerr = float(np.max(np.abs(f64(lse[b]) - rl)))
-            assert lerr <= TOL_LSE, (b, lerr)
+            assert lse_err_ok(f64(lse[b]), rl), (b, lerr)
 
 
 def dev(*ts):

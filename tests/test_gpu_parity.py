@@ -457,6 +457,39 @@ def test_step_dit1k_bf16_sampled():
     step_case("dit1k_bf16", 96, 3)
 
 
+@pytest.mark.parametrize("name", ["dit1k_fp8qk+replay", "dit2k_fp8qk"])
+def test_step_fp8qk_sampled(name):
+    # the bench configuration of the fp8 score GEMM at full size: the codes of the step's
+    # own rotated q and k (and of each prefix K) bit for bit against the oracle's
+    # quantization, then sampled rows of the attention against the oracle's attention of
+    # the dequantized inputs
+    from oracle import fp8 as ofp8
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
+    note(f"step {name} (fp8 score GEMM, sampled rows)")
+    inp = synth.make_inputs(wl)
+    step = AttentionStep(wl, inp)
+    step()
+    torch.cuda.synchronize()
+    qg, kg = f64(step.q.cpu()), f64(step.k.cpu())
+    rq, rqe = ofp8.quantize_fp8(qg)
+    rk, rke = ofp8.quantize_fp8(kg)
+    assert np.array_equal(step.q8.cpu().numpy(), rq) and np.array_equal(step.qe.cpu().numpy(), rqe)
+    assert np.array_equal(step.k8.cpu().numpy(), rk) and np.array_equal(step.ke.cpu().numpy(), rke)
+    dq, dk = ofp8.dequantize_fp8(rq, rqe), ofp8.dequantize_fp8(rk, rke)
+    o = step.o.cpu()
+    for b in range(wl.branches):
+        pre = step.prefix_online[b]
+        dpk = pv = None
+        if pre is not None:
+            pc, pe = ofp8.quantize_fp8(f64(pre[0].cpu())[None])
+            assert np.array_equal(step.pk8[b].cpu().numpy(), pc) and np.array_equal(step.pke[b].cpu().numpy(), pe[0])
+            dpk, pv = ofp8.dequantize_fp8(pc, pe)[0], f64(pre[1].cpu())
+        rows = sample_rows(wl.seq, 48, 700 + b)
+        ref = oracle.attention(dq[b][rows], dk[b], f64(inp.v[b]), dpk, pv, rows=np.arange(len(rows)))
+        err = attention_err(f64(o[b][torch.from_numpy(rows)]), ref)
+        assert err <= TOL["bf16"], (b, err)
+
+
 def test_step_longctx_split_keys_sampled():
     # a short query against a long prefix, keys split into ranges and merged, in the
     # launch configuration the benchmark times

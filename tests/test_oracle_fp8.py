@@ -57,7 +57,8 @@ def test_exponent_rule_matches_search():
     xs += [float(np.nextafter(np.float64(v), np.inf)) for v in (448.0, 224.0, 0.875)]
     xs += [float(np.nextafter(np.float64(v), 0.0)) for v in (448.0, 224.0, 0.875)]
     for a in xs:
-        assert fp8.fp8_exponent(a) == bf_fp8_exponent(a), a
+        assert fp8.fp8_exponent(a) == max(-127, bf_fp8_exponent(a)), a
+    assert fp8.fp8_exponent(1e-40) == -127 and fp8.fp8_exponent(448.0 * 2.0 ** -127) == -127
     assert fp8.fp8_exponent(0.0) == 0
     assert fp8.fp8_exponent(448.0) == 0 and fp8.fp8_exponent(449.0) == 1 and fp8.fp8_exponent(224.0) == -1
 
