@@ -10,6 +10,7 @@
 // combine their maxima with cross-lane swaps, one LDS atomic per row, then one global
 // atomic per (workgroup, head)); the third turns each maximum into e; the fourth writes
 // the codes. HBM-bound: the input is read twice, the codes written once.
+#include <algorithm>
 #include <cmath>
 
 #include "nx_internal.h"
@@ -18,7 +19,7 @@ namespace nx {
 
 namespace quantk {
 
-constexpr int QCH = 16;          // tokens per workgroup
+constexpr int QCH = 16;          // most tokens per workgroup
 constexpr int THREADS = 256;
 constexpr int MAX_HEADS = 4096;
 constexpr int UNROLL = 4;        // items per thread whose loads are issued together
@@ -29,7 +30,7 @@ struct Args {
   int8_t* exps;
   uint32_t* amax;                // [batch, heads] float bits of max |x| (non-negative)
   int64_t sb, ss, sh;            // input strides (elements)
-  int32_t batch, seq, heads, head_dim, nchunks;
+  int32_t batch, seq, heads, head_dim, nchunks, tpw;   // tpw: tokens per workgroup
 };
 
 template <typename T>
@@ -51,26 +52,6 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
 }
 
-// Nearest E4M3 code of y (ties to the even code), saturating at +-448, NaN -> 0x7F; the
-// sign of a value that rounds to zero is kept. Integer arithmetic on the fp32 bits.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7Fu;                          // NaN
-  if (a >= 0x43e00000u) return s | 0x7Eu;                     // |y| >= 448
-  if (a < 0x3c800000u) {                                      // |y| < 2^-6: step 2^-9
-    const float r = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE
-    return s | (uint32_t)r;                                   // 8 -> 0x08 = 2^-6
-  }
-  const uint32_t ef = (a >> 23) - 120u;                       // biased exponent 127 -> field 7
-  const uint32_t mant = a & 0x7fffffu;
-  const uint32_t keep = mant >> 20, rest = mant & 0xfffffu;
-  uint32_t c = (ef << 3) + keep;
-  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++c;   // carries into the exponent
-  return s | (c > 0x7Eu ? 0x7Eu : c);
-}
-
 // smallest integer e with amax <= 448 * 2^e (0 for 0), clamped to the E8M0 range (>= -127)
 __device__ __forceinline__ int fp8_exponent(float amax) {
   if (amax == 0.f) return 0;
@@ -80,45 +61,73 @@ __device__ __forceinline__ int fp8_exponent(float amax) {
   return e < -127 ? -127 : e;
 }
 
+// Rows (token, head) of the workgroup's chunk and the 8-element groups in them. With a
+// power-of-two row width gpr (<= 64) a thread keeps one group g and walks rows
+// rslot, rslot + 256/gpr, ... (its (token, head) advanced without divisions); otherwise
+// it walks flat items.
+struct RowWalk {
+  int g, t, h, rstep, hstep, tstep;
+  __device__ __forceinline__ void next(int heads) {
+    h += hstep;
+    t += tstep;
+    if (h >= heads) { h -= heads; ++t; }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ const T* row_ptr(const Args& a, int b, int t0, int t, int h, int g) {
+  return static_cast<const T*>(a.x) + b * a.sb + (int64_t)(t0 + t) * a.ss + (int64_t)h * a.sh + 8 * g;
+}
+
 template <typename T>
 __global__ __launch_bounds__(THREADS) void amax_kernel(Args a) {
   __shared__ uint32_t smax[MAX_HEADS];
   const int b = blockIdx.x / a.nchunks, ch = blockIdx.x % a.nchunks;
   for (int h = threadIdx.x; h < a.heads; h += THREADS) smax[h] = 0u;
   __syncthreads();
-  const int t0 = ch * QCH;
-  const int nt = min(QCH, a.seq - t0);
+  const int t0 = ch * a.tpw;
+  const int nt = min(a.tpw, a.seq - t0);
   const int gpr = a.head_dim / 8;                             // 8-element groups per row
-  // a power-of-two row width puts each row's gpr groups on gpr aligned lanes of one wave
-  const bool pow2 = (gpr & (gpr - 1)) == 0 && gpr <= 64;
-  const int items = nt * a.heads * gpr;
-  const int span = (items + THREADS * UNROLL - 1) / (THREADS * UNROLL) * (THREADS * UNROLL);  // every lane runs every round
-  const T* x = static_cast<const T*>(a.x);
-  for (int it0 = threadIdx.x; it0 < span; it0 += THREADS * UNROLL) {
-    float v[UNROLL][8];
+  if ((gpr & (gpr - 1)) == 0 && gpr <= 64) {
+    // a row's gpr groups sit on gpr aligned lanes of one wave: combine with lane swaps
+    const int rows = nt * a.heads, rstep = THREADS / gpr;
+    const int rslot = threadIdx.x / gpr;
+    RowWalk w{(int)threadIdx.x % gpr, rslot / a.heads, rslot % a.heads, rstep, rstep % a.heads, rstep / a.heads};
+    const int rounds = (rows + rstep * UNROLL - 1) / (rstep * UNROLL);   // uniform over the workgroup
+    int r = rslot;
+    for (int k = 0; k < rounds; ++k) {
+      float v[UNROLL][8];
+      RowWalk w0 = w;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {              // the round's loads first, then the maxima
-      const int it = it0 + u * THREADS;
-      const int g = it % gpr, r = it / gpr;
-      const int h = r % a.heads, t = r / a.heads;
-      if (it < items) load8<T>(x + b * a.sb + (int64_t)(t0 + t) * a.ss + (int64_t)h * a.sh + 8 * g, v[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int it = it0 + u * THREADS;
-      const bool in = it < items;
-      const int g = it % gpr, h = (it / gpr) % a.heads;
-      float m = 0.f;
-      if (in) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[u][e]));
+      for (int u = 0; u < UNROLL; ++u) {              // the round's loads first, then the maxima
+        if (r + u * rstep < rows) load8<T>(row_ptr<T>(a, b, t0, w.t, w.h, w.g), v[u]);
+        w.next(a.heads);
       }
-      if (pow2) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const bool in = r + u * rstep < rows;
+        float m = 0.f;
+        if (in) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[u][e]));
+        }
         for (int d = 1; d < gpr; d <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
-        if (in && g == 0) atomicMax(&smax[h], __float_as_uint(m));   // non-negative: bit order = value order
-      } else if (in) {
-        atomicMax(&smax[h], __float_as_uint(m));
+        if (in && w0.g == 0) atomicMax(&smax[w0.h], __float_as_uint(m));   // non-negative: bit order = value order
+        w0.next(a.heads);
       }
+      r += rstep * UNROLL;
+    }
+  } else {
+    const int items = nt * a.heads * gpr;
+    for (int it = threadIdx.x; it < items; it += THREADS) {
+      const int g = it % gpr, rr = it / gpr;
+      const int h = rr % a.heads, t = rr / a.heads;
+      float v[8];
+      load8<T>(row_ptr<T>(a, b, t0, t, h, g), v);
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+      atomicMax(&smax[h], __float_as_uint(m));
     }
   }
   __syncthreads();
@@ -137,41 +146,66 @@ __global__ __launch_bounds__(THREADS) void exp_kernel(Args a) {
   if (i < (int64_t)a.batch * a.heads) a.exps[i] = (int8_t)fp8_exponent(__uint_as_float(a.amax[i]));
 }
 
+// codes of 8 values scaled by 2^-e. Every scaled value of a finite input lies in
+// [-448, 448], where the hardware conversion (v_cvt_pk_fp8_f32) is round-to-nearest-even
+// to E4M3 (checked against the integer definition of the rounding on every bf16 value in
+// that range and on exact ties); NaN becomes 0x7F.
+__device__ __forceinline__ u32x2 codes8(const float (&v)[8], float inv) {
+  uint32_t w[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float y0 = v[4 * k] * inv, y1 = v[4 * k + 1] * inv, y2 = v[4 * k + 2] * inv, y3 = v[4 * k + 3] * inv;
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, c, true);
+    uint32_t u = (uint32_t)c;
+    if (y0 != y0) u = (u & 0xffffff00u) | 0x7Fu;
+    if (y1 != y1) u = (u & 0xffff00ffu) | 0x7F00u;
+    if (y2 != y2) u = (u & 0xff00ffffu) | 0x7F0000u;
+    if (y3 != y3) u = (u & 0x00ffffffu) | 0x7F000000u;
+    w[k] = u;
+  }
+  return u32x2{w[0], w[1]};
+}
+
 template <typename T>
 __global__ __launch_bounds__(THREADS) void quant_kernel(Args a) {
   __shared__ int8_t sexp[MAX_HEADS];
   const int b = blockIdx.x / a.nchunks, ch = blockIdx.x % a.nchunks;
   for (int h = threadIdx.x; h < a.heads; h += THREADS) sexp[h] = a.exps[(int64_t)b * a.heads + h];
   __syncthreads();
-  const int t0 = ch * QCH;
-  const int nt = min(QCH, a.seq - t0);
+  const int t0 = ch * a.tpw;
+  const int nt = min(a.tpw, a.seq - t0);
   const int gpr = a.head_dim / 8;
-  const int items = nt * a.heads * gpr;
-  const T* x = static_cast<const T*>(a.x);
-  for (int it0 = threadIdx.x; it0 < items; it0 += THREADS * UNROLL) {
-    float v[UNROLL][8];
+  auto out = [&](int t, int h, int g) {
+    return reinterpret_cast<u32x2*>(a.codes + (((int64_t)b * a.seq + t0 + t) * a.heads + h) * a.head_dim + 8 * g);
+  };
+  auto inv_of = [&](int h) { return __uint_as_float((uint32_t)(127 - sexp[h]) << 23); };   // 2^-e, exact
+  if ((gpr & (gpr - 1)) == 0 && gpr <= 64) {
+    const int rows = nt * a.heads, rstep = THREADS / gpr;
+    const int rslot = threadIdx.x / gpr;
+    RowWalk w{(int)threadIdx.x % gpr, rslot / a.heads, rslot % a.heads, rstep, rstep % a.heads, rstep / a.heads};
+    for (int r = rslot; r < rows; r += rstep * UNROLL) {
+      float v[UNROLL][8];
+      RowWalk w0 = w;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {              // the round's loads first, then the codes
-      const int it = it0 + u * THREADS;
-      const int g = it % gpr, r = it / gpr;
-      const int h = r % a.heads, t = r / a.heads;
-      if (it < items) load8<T>(x + b * a.sb + (int64_t)(t0 + t) * a.ss + (int64_t)h * a.sh + 8 * g, v[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int it = it0 + u * THREADS;
-      if (it >= items) break;
-      const int g = it % gpr, r = it / gpr;
-      const int h = r % a.heads, t = r / a.heads;
-      const float inv = __uint_as_float((uint32_t)(127 - sexp[h]) << 23);   // 2^-e, exact
-      uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo |= e4m3_code(v[u][e] * inv) << (8 * e);
-        hi |= e4m3_code(v[u][4 + e] * inv) << (8 * e);
+      for (int u = 0; u < UNROLL; ++u) {              // the round's loads first, then the codes
+        if (r + u * rstep < rows) load8<T>(row_ptr<T>(a, b, t0, w.t, w.h, w.g), v[u]);
+        w.next(a.heads);
       }
-      *reinterpret_cast<u32x2*>(a.codes + (((int64_t)b * a.seq + t0 + t) * a.heads + h) * a.head_dim + 8 * g) =
-          u32x2{lo, hi};
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        if (r + u * rstep < rows) *out(w0.t, w0.h, w0.g) = codes8(v[u], inv_of(w0.h));
+        w0.next(a.heads);
+      }
+    }
+  } else {
+    const int items = nt * a.heads * gpr;
+    for (int it = threadIdx.x; it < items; it += THREADS) {
+      const int g = it % gpr, rr = it / gpr;
+      const int h = rr % a.heads, t = rr / a.heads;
+      float v[8];
+      load8<T>(row_ptr<T>(a, b, t0, t, h, g), v);
+      *out(t, h, g) = codes8(v, inv_of(h));
     }
   }
 }
@@ -214,7 +248,9 @@ extern "C" int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int6
   if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: x is not 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: codes not 8-byte aligned");
   if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: workspace not 4-byte aligned");
-  const int64_t nchunks = (seq + QCH - 1) / QCH;
+  // tokens per workgroup: QCH, or fewer for short inputs so that ~512 workgroups run
+  const int64_t tpw = std::max<int64_t>(1, std::min<int64_t>(QCH, batch * seq / 512));
+  const int64_t nchunks = (seq + tpw - 1) / tpw;
   const int64_t need = batch * heads * 4;
   if (workspace_bytes < need)
     return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8: workspace_bytes %lld < %lld", (long long)workspace_bytes,
@@ -230,7 +266,7 @@ extern "C" int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int6
   a.x = x; a.codes = codes; a.exps = exps; a.amax = static_cast<uint32_t*>(workspace);
   a.sb = strides[0]; a.ss = strides[1]; a.sh = strides[2];
   a.batch = (int32_t)batch; a.seq = (int32_t)seq; a.heads = (int32_t)heads; a.head_dim = (int32_t)head_dim;
-  a.nchunks = (int32_t)nchunks;
+  a.nchunks = (int32_t)nchunks; a.tpw = (int32_t)tpw;
   const unsigned grid = (unsigned)(batch * nchunks);
   const unsigned egrid = (unsigned)((batch * heads + THREADS - 1) / THREADS);
   clear_kernel<<<egrid, THREADS, 0, stream>>>(a);

@@ -236,7 +236,7 @@ int nxattn_attn_merge(const void* const* part_o, const float* const* part_lse, i
  *         0 for an all-zero slice, at least -127 (the E8M0 range);
  *   codes uint8 [batch, seq, heads, head_dim] contiguous: the nearest E4M3 value of
  *         x * 2^-e (an exact scaling), ties to the even code; the sign of a value that
- *         rounds to zero is kept; NaN -> 0x7F.
+ *         rounds to zero is kept; NaN -> 0x7F. x must not hold infinities.
  * workspace: device memory of nxattn_quantize_fp8_workspace_size() bytes (batch * heads *
  * 4: one running maximum per slice; its contents on entry do not matter); x, codes, exps
  * and workspace must not overlap (NXATTN_ERR_INVALID). Four launches on
