@@ -212,9 +212,10 @@ def main() -> int:
     nbytes = {
         "relayout": sum(2 * 2 * p * wl.heads_kv * wl.head_dim * es for p in wl.prefix_len)
         if wl.prefix_layout == "replay" else 0,
-        "rope": 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
+        "rope": 0 if wl.qk_fp8 else 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
         "cfg": 3 * step.q[0].numel() * es if step.use_cfg else 0,
-        # reads q, k and the prefix K twice (maximum, then codes), writes one byte per element
+        # reads q, k (rotated inside both passes) and the prefix K twice (maximum, then
+        # codes), writes one byte per element
         "quantize": (2 * es + 1) * (step.q.numel() + step.k.numel()
                                     + sum(p[0].numel() for p in step.prefix_online if p is not None))
         if wl.qk_fp8 else 0,
@@ -264,7 +265,7 @@ def main() -> int:
                    if wl.prefix_layout == "replay" else "online [2,P,H,D]",
                    "splits": step.splits,
                    "step": ("relayout + rope(k) + fused attention (q rotated on load)" if step.fuse_q_rope
-                            else "relayout + rope(q,k) + fp8 quantize(q, k, prefix k) + fused attention with fp8 QK"
+                            else "relayout + fp8 quantize(rope(q), rope(k), prefix k) + fused attention with fp8 QK"
                             if wl.qk_fp8 else "relayout + rope(q,k) + fused attention")
                    + (f" over {step.splits} key ranges + merge" if step.splits > 1 else "") + " + cfg",
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},

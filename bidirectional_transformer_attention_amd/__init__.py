@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     nxattn_fwd,
     nxattn_fwd_fp8,
     nxattn_quantize_fp8,
+    nxattn_rope_quantize_fp8,
     quantize_fp8_workspace_bytes,
     nxattn_kv_relayout,
     nxattn_rope_apply,

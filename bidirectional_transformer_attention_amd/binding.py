@@ -22,7 +22,8 @@ MAX_BRANCHES = 8
 MAX_SPLITS = 16
 
 SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_fwd_workspace_size",
-           "nxattn_attn_merge", "nxattn_quantize_fp8_workspace_size", "nxattn_quantize_fp8", "nxattn_fwd_fp8",
+           "nxattn_attn_merge", "nxattn_quantize_fp8_workspace_size", "nxattn_quantize_fp8",
+           "nxattn_rope_quantize_fp8", "nxattn_fwd_fp8",
            "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error", "nxattn_version")
 
 
@@ -36,6 +37,14 @@ class RopeDesc(ctypes.Structure):
     _fields_ = [("n_axes", ctypes.c_int32), ("grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int32 * 3),
                 ("offset", ctypes.c_int32 * 3), ("theta", ctypes.c_double), ("interleaved", ctypes.c_int32),
                 ("global_freq", ctypes.c_int32)]
+
+
+class Fp8Tensor(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("heads", ctypes.c_int64), ("strides", ctypes.c_int64 * 3),
+                ("codes", ctypes.c_void_p), ("exps", ctypes.c_void_p)]
+
+
+MAX_FP8_TENSORS = 4
 
 
 class FwdArgs(ctypes.Structure):
@@ -91,6 +100,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nxattn_quantize_fp8.argtypes = [vp, i32, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), vp, vp, vp,
                                         i64, vp]
     lib.nxattn_quantize_fp8.restype = i32
+    lib.nxattn_rope_quantize_fp8.argtypes = [ctypes.POINTER(Fp8Tensor), i32, i32, i64, i64, i64,
+                                             ctypes.POINTER(RopeDesc), vp, i64, vp]
+    lib.nxattn_rope_quantize_fp8.restype = i32
     lib.nxattn_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), vp]
     lib.nxattn_fwd_fp8.restype = i32
     lib.nxattn_cfg_combine.argtypes = [vp, vp, vp, i64, ctypes.c_float, i32, vp]
@@ -345,12 +357,7 @@ def quantize_fp8_workspace_bytes(batch: int, seq: int, heads: int) -> int:
     return int(n.value)
 
 
-def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, exps: Optional[torch.Tensor] = None,
-                        workspace: Optional[torch.Tensor] = None, stream=None):
-    """E4M3 codes (uint8, contiguous [B,S,H,D]) and per-(b,h) exponents (int8 [B,H]) of x
-    [B,S,H,D] (bf16 or f32, strided, D contiguous); outputs and the workspace are
-    allocated with torch when not given. Returns (codes, exps)."""
-    _gpu(x, codes, exps, workspace)
+def _quant_outputs(x, codes, exps):
     if x.dim() != 4 or x.stride(3) != 1:
         raise NxattnError(1, "x must be [B, S, H, D] with D contiguous")
     B, S, H, D = x.shape
@@ -362,6 +369,17 @@ def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e
         raise NxattnError(1, "codes must be a contiguous uint8 [B, S, H, D] tensor")
     if exps.dtype != torch.int8 or tuple(exps.shape) != (B, H) or not exps.is_contiguous():
         raise NxattnError(1, "exps must be a contiguous int8 [B, H] tensor")
+    return codes, exps
+
+
+def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, exps: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """E4M3 codes (uint8, contiguous [B,S,H,D]) and per-(b,h) exponents (int8 [B,H]) of x
+    [B,S,H,D] (bf16 or f32, strided, D contiguous); outputs and the workspace are
+    allocated with torch when not given. Returns (codes, exps)."""
+    _gpu(x, codes, exps, workspace)
+    codes, exps = _quant_outputs(x, codes, exps)
+    B, S, H, D = x.shape
     if workspace is None:
         workspace = torch.empty(max(4, quantize_fp8_workspace_bytes(B, S, H)), dtype=torch.uint8, device=x.device)
     st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
@@ -369,6 +387,44 @@ def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e
                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
     return codes, exps
+
+
+def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
+                             codes: Optional[Sequence[torch.Tensor]] = None,
+                             exps: Optional[Sequence[torch.Tensor]] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Codes and exponents (as nxattn_quantize_fp8) of each x in xs ([B,S,H_t,D], one
+    dtype, shared B, S, D and positions) rotated as nxattn_rope_apply would rotate it; the
+    x are not modified. Returns [(codes, exps)] in the order of xs."""
+    xs = list(xs)
+    if not 1 <= len(xs) <= MAX_FP8_TENSORS:
+        raise NxattnError(1, f"need 1 to {MAX_FP8_TENSORS} tensors")
+    codes = list(codes) if codes is not None else [None] * len(xs)
+    exps = list(exps) if exps is not None else [None] * len(xs)
+    _gpu(*xs, *[c for c in codes if c is not None], *[e for e in exps if e is not None], workspace)
+    B, S, _, D = xs[0].shape
+    outs = []
+    for x, c, e in zip(xs, codes, exps):
+        if x.dim() != 4 or (x.shape[0], x.shape[1], x.shape[3]) != (B, S, D) or x.dtype != xs[0].dtype:
+            raise NxattnError(1, "tensors must share batch, seq, head_dim and dtype")
+        c, e = _quant_outputs(x, c, e)
+        outs.append((c, e))
+    if len(descs) != B:
+        raise NxattnError(1, "one RopeDesc per batch entry is required")
+    total = sum(x.shape[2] for x in xs)
+    if workspace is None:
+        workspace = torch.empty(max(4, quantize_fp8_workspace_bytes(B, S, total)), dtype=torch.uint8,
+                                device=xs[0].device)
+    arr = (Fp8Tensor * len(xs))()
+    for i, (x, (c, e)) in enumerate(zip(xs, outs)):
+        arr[i].x, arr[i].heads = x.data_ptr(), x.shape[2]
+        for k in range(3):
+            arr[i].strides[k] = x.stride(k)
+        arr[i].codes, arr[i].exps = c.data_ptr(), e.data_ptr()
+    darr = (RopeDesc * max(1, B))(*descs)
+    _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return outs
 
 
 def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_exp: torch.Tensor, v: torch.Tensor,

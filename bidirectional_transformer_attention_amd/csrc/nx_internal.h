@@ -49,6 +49,56 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Checks one nxattn_rope_desc against seq and head_dim (fail() with `who` on error).
 int check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim, const char* who);
 
+// ---- FP8 quantization ----------------------------------------------------------------------
+// Running maxima of the quantizers (float bits of non-negative values): AMAX_SLOTS copies of
+// the [batch * heads] array, each starting on its own 128-byte line; workgroup w updates
+// copy w % AMAX_SLOTS, so that the global atomics of thousands of workgroups on a few
+// slices do not all queue on one cache line. The exponent pass reduces over the copies.
+constexpr int AMAX_SLOTS = 32;
+inline int64_t amax_stride(int64_t n) { return (n + 31) / 32 * 32; }
+inline int64_t amax_words(int64_t n) { return AMAX_SLOTS * amax_stride(n); }
+// zeroes every copy of the n maxima
+void launch_amax_clear(uint32_t* amax, int64_t n, hipStream_t stream);
+// exps[i] = fp8_exponent of the largest of the copies of maximum i, i < n
+void launch_fp8_exponents(const uint32_t* amax, int8_t* exps, int64_t n, hipStream_t stream);
+
+// smallest integer e with amax <= 448 * 2^e (0 for 0), held at -127 or above (E8M0 range)
+__device__ __forceinline__ int fp8_exponent(float amax) {
+  if (amax == 0.f) return 0;
+  int E;
+  const float m = frexpf(amax, &E);          // amax = m * 2^E, 0.5 <= m < 1; 448 = 0.875 * 2^9
+  const int e = E - 9 + (m > 0.875f ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// The tensors of one RoPE launch: they share batch, seq, head_dim, dtype and positions, and
+// their heads are laid end to end (tensor t owns heads hoff[t] .. hoff[t+1]-1 of the
+// launch; hoff[t] = total heads for t >= n). Rotation in place uses x[0] only; the fp8
+// passes read every x and write codes[t] (contiguous [batch, seq, heads_t, head_dim]) and
+// exps[t] ([batch, heads_t]), with the running maxima in amax (AMAX_SLOTS copies of
+// [batch * total heads], copy stride astride).
+constexpr int ROPE_MAX_TENSORS = NXATTN_MAX_FP8_TENSORS;
+struct RopeTensors {
+  void* x[ROPE_MAX_TENSORS];
+  int64_t sb[ROPE_MAX_TENSORS], ss[ROPE_MAX_TENSORS], sh[ROPE_MAX_TENSORS];
+  uint8_t* codes[ROPE_MAX_TENSORS];
+  int8_t* exps[ROPE_MAX_TENSORS];
+  int32_t hoff[ROPE_MAX_TENSORS + 1];
+  int32_t n;
+  uint32_t* amax;
+  int64_t astride;
+};
+enum class RopeMode { Rotate, Max, Codes };
+
+// Validates the RoPE arguments (errors name `who`; rope and the x pointers and strides of
+// every tensor) and launches: with fp8 == false, the in-place rotation of x[0]; with
+// fp8 == true (total heads <= 4096), the clear of the maxima, the pass that takes them
+// from the rotated values and the pass that writes exponents and codes. The caller checks
+// codes, exps and amax.
+int rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64_t seq, int64_t head_dim, int dtype,
+                const nxattn_rope_desc* rope, bool fp8, hipStream_t stream);
+
+
 // RoPE of q applied on load by the fused attention kernel (axes beyond n_axes have grid
 // 1, pairs 0, offset 0)
 struct RopeQ {

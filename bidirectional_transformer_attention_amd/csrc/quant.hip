@@ -5,13 +5,17 @@
 // element x * 2^-e (an exact power-of-two scaling) is rounded to the nearest E4M3 value,
 // ties to the even code.
 //
-// Four launches. A small one clears one maximum per (branch, head) in the caller's
-// workspace; the second reduces |x| over chunks of QCH tokens (lanes that share a row
-// combine their maxima with cross-lane swaps, one LDS atomic per row, then one global
-// atomic per (workgroup, head)); the third turns each maximum into e; the fourth writes
-// the codes. HBM-bound: the input is read twice, the codes written once.
+// Four launches. A small one clears the running maxima in the caller's workspace (32
+// line-separated copies per (branch, head)); the second reduces |x| over chunks of QCH
+// tokens (lanes that share a row combine their maxima with cross-lane swaps, one LDS
+// atomic per row, then one global atomic per (workgroup, head) into the workgroup's
+// copy); the third turns the largest copy into e; the fourth writes the codes. HBM-bound: the input is read twice, the codes written once. Where the input
+// would first be rotated by RoPE, nxattn_rope_quantize_fp8 rotates it inside both reading
+// passes instead (the RoPE kernel's maximum and code modes), so the rotated values are
+// never stored.
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 
 #include "nx_internal.h"
 
@@ -28,7 +32,8 @@ struct Args {
   const void* x;
   uint8_t* codes;
   int8_t* exps;
-  uint32_t* amax;                // [batch, heads] float bits of max |x| (non-negative)
+  uint32_t* amax;                // AMAX_SLOTS copies of [batch, heads] float bits of max |x|
+  int64_t astride;               // amax_stride(batch * heads)
   int64_t sb, ss, sh;            // input strides (elements)
   int32_t batch, seq, heads, head_dim, nchunks, tpw;   // tpw: tokens per workgroup
 };
@@ -50,15 +55,6 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
   for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
-}
-
-// smallest integer e with amax <= 448 * 2^e (0 for 0), clamped to the E8M0 range (>= -127)
-__device__ __forceinline__ int fp8_exponent(float amax) {
-  if (amax == 0.f) return 0;
-  int E;
-  const float m = frexpf(amax, &E);          // amax = m * 2^E, 0.5 <= m < 1; 448 = 0.875 * 2^9
-  const int e = E - 9 + (m > 0.875f ? 1 : 0);
-  return e < -127 ? -127 : e;
 }
 
 // Rows (token, head) of the workgroup's chunk and the 8-element groups in them. With a
@@ -132,18 +128,22 @@ __global__ __launch_bounds__(THREADS) void amax_kernel(Args a) {
   }
   __syncthreads();
   for (int h = threadIdx.x; h < a.heads; h += THREADS)
-    if (smax[h] != 0u) atomicMax(&a.amax[(int64_t)b * a.heads + h], smax[h]);
+    if (smax[h] != 0u) atomicMax(&a.amax[(blockIdx.x % AMAX_SLOTS) * a.astride + (int64_t)b * a.heads + h], smax[h]);
 }
 
-__global__ __launch_bounds__(THREADS) void clear_kernel(Args a) {
+__global__ __launch_bounds__(THREADS) void clear_kernel(uint32_t* amax, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
-  if (i < (int64_t)a.batch * a.heads) a.amax[i] = 0u;
+  if (i < n) amax[i] = 0u;
 }
 
-// one thread per (branch, head): e from the maximum
-__global__ __launch_bounds__(THREADS) void exp_kernel(Args a) {
+// one thread per (branch, head): e from the largest of the maximum's copies
+__global__ __launch_bounds__(THREADS) void exp_kernel(const uint32_t* amax, int8_t* exps, int64_t n, int64_t stride) {
   const int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;   // b * heads + h
-  if (i < (int64_t)a.batch * a.heads) a.exps[i] = (int8_t)fp8_exponent(__uint_as_float(a.amax[i]));
+  if (i >= n) return;
+  uint32_t m = 0u;
+#pragma unroll 8
+  for (int k = 0; k < AMAX_SLOTS; ++k) m = max(m, amax[k * stride + i]);
+  exps[i] = (int8_t)fp8_exponent(__uint_as_float(m));
 }
 
 // codes of 8 values scaled by 2^-e. Every scaled value of a finite input lies in
@@ -212,6 +212,17 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(Args a) {
 
 }  // namespace quantk
 
+void launch_fp8_exponents(const uint32_t* amax, int8_t* exps, int64_t n, hipStream_t stream) {
+  using namespace quantk;
+  exp_kernel<<<(unsigned)((n + THREADS - 1) / THREADS), THREADS, 0, stream>>>(amax, exps, n, amax_stride(n));
+}
+
+void launch_amax_clear(uint32_t* amax, int64_t n, hipStream_t stream) {
+  using namespace quantk;
+  const int64_t words = amax_words(n);
+  clear_kernel<<<(unsigned)((words + THREADS - 1) / THREADS), THREADS, 0, stream>>>(amax, words);
+}
+
 }  // namespace nx
 
 using namespace nx;
@@ -220,64 +231,153 @@ extern "C" int nxattn_quantize_fp8_workspace_size(int64_t batch, int64_t seq, in
   clear_error();
   if (!bytes || batch < 0 || seq < 0 || heads < 0)
     return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8_workspace_size: bad argument");
-  *bytes = batch * heads * 4;
+  *bytes = amax_words(batch * heads) * 4;
   return NXATTN_OK;
 }
+
+namespace {
+
+// Validation and launch geometry shared by both entry points. `empty`: nothing to write.
+int quant_setup(const char* who, const void* x, int dtype, int64_t batch, int64_t seq, int64_t heads,
+                int64_t head_dim, const int64_t strides[3], uint8_t* codes, int8_t* exps, void* workspace,
+                int64_t workspace_bytes, quantk::Args& a, bool& empty) {
+  using namespace quantk;
+  empty = false;
+  if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
+  if (batch < 0 || seq < 0 || heads < 0 || head_dim < 0 || !strides) return fail(NXATTN_ERR_INVALID, "%s: bad sizes", who);
+  if (head_dim % 8 != 0 || head_dim > 1024)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8 up to 1024", who);
+  if (heads > MAX_HEADS) return fail(NXATTN_ERR_UNSUPPORTED, "%s: heads > %d", who, MAX_HEADS);
+  if (seq > INT32_MAX / 2 || batch > INT32_MAX / 2) return fail(NXATTN_ERR_UNSUPPORTED, "%s: size out of range", who);
+  if (batch == 0 || seq == 0 || heads == 0 || head_dim == 0) {
+    empty = true;
+    return NXATTN_OK;
+  }
+  if (!x || !codes || !exps || !workspace) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
+  const int64_t es = esize(dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+    if ((strides[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
+  }
+  if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "%s: x is not 16-byte aligned", who);
+  if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(NXATTN_ERR_ALIGN, "%s: workspace not 4-byte aligned", who);
+  // tokens per workgroup: QCH, or fewer for short inputs so that ~512 workgroups run
+  const int64_t tpw = std::max<int64_t>(1, std::min<int64_t>(QCH, batch * seq / 512));
+  const int64_t nchunks = (seq + tpw - 1) / tpw;
+  const int64_t need = amax_words(batch * heads) * 4;
+  if (workspace_bytes < need)
+    return fail(NXATTN_ERR_INVALID, "%s: workspace_bytes %lld < %lld", who, (long long)workspace_bytes, (long long)need);
+  if (batch * nchunks > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: problem too large", who);
+  const int64_t xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
+  const int64_t cb = batch * seq * heads * head_dim;
+  if (overlaps(x, xb, codes, cb) || overlaps(x, xb, exps, batch * heads) || overlaps(x, xb, workspace, need) ||
+      overlaps(codes, cb, exps, batch * heads) || overlaps(codes, cb, workspace, need) ||
+      overlaps(exps, batch * heads, workspace, need))
+    return fail(NXATTN_ERR_INVALID, "%s: x, codes, exps and workspace must not overlap", who);
+  a.x = x; a.codes = codes; a.exps = exps; a.amax = static_cast<uint32_t*>(workspace);
+  a.astride = amax_stride(batch * heads);
+  a.sb = strides[0]; a.ss = strides[1]; a.sh = strides[2];
+  a.batch = (int32_t)batch; a.seq = (int32_t)seq; a.heads = (int32_t)heads; a.head_dim = (int32_t)head_dim;
+  a.nchunks = (int32_t)nchunks; a.tpw = (int32_t)tpw;
+  return NXATTN_OK;
+}
+
+// exponents from the maxima, then the codes
+void launch_exp_quant(const quantk::Args& a, int dtype, hipStream_t stream) {
+  using namespace quantk;
+  const unsigned grid = (unsigned)((int64_t)a.batch * a.nchunks);
+  launch_fp8_exponents(a.amax, a.exps, (int64_t)a.batch * a.heads, stream);
+  if (dtype == NXATTN_BF16)
+    quant_kernel<uint16_t><<<grid, THREADS, 0, stream>>>(a);
+  else
+    quant_kernel<float><<<grid, THREADS, 0, stream>>>(a);
+}
+
+}  // namespace
 
 extern "C" int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, int64_t heads,
                                    int64_t head_dim, const int64_t strides[3], uint8_t* codes, int8_t* exps,
                                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   using namespace quantk;
   clear_error();
-  if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
-    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_quantize_fp8: dtype %d is not F32 or BF16", dtype);
-  if (batch < 0 || seq < 0 || heads < 0 || head_dim < 0 || !strides)
-    return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8: bad sizes");
-  if (head_dim % 8 != 0 || head_dim > 1024)
-    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_quantize_fp8: head_dim must be a multiple of 8 up to 1024");
-  if (heads > MAX_HEADS) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_quantize_fp8: heads > %d", MAX_HEADS);
-  if (seq > INT32_MAX / 2 || batch > INT32_MAX / 2)
-    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_quantize_fp8: size out of range");
-  if (batch == 0 || seq == 0 || heads == 0 || head_dim == 0) return NXATTN_OK;
-  if (!x || !codes || !exps || !workspace) return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8: NULL pointer");
-  const int64_t es = esize(dtype);
-  for (int i = 0; i < 3; ++i) {
-    if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8: negative stride");
-    if ((strides[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: strides must be multiples of 16 bytes");
-  }
-  if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: x is not 16-byte aligned");
-  if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: codes not 8-byte aligned");
-  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(NXATTN_ERR_ALIGN, "nxattn_quantize_fp8: workspace not 4-byte aligned");
-  // tokens per workgroup: QCH, or fewer for short inputs so that ~512 workgroups run
-  const int64_t tpw = std::max<int64_t>(1, std::min<int64_t>(QCH, batch * seq / 512));
-  const int64_t nchunks = (seq + tpw - 1) / tpw;
-  const int64_t need = batch * heads * 4;
-  if (workspace_bytes < need)
-    return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8: workspace_bytes %lld < %lld", (long long)workspace_bytes,
-                (long long)need);
-  if (batch * nchunks > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_quantize_fp8: problem too large");
-  const int64_t xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
-  const int64_t cb = batch * seq * heads * head_dim;
-  if (overlaps(x, xb, codes, cb) || overlaps(x, xb, exps, batch * heads) || overlaps(x, xb, workspace, need) ||
-      overlaps(codes, cb, exps, batch * heads) || overlaps(codes, cb, workspace, need) ||
-      overlaps(exps, batch * heads, workspace, need))
-    return fail(NXATTN_ERR_INVALID, "nxattn_quantize_fp8: x, codes, exps and workspace must not overlap");
   Args a;
-  a.x = x; a.codes = codes; a.exps = exps; a.amax = static_cast<uint32_t*>(workspace);
-  a.sb = strides[0]; a.ss = strides[1]; a.sh = strides[2];
-  a.batch = (int32_t)batch; a.seq = (int32_t)seq; a.heads = (int32_t)heads; a.head_dim = (int32_t)head_dim;
-  a.nchunks = (int32_t)nchunks; a.tpw = (int32_t)tpw;
-  const unsigned grid = (unsigned)(batch * nchunks);
-  const unsigned egrid = (unsigned)((batch * heads + THREADS - 1) / THREADS);
-  clear_kernel<<<egrid, THREADS, 0, stream>>>(a);
-  if (dtype == NXATTN_BF16) {
+  bool empty;
+  const int st = quant_setup("nxattn_quantize_fp8", x, dtype, batch, seq, heads, head_dim, strides, codes, exps,
+                             workspace, workspace_bytes, a, empty);
+  if (st != NXATTN_OK || empty) return st;
+  const unsigned grid = (unsigned)(batch * a.nchunks);
+  launch_amax_clear(a.amax, batch * heads, stream);
+  if (dtype == NXATTN_BF16)
     amax_kernel<uint16_t><<<grid, THREADS, 0, stream>>>(a);
-    exp_kernel<<<egrid, THREADS, 0, stream>>>(a);
-    quant_kernel<uint16_t><<<grid, THREADS, 0, stream>>>(a);
-  } else {
+  else
     amax_kernel<float><<<grid, THREADS, 0, stream>>>(a);
-    exp_kernel<<<egrid, THREADS, 0, stream>>>(a);
-    quant_kernel<float><<<grid, THREADS, 0, stream>>>(a);
-  }
+  launch_exp_quant(a, dtype, stream);
   return check_launch("nxattn_quantize_fp8");
+}
+
+extern "C" int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype,
+                                        int64_t batch, int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope,
+                                        void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  static const char* who = "nxattn_rope_quantize_fp8";
+  clear_error();
+  if (!tensors || n_tensors < 1 || n_tensors > NXATTN_MAX_FP8_TENSORS)
+    return fail(NXATTN_ERR_INVALID, "%s: need 1 to %d tensors", who, NXATTN_MAX_FP8_TENSORS);
+  if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
+  if (batch < 0 || seq < 0 || head_dim < 0) return fail(NXATTN_ERR_INVALID, "%s: negative size", who);
+  int64_t total = 0;
+  for (int t = 0; t < n_tensors; ++t) {
+    if (tensors[t].heads < 0) return fail(NXATTN_ERR_INVALID, "%s: negative heads", who);
+    total += tensors[t].heads;
+    if (total > quantk::MAX_HEADS) return fail(NXATTN_ERR_UNSUPPORTED, "%s: more than %d heads in total", who, quantk::MAX_HEADS);
+  }
+  if (batch == 0 || seq == 0 || total == 0) return NXATTN_OK;
+  if (!workspace) return fail(NXATTN_ERR_INVALID, "%s: NULL workspace", who);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(NXATTN_ERR_ALIGN, "%s: workspace not 4-byte aligned", who);
+  const int64_t need = amax_words(batch * total) * 4;
+  if (workspace_bytes < need)
+    return fail(NXATTN_ERR_INVALID, "%s: workspace_bytes %lld < %lld", who, (long long)workspace_bytes, (long long)need);
+  // the tensors with heads, heads laid end to end
+  const int64_t es = esize(dtype);
+  RopeTensors tt;
+  memset(&tt, 0, sizeof(tt));
+  struct Span { const void* p; int64_t n; };
+  Span xs[NXATTN_MAX_FP8_TENSORS], outs[2 * NXATTN_MAX_FP8_TENSORS + 1];
+  int nout = 0;
+  outs[nout++] = {workspace, need};
+  for (int t = 0; t < n_tensors; ++t) {
+    const nxattn_fp8_tensor& z = tensors[t];
+    if (z.heads == 0) continue;
+    if (!z.x || !z.codes || !z.exps) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer in tensor %d", who, t);
+    if (reinterpret_cast<uintptr_t>(z.codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
+    for (int i = 0; i < 3; ++i)
+      if (z.strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+    const int k = tt.n++;
+    tt.x[k] = const_cast<void*>(z.x);
+    tt.sb[k] = z.strides[0]; tt.ss[k] = z.strides[1]; tt.sh[k] = z.strides[2];
+    tt.codes[k] = z.codes;
+    tt.exps[k] = z.exps;
+    tt.hoff[k + 1] = tt.hoff[k] + (int32_t)z.heads;
+    xs[k] = {z.x, ((batch - 1) * z.strides[0] + (seq - 1) * z.strides[1] + (z.heads - 1) * z.strides[2] + head_dim) * es};
+    outs[nout++] = {z.codes, batch * seq * z.heads * head_dim};
+    outs[nout++] = {z.exps, batch * z.heads};
+  }
+  for (int i = tt.n + 1; i <= ROPE_MAX_TENSORS; ++i) tt.hoff[i] = tt.hoff[tt.n];
+  // outputs must not overlap one another, an input or the workspace; inputs may overlap
+  // one another but not the workspace
+  for (int i = 0; i < nout; ++i) {
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(NXATTN_ERR_INVALID, "%s: outputs and workspace must not overlap", who);
+    for (int k = 0; k < tt.n; ++k)
+      if (overlaps(outs[i].p, outs[i].n, xs[k].p, xs[k].n))
+        return fail(NXATTN_ERR_INVALID, "%s: an output or the workspace overlaps an input", who);
+  }
+  tt.amax = static_cast<uint32_t*>(workspace);
+  tt.astride = amax_stride(batch * total);
+  // validates the RoPE arguments and the inputs (head_dim 8..256 among them) before the
+  // first launch
+  return rope_launch(who, tt, batch, seq, head_dim, dtype, rope, true, stream);
 }

@@ -10,13 +10,16 @@
 // 2 * B*S*H*D*esize bytes per call.
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "nx_internal.h"
 
 namespace nx {
 
-constexpr int ROPE_TOK = 4;          // tokens per workgroup
+constexpr int ROPE_TOK = 8;          // tokens per workgroup
 constexpr int ROPE_MAX_HALF = 128;   // head_dim / 2 limit
+constexpr int ROPE_MAX_HEADS = 4096; // heads limit of the fused maximum (LDS)
+constexpr int ROPE_UNROLL = 4;       // rows whose loads a thread issues together
 
 struct RopeBranch {
   int32_t n_axes, interleaved, global_freq;
@@ -27,34 +30,117 @@ struct RopeArgs {
   RopeBranch br[NXATTN_MAX_BRANCHES];
 };
 
+// codes of 4 values times inv (an exact power of two); the scaled values of finite inputs
+// lie in [-448, 448], where v_cvt_pk_fp8_f32 rounds to nearest even E4M3; NaN -> 0x7F
+__device__ __forceinline__ uint32_t fp8x4(float y0, float y1, float y2, float y3) {
+  int c = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  c = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, c, true);
+  uint32_t u = (uint32_t)c;
+  if (y0 != y0) u = (u & 0xffffff00u) | 0x7Fu;
+  if (y1 != y1) u = (u & 0xffff00ffu) | 0x7F00u;
+  if (y2 != y2) u = (u & 0xff00ffffu) | 0x7F0000u;
+  if (y3 != y3) u = (u & 0x00ffffffu) | 0x7F000000u;
+  return u;
+}
+
+// 4 consecutive elements as loaded and stored (bf16: two words; fp32: one 16-byte vector)
 template <typename T>
-__global__ __launch_bounds__(256) void rope_kernel(T* x, int64_t seq, int64_t heads, int32_t D,
-                                                   int64_t sb, int64_t ss, int64_t sh, RopeArgs args) {
+struct Quad;
+template <>
+struct Quad<uint16_t> {
+  u32x2 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+  }
+  __device__ __forceinline__ static void store(uint16_t* p, const float (&v)[4]) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+};
+template <>
+struct Quad<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ float get(int e) const { return w[e]; }
+  __device__ __forceinline__ static void store(float* p, const float (&v)[4]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
+
+// tensor t's entry of a per-tensor array (t < ROPE_MAX_TENSORS), without dynamic indexing
+template <typename V>
+__device__ __forceinline__ V pick(const V (&a)[ROPE_MAX_TENSORS], int t) {
+  V r = a[0];
+#pragma unroll
+  for (int i = 1; i < ROPE_MAX_TENSORS; ++i)
+    if (t == i) r = a[i];
+  return r;
+}
+
+// One workgroup: ROPE_TOK tokens of one branch, every head of every tensor (the heads of
+// the tensors laid end to end, `heads` in total). MODE Rotate: x[0] is rotated in place.
+// MODE Max: x is read only; the largest magnitude of the rotated values as
+// nxattn_rope_apply would store them (bf16: after rounding) is taken per (branch, head)
+// into copy blockIdx % AMAX_SLOTS of tt.amax (cleared beforehand). MODE Codes: x is read
+// only; each workgroup first turns the copies of its branch's maxima into the exponents e
+// (the branch's first workgroup also stores them), then writes the E4M3 codes of the
+// rotated, rounded values times 2^-e.
+template <typename T, RopeMode MODE>
+__global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, int32_t heads, int32_t D,
+                                                   RopeArgs args) {
+  constexpr bool FP8 = MODE != RopeMode::Rotate;
   __shared__ float cs[ROPE_TOK][ROPE_MAX_HALF];
   __shared__ float sn[ROPE_TOK][ROPE_MAX_HALF];
+  __shared__ uint32_t hw[FP8 ? ROPE_MAX_HEADS : 1];   // Max: running maxima; Codes: bits of 2^-e
   const int half = D / 2;
-  const int64_t blocks_per_branch = (seq + ROPE_TOK - 1) / ROPE_TOK;
-  const int b = (int)(blockIdx.x / blocks_per_branch);
-  const int64_t s0 = (blockIdx.x % blocks_per_branch) * ROPE_TOK;
+  const int blocks_per_branch = (seq + ROPE_TOK - 1) / ROPE_TOK;
+  const int b = (int)blockIdx.x / blocks_per_branch;
+  const int s0 = ((int)blockIdx.x - b * blocks_per_branch) * ROPE_TOK;
   const RopeBranch& br = args.br[b];
+  // tensor of launch head v: the number of tensor starts at or below v
+  auto tensor_of = [&](int v) {
+    int t = 0;
+#pragma unroll
+    for (int i = 1; i < ROPE_MAX_TENSORS; ++i) t += v >= tt.hoff[i] ? 1 : 0;
+    return t;
+  };
 
-  // 1. angles: token s -> row-major grid coordinates (+ offset) -> per-pair angle
-  for (int idx = threadIdx.x; idx < ROPE_TOK * half; idx += blockDim.x) {
-    const int tk = idx / half, j = idx % half;
-    const int64_t s = s0 + tk;
-    if (s >= seq) continue;
-    int64_t coord[3] = {0, 0, 0};
-    int64_t rem = s;
-    for (int a = br.n_axes - 1; a >= 0; --a) {
-      coord[a] = rem % br.grid[a];
-      rem /= br.grid[a];
+  if constexpr (MODE == RopeMode::Max)
+    for (int v = threadIdx.x; v < heads; v += blockDim.x) hw[v] = 0u;
+  if constexpr (MODE == RopeMode::Codes)
+    for (int v = threadIdx.x; v < heads; v += blockDim.x) {
+      const uint32_t* am = tt.amax + (int64_t)b * heads + v;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int k = 0; k < AMAX_SLOTS; ++k) m = max(m, am[k * tt.astride]);
+      const int e = fp8_exponent(__uint_as_float(m));
+      hw[v] = (uint32_t)(127 - e) << 23;                 // 2^-e, e in [-127, 120]
+      if (s0 == 0) {
+        const int t = tensor_of(v);
+        const int ht = tt.hoff[t + 1] - tt.hoff[t];
+        pick(tt.exps, t)[(int64_t)b * ht + (v - tt.hoff[t])] = (int8_t)e;
+      }
     }
-    int axis = 0, u = j;
-    while (axis < br.n_axes - 1 && u >= br.pairs[axis]) { u -= br.pairs[axis]; ++axis; }
-    const double pos = (double)(coord[axis] + br.offset[axis]);
+  // 1. angles: token s -> row-major grid coordinates (+ offset) -> per-pair angle. Axes
+  // past n_axes have grid 1 and no pairs, so a fixed three-axis unravel and the section
+  // bounds p0, p0 + p1 hold for every n_axes (branch values are uniform: no per-lane
+  // indexing of the descriptor).
+  const int g1 = br.grid[1], g2 = br.grid[2];
+  const int p0 = br.pairs[0], p1 = br.pairs[1], p2 = br.pairs[2];
+  const int f0 = br.offset[0], f1 = br.offset[1], f2 = br.offset[2];
+  for (int idx = threadIdx.x; idx < ROPE_TOK * half; idx += blockDim.x) {
+    const int tk = idx / half, j = idx - tk * half;
+    const int s = s0 + tk;
+    if (s >= seq) continue;
+    const int s12 = s / g2, c2 = s - s12 * g2;
+    const int c0 = s12 / g1, c1 = s12 - c0 * g1;
+    const bool ax1 = j >= p0, ax2 = j >= p0 + p1;
+    const int u = j - (ax1 ? p0 : 0) - (ax2 ? p1 : 0);
+    const int pk = ax2 ? p2 : ax1 ? p1 : p0;
+    const double pos = (double)(ax2 ? c2 + f2 : ax1 ? c1 + f1 : c0 + f0);
     // per-section ladder theta^(-2u / (2 pairs_k)), or one ladder theta^(-2j / D)
     const double inv_freq = br.global_freq ? exp2(br.log2_theta * (-2.0 * (double)j / (double)D))
-                                           : exp2(br.log2_theta * (-2.0 * (double)u / (2.0 * (double)br.pairs[axis])));
+                                           : exp2(br.log2_theta * (-2.0 * (double)u / (2.0 * (double)pk)));
     double sv, cv;
     sincos(pos * inv_freq, &sv, &cv);
     cs[tk][j] = (float)cv;
@@ -62,69 +148,128 @@ __global__ __launch_bounds__(256) void rope_kernel(T* x, int64_t seq, int64_t he
   }
   __syncthreads();
 
-  // 2. rotate: work item = (token, head, quad of 4 pairs)
+  // 2. rotate: work item = (token, head, quad of 4 pairs j0 .. j0+3), one tensor after
+  // another (the tensor's pointers and strides stay uniform). The item's elements form two
+  // groups of 4 at element offsets o1 and o2: (j0, j0 + D/2) for half-split pairs, whose
+  // pair e is (lo[e], hi[e]); (2 j0, 2 j0 + 4) for adjacent pairs, whose pairs are
+  // (lo0, lo1), (lo2, lo3), (hi0, hi1), (hi2, hi3). A row (token, head) has `quads` items
+  // on consecutive lanes; a thread keeps its quad and walks the rows r0, r0 + rstep, ...
+  // with (token, head) advanced without divisions, issuing the loads of ROPE_UNROLL rows
+  // before it uses them (lanes past the end load row 0 and drop it). The trip count is the
+  // same for every thread, so with a power-of-two row width (<= 32 lanes, inside one
+  // wave) the lanes of a row combine their maxima with swaps.
   const int quads = half / 4;
-  const int64_t items = (int64_t)ROPE_TOK * heads * quads;
-  for (int64_t it = threadIdx.x; it < items; it += blockDim.x) {
-    const int tk = (int)(it / (heads * quads));
-    const int64_t r = it % (heads * quads);
-    const int64_t h = r / quads;
-    const int q4 = (int)(r % quads);
-    const int64_t s = s0 + tk;
-    if (s >= seq) continue;
-    T* row = x + b * sb + s * ss + h * sh;
-    const int j0 = 4 * q4;
-    float a[4], c[4];
-    if (!br.interleaved) {
-      // pairs (j, j + D/2) for j = j0 .. j0+3
-      if constexpr (sizeof(T) == 2) {
-        const u32x2 va = *reinterpret_cast<const u32x2*>(row + j0);
-        const u32x2 vb = *reinterpret_cast<const u32x2*>(row + j0 + half);
-        a[0] = __uint_as_float(va[0] << 16); a[1] = __uint_as_float(va[0] & 0xffff0000u);
-        a[2] = __uint_as_float(va[1] << 16); a[3] = __uint_as_float(va[1] & 0xffff0000u);
-        c[0] = __uint_as_float(vb[0] << 16); c[1] = __uint_as_float(vb[0] & 0xffff0000u);
-        c[2] = __uint_as_float(vb[1] << 16); c[3] = __uint_as_float(vb[1] & 0xffff0000u);
-      } else {
-        const f32x4 va = *reinterpret_cast<const f32x4*>(row + j0);
-        const f32x4 vb = *reinterpret_cast<const f32x4*>(row + j0 + half);
-        for (int e = 0; e < 4; ++e) { a[e] = va[e]; c[e] = vb[e]; }
-      }
-    } else {
-      // pairs (2j, 2j+1) for j = j0 .. j0+3: 8 consecutive elements
-      if constexpr (sizeof(T) == 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 2 * j0);
-        for (int e = 0; e < 4; ++e) { a[e] = __uint_as_float(v[e] << 16); c[e] = __uint_as_float(v[e] & 0xffff0000u); }
-      } else {
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(row + 2 * j0);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(row + 2 * j0 + 4);
-        a[0] = v0[0]; c[0] = v0[1]; a[1] = v0[2]; c[1] = v0[3];
-        a[2] = v1[0]; c[2] = v1[1]; a[3] = v1[2]; c[3] = v1[3];
-      }
-    }
-    float ra[4], rb[4];
+  const bool pow2 = (quads & (quads - 1)) == 0;
+  const int rstep = 256 / quads;
+  const int q4 = (int)threadIdx.x % quads;
+  const int j0 = 4 * q4;
+  const int r0 = (int)threadIdx.x / quads;
+  const int ntok = min(ROPE_TOK, seq - s0);
+  // the pair layout is the branch's (uniform): one specialised walk per layout
+  auto walk = [&](auto il_tag) {
+  constexpr bool il = decltype(il_tag)::value;
+  const int o1 = il ? 2 * j0 : j0, o2 = il ? 2 * j0 + 4 : j0 + half;
+  for (int t = 0; t < tt.n; ++t) {
+    const int h0 = tt.hoff[t], ht = tt.hoff[t + 1] - h0;
+    T* const xt = static_cast<T*>(tt.x[t]) + b * tt.sb[t] + (int64_t)s0 * tt.ss[t];
+    const int64_t sst = tt.ss[t], sht = tt.sh[t];
+    uint8_t* const ct = FP8 ? tt.codes[t] + ((int64_t)b * seq + s0) * ht * D : nullptr;
+    const int rows = ntok * ht;
+    const int hstep = rstep % ht, tstep = rstep / ht;
+    int tk = r0 / ht, h = r0 - tk * ht;
+    for (int pass = 0; pass < rows; pass += ROPE_UNROLL * rstep) {   // rows pass .. pass + U * rstep - 1
+      Quad<T> lo[ROPE_UNROLL], hi[ROPE_UNROLL];
+      int hu[ROPE_UNROLL], tku[ROPE_UNROLL];
+      bool in[ROPE_UNROLL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float co = cs[tk][j0 + e], si = sn[tk][j0 + e];
-      ra[e] = __builtin_fmaf(a[e], co, -c[e] * si);
-      rb[e] = __builtin_fmaf(a[e], si, c[e] * co);
-    }
-    if (!br.interleaved) {
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<u32x2*>(row + j0) = u32x2{pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3])};
-        *reinterpret_cast<u32x2*>(row + j0 + half) = u32x2{pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(row + j0) = f32x4{ra[0], ra[1], ra[2], ra[3]};
-        *reinterpret_cast<f32x4*>(row + j0 + half) = f32x4{rb[0], rb[1], rb[2], rb[3]};
+      for (int u = 0; u < ROPE_UNROLL; ++u) {
+        in[u] = r0 < rstep && pass + u * rstep + r0 < rows;
+        hu[u] = in[u] ? h : 0;
+        tku[u] = in[u] ? tk : 0;
+        const T* row = xt + (int64_t)tku[u] * sst + (int64_t)hu[u] * sht;
+        lo[u].load(row + o1);
+        hi[u].load(row + o2);
+        h += hstep;
+        tk += tstep;
+        if (h >= ht) { h -= ht; ++tk; }
       }
-    } else {
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<u32x4*>(row + 2 * j0) =
-            u32x4{pack_bf16x2(ra[0], rb[0]), pack_bf16x2(ra[1], rb[1]), pack_bf16x2(ra[2], rb[2]), pack_bf16x2(ra[3], rb[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(row + 2 * j0) = f32x4{ra[0], rb[0], ra[1], rb[1]};
-        *reinterpret_cast<f32x4*>(row + 2 * j0 + 4) = f32x4{ra[2], rb[2], ra[3], rb[3]};
+#pragma unroll
+      for (int u = 0; u < ROPE_UNROLL; ++u) {
+        float a[4], c[4];
+        if constexpr (!il) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { a[e] = lo[u].get(e); c[e] = hi[u].get(e); }
+        } else {
+          a[0] = lo[u].get(0); c[0] = lo[u].get(1); a[1] = lo[u].get(2); c[1] = lo[u].get(3);
+          a[2] = hi[u].get(0); c[2] = hi[u].get(1); a[3] = hi[u].get(2); c[3] = hi[u].get(3);
+        }
+        float ra[4], rb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float co = cs[tku[u]][j0 + e], si = sn[tku[u]][j0 + e];
+          ra[e] = __builtin_fmaf(a[e], co, -c[e] * si);
+          rb[e] = __builtin_fmaf(a[e], si, c[e] * co);
+        }
+        // the two output groups, in the positions of lo and hi
+        float wl[4], wh[4];
+        if constexpr (!il) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { wl[e] = ra[e]; wh[e] = rb[e]; }
+        } else {
+          wl[0] = ra[0]; wl[1] = rb[0]; wl[2] = ra[1]; wl[3] = rb[1];
+          wh[0] = ra[2]; wh[1] = rb[2]; wh[2] = ra[3]; wh[3] = rb[3];
+        }
+        float m = 0.f;
+        if constexpr (MODE == RopeMode::Rotate) {
+          if (in[u]) {
+            T* row = xt + (int64_t)tku[u] * sst + (int64_t)hu[u] * sht;
+            Quad<T>::store(row + o1, wl);
+            Quad<T>::store(row + o2, wh);
+          }
+        } else {
+          // the values as nxattn_rope_apply stores them (bf16: rounded to nearest even)
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t p = pack_bf16x2(wl[e], wh[e]);
+              wl[e] = __uint_as_float(p << 16);
+              wh[e] = __uint_as_float(p & 0xffff0000u);
+            }
+          }
+          if constexpr (MODE == RopeMode::Max) {
+            if (in[u]) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(wl[e]), __builtin_fabsf(wh[e])));
+            }
+          } else if (in[u]) {
+            const float inv = __uint_as_float(hw[h0 + hu[u]]);
+            uint8_t* crow = ct + ((int64_t)tku[u] * ht + hu[u]) * D;   // contiguous
+            *reinterpret_cast<uint32_t*>(crow + o1) = fp8x4(wl[0] * inv, wl[1] * inv, wl[2] * inv, wl[3] * inv);
+            *reinterpret_cast<uint32_t*>(crow + o2) = fp8x4(wh[0] * inv, wh[1] * inv, wh[2] * inv, wh[3] * inv);
+          }
+        }
+        if constexpr (MODE == RopeMode::Max) {
+          // non-negative floats: bit order = value order
+          if (pow2) {
+            for (int d = 1; d < quads; d <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+            if (in[u] && q4 == 0) atomicMax(&hw[h0 + hu[u]], __float_as_uint(m));
+          } else if (in[u]) {
+            atomicMax(&hw[h0 + hu[u]], __float_as_uint(m));
+          }
+        }
       }
     }
+  }
+  };
+  if (br.interleaved)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
+  if constexpr (MODE == RopeMode::Max) {
+    __syncthreads();
+    uint32_t* am = tt.amax + (blockIdx.x % AMAX_SLOTS) * tt.astride + (int64_t)b * heads;
+    for (int w = threadIdx.x; w < heads; w += blockDim.x)
+      if (hw[w] != 0u) atomicMax(&am[w], hw[w]);
   }
 }
 
@@ -148,24 +293,24 @@ int nx::check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim
   return NXATTN_OK;
 }
 
-extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
-                                 const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
-                                 hipStream_t stream) {
-  clear_error();
+int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64_t seq, int64_t head_dim,
+                    int dtype, const nxattn_rope_desc* rope, bool fp8, hipStream_t stream) {
   if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
-    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_rope_apply: dtype %d is not F32 or BF16", dtype);
-  if (batch < 0 || seq < 0 || heads < 0 || head_dim < 0) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: negative size");
-  if (batch > NXATTN_MAX_BRANCHES) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_rope_apply: batch > %d", NXATTN_MAX_BRANCHES);
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
+  const int64_t heads = tt.hoff[tt.n];
+  if (batch < 0 || seq < 0 || heads < 0 || head_dim < 0) return fail(NXATTN_ERR_INVALID, "%s: negative size", who);
+  if (batch > NXATTN_MAX_BRANCHES) return fail(NXATTN_ERR_UNSUPPORTED, "%s: batch > %d", who, NXATTN_MAX_BRANCHES);
   if (head_dim % 8 != 0 || head_dim < 8 || head_dim > 2 * ROPE_MAX_HALF)
-    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_rope_apply: head_dim %lld must be a multiple of 8 in [8, 256]", (long long)head_dim);
-  if (seq > INT32_MAX || heads > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_rope_apply: size out of range");
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: head_dim %lld must be a multiple of 8 in [8, 256]", who, (long long)head_dim);
+  if (seq > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: size out of range", who);
+  if (fp8 && heads > ROPE_MAX_HEADS) return fail(NXATTN_ERR_UNSUPPORTED, "%s: heads > %d in total", who, ROPE_MAX_HEADS);
   if (batch == 0 || seq == 0 || heads == 0) return NXATTN_OK;
-  if (!x || !strides || !rope) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: NULL pointer");
+  if (!rope) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
   RopeArgs args;
   memset(&args, 0, sizeof(args));
   for (int64_t b = 0; b < batch; ++b) {
     const nxattn_rope_desc& d = rope[b];
-    const int st = check_rope_desc(d, seq, head_dim, "nxattn_rope_apply");
+    const int st = check_rope_desc(d, seq, head_dim, who);
     if (st != NXATTN_OK) return st;
     RopeBranch& r = args.br[b];
     r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.global_freq = d.global_freq;
@@ -177,18 +322,50 @@ extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t he
     }
   }
   const int64_t es = esize(dtype);
-  if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "nxattn_rope_apply: x must be 16-byte aligned");
-  for (int i = 0; i < 3; ++i) {
-    if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: negative stride");
-    if ((strides[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_rope_apply: strides must be multiples of 16 bytes");
+  for (int t = 0; t < tt.n; ++t) {
+    if (!tt.x[t]) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
+    if (!aligned16(tt.x[t])) return fail(NXATTN_ERR_ALIGN, "%s: x must be 16-byte aligned", who);
+    const int64_t st[3] = {tt.sb[t], tt.ss[t], tt.sh[t]};
+    for (int i = 0; i < 3; ++i) {
+      if (st[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+      if ((st[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
+    }
   }
   const int64_t blocks = batch * ((seq + ROPE_TOK - 1) / ROPE_TOK);
-  if (blocks > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_rope_apply: too many tokens");
-  if (dtype == NXATTN_BF16)
-    rope_kernel<uint16_t><<<(int)blocks, 256, 0, stream>>>(static_cast<uint16_t*>(x), seq, heads, (int32_t)head_dim,
-                                                           strides[0], strides[1], strides[2], args);
-  else
-    rope_kernel<float><<<(int)blocks, 256, 0, stream>>>(static_cast<float*>(x), seq, heads, (int32_t)head_dim,
-                                                        strides[0], strides[1], strides[2], args);
-  return check_launch("nxattn_rope_apply");
+  if (blocks > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: too many tokens", who);
+  const unsigned grid = (unsigned)blocks;
+  auto launch = [&](auto* tp, auto mode_tag) {
+    using T = std::remove_pointer_t<decltype(tp)>;
+    constexpr RopeMode M = decltype(mode_tag)::value;
+    rope_kernel<T, M><<<grid, 256, 0, stream>>>(tt, (int32_t)seq, (int32_t)heads, (int32_t)head_dim, args);
+  };
+  using Rot = std::integral_constant<RopeMode, RopeMode::Rotate>;
+  using Max = std::integral_constant<RopeMode, RopeMode::Max>;
+  using Codes = std::integral_constant<RopeMode, RopeMode::Codes>;
+  const bool bf = dtype == NXATTN_BF16;
+  if (!fp8) {
+    if (bf) launch((uint16_t*)nullptr, Rot{}); else launch((float*)nullptr, Rot{});
+    return check_launch(who);
+  }
+  // maxima of the rotated values, then exponents and codes
+  launch_amax_clear(tt.amax, batch * heads, stream);
+  if (bf) launch((uint16_t*)nullptr, Max{}); else launch((float*)nullptr, Max{});
+  if (bf) launch((uint16_t*)nullptr, Codes{}); else launch((float*)nullptr, Codes{});
+  return check_launch(who);
+}
+
+extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                                 const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
+                                 hipStream_t stream) {
+  clear_error();
+  if (heads < 0 || heads > (1 << 28))
+    return fail(heads < 0 ? NXATTN_ERR_INVALID : NXATTN_ERR_UNSUPPORTED, "nxattn_rope_apply: heads out of range");
+  if (batch > 0 && seq > 0 && heads > 0 && !strides) return fail(NXATTN_ERR_INVALID, "nxattn_rope_apply: NULL pointer");
+  RopeTensors tt;
+  memset(&tt, 0, sizeof(tt));
+  tt.n = 1;
+  tt.x[0] = x;
+  if (strides) { tt.sb[0] = strides[0]; tt.ss[0] = strides[1]; tt.sh[0] = strides[2]; }
+  for (int i = 1; i <= ROPE_MAX_TENSORS; ++i) tt.hoff[i] = (int32_t)heads;
+  return rope_launch("nxattn_rope_apply", tt, batch, seq, head_dim, dtype, rope, false, stream);
 }

@@ -71,7 +71,8 @@ class AttentionStep:
             self.pk8 = [None if p is None else torch.empty((1, p.shape[1], self.Hkv, self.D), dtype=torch.uint8,
                                                            device=dev) for p in self.prefix_online]
             plen = max([p.shape[1] for p in self.prefix_online if p is not None] + [1])
-            n = max(nx.quantize_fp8_workspace_bytes(self.B, self.S, self.Hq), nx.quantize_fp8_workspace_bytes(1, plen, self.Hkv))
+            n = max(nx.quantize_fp8_workspace_bytes(self.B, self.S, self.Hq + self.Hkv),
+                    nx.quantize_fp8_workspace_bytes(1, plen, self.Hkv))
             self.qws = torch.empty(max(4, n), dtype=torch.uint8, device=dev)
         self.use_cfg = self.B == 2 and wl.guidance > 1.0
         self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
@@ -82,16 +83,19 @@ class AttentionStep:
                 nx.nxattn_kv_relayout(src, dst.unsqueeze(0), 0)
 
     def rope(self) -> None:
+        if self.wl.qk_fp8:
+            return                      # rotated inside quantize(): only the codes are needed
         if not self.fuse_q_rope:
             nx.nxattn_rope_apply(self.q, self.descs)
         nx.nxattn_rope_apply(self.k, self.descs)
 
     def quantize(self) -> None:
-        """E4M3 codes of the rotated q and k and of each prefix K (fp8 workloads only)."""
+        """E4M3 codes of the rotated q and k (one call for both: the rotation evaluated
+        inside the quantizer's passes, q and k left as given) and of each prefix K (fp8
+        workloads only)."""
         if not self.wl.qk_fp8:
             return
-        nx.nxattn_quantize_fp8(self.q, self.q8, self.qe, self.qws)
-        nx.nxattn_quantize_fp8(self.k, self.k8, self.ke, self.qws)
+        nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qe, self.ke], self.qws)
         for b, p in enumerate(self.prefix_online):
             if p is not None:
                 nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)

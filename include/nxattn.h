@@ -237,15 +237,51 @@ int nxattn_attn_merge(const void* const* part_o, const float* const* part_lse, i
  *   codes uint8 [batch, seq, heads, head_dim] contiguous: the nearest E4M3 value of
  *         x * 2^-e (an exact scaling), ties to the even code; the sign of a value that
  *         rounds to zero is kept; NaN -> 0x7F. x must not hold infinities.
- * workspace: device memory of nxattn_quantize_fp8_workspace_size() bytes (batch * heads *
- * 4: one running maximum per slice; its contents on entry do not matter); x, codes, exps
- * and workspace must not overlap (NXATTN_ERR_INVALID). Four launches on
+ * workspace: device memory of nxattn_quantize_fp8_workspace_size() bytes (32 running
+ * maxima per slice on separate 128-byte lines, 4-byte aligned: 128 * ceil(batch * heads /
+ * 32) * 32 bytes; its contents on entry do not matter); x, codes, exps and workspace must
+ * not overlap (NXATTN_ERR_INVALID). Four launches on
  * `stream`; bit-exact by construction.
  */
 int nxattn_quantize_fp8_workspace_size(int64_t batch, int64_t seq, int64_t heads, int64_t* bytes);
 int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                         const int64_t strides[3], uint8_t* codes, int8_t* exps, void* workspace,
                         int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * RoPE and FP8 quantization together, for tensors that share positions (the q and k of
+ * the own tokens): for each tensor t, codes_t and exps_t are exactly what
+ * nxattn_quantize_fp8 gives for x_t after nxattn_rope_apply(x_t, rope), bit for bit, but
+ * x_t is only read. For the fp8 score GEMM the rotated q and k are needed only as codes,
+ * so the rotation is evaluated inside the two reading passes (the maxima, then the codes)
+ * and never stored, and one evaluation of the angles per token serves the heads of every
+ * tensor.
+ *
+ * tensors[0 .. n_tensors) (host memory, 1 <= n_tensors <= NXATTN_MAX_FP8_TENSORS):
+ *   x       [batch, seq, heads, head_dim] of dtype, element strides {b, s, h} (multiples
+ *           of 16 bytes; head_dim contiguous), 16-byte aligned; read only (tensors may
+ *           share or overlap their x);
+ *   codes   out, uint8 [batch, seq, heads, head_dim] contiguous, 8-byte aligned;
+ *   exps    out, int8 [batch, heads].
+ * Shared: dtype F32 or BF16; head_dim a multiple of 8 in [8, 256]; batch <=
+ * NXATTN_MAX_BRANCHES; rope as in nxattn_rope_apply (grid product == seq); the total of
+ * the heads at most 4096. workspace: nxattn_quantize_fp8_workspace_size(batch, seq, total
+ * heads) bytes, 4-byte aligned, contents on entry irrelevant. No output may overlap an x,
+ * another output or the workspace, and no x the workspace (NXATTN_ERR_INVALID). The
+ * rotated values must be finite. Three launches on `stream`.
+ */
+#define NXATTN_MAX_FP8_TENSORS 4
+typedef struct {
+  const void* x;
+  int64_t heads;
+  int64_t strides[3];
+  uint8_t* codes;
+  int8_t* exps;
+} nxattn_fp8_tensor;
+
+int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
+                             int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * Attention of nxattn_fwd with the fp8 score GEMM above (head_dim 128, heads_q % heads_kv

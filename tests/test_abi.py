@@ -230,13 +230,68 @@ def test_quantize_fp8_rejects(lib):
     assert call(x=None) == INVALID
     assert call(x=X + 8) == ALIGN
     assert call(c=C + 4) == ALIGN
-    assert call(wb=4) == INVALID                                 # workspace too small (32 needed)
+    assert call(wb=4) == INVALID                                 # workspace too small (4096 needed)
+    assert call(wb=4095) == INVALID
     assert call(c=X + 64) == INVALID                             # codes overlap x
     assert call(e=C + 100) == INVALID                            # exps overlap codes
     assert call(S=0) == OK
     n = ctypes.c_int64(-1)
-    assert lib.nxattn_quantize_fp8_workspace_size(2, 64, 4, ctypes.byref(n)) == OK and n.value == 2 * 4 * 4
+    # 32 copies of the 8 maxima, each copy padded to 32 words (one 128-byte line)
+    assert lib.nxattn_quantize_fp8_workspace_size(2, 64, 4, ctypes.byref(n)) == OK and n.value == 32 * 32 * 4
+    assert lib.nxattn_quantize_fp8_workspace_size(3, 64, 40, ctypes.byref(n)) == OK and n.value == 32 * 128 * 4
     assert lib.nxattn_quantize_fp8_workspace_size(-1, 64, 4, ctypes.byref(n)) == INVALID
+
+
+def test_rope_quantize_fp8_rejects(lib):
+    f = lib.nxattn_rope_quantize_fp8
+    Q, K, CQ, CK, EQ, EK, W = (FAKE + i * GB for i in range(7))
+
+    def desc(grid=64, pairs=64, theta=10000.0):
+        d = binding.RopeDesc()
+        d.n_axes, d.grid[0], d.pairs[0], d.theta = 1, grid, pairs, theta
+        return d
+
+    def tensor(x, heads, codes, exps, strides=None):
+        t = binding.Fp8Tensor()
+        t.x, t.heads, t.codes, t.exps = x, heads, codes, exps
+        for i, v in enumerate(strides or (64 * heads * 128, heads * 128, 128)):
+            t.strides[i] = v
+        return t
+    good = [tensor(Q, 8, CQ, EQ), tensor(K, 2, CK, EK)]
+    ok = dict(t=good, n=2, dtype=1, B=2, S=64, D=128, r=[desc(), desc()], w=W, wb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        ts = (binding.Fp8Tensor * max(1, len(a["t"])))(*a["t"])
+        rs = None if a["r"] is None else (binding.RopeDesc * len(a["r"]))(*a["r"])
+        return f(ts, a["n"], a["dtype"], a["B"], a["S"], a["D"], rs, a["w"], a["wb"], None)
+    # every rejection below comes before the first launch
+    assert call(n=0) == INVALID
+    assert call(n=5) == INVALID
+    assert call(dtype=7) == UNSUPPORTED
+    assert call(D=12) == UNSUPPORTED
+    assert call(D=512) == UNSUPPORTED                            # quantizable, but beyond RoPE's 256
+    assert call(t=[tensor(Q, 4000, CQ, EQ), tensor(K, 200, CK, EK)]) == UNSUPPORTED   # > 4096 heads in total
+    assert call(B=9, r=[desc()] * 9) == UNSUPPORTED
+    assert call(B=-1) == INVALID
+    assert call(t=[tensor(Q, -1, CQ, EQ), good[1]]) == INVALID
+    assert call(t=[good[0], tensor(0, 2, CK, EK)]) == INVALID    # NULL x
+    assert call(t=[good[0], tensor(K, 2, 0, EK)]) == INVALID     # NULL codes
+    assert call(r=None) == INVALID
+    assert b"nxattn_rope_quantize_fp8" in lib.nxattn_last_error()           # errors name the entry point
+    assert call(r=[desc(), desc(grid=63)]) == INVALID            # grid product != seq
+    assert call(r=[desc(pairs=32), desc()]) == INVALID           # 2 * pairs != head_dim
+    assert call(r=[desc(), desc(theta=1.0)]) == INVALID
+    assert call(t=[tensor(Q + 8, 8, CQ, EQ), good[1]]) == ALIGN
+    assert call(t=[good[0], tensor(K, 2, CK + 4, EK)]) == ALIGN
+    assert call(t=[good[0], tensor(K, 2, CK, EK, (64 * 264, 264, 132))]) == ALIGN  # head stride of 264 bytes
+    assert call(w=W + 2) == ALIGN
+    assert call(wb=32 * 32 * 4 - 1) == INVALID                   # 20 maxima: 32 copies of 32 words
+    assert call(t=[good[0], tensor(K, 2, CQ + 64, EK)]) == INVALID   # codes of k overlap codes of q
+    assert call(t=[good[0], tensor(K, 2, Q + 64, EK)]) == INVALID    # codes of k overlap q
+    assert call(t=[good[0], tensor(K, 2, CK, EK)], w=K + 128) == INVALID   # workspace overlaps k
+    assert call(S=0, r=None) == OK
+    assert call(t=[tensor(Q, 0, 0, 0)], n=1, r=None) == OK      # no heads at all
 
 
 def fp8_args(**kw):

@@ -56,6 +56,70 @@ def test_quantize_strided_and_tiny():
     assert int(re[:, 2].min()) == -127
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", [
+    # (B, grid, pairs, heads per tensor, D, interleaved, global_freq)
+    ((2, (15, 20), (32, 32), (5,), 128, False, False)),
+    ((2, (15, 20), (32, 32), (5, 2), 128, False, False)),
+    ((2, (4, 6, 8), (16, 24, 24), (3, 1, 4), 128, True, False)),
+    ((1, (37,), (36,), (4, 2, 1, 3), 72, False, True)),
+])
+def test_rope_quantize_matches_rope_then_quantize(dtype, case):
+    B, grid, pairs, heads, D, inter, gf = case
+    S = int(np.prod(grid))
+    note(f"rope+quantize fp8 {dtype} B={B} grid={grid} heads={heads} D={D} inter={inter} gf={gf}")
+    mult = torch.tensor([1.0, 300.0, 1e-3, 0.0, 7.0])
+    xs = []
+    for t, H in enumerate(heads):
+        x = synth.random_tensor((B, S, H, D), 4200 + 10 * t + S, torch.float32)
+        m = torch.roll(mult, t)[:H] if H <= 5 else torch.ones(H)
+        xs.append((x * m[None, None, :, None]).to(dtype).to(DEV))    # some heads all zero
+    descs = [nx.rope_desc(grid, pairs, tuple(3 * b + a for a in range(len(grid))), 10000.0, inter, gf)
+             for b in range(B)]
+    ws = torch.full((max(4, nx.quantize_fp8_workspace_bytes(B, S, sum(heads))),), 0x7f, dtype=torch.uint8,
+                    device=DEV)                                              # stale workspace contents
+    x0 = [x.clone() for x in xs]
+    seps = [x.clone() for x in xs]
+    for sx in seps:
+        nx.nxattn_rope_apply(sx, descs)
+    outs = nx.nxattn_rope_quantize_fp8(xs, descs, workspace=ws)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    for x, xo, sx, (codes, exps) in zip(xs, x0, seps, outs):
+        assert torch.equal(x.view(bits).cpu(), xo.view(bits).cpu())     # x is only read
+        rc, re = ofp8.quantize_fp8(f64(sx.cpu()))       # the oracle's codes of the stored rotation
+        assert np.array_equal(exps.cpu().numpy(), re)
+        assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_rope_quantize_strided_then_smaller():
+    note("rope+quantize fp8 on strided views of one buffer, then a smaller input on the same workspace")
+    B, grid, pairs, H, D = 2, (8, 12), (32, 32), 6, 128
+    S = 96
+    base = synth.random_tensor((B, S, H + 2, D), 4300, torch.float32).to(torch.bfloat16).to(DEV)
+    qv, kv = base[:, :, 1:H + 1, :], base[:, :, 0:3, :]           # overlapping read-only inputs
+    descs = [nx.rope_desc(grid, pairs, (b, 2 * b)) for b in range(B)]
+    ws = torch.empty(max(4, nx.quantize_fp8_workspace_bytes(B, S, H + 3)), dtype=torch.uint8, device=DEV)
+    base0 = base.clone()
+    seps = [qv.clone(), kv.clone()]
+    for sx in seps:
+        nx.nxattn_rope_apply(sx, descs)
+    outs = nx.nxattn_rope_quantize_fp8([qv, kv], descs, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int16).cpu(), base0.view(torch.int16).cpu())
+    for sx, (codes, exps) in zip(seps, outs):
+        rc, re = ofp8.quantize_fp8(f64(sx.cpu()))
+        assert np.array_equal(exps.cpu().numpy(), re) and np.array_equal(codes.cpu().numpy(), rc)
+    small = (synth.random_tensor((1, 24, 2, D), 4301, torch.float32) * 1e-3).to(torch.bfloat16).to(DEV)
+    sep2 = small.clone()
+    d2 = [nx.rope_desc((24,), (64,), (9,))]
+    nx.nxattn_rope_apply(sep2, d2)
+    [(codes2, exps2)] = nx.nxattn_rope_quantize_fp8([small], d2, workspace=ws)   # maxima of the call above remain
+    torch.cuda.synchronize()
+    rc2, re2 = ofp8.quantize_fp8(f64(sep2.cpu()))
+    assert np.array_equal(exps2.cpu().numpy(), re2) and np.array_equal(codes2.cpu().numpy(), rc2)
+
+
 def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True):
     D = 128
     note(f"fwd fp8 B={B} S={S} Hq={Hq} Hkv={Hkv} P={P} prefix x{pre_mult} seed={seed}")

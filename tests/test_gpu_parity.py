@@ -460,9 +460,9 @@ def test_step_dit1k_bf16_sampled():
 @pytest.mark.parametrize("name", ["dit1k_fp8qk+replay", "dit2k_fp8qk"])
 def test_step_fp8qk_sampled(name):
     # the bench configuration of the fp8 score GEMM at full size: the codes of the step's
-    # own rotated q and k (and of each prefix K) bit for bit against the oracle's
-    # quantization, then sampled rows of the attention against the oracle's attention of
-    # the dequantized inputs
+    # own q and k as nxattn_rope_apply rotates them (and of each prefix K) bit for bit
+    # against the oracle's quantization, then sampled rows of the attention against the
+    # oracle's attention of the dequantized inputs
     from oracle import fp8 as ofp8
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
     note(f"step {name} (fp8 score GEMM, sampled rows)")
@@ -470,7 +470,14 @@ def test_step_fp8qk_sampled(name):
     step = AttentionStep(wl, inp)
     step()
     torch.cuda.synchronize()
-    qg, kg = f64(step.q.cpu()), f64(step.k.cpu())
+    # the step rotates inside the quantizer and leaves q and k as given
+    assert torch.equal(step.q.cpu().view(torch.int16), inp.q.view(torch.int16))
+    assert torch.equal(step.k.cpu().view(torch.int16), inp.k.view(torch.int16))
+    qr, kr = step.q.clone(), step.k.clone()
+    nx.nxattn_rope_apply(qr, step.descs)
+    nx.nxattn_rope_apply(kr, step.descs)
+    torch.cuda.synchronize()
+    qg, kg = f64(qr.cpu()), f64(kr.cpu())
     rq, rqe = ofp8.quantize_fp8(qg)
     rk, rke = ofp8.quantize_fp8(kg)
     assert np.array_equal(step.q8.cpu().numpy(), rq) and np.array_equal(step.qe.cpu().numpy(), rqe)
