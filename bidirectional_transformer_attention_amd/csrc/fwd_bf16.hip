@@ -61,6 +61,7 @@ constexpr int TILEB = BN * ROWB;  // bytes per K or V tile (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_T = 8.0f; // running max moves only when it grows by > 2^8
+constexpr float RESCALE_LIM = 256.0f;  // 2^RESCALE_T
 // raw buffer descriptors for the tile loads: no stride, bounds check effectively off
 // (every steady-state tile lies inside its tensor), 32-bit data format
 constexpr int BUF_RECORDS = 0x7fffffff;
@@ -160,6 +161,7 @@ struct Wave {
   float thr;          // FOLD: row max of the shifted scores above which m moves (-inf
                       // before the first tile); else (m + RESCALE_T) / c on raw scores
   f32x16 negm;        // FOLD: -m in every register, the score accumulators' start value
+  bool primed;        // m has been set by a first tile (wave-uniform)
   // lane parts of the LDS byte addresses: K fragment of k-step ks at kbase + (32ks ^ kx),
   // V^T fragment of d-block db at vbase + (64db ^ vy)
   int kbase, kx, vbase, vy;
@@ -342,67 +344,10 @@ __device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, in
   }
 }
 
-// Online softmax of w.s (tile with `valid` keys, < BN only for the last tile) -> w.p.
-// FOLD: w.s already holds c s - m (q pre-scaled, accumulators started at -m).
-template <bool MASK, bool FOLD>
-__device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
-  // MASK = false: the tile is known to be whole (no per-key compare/select is compiled)
-  if (MASK && valid < BN) {
-    // key of register i in block kb is kb*32 + 8(i/4) + 4hh + (i%4): compare the
-    // compile-time part against valid - 4hh
-    const int lim = valid - 4 * hh;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) w.s[kb][i] = -__builtin_inff();
-  }
-  float t0 = __builtin_fmaxf(w.s[0][0], w.s[0][1]);
-  float t1 = __builtin_fmaxf(w.s[1][0], w.s[1][1]);
-#pragma unroll
-  for (int i = 2; i < 16; ++i) {
-    t0 = __builtin_fmaxf(t0, w.s[0][i]);
-    t1 = __builtin_fmaxf(t1, w.s[1][i]);
-  }
-  float tmax = __builtin_fmaxf(t0, t1);
-  {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
-    tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
-  }
-  const bool grow = tmax > w.thr;
-  if constexpr (FOLD) {
-    // the scores arrive as c s - m: a row moves its max by d = tmax, and this tile's
-    // scores by -d
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float d = grow ? tmax : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-d);
-      w.l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
-      w.m += d;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        w.negm[i] = -w.m;
-        w.s[0][i] -= d;
-        w.s[1][i] -= d;
-      }
-      w.thr = RESCALE_T;
-    }
-  } else {
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mnew = grow ? tmax * c : w.m;
-      const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
-      w.l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
-      w.m = mnew;
-      w.thr = (mnew + RESCALE_T) / c;
-    }
-  }
+// Weights of the tile against the current m, rounded to bf16 into w.p (the B operand of
+// the P V step); returns this lane's sum of them (unrounded).
+template <bool FOLD>
+__device__ __forceinline__ float weights(Wave& w, float c) {
   const float nm = -w.m;
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
@@ -422,7 +367,103 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       }
       w.p[2 * kb + hs] = as_bf16x8(pk);
     }
-  w.l += l0 + l1;
+  return l0 + l1;
+}
+
+// FOLD: -m into every register of the next scores' start block. Rebuilt at the end of
+// each softmax rather than kept: its registers are then free while the softmax runs,
+// which is where the kernel's register pressure peaks.
+template <bool FOLD>
+__device__ __forceinline__ void set_negm(Wave& w) {
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w.negm[i] = -w.m;
+  }
+}
+
+// Online softmax of w.s (tile with `valid` keys, < BN only for the last tile) -> w.p.
+// FOLD: w.s already holds c s - m (q pre-scaled, accumulators started at -m).
+//
+// The running max m moves only when a row's tile max exceeds m by more than RESCALE_T
+// (in log2 units), i.e. when some weight 2^(c s - m) exceeds 2^RESCALE_T. Once a first
+// tile has set m, the weights are therefore taken against the current m first, with no
+// max: the weights are non-negative, so when every lane's sum of them is at most
+// 2^RESCALE_T, every weight is too, m would not have moved, and the weights stand
+// (bit for bit what the full update below computes in that case). A larger sum (or inf
+// or NaN) anywhere in the wave sends it through the full update: row max, rescale if a
+// row grew, weights again. After the first tiles of a row the full update is rare, and
+// the fast path saves the max (about 20 of the softmax's ~120 VALU instructions).
+template <bool MASK, bool FOLD>
+__device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
+  // MASK = false: the tile is known to be whole (no per-key compare/select is compiled)
+  if (MASK && valid < BN) {
+    // key of register i in block kb is kb*32 + 8(i/4) + 4hh + (i%4): compare the
+    // compile-time part against valid - 4hh
+    const int lim = valid - 4 * hh;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) w.s[kb][i] = -__builtin_inff();
+  }
+  // pass 0 (once m is set): the weights against the current m; pass 1: the full update,
+  // then the weights again (one copy of the weight code for both)
+  float lt = 0.f;
+#pragma nounroll
+  for (int pass = w.primed ? 0 : 1; pass < 2; ++pass) {
+    if (pass == 1) {
+      float t0 = __builtin_fmaxf(w.s[0][0], w.s[0][1]);
+      float t1 = __builtin_fmaxf(w.s[1][0], w.s[1][1]);
+#pragma unroll
+      for (int i = 2; i < 16; ++i) {
+        t0 = __builtin_fmaxf(t0, w.s[0][i]);
+        t1 = __builtin_fmaxf(t1, w.s[1][i]);
+      }
+      float tmax = __builtin_fmaxf(t0, t1);
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
+        tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+      }
+      const bool grow = tmax > w.thr;
+      if constexpr (FOLD) {
+        // the scores arrive as c s - m: a row moves its max by d = tmax, and this tile's
+        // scores by -d
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float d = grow ? tmax : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(-d);
+          w.l *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+          w.m += d;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            w.s[0][i] -= d;
+            w.s[1][i] -= d;
+          }
+          w.thr = RESCALE_T;
+        }
+      } else {
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mnew = grow ? tmax * c : w.m;
+          const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
+          w.l *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+          w.m = mnew;
+          w.thr = (mnew + RESCALE_T) / c;
+        }
+      }
+      w.primed = true;
+    }
+    lt = weights<FOLD>(w, c);
+    if (pass == 1 || !__builtin_amdgcn_ballot_w64(!(lt <= RESCALE_LIM))) break;
+  }
+  w.l += lt;
+  set_negm<FOLD>(w);
 }
 
 // The per-wave program. Group A (waves 0-3) and group B (waves 4-7) run it half a tile
@@ -465,6 +506,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   // moves it to its row max
   w.m = FOLD ? 0.f : -__builtin_inff();
   w.thr = -__builtin_inff();
+  w.primed = false;
 #pragma unroll
   for (int i = 0; i < 16; ++i) w.negm[i] = 0.f;
   w.l = 0.f;
