@@ -24,9 +24,11 @@
 // Ping-pong. Waves 0-3 and 4-7 (one of each per SIMD) run the same program half a
 // tile apart: while one group issues the MFMAs of tile t (scores of t+1 and P V of t),
 // the other group runs the exp2/max/sum of its softmax, so matrix cores and VALU of a
-// SIMD overlap. Each half-iteration ends at a workgroup barrier, and the wave that
-// issues MFMAs in a half-iteration runs at the higher s_setprio level (the issue
-// arbiter otherwise favours the older wave, which starves the second group's GEMM).
+// SIMD overlap. Each iteration ends at one workgroup barrier (after the tile loads have
+// landed); inside it the groups pace themselves, since no LDS buffer read in the second
+// half is written in the first. The wave that issues MFMAs in a half-iteration runs at
+// the higher s_setprio level (the issue arbiter otherwise favours the older wave, which
+// starves the second group's GEMM).
 //
 // Tile loads. Direct-to-LDS loads issued by waves 0-3 and interleaved with their
 // score MFMAs. Tiles wholly inside the prefix or the own keys use buffer loads
@@ -112,6 +114,14 @@ __device__ __forceinline__ void barrier_prio() {
   if constexpr (BEFORE >= 0) asm volatile("s_setprio %0" :: "n"(BEFORE));
   asm volatile("s_barrier" ::: "memory");
   if constexpr (AFTER >= 0) asm volatile("s_setprio %0" :: "n"(AFTER));
+  __builtin_amdgcn_sched_barrier(0);
+}
+// s_setprio alone (the half-iteration boundary inside an iteration): a second barrier
+// there cost about 100 cycles per tile and guards no LDS hazard
+template <int PRIO>
+__device__ __forceinline__ void prio_only() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_setprio %0" :: "n"(PRIO));
   __builtin_amdgcn_sched_barrier(0);
 }
 template <int BEFORE, int AFTER>
@@ -619,8 +629,10 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   // allocation of S and P straight). The multiplying wave holds the higher priority.
   // Group A fetches K of position t+2 into K buffer t&1 and V of position t+1 into V
   // buffer (t+1)&1, both last read in the previous iteration; the loads land before
-  // the barrier that ends slot 2t+1. FAST: both are whole tiles, and the loads are
-  // interleaved with the score MFMAs (after the phase's last V read).
+  // the barrier that ends slot 2t+1, the iteration's only barrier (slot 2t+1 reads V
+  // buffer t&1 and K buffer (t+1)&1, which no load of the iteration writes). FAST: both
+  // are whole tiles, and the loads are interleaved with the score MFMAs (after the
+  // phase's last V read).
   auto iter_a = [&](int t, auto par, auto fast) {
     constexpr int PAR = decltype(par)::value;        // t & 1
     constexpr bool FAST = decltype(fast)::value;
@@ -635,7 +647,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
       if (t + 2 < T) dma_tile(tile_at(t + 2), false, kbuf<PAR>(), wave, Half{});
       if (t + 1 < T) dma_tile(tile_at(t + 1), true, vbuf<PAR ^ 1>(), wave, Half{});
     }
-    barrier_prio<0, -1>();
+    prio_only<0>();
     // a fast iteration's next position is a whole tile
     if (t + 1 < T) softmax<!FAST, FOLD>(w, c, valid_at(t + 1), hh);
     wait_dma_barrier_prio<-1, 2>();
@@ -645,7 +657,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     constexpr int PAR = decltype(par)::value;
     asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
     softmax<decltype(mask)::value, FOLD>(w, c, valid_at(t), hh);
-    barrier_prio<-1, 2>();
+    prio_only<2>();
     gemm_phase<PAR, PAR ^ 1, true, FOLD>(w);
     wait_dma_barrier_prio<0, -1>();
   };
