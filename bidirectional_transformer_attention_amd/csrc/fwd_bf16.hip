@@ -391,18 +391,71 @@ __device__ __forceinline__ void set_negm(Wave& w) {
   }
 }
 
+// The full softmax update: row max of the tile; rows whose max exceeds their threshold
+// move m (rescaling l and O).
+template <bool FOLD>
+__device__ __forceinline__ void full_update(Wave& w, float c) {
+  float t0 = __builtin_fmaxf(w.s[0][0], w.s[0][1]);
+  float t1 = __builtin_fmaxf(w.s[1][0], w.s[1][1]);
+#pragma unroll
+  for (int i = 2; i < 16; ++i) {
+    t0 = __builtin_fmaxf(t0, w.s[0][i]);
+    t1 = __builtin_fmaxf(t1, w.s[1][i]);
+  }
+  float tmax = __builtin_fmaxf(t0, t1);
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
+    tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+  }
+  const bool grow = tmax > w.thr;
+  if constexpr (FOLD) {
+    // the scores arrive as c s - m: a row moves its max by d = tmax, and this tile's
+    // scores by -d
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float d = grow ? tmax : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      w.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+      w.m += d;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        w.s[0][i] -= d;
+        w.s[1][i] -= d;
+      }
+      w.thr = RESCALE_T;
+    }
+  } else {
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? tmax * c : w.m;
+      const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
+      w.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+      w.m = mnew;
+      w.thr = (mnew + RESCALE_T) / c;
+    }
+  }
+  w.primed = true;
+}
+
 // Online softmax of w.s (tile with `valid` keys, < BN only for the last tile) -> w.p.
 // FOLD: w.s already holds c s - m (q pre-scaled, accumulators started at -m).
 //
-// The running max m moves only when a row's tile max exceeds m by more than RESCALE_T
-// (in log2 units), i.e. when some weight 2^(c s - m) exceeds 2^RESCALE_T. Once a first
-// tile has set m, the weights are therefore taken against the current m first, with no
-// max: the weights are non-negative, so when every lane's sum of them is at most
-// 2^RESCALE_T, every weight is too, m would not have moved, and the weights stand
-// (bit for bit what the full update below computes in that case). A larger sum (or inf
-// or NaN) anywhere in the wave sends it through the full update: row max, rescale if a
-// row grew, weights again. After the first tiles of a row the full update is rare, and
-// the fast path saves the max (about 20 of the softmax's ~120 VALU instructions).
+// FOLD: the weights first, the max only when needed. m moves only when a row's tile max
+// exceeds m by more than RESCALE_T (in log2 units), i.e. when some weight 2^(c s - m)
+// exceeds 2^RESCALE_T. Once a first tile has set m, the weights are taken against the
+// current m with no max: they are non-negative, so when every lane's sum of them is at
+// most 2^RESCALE_T, every weight is too, m would not have moved, and the weights stand
+// (bit for bit what the full update computes in that case). A larger sum (or inf or NaN)
+// anywhere in the wave sends it through the full update and the weights again (one copy
+// of the weight code, in a loop that is never unrolled: two inlined copies made the
+// register allocator spill). With a stored q (an FMA per score in front of each exp) the
+// two-pass form measured slower, so that variant keeps the single pass.
 template <bool MASK, bool FOLD>
 __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
   // MASK = false: the tile is known to be whole (no per-key compare/select is compiled)
@@ -416,61 +469,17 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       for (int i = 0; i < 16; ++i)
         if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) w.s[kb][i] = -__builtin_inff();
   }
-  // pass 0 (once m is set): the weights against the current m; pass 1: the full update,
-  // then the weights again (one copy of the weight code for both)
   float lt = 0.f;
+  if constexpr (FOLD) {
 #pragma nounroll
-  for (int pass = w.primed ? 0 : 1; pass < 2; ++pass) {
-    if (pass == 1) {
-      float t0 = __builtin_fmaxf(w.s[0][0], w.s[0][1]);
-      float t1 = __builtin_fmaxf(w.s[1][0], w.s[1][1]);
-#pragma unroll
-      for (int i = 2; i < 16; ++i) {
-        t0 = __builtin_fmaxf(t0, w.s[0][i]);
-        t1 = __builtin_fmaxf(t1, w.s[1][i]);
-      }
-      float tmax = __builtin_fmaxf(t0, t1);
-      {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
-        tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
-      }
-      const bool grow = tmax > w.thr;
-      if constexpr (FOLD) {
-        // the scores arrive as c s - m: a row moves its max by d = tmax, and this tile's
-        // scores by -d
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float d = grow ? tmax : 0.f;
-          const float alpha = __builtin_amdgcn_exp2f(-d);
-          w.l *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
-          w.m += d;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            w.s[0][i] -= d;
-            w.s[1][i] -= d;
-          }
-          w.thr = RESCALE_T;
-        }
-      } else {
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float mnew = grow ? tmax * c : w.m;
-          const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
-          w.l *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
-          w.m = mnew;
-          w.thr = (mnew + RESCALE_T) / c;
-        }
-      }
-      w.primed = true;
+    for (int pass = w.primed ? 0 : 1; pass < 2; ++pass) {
+      if (pass == 1) full_update<FOLD>(w, c);
+      lt = weights<FOLD>(w, c);
+      if (pass == 1 || !__builtin_amdgcn_ballot_w64(!(lt <= RESCALE_LIM))) break;
     }
+  } else {
+    full_update<FOLD>(w, c);
     lt = weights<FOLD>(w, c);
-    if (pass == 1 || !__builtin_amdgcn_ballot_w64(!(lt <= RESCALE_LIM))) break;
   }
   w.l += lt;
   set_negm<FOLD>(w);

@@ -73,6 +73,15 @@ __device__ __forceinline__ void barrier_prio() {
   if constexpr (AFTER >= 0) asm volatile("s_setprio %0" :: "n"(AFTER));
   __builtin_amdgcn_sched_barrier(0);
 }
+// s_setprio alone at the half-iteration boundary: the iteration's one barrier is the
+// one after the tile loads land (the second slot reads only buffers no load of the
+// iteration writes)
+template <int PRIO>
+__device__ __forceinline__ void prio_only() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_setprio %0" :: "n"(PRIO));
+  __builtin_amdgcn_sched_barrier(0);
+}
 template <int BEFORE, int AFTER>
 __device__ __forceinline__ void wait_dma_barrier_prio() {
   __builtin_amdgcn_sched_barrier(0);
@@ -422,7 +431,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
       if (t + 2 < T) dma_k(tile_at(t + 2), kbuf<PAR>(), wave, Half{});
       if (t + 1 < T) dma_v(tile_at(t + 1), vbuf<PAR ^ 1>(), wave, Half{});
     }
-    barrier_prio<0, -1>();
+    prio_only<0>();
     if (t + 1 < T) softmax<!FAST>(w, c, valid_at(t + 1), hh);
     wait_dma_barrier_prio<-1, 2>();
   };
@@ -430,7 +439,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     constexpr int PAR = decltype(par)::value;
     asm volatile("" : "+v"(w.kbase), "+v"(w.kxh), "+v"(w.vbase), "+v"(w.vy));
     softmax<decltype(mask)::value>(w, c, valid_at(t), hh);
-    barrier_prio<-1, 2>();
+    prio_only<2>();
     const int ts = t + 1 < T ? tile_at(t + 1) : 0;
     gemm_phase<PAR, PAR ^ 1>(w, ksc(ts, 0), ksc(ts, 1));
     wait_dma_barrier_prio<0, -1>();
