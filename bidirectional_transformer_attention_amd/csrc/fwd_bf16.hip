@@ -185,26 +185,29 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* smem, int byte) {
 }
 
 // Scheduling-group helpers (compile-time sequences for __builtin_amdgcn_sched_group_barrier):
-// step i reads two transposed halves (P V steps, i < 16) or one b128 (score steps).
-template <int I, int N>
+// With scores, steps 0-15 are score steps (one b128 read each) and steps 16-31 P V steps
+// (two transposed halves each); without, all 16 steps are P V steps.
+template <bool SCORE>
+constexpr int reads_of(int i) { return SCORE ? (i < 16 ? 1 : 2) : 2; }
+template <int I, int N, bool SCORE>
 __device__ __forceinline__ void sched_reads() {
   if constexpr (I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x100, I < 16 ? 2 : 1, 0);
-    sched_reads<I + 1, N>();
+    __builtin_amdgcn_sched_group_barrier(0x100, reads_of<SCORE>(I), 0);
+    sched_reads<I + 1, N, SCORE>();
   }
 }
-template <int I, int N, int DIST, bool DMA>
+template <int I, int N, int DIST, bool DMA, bool SCORE>
 __device__ __forceinline__ void sched_steps() {
   if constexpr (I < N) {
-    if constexpr (I + DIST < N) __builtin_amdgcn_sched_group_barrier(0x100, I + DIST < 16 ? 2 : 1, 0);
+    if constexpr (I + DIST < N) __builtin_amdgcn_sched_group_barrier(0x100, reads_of<SCORE>(I + DIST), 0);
     if constexpr (DMA && I >= 16 && ((I - 16) & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    sched_steps<I + 1, N, DIST, DMA>();
+    sched_steps<I + 1, N, DIST, DMA, SCORE>();
   }
 }
 
-// One GEMM phase of a wave: O^T += V_t^T P_t^T (16 MFMAs) and, if `score`, S^T =
-// K_{t+1} Q^T (16 MFMAs). Fragments are read from LDS three MFMAs ahead so the
+// One GEMM phase of a wave: if `score`, S^T = K_{t+1} Q^T (16 MFMAs, issued first), and
+// O^T += V_t^T P_t^T (16 MFMAs). Fragments are read from LDS three MFMAs ahead so the
 // matrix core never waits on LDS latency; consecutive MFMAs target different
 // accumulators. VPAR / KPAR select the V and K buffers (compile-time LDS offsets).
 template <int VPAR, int KPAR, bool SCORE, bool FOLD, bool DMA = false>
@@ -213,22 +216,27 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullpt
   const uint8_t* ksm = kbuf<KPAR>();
   constexpr int DIST = 3;
   constexpr int nsteps = SCORE ? 32 : 16;
-  // step i < 16: PV, (kbhs = i / 4, db = i % 4); step i >= 16: S, (ks = (i-16)/2, kb = (i-16)%2)
+  // with SCORE: step i < 16: S, (ks = i/2, kb = i%2); step i >= 16: PV, (kbhs = (i-16)/4,
+  // db = (i-16)%4). Scores first: the next softmax's inputs are complete when the phase
+  // ends, and only the P V MFMAs are still in flight.
+  auto is_pv = [&](int i) { return SCORE ? i >= 16 : true; };
+  auto pv_of = [&](int i) { return SCORE ? i - 16 : i; };
   auto read = [&](int i) -> bf16x8 {
-    if (i < 16) {
-      const int kbhs = i >> 2, db = i & 3;
+    if (is_pv(i)) {
+      const int ip = pv_of(i);
+      const int kbhs = ip >> 2, db = ip & 3;
       const int rbase = (kbhs >> 1) * 32 + (kbhs & 1) * 16;   // kb*32 + 16*hs
       const int off = w.vbase + ((64 * db) ^ w.vy);
       const bf16x4 a = lds_read_tr(vsm, rbase * ROWB + off);
       const bf16x4 b = lds_read_tr(vsm, (rbase + 8) * ROWB + off);
       return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    const int j = i - 16, ks = j >> 1, kb = j & 1;
+    const int j = i, ks = j >> 1, kb = j & 1;
     return as_bf16x8(lds_read_b128(ksm, kb * 32 * ROWB + w.kbase + ((32 * ks) ^ w.kx)));
   };
-  // DMA instruction d (after the last V read of the phase, so every later LDS read of
-  // the phase is of the other K buffer): K_{t+2} into K buffer KPAR^1, V_{t+1} into V
-  // buffer VPAR^1, both last read in the previous iteration
+  // DMA instruction d (during the P V steps, after the phase's last K read): K_{t+2}
+  // into K buffer KPAR^1, V_{t+1} into V buffer VPAR^1, both last read in the previous
+  // iteration
   auto dma = [&](int d) {
     const int i = d & 3;
     const bool isv = d >= 4;
@@ -254,11 +262,12 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullpt
         if (i >= 16 && ((i - 16) & 1) == 0) dma((i - 16) >> 1);
       }
       const bf16x8 f = ring[i % (DIST + 1)];
-      if (i < 16) {
-        const int kbhs = i >> 2, db = i & 3;
+      if (is_pv(i)) {
+        const int ip = pv_of(i);
+        const int kbhs = ip >> 2, db = ip & 3;
         w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.p[kbhs], w.o[db], 0, 0, 0);
       } else {
-        const int j = i - 16, ks = j >> 1, kb = j & 1;
+        const int j = i, ks = j >> 1, kb = j & 1;
         if (ks == 0) w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], FOLD ? w.negm : f32x16{}, 0, 0, 0);
         else w.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, w.qf[ks], w.s[kb], 0, 0, 0);
       }
@@ -266,8 +275,8 @@ __device__ __forceinline__ void gemm_phase(Wave& w, const DmaPlan* plan = nullpt
   }
   // keep the issue order: the first DIST fragments' reads, then per step the reads of
   // step i+DIST followed by MFMA i
-  sched_reads<0, DIST>();
-  sched_steps<0, nsteps, DIST, DMA>();
+  sched_reads<0, DIST, SCORE>();
+  sched_steps<0, nsteps, DIST, DMA, SCORE>();
 }
 
 // S^T only (prologue).
