@@ -137,8 +137,8 @@ def main() -> int:
                          "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described, not built)"}))
+        print(json.dumps({"error": "nxattn runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is not implemented)"}))
         return 2
 
     import torch
