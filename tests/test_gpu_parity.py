@@ -393,6 +393,37 @@ def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter, gf):
         assert err <= TOL["bf16"] + share, (b, err, share)
 
 
+@pytest.mark.parametrize("k_mult", [6.0, 60.0])
+def test_fwd_q_rope_score_jumps(k_mult):
+    # q rotated on load (the folded softmax, which tries the weights against the running max
+    # before computing a tile max): one tile of ordinary prefix keys sets m, then the own
+    # keys, scaled up, raise the scores far above it. x6: jumps of tens in log2 units (a
+    # tile's weight sum exceeds 2^8, the full update rescales); x60: jumps beyond 128
+    # (the first try overflows to inf). Both must match the oracle like ordinary data.
+    grid, pairs, S, Hq, Hkv, D = (8, 12), (32, 32), 96, 8, 2, 128
+    note(f"fwd q_rope score jumps, own k x{k_mult}")
+    q = synth.random_tensor((2, S, Hq, D), 95, torch.bfloat16)
+    k = (synth.random_tensor((2, S, Hkv, D), 96, torch.float32) * k_mult).to(torch.bfloat16)
+    v = synth.random_tensor((2, S, Hkv, D), 97, torch.bfloat16)
+    pre = [synth.random_tensor((2, 64, Hkv, D), 98 + b, torch.bfloat16) for b in range(2)]
+    offsets = ((3, 5), (11, 2))
+    rnd = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    k_rot = torch.stack([rnd(oracle.rope(f64(k[b]), grid, pairs, offsets[b], 10000.0)) for b in range(2)])
+    descs = [nx.rope_desc(grid, pairs, offsets[b]) for b in range(2)]
+    o = torch.empty((2, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+    nx.nxattn_fwd(q.to(DEV), k_rot.to(DEV), v.to(DEV), o, [p.to(DEV) for p in pre], q_rope=descs)
+    torch.cuda.synchronize()
+    got = f64(o.cpu())
+    assert np.all(np.isfinite(got))
+    for b in range(2):
+        q_ex = oracle.rope(f64(q[b]), grid, pairs, offsets[b], 10000.0)
+        pk, pv = f64(pre[b][0]), f64(pre[b][1])
+        ref = oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv)
+        share = attention_err(oracle.attention(fused_q(q_ex, D), f64(k_rot[b]), f64(v[b]), pk, pv), ref)
+        err = attention_err(got[b], ref)
+        assert err <= TOL["bf16"] + share, (b, err, share)
+
+
 # ---------------------------------------------------------------------------- whole workloads
 def step_case(name, rows_per_branch, seed_rows):
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
