@@ -106,9 +106,12 @@ def _cpu_baseline(wl, rows_per_branch, cores, np, torch, oracle, synth):
             pre = oracle.relayout(pre[None], 0)[0]
         pk = None if pre is None else pre[0]
         if wl.qk_fp8:
-            # the fp8 score GEMM's inputs: q, k and the prefix K through E4M3 and back
+            # the fp8 score GEMM's inputs: q (carrying softmax_scale*log2(e)), k and the
+            # prefix K through E4M3 and back
             from oracle import fp8 as ofp8
-            q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None]))[0]
+            from bidirectional_transformer_attention_amd.binding import fold_factor
+            cf = fold_factor(wl.head_dim)
+            q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None] * cf))[0] / cf
             k = ofp8.dequantize_fp8(*ofp8.quantize_fp8(k[None]))[0]
             pk = None if pk is None else ofp8.dequantize_fp8(*ofp8.quantize_fp8(pk[None]))[0]
         oracle.attention(q, k, f64(inp.v[b]), pk, None if pre is None else pre[1])
@@ -232,7 +235,7 @@ def main() -> int:
             "frac": round(achieved / peak, 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
                         and not wl.qk_fp8 else None),
-            "kernel": ("nx::fp8k::fwd_fp8_kernel" if wl.qk_fp8 else
+            "kernel": (f"nx::fp8k::fwd_fp8_kernel<{'true' if step.fold_q else 'false'}>" if wl.qk_fp8 else
                        (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
                        if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),

@@ -8,6 +8,7 @@ if the library is not built, or a tensor is not on the GPU, the call fails.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import List, Optional, Sequence
 
@@ -41,7 +42,7 @@ class RopeDesc(ctypes.Structure):
 
 class Fp8Tensor(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("heads", ctypes.c_int64), ("strides", ctypes.c_int64 * 3),
-                ("codes", ctypes.c_void_p), ("exps", ctypes.c_void_p)]
+                ("codes", ctypes.c_void_p), ("exps", ctypes.c_void_p), ("mult", ctypes.c_float)]
 
 
 MAX_FP8_TENSORS = 4
@@ -67,7 +68,7 @@ class FwdFp8Args(ctypes.Structure):
                 ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
                 ("prefix_k8", ctypes.c_void_p * MAX_BRANCHES), ("prefix_v", ctypes.c_void_p * MAX_BRANCHES),
                 ("prefix_len", ctypes.c_int32 * MAX_BRANCHES), ("prefix_k_exp", ctypes.c_void_p),
-                ("scale", ctypes.c_float), ("lse", ctypes.c_void_p)]
+                ("scale", ctypes.c_float), ("lse", ctypes.c_void_p), ("q_folded", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -392,10 +393,12 @@ def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e
 def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
                              codes: Optional[Sequence[torch.Tensor]] = None,
                              exps: Optional[Sequence[torch.Tensor]] = None,
-                             workspace: Optional[torch.Tensor] = None, stream=None):
+                             workspace: Optional[torch.Tensor] = None,
+                             mults: Optional[Sequence[float]] = None, stream=None):
     """Codes and exponents (as nxattn_quantize_fp8) of each x in xs ([B,S,H_t,D], one
-    dtype, shared B, S, D and positions) rotated as nxattn_rope_apply would rotate it; the
-    x are not modified. Returns [(codes, exps)] in the order of xs."""
+    dtype, shared B, S, D and positions) rotated as nxattn_rope_apply would rotate it and,
+    where mults gives a factor other than 0 or 1, multiplied by it in fp32 after the
+    rotation's rounding; the x are not modified. Returns [(codes, exps)] in the order of xs."""
     xs = list(xs)
     if not 1 <= len(xs) <= MAX_FP8_TENSORS:
         raise NxattnError(1, f"need 1 to {MAX_FP8_TENSORS} tensors")
@@ -421,20 +424,31 @@ def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
         for k in range(3):
             arr[i].strides[k] = x.stride(k)
         arr[i].codes, arr[i].exps = c.data_ptr(), e.data_ptr()
+        arr[i].mult = float(mults[i]) if mults is not None else 0.0
     darr = (RopeDesc * max(1, B))(*descs)
     _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, workspace.data_ptr(),
                                            workspace.numel() * workspace.element_size(), _stream(stream)))
     return outs
 
 
+def fold_factor(head_dim: int, scale: float = 0.0) -> float:
+    """softmax_scale * log2(e) rounded to fp32 (scale <= 0: 1/sqrt(head_dim)), the factor
+    that q's codes carry for nxattn_fwd_fp8(q_folded=True)."""
+    f32 = lambda x: ctypes.c_float(x).value                       # round to fp32
+    s = f32(scale) if scale > 0 else f32(1.0 / f32(math.sqrt(f32(head_dim))))
+    return f32(s * f32(1.4426950408889634))
+
+
 def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_exp: torch.Tensor, v: torch.Tensor,
                    o: torch.Tensor, prefix_k8: Sequence[Optional[torch.Tensor]] = (),
                    prefix_v: Sequence[Optional[torch.Tensor]] = (), prefix_k_exp: Optional[torch.Tensor] = None,
-                   scale: float = 0.0, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+                   scale: float = 0.0, lse: Optional[torch.Tensor] = None, q_folded: bool = False,
+                   stream=None) -> None:
     """Attention with the fp8 score GEMM: q8 [B,S,Hq,128], k8 [B,S,Hkv,128] uint8 codes
     (contiguous), q_exp [B,Hq], k_exp [B,Hkv] int8; v [B,S,Hkv,128] and o [B,S,Hq,128] bf16;
     prefix_k8[b] uint8 [P_b,Hkv,128] and prefix_v[b] bf16 [P_b,Hkv,128] contiguous (or None),
-    prefix_k_exp int8 [B,Hkv]."""
+    prefix_k_exp int8 [B,Hkv]. With q_folded, q8 holds the codes of q times
+    softmax_scale*log2(e) (see nxattn_rope_quantize_fp8's mults) and scale is not used."""
     _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, *[t for t in prefix_k8 if t is not None],
          *[t for t in prefix_v if t is not None])
     B, S, Hq, D = q8.shape
@@ -455,6 +469,7 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_ex
         raise NxattnError(1, "lse must be a contiguous float32 [B, Hq, S] tensor")
     a = FwdFp8Args()
     a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, Hkv, D
+    a.q_folded = 1 if q_folded else 0
     a.q8, a.k8, a.q_exp, a.k_exp = q8.data_ptr(), k8.data_ptr(), q_exp.data_ptr(), k_exp.data_ptr()
     a.v, a.o = v.data_ptr(), o.data_ptr()
     for i in range(3):

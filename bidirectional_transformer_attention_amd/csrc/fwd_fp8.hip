@@ -102,7 +102,9 @@ struct Wave {
   f32x16 s[2];        // S^T accumulators of the tile being scored (2 key blocks of 32)
   bf16x8 p[4];        // P^T operand of the tile being accumulated
   float m, l;
-  float thr;          // (m + RESCALE_T) / c: the raw row max above which m moves
+  float thr;          // FOLD: row max of the shifted scores above which m moves (-inf before
+                      // the first tile); else (m + RESCALE_T) / c on raw scores
+  f32x16 negm;        // FOLD: -m in every register, the score accumulators' start value
   int kbase, kxh;     // K fragment (kb, ks, half e): kbase + kb*32*KROWB + ((64ks + 16e) ^ kxh)
   int vbase, vy;      // V^T fragment of d-block db at vbase + (64db ^ vy)
   int qsc;            // E8M0 scale of the wave's q head (B operand)
@@ -148,7 +150,7 @@ __device__ __forceinline__ void sched8_steps() {
   }
 }
 
-template <int VPAR, int KPAR, bool DMA = false>
+template <int VPAR, int KPAR, bool FOLD, bool DMA = false>
 __device__ __forceinline__ void gemm_phase(Wave& w, int ksc0, int ksc1, const DmaPlan* plan = nullptr) {
   const uint8_t* vsm = vbuf<VPAR>();
   const uint8_t* ksm = kbuf<KPAR>();
@@ -194,7 +196,7 @@ __device__ __forceinline__ void gemm_phase(Wave& w, int ksc0, int ksc1, const Dm
       w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (DIST + 1)], w.p[kbhs], w.o[db], 0, 0, 0);
     } else {
       const int j = i - 16, ks = j >> 1, kb = j & 1;
-      w.s[kb] = mfma_s(kf[j], w.q8[ks], ks == 0 ? f32x16{} : w.s[kb], kb ? ksc1 : ksc0, w.qsc);
+      w.s[kb] = mfma_s(kf[j], w.q8[ks], ks == 0 ? (FOLD ? w.negm : f32x16{}) : w.s[kb], kb ? ksc1 : ksc0, w.qsc);
     }
   }
   sched8_reads<0, DIST>();
@@ -202,19 +204,23 @@ __device__ __forceinline__ void gemm_phase(Wave& w, int ksc0, int ksc1, const Dm
 }
 
 // S^T only (prologue).
-template <int KPAR>
+template <int KPAR, bool FOLD>
 __device__ __forceinline__ void gemm_s_only(Wave& w, int ksc0, int ksc1) {
   const uint8_t* ksm = kbuf<KPAR>();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      w.s[kb] = mfma_s(kfrag(ksm, w, kb, ks), w.q8[ks], ks == 0 ? f32x16{} : w.s[kb], kb ? ksc1 : ksc0, w.qsc);
+      w.s[kb] = mfma_s(kfrag(ksm, w, kb, ks), w.q8[ks], ks == 0 ? (FOLD ? w.negm : f32x16{}) : w.s[kb],
+                       kb ? ksc1 : ksc0, w.qsc);
 }
 
-// Online softmax of w.s (raw scores; the tile holds `valid` keys, < BN only for the
-// last tile of a branch) -> w.p. MASK = false: the tile is known to be whole.
-template <bool MASK>
+// Online softmax of w.s (the tile holds `valid` keys, < BN only for the last tile of a
+// branch) -> w.p. MASK = false: the tile is known to be whole. FOLD: q's codes carry
+// c = scale * log2(e) and the score accumulators start at -m, so w.s holds c s - m and each
+// weight is one exp2 (a rescale moves m by the tile max d and shifts the tile by -d);
+// otherwise w.s holds the raw scores and each weight is exp2(fma(s, c, -m)).
+template <bool MASK, bool FOLD>
 __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
   if (MASK && valid < BN) {
     const int lim = valid - 4 * hh;
@@ -237,16 +243,35 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
     tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
   }
   const bool grow = tmax > w.thr;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float mnew = grow ? tmax * c : w.m;
-    const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
-    w.l *= alpha;
+  if constexpr (FOLD) {
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float d = grow ? tmax : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      w.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
-    w.m = mnew;
-    w.thr = (mnew + RESCALE_T) / c;
+        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+      w.m += d;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        w.s[0][i] -= d;
+        w.s[1][i] -= d;
+      }
+      w.thr = RESCALE_T;
+    }
+  } else {
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? tmax * c : w.m;
+      const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
+      w.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[db][i] *= alpha;
+      w.m = mnew;
+      w.thr = (mnew + RESCALE_T) / c;
+    }
   }
   const float nm = -w.m;
   float l0 = 0.f, l1 = 0.f;
@@ -257,8 +282,9 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       u32x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e], c, nm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e + 1], c, nm));
+        const float x0 = w.s[kb][8 * hs + 2 * e], x1 = w.s[kb][8 * hs + 2 * e + 1];
+        const float p0 = __builtin_amdgcn_exp2f(FOLD ? x0 : __builtin_fmaf(x0, c, nm));
+        const float p1 = __builtin_amdgcn_exp2f(FOLD ? x1 : __builtin_fmaf(x1, c, nm));
         l0 += p0;
         l1 += p1;
         pk[e] = pack_bf16x2(p0, p1);
@@ -266,9 +292,13 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       w.p[2 * kb + hs] = as_bf16x8(pk);
     }
   w.l += l0 + l1;
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w.negm[i] = -w.m;
+  }
 }
 
-template <bool GROUP_A>
+template <bool GROUP_A, bool FOLD>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
@@ -300,9 +330,13 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   w.qsc = 127 + (int)a.q_exp[b * a.heads_q + hq];
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
-  w.m = -__builtin_inff();
+  // FOLD: m starts at 0 (the accumulators start at -m = 0) and the first tile always
+  // moves it to its row max
+  w.m = FOLD ? 0.f : -__builtin_inff();
   w.thr = -__builtin_inff();
   w.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w.negm[i] = 0.f;
   // K fragment of key block kb, k-step ks, half e: row kb*32 + n, 16-byte chunk
   // 4ks + 2hh + e at slot chunk ^ (n & 7): byte n*KROWB + ((64ks + 16e) ^ (32hh ^ 16(n&7)))
   w.kbase = n * KROWB;
@@ -392,8 +426,8 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   dma_v(tile_at(0), vbuf<0>(), wave, All{});
   if (T > 1) dma_k(tile_at(1), kbuf<1>(), wave, All{});
   wait_dma_barrier();
-  gemm_s_only<0>(w, ksc(tile_at(0), 0), ksc(tile_at(0), 1));
-  if (GROUP_A) softmax<true>(w, c, valid_at(0), hh);
+  gemm_s_only<0, FOLD>(w, ksc(tile_at(0), 0), ksc(tile_at(0), 1));
+  if (GROUP_A) softmax<true, FOLD>(w, c, valid_at(0), hh);
   barrier_only();
 
   auto iter_a = [&](int t, auto par, auto fast) {
@@ -403,23 +437,23 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     const int ts = t + 1 < T ? tile_at(t + 1) : 0;
     if constexpr (FAST) {
       const DmaPlan pl = plan_of(t);
-      gemm_phase<PAR, PAR ^ 1, true>(w, ksc(ts, 0), ksc(ts, 1), &pl);
+      gemm_phase<PAR, PAR ^ 1, FOLD, true>(w, ksc(ts, 0), ksc(ts, 1), &pl);
     } else {
-      gemm_phase<PAR, PAR ^ 1>(w, ksc(ts, 0), ksc(ts, 1));
+      gemm_phase<PAR, PAR ^ 1, FOLD>(w, ksc(ts, 0), ksc(ts, 1));
       if (t + 2 < T) dma_k(tile_at(t + 2), kbuf<PAR>(), wave, Half{});
       if (t + 1 < T) dma_v(tile_at(t + 1), vbuf<PAR ^ 1>(), wave, Half{});
     }
     __builtin_amdgcn_sched_barrier(0);   // the GEMM phase's work stays ahead of the softmax
-    if (t + 1 < T) softmax<!FAST>(w, c, valid_at(t + 1), hh);
+    if (t + 1 < T) softmax<!FAST, FOLD>(w, c, valid_at(t + 1), hh);
     wait_dma_barrier();
   };
   auto iter_b = [&](int t, auto par, auto mask) {
     constexpr int PAR = decltype(par)::value;
     asm volatile("" : "+v"(w.kbase), "+v"(w.kxh), "+v"(w.vbase), "+v"(w.vy));
-    softmax<decltype(mask)::value>(w, c, valid_at(t), hh);
+    softmax<decltype(mask)::value, FOLD>(w, c, valid_at(t), hh);
     __builtin_amdgcn_sched_barrier(0);
     const int ts = t + 1 < T ? tile_at(t + 1) : 0;
-    gemm_phase<PAR, PAR ^ 1>(w, ksc(ts, 0), ksc(ts, 1));
+    gemm_phase<PAR, PAR ^ 1, FOLD>(w, ksc(ts, 0), ksc(ts, 1));
     wait_dma_barrier();
   };
   using P0 = std::integral_constant<int, 0>;
@@ -471,11 +505,12 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
 }
 
+template <bool FOLD>
 __global__ __launch_bounds__(THREADS) void fwd_fp8_kernel(Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true>(a, lane, wave);
-  else wave_program<false>(a, lane, wave);
+  if (wave < 4) wave_program<true, FOLD>(a, lane, wave);
+  else wave_program<false, FOLD>(a, lane, wave);
 }
 
 }  // namespace fp8k
@@ -561,6 +596,9 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   const float scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)D);
   a.c = scale * LOG2E;
   a.lse = p->lse;
-  fwd_fp8_kernel<<<a.total_wg, THREADS, 0, stream>>>(a);
+  if (p->q_folded)
+    fwd_fp8_kernel<true><<<a.total_wg, THREADS, 0, stream>>>(a);
+  else
+    fwd_fp8_kernel<false><<<a.total_wg, THREADS, 0, stream>>>(a);
   return check_launch("nxattn_fwd_fp8");
 }

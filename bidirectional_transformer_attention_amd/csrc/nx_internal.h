@@ -83,6 +83,7 @@ struct RopeTensors {
   int64_t sb[ROPE_MAX_TENSORS], ss[ROPE_MAX_TENSORS], sh[ROPE_MAX_TENSORS];
   uint8_t* codes[ROPE_MAX_TENSORS];
   int8_t* exps[ROPE_MAX_TENSORS];
+  float mult[ROPE_MAX_TENSORS];   // fp8 passes: multiplier of the stored rotated values (1: none)
   int32_t hoff[ROPE_MAX_TENSORS + 1];
   int32_t n;
   uint32_t* amax;

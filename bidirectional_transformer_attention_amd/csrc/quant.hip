@@ -354,7 +354,10 @@ extern "C" int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_
     if (reinterpret_cast<uintptr_t>(z.codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
     for (int i = 0; i < 3; ++i)
       if (z.strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+    if (!(z.mult >= 0.f) || std::isinf(z.mult))
+      return fail(NXATTN_ERR_INVALID, "%s: mult of tensor %d must be finite and >= 0", who, t);
     const int k = tt.n++;
+    tt.mult[k] = z.mult == 0.f ? 1.f : z.mult;
     tt.x[k] = const_cast<void*>(z.x);
     tt.sb[k] = z.strides[0]; tt.ss[k] = z.strides[1]; tt.sh[k] = z.strides[2];
     tt.codes[k] = z.codes;

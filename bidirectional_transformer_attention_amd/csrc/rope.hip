@@ -174,6 +174,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
     T* const xt = static_cast<T*>(tt.x[t]) + b * tt.sb[t] + (int64_t)s0 * tt.ss[t];
     const int64_t sst = tt.ss[t], sht = tt.sh[t];
     uint8_t* const ct = FP8 ? tt.codes[t] + ((int64_t)b * seq + s0) * ht * D : nullptr;
+    const float mu = FP8 ? tt.mult[t] : 1.f;
     const int rows = ntok * ht;
     const int hstep = rstep % ht, tstep = rstep / ht;
     int tk = r0 / ht, h = r0 - tk * ht;
@@ -227,13 +228,21 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
             Quad<T>::store(row + o2, wh);
           }
         } else {
-          // the values as nxattn_rope_apply stores them (bf16: rounded to nearest even)
+          // the values as nxattn_rope_apply stores them (bf16: rounded to nearest even),
+          // times the tensor's multiplier (one fp32 multiply)
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t p = pack_bf16x2(wl[e], wh[e]);
               wl[e] = __uint_as_float(p << 16);
               wh[e] = __uint_as_float(p & 0xffff0000u);
+            }
+          }
+          if (mu != 1.f) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              wl[e] *= mu;
+              wh[e] *= mu;
             }
           }
           if constexpr (MODE == RopeMode::Max) {

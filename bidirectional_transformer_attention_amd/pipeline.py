@@ -25,8 +25,11 @@ from .synth import Inputs, Workload
 
 class AttentionStep:
     def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None,
-                 splits: Optional[int] = None):
+                 splits: Optional[int] = None, fold_q: bool = True):
         self.wl = wl
+        # fp8: q's codes carry softmax_scale*log2(e), so the attention's softmax takes one
+        # exp2 per score with no multiply in front
+        self.fold_q = bool(fold_q) and wl.qk_fp8
         self.splits = wl.splits if splits is None else int(splits)
         # bf16: q is rotated inside the attention kernel (no separate pass over q)
         self.fuse_q_rope = (wl.dtype == "bf16" and not wl.qk_fp8) if fuse_q_rope is None else bool(fuse_q_rope)
@@ -95,7 +98,8 @@ class AttentionStep:
         workloads only)."""
         if not self.wl.qk_fp8:
             return
-        nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qe, self.ke], self.qws)
+        nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qe, self.ke], self.qws,
+                                    mults=[nx.fold_factor(self.D) if self.fold_q else 0.0, 0.0])
         for b, p in enumerate(self.prefix_online):
             if p is not None:
                 nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)
@@ -105,7 +109,8 @@ class AttentionStep:
             nx.nxattn_fwd_fp8(self.q8, self.k8, self.qe, self.ke, self.v, self.o,
                               [None if p is None else p[0] for p in self.pk8],
                               [None if p is None else p[1] for p in self.prefix_online],
-                              self.pke if any(p is not None for p in self.prefix_online) else None)
+                              self.pke if any(p is not None for p in self.prefix_online) else None,
+                              q_folded=self.fold_q)
             return
         nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online,
                       q_rope=self.descs if self.fuse_q_rope else None,

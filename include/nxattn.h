@@ -262,7 +262,11 @@ int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, in
  *           of 16 bytes; head_dim contiguous), 16-byte aligned; read only (tensors may
  *           share or overlap their x);
  *   codes   out, uint8 [batch, seq, heads, head_dim] contiguous, 8-byte aligned;
- *   exps    out, int8 [batch, heads].
+ *   exps    out, int8 [batch, heads];
+ *   mult    0 or 1: none; else a finite multiplier > 0 applied (fp32 multiply) to each
+ *           rotated value as stored in dtype before quantization, so that the codes are
+ *           those of mult * rope(x). With mult = scale * log2(e) (fp32) for q, the fp8
+ *           attention can take q folded (nxattn_fwd_fp8_args.q_folded).
  * Shared: dtype F32 or BF16; head_dim a multiple of 8 in [8, 256]; batch <=
  * NXATTN_MAX_BRANCHES; rope as in nxattn_rope_apply (grid product == seq); the total of
  * the heads at most 4096. workspace: nxattn_quantize_fp8_workspace_size(batch, seq, total
@@ -277,6 +281,7 @@ typedef struct {
   int64_t strides[3];
   uint8_t* codes;
   int8_t* exps;
+  float mult;
 } nxattn_fp8_tensor;
 
 int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
@@ -295,6 +300,12 @@ int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors
  * contiguous (the V half of one layer slice of the online cache); exponents int8 in
  * device memory. lse as in nxattn_fwd. Outputs must not overlap inputs. scale <= 0 selects
  * 1/sqrt(128).
+ *
+ * q_folded != 0: q8 holds the codes of c * q with c = scale * log2(e), as
+ * nxattn_rope_quantize_fp8 writes them with mult = c. The products then are the scores
+ * in base-2 units, s_j * log2(e) = 2^(q_exp + e_j) <dec(q8), dec(k8_j)>, `scale` is not
+ * used, and the kernel's softmax takes one exp2 per score with no multiply in front
+ * (its score accumulators start at minus the running max), the bf16 kernel's q_rope fold.
  */
 typedef struct {
   int32_t batch;
@@ -316,6 +327,7 @@ typedef struct {
   const int8_t* prefix_k_exp;                         /* [batch, heads_kv]; needed if any prefix */
   float scale;
   float* lse;                                         /* NULL, or [batch, heads_q, seq_q] fp32 */
+  int32_t q_folded;                                   /* see above */
 } nxattn_fwd_fp8_args;
 
 int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* args, hipStream_t stream);

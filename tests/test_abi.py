@@ -288,6 +288,10 @@ def test_rope_quantize_fp8_rejects(lib):
     assert call(w=W + 2) == ALIGN
     assert call(wb=32 * 32 * 4 - 1) == INVALID                   # 20 maxima: 32 copies of 32 words
     assert call(t=[good[0], tensor(K, 2, CQ + 64, EK)]) == INVALID   # codes of k overlap codes of q
+    for bad in (-1.0, float("inf"), float("nan")):                  # multipliers: 0, or finite > 0
+        t = tensor(Q, 8, CQ, EQ)
+        t.mult = bad
+        assert call(t=[t, good[1]]) == INVALID
     assert call(t=[good[0], tensor(K, 2, Q + 64, EK)]) == INVALID    # codes of k overlap q
     assert call(t=[good[0], tensor(K, 2, CK, EK)], w=K + 128) == INVALID   # workspace overlaps k
     assert call(S=0, r=None) == OK

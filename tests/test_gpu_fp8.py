@@ -82,12 +82,16 @@ def test_rope_quantize_matches_rope_then_quantize(dtype, case):
     seps = [x.clone() for x in xs]
     for sx in seps:
         nx.nxattn_rope_apply(sx, descs)
-    outs = nx.nxattn_rope_quantize_fp8(xs, descs, workspace=ws)
+    # per-tensor multipliers: the softmax fold factor, none (0 and 1), and a plain 3
+    mults = [nx.fold_factor(128), 0.0, 3.0, 1.0][:len(xs)]
+    outs = nx.nxattn_rope_quantize_fp8(xs, descs, workspace=ws, mults=mults)
     torch.cuda.synchronize()
     bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
-    for x, xo, sx, (codes, exps) in zip(xs, x0, seps, outs):
+    for x, xo, sx, mu, (codes, exps) in zip(xs, x0, seps, mults, outs):
         assert torch.equal(x.view(bits).cpu(), xo.view(bits).cpu())     # x is only read
-        rc, re = ofp8.quantize_fp8(f64(sx.cpu()))       # the oracle's codes of the stored rotation
+        # the oracle's codes of the stored rotation times mult (one fp32 multiply)
+        sm = sx.cpu().float() * torch.tensor(mu if mu else 1.0, dtype=torch.float32)
+        rc, re = ofp8.quantize_fp8(f64(sm))
         assert np.array_equal(exps.cpu().numpy(), re)
         assert np.array_equal(codes.cpu().numpy(), rc)
 
@@ -120,16 +124,28 @@ def test_rope_quantize_strided_then_smaller():
     assert np.array_equal(exps2.cpu().numpy(), re2) and np.array_equal(codes2.cpu().numpy(), rc2)
 
 
-def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True):
+def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True, fold=False):
     D = 128
-    note(f"fwd fp8 B={B} S={S} Hq={Hq} Hkv={Hkv} P={P} prefix x{pre_mult} seed={seed}")
+    note(f"fwd fp8 B={B} S={S} Hq={Hq} Hkv={Hkv} P={P} prefix x{pre_mult} seed={seed} fold={fold}")
     q = synth.random_tensor((B, S, Hq, D), seed, torch.bfloat16)
     k = synth.random_tensor((B, S, Hkv, D), seed + 1, torch.bfloat16)
     v = synth.random_tensor((B, S, Hkv, D), seed + 2, torch.bfloat16)
     pk = [(synth.random_tensor((p, Hkv, D), seed + 3 + b, torch.float32) * pre_mult).to(torch.bfloat16) if p else None
           for b, p in enumerate(P)]
     pv = [synth.random_tensor((p, Hkv, D), seed + 13 + b, torch.bfloat16) if p else None for b, p in enumerate(P)]
-    q8, qe = nx.nxattn_quantize_fp8(q.to(DEV))
+    cf = nx.fold_factor(D)
+    if fold:
+        # q rotated and multiplied by softmax_scale*log2(e) inside the quantizer; the
+        # reference takes the GPU's rotation (parity-tested on its own) times cf in fp32
+        descs = [nx.rope_desc((S,), (64,), (5 * b,)) for b in range(B)]
+        qd = q.to(DEV)
+        [(q8, qe)] = nx.nxattn_rope_quantize_fp8([qd], descs, mults=[cf])
+        nx.nxattn_rope_apply(qd, descs)
+        q = qd.cpu()
+        qref = q.float() * torch.tensor(cf, dtype=torch.float32)
+    else:
+        q8, qe = nx.nxattn_quantize_fp8(q.to(DEV))
+        qref = q
     k8, ke = nx.nxattn_quantize_fp8(k.to(DEV))
     pk8, pke = [], torch.zeros((B, Hkv), dtype=torch.int8, device=DEV)
     for b in range(B):
@@ -142,13 +158,16 @@ def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True):
     o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
     ls = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV) if lse else None
     nx.nxattn_fwd_fp8(q8, k8, qe, ke, v.to(DEV), o, pk8, [t.to(DEV) if t is not None else None for t in pv],
-                      pke if any(P) else None, lse=ls)
+                      pke if any(P) else None, lse=ls, q_folded=fold)
     torch.cuda.synchronize()
-    # the reference dequantizes the oracle's own codes (equal to the GPU's: checked here too)
-    rq, rqe = ofp8.quantize_fp8(f64(q))
+    # the reference dequantizes the oracle's own codes (equal to the GPU's: checked here too);
+    # folded q codes stand for cf * q, so their dequantized values are divided by cf
+    rq, rqe = ofp8.quantize_fp8(f64(qref))
     rk, rke = ofp8.quantize_fp8(f64(k))
     assert np.array_equal(q8.cpu().numpy(), rq) and np.array_equal(k8.cpu().numpy(), rk)
     dq, dk = ofp8.dequantize_fp8(rq, rqe), ofp8.dequantize_fp8(rk, rke)
+    if fold:
+        dq = dq / cf
     for b in range(B):
         dpk = None
         if pk[b] is not None:
@@ -179,3 +198,17 @@ def test_fwd_fp8_prefix_scale_differs():
     # prefix keys 100x larger than own keys: their exponents differ by ~7, so the tile that
     # straddles the prefix end mixes two E8M0 row scales
     fp8_case(2, 160, 8, 2, (100, 30), 4300, pre_mult=100.0)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,P", [
+    (2, 300, 8, 2, (37, 0)),
+    (1, 1, 8, 1, (200,)),
+    (2, 200, 4, 2, (300, 7)),
+])
+def test_fwd_fp8_folded_q(B, S, Hq, Hkv, P):
+    # q's codes carry softmax_scale*log2(e): same attention as the unfolded call
+    fp8_case(B, S, Hq, Hkv, P, 4400 + S, fold=True)
+
+
+def test_fwd_fp8_folded_q_prefix_scale_differs():
+    fp8_case(2, 160, 8, 2, (100, 30), 4500, pre_mult=100.0, fold=True)

@@ -508,12 +508,16 @@ def test_step_fp8qk_sampled(name):
     nx.nxattn_rope_apply(qr, step.descs)
     nx.nxattn_rope_apply(kr, step.descs)
     torch.cuda.synchronize()
-    qg, kg = f64(qr.cpu()), f64(kr.cpu())
+    # the step's q codes carry softmax_scale*log2(e) (one fp32 multiply of the stored rotation)
+    assert step.fold_q
+    cf = nx.fold_factor(wl.head_dim)
+    qg = f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32))
+    kg = f64(kr.cpu())
     rq, rqe = ofp8.quantize_fp8(qg)
     rk, rke = ofp8.quantize_fp8(kg)
     assert np.array_equal(step.q8.cpu().numpy(), rq) and np.array_equal(step.qe.cpu().numpy(), rqe)
     assert np.array_equal(step.k8.cpu().numpy(), rk) and np.array_equal(step.ke.cpu().numpy(), rke)
-    dq, dk = ofp8.dequantize_fp8(rq, rqe), ofp8.dequantize_fp8(rk, rke)
+    dq, dk = ofp8.dequantize_fp8(rq, rqe) / cf, ofp8.dequantize_fp8(rk, rke)
     o = step.o.cpu()
     for b in range(wl.branches):
         pre = step.prefix_online[b]
