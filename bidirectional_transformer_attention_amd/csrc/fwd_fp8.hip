@@ -37,6 +37,7 @@ constexpr int KTILEB = BN * KROWB; // 8 KB
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_T = 8.0f;  // running max moves only when it grows by > 2^8
+constexpr float RESCALE_LIM = 256.0f;  // 2^RESCALE_T
 constexpr int BUF_RECORDS = 0x7fffffff;
 constexpr int BUF_FLAGS = 0x00020000;
 
@@ -102,6 +103,7 @@ struct Wave {
   f32x16 s[2];        // S^T accumulators of the tile being scored (2 key blocks of 32)
   bf16x8 p[4];        // P^T operand of the tile being accumulated
   float m, l;
+  bool primed;        // FOLD: a first tile has set m (weights may be taken before the max)
   float thr;          // FOLD: row max of the shifted scores above which m moves (-inf before
                       // the first tile); else (m + RESCALE_T) / c on raw scores
   f32x16 negm;        // FOLD: -m in every register, the score accumulators' start value
@@ -215,21 +217,9 @@ __device__ __forceinline__ void gemm_s_only(Wave& w, int ksc0, int ksc1) {
                        kb ? ksc1 : ksc0, w.qsc);
 }
 
-// Online softmax of w.s (the tile holds `valid` keys, < BN only for the last tile of a
-// branch) -> w.p. MASK = false: the tile is known to be whole. FOLD: q's codes carry
-// c = scale * log2(e) and the score accumulators start at -m, so w.s holds c s - m and each
-// weight is one exp2 (a rescale moves m by the tile max d and shifts the tile by -d);
-// otherwise w.s holds the raw scores and each weight is exp2(fma(s, c, -m)).
-template <bool MASK, bool FOLD>
-__device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
-  if (MASK && valid < BN) {
-    const int lim = valid - 4 * hh;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) w.s[kb][i] = -__builtin_inff();
-  }
+// Row max of the tile; rows whose max exceeds their threshold move m (rescaling l, O).
+template <bool FOLD>
+__device__ __forceinline__ void max_update(Wave& w, float c) {
   float t0 = __builtin_fmaxf(w.s[0][0], w.s[0][1]);
   float t1 = __builtin_fmaxf(w.s[1][0], w.s[1][1]);
 #pragma unroll
@@ -273,6 +263,12 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       w.thr = (mnew + RESCALE_T) / c;
     }
   }
+}
+
+// Weights of the tile against the current m, rounded to bf16 into w.p; returns this
+// lane's (unrounded) sum of them.
+template <bool FOLD>
+__device__ __forceinline__ float weights(Wave& w, float c) {
   const float nm = -w.m;
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
@@ -291,10 +287,45 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       }
       w.p[2 * kb + hs] = as_bf16x8(pk);
     }
-  w.l += l0 + l1;
+  return l0 + l1;
+}
+
+// Online softmax of w.s (the tile holds `valid` keys, < BN only for the last tile of a
+// branch) -> w.p. MASK = false: the tile is known to be whole. FOLD: q's codes carry
+// c = scale * log2(e) and the score accumulators start at -m, so w.s holds c s - m and each
+// weight is one exp2 (a rescale moves m by the tile max d and shifts the tile by -d);
+// otherwise w.s holds the raw scores and each weight is exp2(fma(s, c, -m)).
+template <bool MASK, bool FOLD>
+__device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
+  if (MASK && valid < BN) {
+    const int lim = valid - 4 * hh;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim) w.s[kb][i] = -__builtin_inff();
+  }
   if constexpr (FOLD) {
+    // weights first against the current m; the row max only when some lane's sum of
+    // them exceeds 2^RESCALE_T (then every weight might have, and m may have to move),
+    // or before a first tile has set m. One copy of the weight code in a loop that is
+    // never unrolled.
+    float lt = 0.f;
+#pragma nounroll
+    for (int pass = w.primed ? 0 : 1; pass < 2; ++pass) {
+      if (pass == 1) {
+        max_update<FOLD>(w, c);
+        w.primed = true;
+      }
+      lt = weights<FOLD>(w, c);
+      if (pass == 1 || !__builtin_amdgcn_ballot_w64(!(lt <= RESCALE_LIM))) break;
+    }
+    w.l += lt;
 #pragma unroll
     for (int i = 0; i < 16; ++i) w.negm[i] = -w.m;
+  } else {
+    max_update<FOLD>(w, c);
+    w.l += weights<FOLD>(w, c);
   }
 }
 
@@ -333,6 +364,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   // FOLD: m starts at 0 (the accumulators start at -m = 0) and the first tile always
   // moves it to its row max
   w.m = FOLD ? 0.f : -__builtin_inff();
+  w.primed = false;
   w.thr = -__builtin_inff();
   w.l = 0.f;
 #pragma unroll
