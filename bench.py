@@ -6,10 +6,14 @@ One step = one pass of the whole path over one synthetic batch, inputs resident 
 prefix relayout (replay -> online layout), RoPE on own k (and q) of both CFG branches,
 the fused attention launch over [prefix ++ own] for both branches (on the bf16 path it
 rotates q as it loads it), CFG combine.
+A multi-layer workload (the 27-layer ViT encoder) runs every layer, each on its own seeded
+inputs, in one step.
 Prints one JSON line. ``value`` is attention TFLOP/s (4*Sq*Skv*Hq*D summed over the
 branches, divided by the step time). ``roofline`` is measured on the fused attention
 kernel with HIP events recorded on the stream it runs on; ``cpu_baseline`` times the
-CPU fp64 oracle on a bounded sample of the same workload.
+CPU fp64 oracle on a bounded sample of the same workload. ``gate_16k_tokens`` times the
+16K-token 2K DiT step (both CFG branches) beside the headline workload, with its kernel's
+fraction of the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ PEAK = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}   # TFLOP/s, dense MFMA, MI
 # at both peaks a step would take F/2/fp8 + F/2/bf16, i.e. an effective peak of
 PEAK_FP8QK = 2.0 / (1.0 / PEAK["fp8"] + 1.0 / PEAK["bf16"])
 HBM_PEAK = 8000.0                               # GB/s
+GATE_WORKLOAD = "dit2k_bf16"   # its prefix is given in the replay layout
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_dit1k_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "bidirectional_transformer_attention_amd", "csrc", "fwd_bf16.hip")
 
@@ -69,9 +74,25 @@ def time_call(fn, stream, reps: int = 20) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(wl, rows_per_branch: int, threads: int = 0):
-    """Time the CPU fp64 oracle on the first rows of every branch (full keys); threads > 0
-    limits the BLAS thread pool to that many threads."""
+def host_cores() -> int:
+    """CPU cores this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def fold_constant(head_dim: int) -> float:
+    """The softmax fold factor the library documents for q's fp8 codes: fl32(s * fl32(log2 e)),
+    s = fl32(1 / fl32(sqrt(head_dim))) (used to build the oracle's fp8 inputs)."""
+    import numpy as np
+    f32 = np.float32
+    return float(f32(f32(1.0) / np.sqrt(f32(head_dim)) * f32(1.4426950408889634)))
+
+
+def cpu_baseline(wl, rows_per_branch: int, threads: int = 0, layers: int = 1):
+    """Time the CPU fp64 oracle on the first rows of every branch (full keys) of the first
+    `layers` layers; threads > 0 limits the BLAS thread pool to that many threads."""
     import contextlib
 
     import numpy as np
@@ -84,42 +105,81 @@ def cpu_baseline(wl, rows_per_branch: int, threads: int = 0):
         from threadpoolctl import threadpool_info, threadpool_limits
         limit = threadpool_limits(limits=threads) if threads > 0 else contextlib.nullcontext()
         with limit:
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        limit, cores = contextlib.nullcontext(), 1
+        limit, blas = contextlib.nullcontext(), 1
     with limit:
-        return _cpu_baseline(wl, rows_per_branch, cores, np, torch, oracle, synth)
+        return _cpu_baseline(wl, rows_per_branch, blas, layers, np, torch, oracle, synth)
 
 
-def _cpu_baseline(wl, rows_per_branch, cores, np, torch, oracle, synth):
-    inp = synth.make_inputs(wl)
+def _cpu_baseline(wl, rows_per_branch, blas, layers, np, torch, oracle, synth):
     f64 = lambda t: t.to(torch.float32).numpy().astype(np.float64)  # noqa: E731
     rows = np.arange(wl.seq if rows_per_branch <= 0 else min(rows_per_branch, wl.seq))
-    t0 = time.perf_counter()
+    dt = 0.0
     flops = 0.0
-    for b in range(wl.branches):
-        q = oracle.rope(f64(inp.q[b][: len(rows)]), wl.grid, wl.pairs, wl.offsets[b], wl.theta, rows=rows)
-        k = oracle.rope(f64(inp.k[b]), wl.grid, wl.pairs, wl.offsets[b], wl.theta)
-        p = inp.prefix[b]
-        pre = None if p is None else f64(p)
-        if pre is not None and wl.prefix_layout == "replay":
-            pre = oracle.relayout(pre[None], 0)[0]
-        pk = None if pre is None else pre[0]
-        if wl.qk_fp8:
-            # the fp8 score GEMM's inputs: q (carrying softmax_scale*log2(e)), k and the
-            # prefix K through E4M3 and back
-            from oracle import fp8 as ofp8
-            from bidirectional_transformer_attention_amd.binding import fold_factor
-            cf = fold_factor(wl.head_dim)
-            q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None] * cf))[0] / cf
-            k = ofp8.dequantize_fp8(*ofp8.quantize_fp8(k[None]))[0]
-            pk = None if pk is None else ofp8.dequantize_fp8(*ofp8.quantize_fp8(pk[None]))[0]
-        oracle.attention(q, k, f64(inp.v[b]), pk, None if pre is None else pre[1])
-        flops += 4.0 * len(rows) * (wl.prefix_len[b] + wl.seq) * wl.heads_q * wl.head_dim
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{wl.name}: first {len(rows)} query rows of each of {wl.branches} branches against all "
-                      f"keys (RoPE, relayout, fp64 attention), {dt:.1f} s"}
+    for layer in range(layers):
+        inp = synth.make_inputs(wl, layer=layer)
+        t0 = time.perf_counter()
+        for b in range(wl.branches):
+            q = oracle.rope(f64(inp.q[b][: len(rows)]), wl.grid, wl.pairs, wl.offsets[b], wl.theta, rows=rows)
+            k = oracle.rope(f64(inp.k[b]), wl.grid, wl.pairs, wl.offsets[b], wl.theta)
+            p = inp.prefix[b]
+            pre = None if p is None else f64(p)
+            if pre is not None and wl.prefix_layout == "replay":
+                pre = oracle.relayout(pre[None], 0)[0]
+            pk = None if pre is None else pre[0]
+            if wl.qk_fp8:
+                # the fp8 score GEMM's inputs: q (carrying softmax_scale*log2(e)), k and the
+                # prefix K through E4M3 and back
+                from oracle import fp8 as ofp8
+                cf = fold_constant(wl.head_dim)
+                q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None] * cf))[0] / cf
+                k = ofp8.dequantize_fp8(*ofp8.quantize_fp8(k[None]))[0]
+                pk = None if pk is None else ofp8.dequantize_fp8(*ofp8.quantize_fp8(pk[None]))[0]
+            oracle.attention(q, k, f64(inp.v[b]), pk, None if pre is None else pre[1])
+            flops += 4.0 * len(rows) * (wl.prefix_len[b] + wl.seq) * wl.heads_q * wl.head_dim
+        dt += time.perf_counter() - t0
+    full = wl.flops() * layers
+    part = "all" if len(rows) == wl.seq else f"the first {len(rows)}"
+    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": host_cores(), "blas_threads": int(blas),
+           "kind": "oracle",
+           "sample": f"{wl.name}: {part} query rows of each of {wl.branches} branches"
+                     + (f" of {layers} layers" if layers > 1 else "")
+                     + f" against all keys (RoPE, relayout, fp64 attention), {dt:.1f} s"}
+    if len(rows) < wl.seq:
+        out["extrapolated_full_step_s"] = round(dt * full / flops, 2)
+    return out
+
+
+def time_step(step, steps: int, warmup: int, torch):
+    """Whole-step and attention-launch times (ms) of an AttentionStep (or of a list of them,
+    one per layer, run back to back as one step), with HIP events on the current stream."""
+    layers = step if isinstance(step, list) else [step]
+    for _ in range(warmup):
+        for st in layers:
+            st()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+          for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        for st, (e0, e1) in zip(layers, ev[i]):
+            st.relayout()
+            st.rope()
+            st.quantize()
+            e0.record(stream)
+            st.attention()
+            e1.record(stream)
+            st.cfg()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / steps
+    # attention launches of one step (summed over layers)
+    fwd = sorted(sum(a.elapsed_time(b) for a, b in row) for row in ev)
+    return ms_step, sum(fwd) / len(fwd), fwd[0]
 
 
 def main() -> int:
@@ -133,6 +193,10 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=None,
                     help="key ranges per branch in the attention call (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate-steps", type=int, default=10,
+                    help="timed steps of the 16K-token gate workload (2K DiT, both branches); 0: skip")
+    ap.add_argument("--cpu-layers", type=int, default=1,
+                    help="layers of a multi-layer workload that the CPU oracle timing covers")
     ap.add_argument("--cpu-1thread-rows", type=int, default=-1,
                     help="query rows per branch for the 1-thread CPU oracle timing (-1: seq/16, 0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -154,32 +218,15 @@ def main() -> int:
     wl = synth.bench_workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    step = AttentionStep(wl, synth.make_inputs(wl), "cuda:0", splits=args.splits)
-    flops_step = wl.flops()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step.relayout()
-        step.rope()
-        step.quantize()
-        ev[i][0].record(stream)
-        step.attention()
-        ev[i][1].record(stream)
-        step.cfg()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    fwd_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    # a step of a multi-layer workload (the 27-layer ViT encoder) runs every layer, each
+    # on its own seeded inputs
+    layers = wl.layers
+    steps_all = [AttentionStep(wl, synth.make_inputs(wl, layer=l), "cuda:0", splits=args.splits)
+                 for l in range(layers)]
+    step = steps_all[0]
+    flops_step = wl.flops() * layers
+    ms_step, fwd_avg, fwd_min = time_step(steps_all if layers > 1 else step, args.steps, args.warmup, torch)
     value = flops_step / (ms_step * 1e-3) / 1e12
 
     # the headline shape alone: the cond branch, 4096 x (4096 + 512), as a batch-1 launch
@@ -217,11 +264,9 @@ def main() -> int:
         if wl.prefix_layout == "replay" else 0,
         "rope": 0 if wl.qk_fp8 else 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
         "cfg": 3 * step.q[0].numel() * es if step.use_cfg else 0,
-        # reads q, k (rotated inside both passes) and the prefix K twice (maximum, then
-        # codes), writes one byte per element
-        "quantize": (2 * es + 1) * (step.q.numel() + step.k.numel()
-                                    + sum(p[0].numel() for p in step.prefix_online if p is not None))
-        if wl.qk_fp8 else 0,
+        # reads q and k twice (rotated inside both passes: maximum, then codes), writes one
+        # byte per element (the prefix K is quantized once, outside the step)
+        "quantize": (2 * es + 1) * (step.q.numel() + step.k.numel()) if wl.qk_fp8 else 0,
     }
     for name, fn in (("relayout", step.relayout), ("rope", step.rope), ("quantize", step.quantize),
                      ("cfg", step.cfg)):
@@ -239,7 +284,9 @@ def main() -> int:
                        (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
                        if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),
-            "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_ms[0], 4)}
+            "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_min, 4)}
+    if layers > 1:
+        roof["launches_per_step"] = layers
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 2
@@ -250,9 +297,28 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # the >= 50 % gate is set on the 16K-token step (2K DiT, both CFG branches, prefix in the
+    # replay layout): time it beside the headline workload
+    gate = None
+    if args.gate_steps > 0 and wl.name != GATE_WORKLOAD:
+        gwl = synth.bench_workload(GATE_WORKLOAD)
+        gstep = AttentionStep(gwl, synth.make_inputs(gwl), "cuda:0")
+        g_ms, g_fwd, g_min = time_step(gstep, args.gate_steps, 2, torch)
+        gfl = gwl.flops()
+        gate = {"workload": gwl.name, "steps": args.gate_steps, "gflop_per_step": round(gfl / 1e9, 1),
+                "ms_per_step": round(g_ms, 4), "step_tflops": round(gfl / g_ms / 1e9, 1),
+                "step_frac": round(gfl / g_ms / 1e9 / PEAK["bf16"], 4),
+                "kernel": "nx::bf16k::fwd_bf16_kernel<true>", "kernel_ms_avg": round(g_fwd, 4),
+                "kernel_ms_min": round(g_min, 4), "kernel_tflops": round(gfl / g_fwd / 1e9, 1),
+                "kernel_frac": round(gfl / g_fwd / 1e9 / PEAK["bf16"], 4), "gate_frac": 0.5,
+                "gate_ms": round(gfl / (0.5 * PEAK["bf16"]) / 1e9, 4)}
+        if not args.no_cpu_baseline:
+            # a row subset of the same step, with the full-step time extrapolated from it
+            gate["cpu_baseline"] = cpu_baseline(gwl, max(32, gwl.seq // 128))
+
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu = cpu_baseline(wl, args.cpu_rows, layers=min(layers, args.cpu_layers))
         r1 = max(32, wl.seq // 16) if args.cpu_1thread_rows < 0 else args.cpu_1thread_rows
         if r1 > 0:
             cpu1 = cpu_baseline(wl, r1, threads=1)
@@ -266,17 +332,20 @@ def main() -> int:
                    "head_dim": wl.head_dim, "rope_offsets": [list(o) for o in wl.offsets],
                    "guidance": wl.guidance, "prefix_layout_in": "replay [2,H,P,D] relaid each step"
                    if wl.prefix_layout == "replay" else "online [2,P,H,D]",
-                   "splits": step.splits,
+                   "splits": step.splits, "layers_per_step": layers,
                    "step": ("relayout + rope(k) + fused attention (q rotated on load)" if step.fuse_q_rope
-                            else "relayout + fp8 quantize(rope(q), rope(k), prefix k) + fused attention with fp8 QK"
+                            else "relayout + fp8 quantize(rope(q), rope(k)) + fused attention with fp8 QK "
+                                 "(prefix K codes made once per conditioning cache)"
                             if wl.qk_fp8 else "relayout + rope(q,k) + fused attention")
-                   + (f" over {step.splits} key ranges + merge" if step.splits > 1 else "") + " + cfg",
+                   + (f" over {step.splits} key ranges + merge" if step.splits > 1 else "")
+                   + (" + cfg" if step.use_cfg else "") + (f", x {layers} layers" if layers > 1 else ""),
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
         "side_calls": side,
         "headline_cond_branch": headline,
+        "gate_16k_tokens": gate,
     }
     print(json.dumps(out))
     return 0

@@ -9,7 +9,6 @@ four calls into one attention step of a DiT layer.
 from .binding import (  # noqa: F401
     NxattnError,
     RopeDesc,
-    fold_factor,
     fwd_workspace_bytes,
     load,
     nxattn_attn_merge,

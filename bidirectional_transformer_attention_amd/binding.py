@@ -8,14 +8,15 @@ if the library is not built, or a tensor is not on the GPU, the call fails.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import List, Optional, Sequence
 
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnxattn.so")
+# the in-tree library; NXATTN_LIBRARY names another build of it (for instance one with
+# host-side sanitizers)
+LIB_PATH = os.environ.get("NXATTN_LIBRARY") or os.path.join(_HERE, "libnxattn.so")
 
 NXATTN_F32 = 0
 NXATTN_BF16 = 1
@@ -42,7 +43,8 @@ class RopeDesc(ctypes.Structure):
 
 class Fp8Tensor(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("heads", ctypes.c_int64), ("strides", ctypes.c_int64 * 3),
-                ("codes", ctypes.c_void_p), ("exps", ctypes.c_void_p), ("mult", ctypes.c_float)]
+                ("codes", ctypes.c_void_p), ("exps", ctypes.c_void_p), ("mult", ctypes.c_float),
+                ("fold_softmax", ctypes.c_int32)]
 
 
 MAX_FP8_TENSORS = 4
@@ -394,17 +396,35 @@ def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
                              codes: Optional[Sequence[torch.Tensor]] = None,
                              exps: Optional[Sequence[torch.Tensor]] = None,
                              workspace: Optional[torch.Tensor] = None,
-                             mults: Optional[Sequence[float]] = None, stream=None):
+                             mults: Optional[Sequence[float]] = None,
+                             folds: Optional[Sequence[bool]] = None, stream=None):
     """Codes and exponents (as nxattn_quantize_fp8) of each x in xs ([B,S,H_t,D], one
     dtype, shared B, S, D and positions) rotated as nxattn_rope_apply would rotate it and,
     where mults gives a factor other than 0 or 1, multiplied by it in fp32 after the
-    rotation's rounding; the x are not modified. Returns [(codes, exps)] in the order of xs."""
+    rotation's rounding; where folds[t] is true the library multiplies by the softmax
+    fold factor instead (the codes nxattn_fwd_fp8 takes with q_folded; mults[t] > 0 then
+    gives the softmax scale). The x are not modified. Returns [(codes, exps)] in the
+    order of xs."""
     xs = list(xs)
     if not 1 <= len(xs) <= MAX_FP8_TENSORS:
         raise NxattnError(1, f"need 1 to {MAX_FP8_TENSORS} tensors")
     codes = list(codes) if codes is not None else [None] * len(xs)
     exps = list(exps) if exps is not None else [None] * len(xs)
     _gpu(*xs, *[c for c in codes if c is not None], *[e for e in exps if e is not None], workspace)
+    outs = _rope_quant_outputs(xs, descs, codes, exps)
+    B, S, _, D = xs[0].shape
+    total = sum(x.shape[2] for x in xs)
+    if workspace is None:
+        workspace = torch.empty(max(4, quantize_fp8_workspace_bytes(B, S, total)), dtype=torch.uint8,
+                                device=xs[0].device)
+    arr = _fp8_tensors(xs, outs, mults, folds)
+    darr = (RopeDesc * max(1, B))(*descs)
+    _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return outs
+
+
+def _rope_quant_outputs(xs, descs, codes, exps):
     B, S, _, D = xs[0].shape
     outs = []
     for x, c, e in zip(xs, codes, exps):
@@ -414,10 +434,10 @@ def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
         outs.append((c, e))
     if len(descs) != B:
         raise NxattnError(1, "one RopeDesc per batch entry is required")
-    total = sum(x.shape[2] for x in xs)
-    if workspace is None:
-        workspace = torch.empty(max(4, quantize_fp8_workspace_bytes(B, S, total)), dtype=torch.uint8,
-                                device=xs[0].device)
+    return outs
+
+
+def _fp8_tensors(xs, outs, mults, folds):
     arr = (Fp8Tensor * len(xs))()
     for i, (x, (c, e)) in enumerate(zip(xs, outs)):
         arr[i].x, arr[i].heads = x.data_ptr(), x.shape[2]
@@ -425,18 +445,8 @@ def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
             arr[i].strides[k] = x.stride(k)
         arr[i].codes, arr[i].exps = c.data_ptr(), e.data_ptr()
         arr[i].mult = float(mults[i]) if mults is not None else 0.0
-    darr = (RopeDesc * max(1, B))(*descs)
-    _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, workspace.data_ptr(),
-                                           workspace.numel() * workspace.element_size(), _stream(stream)))
-    return outs
-
-
-def fold_factor(head_dim: int, scale: float = 0.0) -> float:
-    """softmax_scale * log2(e) rounded to fp32 (scale <= 0: 1/sqrt(head_dim)), the factor
-    that q's codes carry for nxattn_fwd_fp8(q_folded=True)."""
-    f32 = lambda x: ctypes.c_float(x).value                       # round to fp32
-    s = f32(scale) if scale > 0 else f32(1.0 / f32(math.sqrt(f32(head_dim))))
-    return f32(s * f32(1.4426950408889634))
+        arr[i].fold_softmax = 1 if (folds is not None and folds[i]) else 0
+    return arr
 
 
 def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_exp: torch.Tensor, v: torch.Tensor,
@@ -448,7 +458,7 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_ex
     (contiguous), q_exp [B,Hq], k_exp [B,Hkv] int8; v [B,S,Hkv,128] and o [B,S,Hq,128] bf16;
     prefix_k8[b] uint8 [P_b,Hkv,128] and prefix_v[b] bf16 [P_b,Hkv,128] contiguous (or None),
     prefix_k_exp int8 [B,Hkv]. With q_folded, q8 holds the codes of q times
-    softmax_scale*log2(e) (see nxattn_rope_quantize_fp8's mults) and scale is not used."""
+    softmax_scale*log2(e) (see nxattn_rope_quantize_fp8's folds) and scale is not used."""
     _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, *[t for t in prefix_k8 if t is not None],
          *[t for t in prefix_v if t is not None])
     B, S, Hq, D = q8.shape

@@ -99,6 +99,11 @@ enum class RopeMode { Rotate, Max, Codes };
 int rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64_t seq, int64_t head_dim, int dtype,
                 const nxattn_rope_desc* rope, bool fp8, hipStream_t stream);
 
+// nxattn_rope_quantize_fp8 (validation and launches; errors name `who`) with the running
+// maxima in `workspace`.
+int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
+                  int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope, void* workspace,
+                  int64_t workspace_bytes, hipStream_t stream);
 
 // RoPE of q applied on load by the fused attention kernel (axes beyond n_axes have grid
 // 1, pairs 0, offset 0)

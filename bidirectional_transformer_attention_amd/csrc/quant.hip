@@ -317,11 +317,13 @@ extern "C" int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int6
   return check_launch("nxattn_quantize_fp8");
 }
 
-extern "C" int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype,
-                                        int64_t batch, int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope,
-                                        void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  static const char* who = "nxattn_rope_quantize_fp8";
-  clear_error();
+namespace nx {
+
+// Validation and launches of nxattn_rope_quantize_fp8 with the running maxima in
+// `workspace` (the caller's memory, or the static scratch of the no-allocation variant).
+int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
+                  int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope, void* workspace,
+                  int64_t workspace_bytes, hipStream_t stream) {
   if (!tensors || n_tensors < 1 || n_tensors > NXATTN_MAX_FP8_TENSORS)
     return fail(NXATTN_ERR_INVALID, "%s: need 1 to %d tensors", who, NXATTN_MAX_FP8_TENSORS);
   if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
@@ -356,8 +358,18 @@ extern "C" int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_
       if (z.strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
     if (!(z.mult >= 0.f) || std::isinf(z.mult))
       return fail(NXATTN_ERR_INVALID, "%s: mult of tensor %d must be finite and >= 0", who, t);
+    if (z.fold_softmax != 0 && z.fold_softmax != 1)
+      return fail(NXATTN_ERR_INVALID, "%s: fold_softmax of tensor %d must be 0 or 1", who, t);
+    if (z.fold_softmax && head_dim <= 0) return fail(NXATTN_ERR_INVALID, "%s: fold_softmax needs head_dim > 0", who);
     const int k = tt.n++;
-    tt.mult[k] = z.mult == 0.f ? 1.f : z.mult;
+    if (z.fold_softmax) {
+      // c = softmax scale * log2(e) in fp32, the scale given in mult or 1/sqrt(head_dim)
+      // formed as nxattn_fwd and nxattn_fwd_fp8 form their default
+      const float sc = z.mult > 0.f ? z.mult : 1.0f / std::sqrt((float)head_dim);
+      tt.mult[k] = sc * 1.4426950408889634f;
+    } else {
+      tt.mult[k] = z.mult == 0.f ? 1.f : z.mult;
+    }
     tt.x[k] = const_cast<void*>(z.x);
     tt.sb[k] = z.strides[0]; tt.ss[k] = z.strides[1]; tt.sh[k] = z.strides[2];
     tt.codes[k] = z.codes;
@@ -384,3 +396,14 @@ extern "C" int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_
   // first launch
   return rope_launch(who, tt, batch, seq, head_dim, dtype, rope, true, stream);
 }
+
+}  // namespace nx
+
+extern "C" int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype,
+                                        int64_t batch, int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope,
+                                        void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  return rope_quantize("nxattn_rope_quantize_fp8", tensors, n_tensors, dtype, batch, seq, head_dim, rope, workspace,
+                       workspace_bytes, stream);
+}
+

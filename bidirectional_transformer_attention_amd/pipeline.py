@@ -6,8 +6,10 @@
     -> fused attention over [prefix ++ own] for all branches in one launch (or, with
        key splits, one launch over key ranges plus one merge launch)
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
-With the fp8 score GEMM (``qk_fp8`` workloads) q is rotated by the RoPE kernel too, and q,
-own k and each prefix K are quantized to E4M3 before the attention call.
+With the fp8 score GEMM (``qk_fp8`` workloads) q and own k are rotated and quantized to
+E4M3 in one call before the attention call. Each prefix K is quantized once, when the
+step is set up: the injected conditioning cache is the same for every denoising step
+(NeoPP page, intro), so its codes are too.
 
 Only tensor allocation and argument marshalling happen here; every step runs in the HIP
 library. The prefix of branch b is passed as one layer slice [2, P_b, Hkv, D] of the
@@ -79,6 +81,15 @@ class AttentionStep:
             self.qws = torch.empty(max(4, n), dtype=torch.uint8, device=dev)
         self.use_cfg = self.B == 2 and wl.guidance > 1.0
         self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
+        if wl.qk_fp8:
+            self.relayout()
+            self.quantize_prefix()
+
+    def quantize_prefix(self) -> None:
+        """E4M3 codes of each prefix K (fp8 workloads), once per conditioning cache."""
+        for b, p in enumerate(self.prefix_online):
+            if p is not None:
+                nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)
 
     def relayout(self) -> None:
         for src, dst in zip(self.prefix_src, self.prefix_online):
@@ -94,15 +105,12 @@ class AttentionStep:
 
     def quantize(self) -> None:
         """E4M3 codes of the rotated q and k (one call for both: the rotation evaluated
-        inside the quantizer's passes, q and k left as given) and of each prefix K (fp8
-        workloads only)."""
+        inside the quantizer's passes, q and k left as given; fp8 workloads only). q's
+        codes carry the softmax fold factor, which the library forms."""
         if not self.wl.qk_fp8:
             return
         nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qe, self.ke], self.qws,
-                                    mults=[nx.fold_factor(self.D) if self.fold_q else 0.0, 0.0])
-        for b, p in enumerate(self.prefix_online):
-            if p is not None:
-                nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)
+                                    folds=[self.fold_q, False])
 
     def attention(self) -> None:
         if self.wl.qk_fp8:

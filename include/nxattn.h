@@ -263,10 +263,14 @@ int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, in
  *           share or overlap their x);
  *   codes   out, uint8 [batch, seq, heads, head_dim] contiguous, 8-byte aligned;
  *   exps    out, int8 [batch, heads];
- *   mult    0 or 1: none; else a finite multiplier > 0 applied (fp32 multiply) to each
- *           rotated value as stored in dtype before quantization, so that the codes are
- *           those of mult * rope(x). With mult = scale * log2(e) (fp32) for q, the fp8
- *           attention can take q folded (nxattn_fwd_fp8_args.q_folded).
+ *   mult    with fold_softmax == 0: 0 or 1: none; else a finite multiplier > 0 applied
+ *           (fp32 multiply) to each rotated value as stored in dtype before quantization,
+ *           so that the codes are those of mult * rope(x).
+ *   fold_softmax  0 or 1. 1: the multiplier is c = s * log2(e), formed by the library in
+ *           fp32 as fl(s * fl(log2 e)), with s = mult when mult > 0, else the default
+ *           softmax scale fl(1 / fl(sqrt(head_dim))) of nxattn_fwd and nxattn_fwd_fp8.
+ *           These are the codes of q that nxattn_fwd_fp8 takes with q_folded != 0 (the
+ *           scores then arrive in base-2 units), so a caller never forms c itself.
  * Shared: dtype F32 or BF16; head_dim a multiple of 8 in [8, 256]; batch <=
  * NXATTN_MAX_BRANCHES; rope as in nxattn_rope_apply (grid product == seq); the total of
  * the heads at most 4096. workspace: nxattn_quantize_fp8_workspace_size(batch, seq, total
@@ -282,6 +286,7 @@ typedef struct {
   uint8_t* codes;
   int8_t* exps;
   float mult;
+  int32_t fold_softmax;
 } nxattn_fp8_tensor;
 
 int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
@@ -302,7 +307,7 @@ int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors
  * 1/sqrt(128).
  *
  * q_folded != 0: q8 holds the codes of c * q with c = scale * log2(e), as
- * nxattn_rope_quantize_fp8 writes them with mult = c. The products then are the scores
+ * nxattn_rope_quantize_fp8 writes them with fold_softmax = 1. The products then are the scores
  * in base-2 units, s_j * log2(e) = 2^(q_exp + e_j) <dec(q8), dec(k8_j)>, `scale` is not
  * used, and the kernel's softmax takes one exp2 per score with no multiply in front
  * (its score accumulators start at minus the running max), the bf16 kernel's q_rope fold.

@@ -26,13 +26,20 @@ def lse_err_ok(got, ref) -> bool:
     return bool(np.all(np.abs(got - ref) <= TOL_LSE + TOL_LSE_REL * np.abs(ref)))
 
 
+def fold_factor(head_dim: int, scale: float = 0.0) -> float:
+    """The softmax fold factor as the library documents it: c = fl32(s * fl32(log2 e)) with
+    s = fl32(scale), or fl32(1 / fl32(sqrt(head_dim))) for the default scale."""
+    f32 = np.float32
+    s = f32(scale) if scale > 0 else f32(1.0) / np.sqrt(f32(head_dim))
+    return float(f32(s * f32(1.4426950408889634)))
+
+
 def fused_q(q_rot: np.ndarray, head_dim: int, scale: float = 0.0) -> np.ndarray:
     """The q that the bf16 kernel uses when it rotates q on load, given the exact rotated
     q: the rotated value times c = scale*log2(e) (fp32, as the library forms it), rounded
     once to bf16 (nearest even), divided back by c. The rounding point is the library's
     documented one; everything else comes from the oracle."""
-    sc = np.float32(scale) if scale > 0 else np.float32(1.0) / np.sqrt(np.float32(head_dim))
-    c = float(np.float32(sc * np.float32(1.4426950408889634)))
+    c = fold_factor(head_dim, scale)
     r = torch.from_numpy(np.asarray(q_rot, dtype=np.float64) * c).to(torch.float32).to(torch.bfloat16)
     return r.to(torch.float64).numpy() / c
 
@@ -101,6 +108,22 @@ def slice_err(got: np.ndarray, ref: np.ndarray) -> float:
 def attention_err(got: np.ndarray, ref: np.ndarray) -> float:
     """Worst slice error over heads of arrays shaped [R, H, D]."""
     return max(slice_err(got[:, h, :], ref[:, h, :]) for h in range(ref.shape[1]))
+
+
+def global_maxrel(got: np.ndarray, ref: np.ndarray) -> float:
+    """max|g - r| / max|r| over the whole array (reported, not gated)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    m = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return float(np.max(np.abs(got - ref))) / m if m > 0 else 0.0
+
+
+def cosine(got: np.ndarray, ref: np.ndarray) -> float:
+    """Cosine similarity of the flattened arrays (reported, not gated)."""
+    g = np.asarray(got, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    den = float(np.linalg.norm(g) * np.linalg.norm(r))
+    return float(g @ r) / den if den > 0 else 1.0
 
 
 def sample_rows(S: int, count: int, seed: int, extra: Sequence[int] = ()) -> np.ndarray:

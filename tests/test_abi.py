@@ -292,6 +292,10 @@ def test_rope_quantize_fp8_rejects(lib):
         t = tensor(Q, 8, CQ, EQ)
         t.mult = bad
         assert call(t=[t, good[1]]) == INVALID
+    for bad in (-1, 2):                                              # fold_softmax: 0 or 1
+        t = tensor(Q, 8, CQ, EQ)
+        t.fold_softmax = bad
+        assert call(t=[t, good[1]]) == INVALID
     assert call(t=[good[0], tensor(K, 2, Q + 64, EK)]) == INVALID    # codes of k overlap q
     assert call(t=[good[0], tensor(K, 2, CK, EK)], w=K + 128) == INVALID   # workspace overlaps k
     assert call(S=0, r=None) == OK

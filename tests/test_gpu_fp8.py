@@ -11,7 +11,7 @@ import oracle
 from oracle import fp8 as ofp8
 import bidirectional_transformer_attention_amd as nx
 from bidirectional_transformer_attention_amd import synth
-from helpers import TOL, attention_err, f64, lse_err_ok
+from helpers import TOL, attention_err, f64, fold_factor, lse_err_ok
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -82,12 +82,14 @@ def test_rope_quantize_matches_rope_then_quantize(dtype, case):
     seps = [x.clone() for x in xs]
     for sx in seps:
         nx.nxattn_rope_apply(sx, descs)
-    # per-tensor multipliers: the softmax fold factor, none (0 and 1), and a plain 3
-    mults = [nx.fold_factor(128), 0.0, 3.0, 1.0][:len(xs)]
-    outs = nx.nxattn_rope_quantize_fp8(xs, descs, workspace=ws, mults=mults)
+    # per tensor: the softmax fold factor formed by the library, none (0 and 1), a plain 3
+    mults = [0.0, 0.0, 3.0, 1.0][:len(xs)]
+    folds = [True, False, False, False][:len(xs)]
+    outs = nx.nxattn_rope_quantize_fp8(xs, descs, workspace=ws, mults=mults, folds=folds)
     torch.cuda.synchronize()
     bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
-    for x, xo, sx, mu, (codes, exps) in zip(xs, x0, seps, mults, outs):
+    refm = [fold_factor(D) if f else m for m, f in zip(mults, folds)]
+    for x, xo, sx, mu, (codes, exps) in zip(xs, x0, seps, refm, outs):
         assert torch.equal(x.view(bits).cpu(), xo.view(bits).cpu())     # x is only read
         # the oracle's codes of the stored rotation times mult (one fp32 multiply)
         sm = sx.cpu().float() * torch.tensor(mu if mu else 1.0, dtype=torch.float32)
@@ -133,13 +135,13 @@ def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True, fold=False):
     pk = [(synth.random_tensor((p, Hkv, D), seed + 3 + b, torch.float32) * pre_mult).to(torch.bfloat16) if p else None
           for b, p in enumerate(P)]
     pv = [synth.random_tensor((p, Hkv, D), seed + 13 + b, torch.bfloat16) if p else None for b, p in enumerate(P)]
-    cf = nx.fold_factor(D)
+    cf = fold_factor(D)
     if fold:
         # q rotated and multiplied by softmax_scale*log2(e) inside the quantizer; the
         # reference takes the GPU's rotation (parity-tested on its own) times cf in fp32
         descs = [nx.rope_desc((S,), (64,), (5 * b,)) for b in range(B)]
         qd = q.to(DEV)
-        [(q8, qe)] = nx.nxattn_rope_quantize_fp8([qd], descs, mults=[cf])
+        [(q8, qe)] = nx.nxattn_rope_quantize_fp8([qd], descs, folds=[True])
         nx.nxattn_rope_apply(qd, descs)
         q = qd.cpu()
         qref = q.float() * torch.tensor(cf, dtype=torch.float32)
@@ -212,3 +214,27 @@ def test_fwd_fp8_folded_q(B, S, Hq, Hkv, P):
 
 def test_fwd_fp8_folded_q_prefix_scale_differs():
     fp8_case(2, 160, 8, 2, (100, 30), 4500, pre_mult=100.0, fold=True)
+
+
+def test_fwd_fp8_deterministic():
+    # the same fp8 attention call twice gives the same bits (q folded, prefix on one branch)
+    note("fwd fp8 determinism")
+    B, S, Hq, Hkv, D, P = 2, 300, 8, 2, 128, 99
+    q = synth.random_tensor((B, S, Hq, D), 4600, torch.bfloat16).to(DEV)
+    k = synth.random_tensor((B, S, Hkv, D), 4601, torch.bfloat16).to(DEV)
+    v = synth.random_tensor((B, S, Hkv, D), 4602, torch.bfloat16).to(DEV)
+    pk = synth.random_tensor((1, P, Hkv, D), 4603, torch.bfloat16).to(DEV)
+    pv = synth.random_tensor((P, Hkv, D), 4604, torch.bfloat16).to(DEV)
+    descs = [nx.rope_desc((S,), (64,), (7 * b,)) for b in range(B)]
+    [(q8, qe), (k8, ke)] = nx.nxattn_rope_quantize_fp8([q, k], descs, folds=[True, False])
+    pk8, pe = nx.nxattn_quantize_fp8(pk)
+    pke = torch.zeros((B, Hkv), dtype=torch.int8, device=DEV)
+    pke[0] = pe[0]
+    outs = []
+    for _ in range(2):
+        o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+        ls = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+        nx.nxattn_fwd_fp8(q8, k8, qe, ke, v, o, [pk8[0], None], [pv, None], pke, lse=ls, q_folded=True)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), ls.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

@@ -14,7 +14,8 @@ import oracle
 import bidirectional_transformer_attention_amd as nx
 from bidirectional_transformer_attention_amd import synth
 from bidirectional_transformer_attention_amd.pipeline import AttentionStep
-from helpers import TOL, attention_err, f64, fused_q, oracle_attention, oracle_rope, sample_rows
+from helpers import (TOL, attention_err, cosine, f64, fold_factor, fused_q, global_maxrel, oracle_attention,
+                     oracle_rope, sample_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -248,16 +249,18 @@ def test_fwd_constant_v_and_zero_q():
     assert np.all(np.isfinite(f64(oz)))
 
 
-def test_fwd_bit_exact_selection():
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 72), (torch.float32, 64)])
+def test_fwd_bit_exact_selection(dtype, D):
     """Each query selects exactly one key (others underflow to weight 0); V rows encode
     (key mod 256, key // 256, branch, kv head) so the output must decode bit for bit to
     the expected key of the expected branch and kv head: pins prefix ++ own, the GQA
-    mapping and the branch indexing."""
-    D, B, S, Hq, Hkv = 128, 2, 200, 8, 2
+    mapping and the branch indexing, in both attention kernels."""
+    B, S, Hq, Hkv = 2, 200, 8, 2
     plens = (70, 135)
     rng = np.random.default_rng(7)
-    for dtype in (torch.bfloat16,):
-        note(f"fwd bit-exact selection {dtype}")
+    cast = bf if dtype == torch.bfloat16 else (lambda x: x)
+    for _ in (0,):
+        note(f"fwd bit-exact selection {dtype} D={D}")
         q = torch.zeros((B, S, Hq, D))
         k = torch.zeros((B, S, Hkv, D))
         v = torch.full((B, S, Hkv, D), 0.5)          # non-selected rows: must get weight 0
@@ -287,25 +290,45 @@ def test_fwd_bit_exact_selection():
                     for i in range(S):
                         q[b, i, h, pick[i]] = 48.0
                         expect[b, i, h] = active[pick[i]]
-        o = run_fwd(bf(q).to(DEV), bf(k).to(DEV), bf(v).to(DEV), [bf(p).to(DEV) for p in pre])
+        o = run_fwd(cast(q).to(DEV), cast(k).to(DEV), cast(v).to(DEV), [cast(p).to(DEV) for p in pre])
         got = f64(o)
         for b in range(B):
             for h in range(Hq):
                 g = h // (Hq // Hkv)
                 exp_rows = np.stack([expect[b, :, h] % 256, expect[b, :, h] // 256,
                                      np.full(S, b), np.full(S, g)], 1).astype(np.float64)
-                assert np.array_equal(got[b, :, h, :4], exp_rows), (b, h)
+                dec = got[b, :, h, :4]
+                if dtype == torch.float32:
+                    # the single weight is exp(0) = 1 up to the rounding of the fp32 score
+                    # arithmetic, and o = (p v) / l with l = p can move v's last bits: the
+                    # code is decoded by rounding, after checking it sits within 4 ulp of an
+                    # integer
+                    assert np.all(np.abs(dec - np.round(dec)) <= 4 * 2.0 ** -23 * np.abs(dec)), (b, h)
+                    dec = np.round(dec)
+                bad = np.nonzero(np.any(dec != exp_rows, axis=1))[0]
+                assert bad.size == 0, (b, h, [(int(i), dec[i].tolist(), exp_rows[i].tolist()) for i in bad[:8]])
 
 
-def test_fwd_deterministic():
-    note("fwd determinism")
-    q = synth.random_tensor((2, 257, 8, 128), 51, torch.bfloat16).to(DEV)
-    k = synth.random_tensor((2, 257, 2, 128), 52, torch.bfloat16).to(DEV)
-    v = synth.random_tensor((2, 257, 2, 128), 53, torch.bfloat16).to(DEV)
-    pre = [synth.random_tensor((2, 99, 2, 128), 54, torch.bfloat16).to(DEV), None]
-    a = run_fwd(q, k, v, pre)
-    b = run_fwd(q, k, v, pre)
-    assert torch.equal(a, b)
+@pytest.mark.parametrize("dtype,D,splits", [(torch.bfloat16, 128, 0), (torch.float32, 72, 0),
+                                             (torch.bfloat16, 128, 4), (torch.float32, 64, 3)])
+def test_fwd_deterministic(dtype, D, splits):
+    # the same call twice gives the same bits: one pass, and key ranges plus the merge (a
+    # long prefix against few queries, so that the planner does split)
+    S, P = (257, 99) if splits == 0 else (64, 3000)
+    note(f"fwd determinism {dtype} D={D} splits={splits}")
+    q = synth.random_tensor((2, S, 8, D), 51, dtype).to(DEV)
+    k = synth.random_tensor((2, S, 2, D), 52, dtype).to(DEV)
+    v = synth.random_tensor((2, S, 2, D), 53, dtype).to(DEV)
+    pre = [synth.random_tensor((2, P, 2, D), 54, dtype).to(DEV), None]
+    lse = [torch.empty((2, 8, S), dtype=torch.float32, device=DEV) for _ in range(2)]
+    outs = []
+    for i in range(2):
+        o = torch.empty_like(q)
+        nx.nxattn_fwd(q, k, v, o, pre, lse=lse[i], num_splits=splits)
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(lse[0].cpu(), lse[1].cpu())
 
 
 def test_fwd_key_permutation_invariance():
@@ -386,11 +409,9 @@ def test_fwd_q_rope_on_load(grid, pairs, offsets, P, inter, gf):
         pk = f64(pre[b][0]) if pre[b] is not None else None
         pv = f64(pre[b][1]) if pre[b] is not None else None
         ref = oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv)
-        # the kernel rounds the rotated (and scaled) q to bf16: that rounding alone,
-        # measured with the oracle
-        share = attention_err(oracle.attention(fused_q(q_ex, D), f64(k_rot[b]), f64(v[b]), pk, pv), ref)
         err = attention_err(f64(o.cpu()[b]), ref)
-        assert err <= TOL["bf16"] + share, (b, err, share)
+        note(f"  branch {b}: error {err:.3e} against the exact oracle (gate {TOL['bf16']:.0e})")
+        assert err <= TOL["bf16"], (b, err)
 
 
 @pytest.mark.parametrize("k_mult", [6.0, 60.0])
@@ -400,6 +421,11 @@ def test_fwd_q_rope_score_jumps(k_mult):
     # keys, scaled up, raise the scores far above it. x6: jumps of tens in log2 units (a
     # tile's weight sum exceeds 2^8, the full update rescales); x60: jumps beyond 128
     # (the first try overflows to inf). Both must match the oracle like ordinary data.
+    # Scores 6x and 60x the usual scale make the output that much more sensitive to the one
+    # bf16 rounding of the rotated q that any bf16 pipeline takes (at 60x a rounding moves a
+    # score by about 0.1 nat), so the gate holds against the oracle's attention of q as the
+    # kernel rounds it (the rotation times scale*log2(e), rounded once to bf16); the error
+    # against the unrounded q is printed too.
     grid, pairs, S, Hq, Hkv, D = (8, 12), (32, 32), 96, 8, 2, 128
     note(f"fwd q_rope score jumps, own k x{k_mult}")
     q = synth.random_tensor((2, S, Hq, D), 95, torch.bfloat16)
@@ -418,14 +444,21 @@ def test_fwd_q_rope_score_jumps(k_mult):
     for b in range(2):
         q_ex = oracle.rope(f64(q[b]), grid, pairs, offsets[b], 10000.0)
         pk, pv = f64(pre[b][0]), f64(pre[b][1])
-        ref = oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv)
-        share = attention_err(oracle.attention(fused_q(q_ex, D), f64(k_rot[b]), f64(v[b]), pk, pv), ref)
+        ref = oracle.attention(fused_q(q_ex, D), f64(k_rot[b]), f64(v[b]), pk, pv)
         err = attention_err(got[b], ref)
-        assert err <= TOL["bf16"] + share, (b, err, share)
+        e_ex = attention_err(got[b], oracle.attention(q_ex, f64(k_rot[b]), f64(v[b]), pk, pv))
+        note(f"  branch {b}: error {err:.3e} against the oracle with q rounded as the kernel rounds it "
+             f"(gate {TOL['bf16']:.0e}); {e_ex:.3e} against the unrounded q")
+        assert err <= TOL["bf16"], (b, err)
 
 
 # ---------------------------------------------------------------------------- whole workloads
 def step_case(name, rows_per_branch, seed_rows):
+    """The whole step (relayout, RoPE, fused attention, CFG) on sampled rows of a full-size
+    workload. Every branch is held to the plain gate against the exact oracle (the
+    oracle's own RoPE in fp64, nothing rounded); a second check isolates the fused kernel
+    (the oracle's attention over the rotated q and k the kernel actually used). The
+    errors are printed for the record."""
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
     note(f"step {name} (sampled rows {rows_per_branch})")
     inp = synth.make_inputs(wl)
@@ -434,45 +467,47 @@ def step_case(name, rows_per_branch, seed_rows):
     torch.cuda.synchronize()
     o_gpu = step.o.cpu()
     rows = {b: sample_rows(wl.seq, rows_per_branch, seed_rows + b) for b in range(wl.branches)}
-    # the whole step against the oracle's own RoPE. The bf16 path rounds the rotated q
-    # and k to bf16 (one rounding each, as any bf16 pipeline does), which by itself moves
-    # the exact attention output; that share of the error is measured with the oracle
-    # alone (its own RoPE outputs rounded to bf16) and added to the kernel's bar.
     ref = oracle_attention(wl, inp, rows)
     tol = TOL[wl.dtype]
     qg, kg = step.q.cpu(), step.k.cpu()
-    if wl.dtype == "bf16":
-        rnd = lambda a: \
-            torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()  # noqa: E731
-        # q rotated on load is rounded after scaling by scale*log2(e) (the kernel's
-        # documented rounding point); a stored q is rounded as it is
-        rq = (lambda a: fused_q(a, wl.head_dim)) if step.fuse_q_rope else rnd
-        q_r = [rq(oracle_rope(wl, inp.q, b, rows[b])) for b in range(wl.branches)]
-        k_r = [rnd(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)]
-        ref_r = oracle_attention(wl, inp, rows, q_r, k_r, q_rot_rows_only=True)
-        rope_share = max(attention_err(ref_r[b], ref[b]) for b in range(wl.branches))
-    else:
-        rope_share = 0.0
-    # isolate the fused kernel: oracle attention over the GPU's own rotated k and q (q
-    # rotated on load inside the kernel is stood in for by the oracle's rotation rounded
-    # to bf16, the rounding the kernel applies)
+    # isolation reference: oracle attention over the GPU's own rotated k and, for q rotated
+    # on load inside the kernel, the oracle's rotation rounded where the kernel rounds it
     if step.fuse_q_rope:
+        q_r = [fused_q(oracle_rope(wl, inp.q, b, rows[b]), wl.head_dim) for b in range(wl.branches)]
         ref_iso = oracle_attention(wl, inp, rows, q_r, [f64(kg[b]) for b in range(wl.branches)],
                                    q_rot_rows_only=True)
     else:
         ref_iso = oracle_attention(wl, inp, rows, [f64(qg[b]) for b in range(wl.branches)],
                                    [f64(kg[b]) for b in range(wl.branches)])
+    errs = []
     for b in range(wl.branches):
         g = f64(o_gpu[b][rows[b]])
-        assert attention_err(g, ref_iso[b]) <= tol
-        assert attention_err(g, ref[b]) <= tol + rope_share, (attention_err(g, ref[b]), rope_share)
+        e = attention_err(g, ref[b])
+        e_iso = attention_err(g, ref_iso[b])
+        note(f"  branch {b}: error {e:.3e} against the exact oracle, {e_iso:.3e} against the isolated kernel "
+             f"reference (gate {tol:.0e}); global max-rel {global_maxrel(g, ref[b]):.3e}, "
+             f"cosine {cosine(g, ref[b]):.9f}")
+        errs.append((b, e, e_iso))
+    for b, e, e_iso in errs:
+        assert e_iso <= tol, (b, e_iso)
+        assert e <= tol, (b, e)
     if step.use_cfg:
         r = rows[0]
         both = sorted(set(rows[0]).intersection(rows[1]))
-        c = oracle.cfg_combine(ref[0][np.searchsorted(r, both)], ref[1][np.searchsorted(rows[1], both)], wl.guidance)
+        i0, i1 = np.searchsorted(r, both), np.searchsorted(rows[1], both)
         got = f64(out.cpu()[both])
-        # guidance amplifies the branch errors by up to (1 + 2s)
-        assert attention_err(got, c) <= tol * (1 + 2 * wl.guidance)
+        # the combine itself: one fp32 fma of the GPU's own branch outputs, rounded once
+        own = oracle.cfg_combine(f64(o_gpu[0][both]), f64(o_gpu[1][both]), wl.guidance)
+        e_own = attention_err(got, own)
+        # end to end: u + s (c - u) carries (1 + s) e_c + s e_u of the branch errors, at most
+        # (1 + 2s) times the branch gate
+        c = oracle.cfg_combine(ref[0][i0], ref[1][i1], wl.guidance)
+        e_cfg = attention_err(got, c)
+        note(f"  cfg (s = {wl.guidance}): error {e_cfg:.3e} against the exact oracle (gate "
+             f"{tol * (1 + 2 * wl.guidance):.2e}), {e_own:.3e} against the combine of the GPU branches")
+        # one bf16 rounding (< 2^-8 relative) after the fp32 fma, or the fp32 fma alone
+        assert e_own <= (2.0 ** -8 + 2.0 ** -16 if wl.dtype == "bf16" else 1e-6)
+        assert e_cfg <= tol * (1 + 2 * wl.guidance)
     return wl
 
 
@@ -490,10 +525,20 @@ def test_step_dit1k_bf16_sampled():
 
 @pytest.mark.parametrize("name", ["dit1k_fp8qk+replay", "dit2k_fp8qk"])
 def test_step_fp8qk_sampled(name):
-    # the bench configuration of the fp8 score GEMM at full size: the codes of the step's
-    # own q and k as nxattn_rope_apply rotates them (and of each prefix K) bit for bit
-    # against the oracle's quantization, then sampled rows of the attention against the
-    # oracle's attention of the dequantized inputs
+    """The bench configuration of the fp8 score GEMM at full size.
+
+    1. Isolation: the codes of the step's q and k as nxattn_rope_apply rotates them (q
+       times the softmax fold factor), and of each prefix K, bit for bit against the
+       oracle's quantization; sampled rows of the attention against the oracle's
+       attention of those dequantized codes.
+    2. The oracle chain alone: the oracle's fp64 RoPE rounded to bf16 (as a stored
+       rotation), q times the fold factor in fp32, the oracle's quantization; the GPU
+       attention against the oracle's attention of that chain's dequantized codes, at the
+       bf16 gate. Codes that differ from the chain's (a bf16 rounding of the rotation
+       that falls the other way) are counted and printed.
+    3. The recipe's own error, printed and not gated: the GPU attention against the
+       exact oracle attention of the unquantized inputs.
+    """
     from oracle import fp8 as ofp8
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
     note(f"step {name} (fp8 score GEMM, sampled rows)")
@@ -504,32 +549,54 @@ def test_step_fp8qk_sampled(name):
     # the step rotates inside the quantizer and leaves q and k as given
     assert torch.equal(step.q.cpu().view(torch.int16), inp.q.view(torch.int16))
     assert torch.equal(step.k.cpu().view(torch.int16), inp.k.view(torch.int16))
+    assert step.fold_q
+    cf = fold_factor(wl.head_dim)
+    q8, qe, k8, ke = (t.cpu().numpy() for t in (step.q8, step.qe, step.k8, step.ke))
+    o = step.o.cpu()
+    # 1. isolation
     qr, kr = step.q.clone(), step.k.clone()
     nx.nxattn_rope_apply(qr, step.descs)
     nx.nxattn_rope_apply(kr, step.descs)
     torch.cuda.synchronize()
-    # the step's q codes carry softmax_scale*log2(e) (one fp32 multiply of the stored rotation)
-    assert step.fold_q
-    cf = nx.fold_factor(wl.head_dim)
-    qg = f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32))
-    kg = f64(kr.cpu())
-    rq, rqe = ofp8.quantize_fp8(qg)
-    rk, rke = ofp8.quantize_fp8(kg)
-    assert np.array_equal(step.q8.cpu().numpy(), rq) and np.array_equal(step.qe.cpu().numpy(), rqe)
-    assert np.array_equal(step.k8.cpu().numpy(), rk) and np.array_equal(step.ke.cpu().numpy(), rke)
-    dq, dk = ofp8.dequantize_fp8(rq, rqe) / cf, ofp8.dequantize_fp8(rk, rke)
-    o = step.o.cpu()
+    rq, rqe = ofp8.quantize_fp8(f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32)))
+    rk, rke = ofp8.quantize_fp8(f64(kr.cpu()))
+    del qr, kr
+    assert np.array_equal(q8, rq) and np.array_equal(qe, rqe)
+    assert np.array_equal(k8, rk) and np.array_equal(ke, rke)
+    dq_iso, dk_iso = ofp8.dequantize_fp8(rq, rqe) / cf, ofp8.dequantize_fp8(rk, rke)
+    del rq, rk
+    # 2. the oracle chain
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    q_chain = torch.stack([bf(oracle_rope(wl, inp.q, b)) for b in range(wl.branches)])
+    k_chain = torch.stack([bf(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)])
+    cq, cqe = ofp8.quantize_fp8(f64(q_chain.float() * torch.tensor(cf, dtype=torch.float32)))
+    ck, cke = ofp8.quantize_fp8(f64(k_chain))
+    del q_chain, k_chain
+    nq, nk = int(np.count_nonzero(q8 != cq)), int(np.count_nonzero(k8 != ck))
+    note(f"  codes that differ from the oracle chain's: q {nq} of {q8.size}, k {nk} of {k8.size}; "
+         f"exponents differing: q {int(np.count_nonzero(qe != cqe))}, k {int(np.count_nonzero(ke != cke))}")
+    dq_ch, dk_ch = ofp8.dequantize_fp8(cq, cqe) / cf, ofp8.dequantize_fp8(ck, cke)
+    del cq, ck
     for b in range(wl.branches):
         pre = step.prefix_online[b]
-        dpk = pv = None
+        dpk = pv = pk_ex = None
         if pre is not None:
             pc, pe = ofp8.quantize_fp8(f64(pre[0].cpu())[None])
             assert np.array_equal(step.pk8[b].cpu().numpy(), pc) and np.array_equal(step.pke[b].cpu().numpy(), pe[0])
-            dpk, pv = ofp8.dequantize_fp8(pc, pe)[0], f64(pre[1].cpu())
+            dpk, pv, pk_ex = ofp8.dequantize_fp8(pc, pe)[0], f64(pre[1].cpu()), f64(pre[0].cpu())
         rows = sample_rows(wl.seq, 48, 700 + b)
-        ref = oracle.attention(dq[b][rows], dk[b], f64(inp.v[b]), dpk, pv, rows=np.arange(len(rows)))
-        err = attention_err(f64(o[b][torch.from_numpy(rows)]), ref)
-        assert err <= TOL["bf16"], (b, err)
+        ar = np.arange(len(rows))
+        g = f64(o[b][torch.from_numpy(rows)])
+        vb = f64(inp.v[b])
+        e_iso = attention_err(g, oracle.attention(dq_iso[b][rows], dk_iso[b], vb, dpk, pv, rows=ar))
+        e_ch = attention_err(g, oracle.attention(dq_ch[b][rows], dk_ch[b], vb, dpk, pv, rows=ar))
+        ex = oracle.attention(oracle_rope(wl, inp.q, b, rows), oracle_rope(wl, inp.k, b), vb, pk_ex, pv, rows=ar)
+        e_ex = attention_err(g, ex)
+        note(f"  branch {b}: error {e_ch:.3e} against the oracle chain, {e_iso:.3e} against the isolated "
+             f"reference (gate {TOL['bf16']:.0e}); the recipe against unquantized attention (not gated): "
+             f"{e_ex:.3e}, global max-rel {global_maxrel(g, ex):.3e}, cosine {cosine(g, ex):.9f}")
+        assert e_iso <= TOL["bf16"], (b, e_iso)
+        assert e_ch <= TOL["bf16"], (b, e_ch)
 
 
 def test_step_longctx_split_keys_sampled():
