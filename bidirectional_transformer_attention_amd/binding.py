@@ -25,7 +25,7 @@ MAX_SPLITS = 16
 
 SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_fwd_workspace_size",
            "nxattn_attn_merge", "nxattn_quantize_fp8_workspace_size", "nxattn_quantize_fp8",
-           "nxattn_rope_quantize_fp8", "nxattn_fwd_fp8",
+           "nxattn_rope_quantize_fp8", "nxattn_rope_quantize_fp8_noalloc", "nxattn_fwd_fp8",
            "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error", "nxattn_version")
 
 
@@ -106,6 +106,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nxattn_rope_quantize_fp8.argtypes = [ctypes.POINTER(Fp8Tensor), i32, i32, i64, i64, i64,
                                              ctypes.POINTER(RopeDesc), vp, i64, vp]
     lib.nxattn_rope_quantize_fp8.restype = i32
+    lib.nxattn_rope_quantize_fp8_noalloc.argtypes = [ctypes.POINTER(Fp8Tensor), i32, i32, i64, i64, i64,
+                                                     ctypes.POINTER(RopeDesc), vp]
+    lib.nxattn_rope_quantize_fp8_noalloc.restype = i32
     lib.nxattn_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), vp]
     lib.nxattn_fwd_fp8.restype = i32
     lib.nxattn_cfg_combine.argtypes = [vp, vp, vp, i64, ctypes.c_float, i32, vp]
@@ -421,6 +424,28 @@ def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
     darr = (RopeDesc * max(1, B))(*descs)
     _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, workspace.data_ptr(),
                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return outs
+
+
+def nxattn_rope_quantize_fp8_noalloc(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
+                                     codes: Sequence[torch.Tensor], exps: Sequence[torch.Tensor],
+                                     mults: Optional[Sequence[float]] = None,
+                                     folds: Optional[Sequence[bool]] = None, stream=None):
+    """nxattn_rope_quantize_fp8 into the given codes and exps without a workspace (the
+    library's static scratch holds the running maxima); nothing is allocated here either.
+    Returns [(codes, exps)] in the order of xs."""
+    xs = list(xs)
+    if not 1 <= len(xs) <= MAX_FP8_TENSORS:
+        raise NxattnError(1, f"need 1 to {MAX_FP8_TENSORS} tensors")
+    codes, exps = list(codes), list(exps)
+    if len(codes) != len(xs) or len(exps) != len(xs) or any(t is None for t in codes + exps):
+        raise NxattnError(1, "codes and exps must be given for every tensor")
+    _gpu(*xs, *codes, *exps)
+    outs = _rope_quant_outputs(xs, descs, codes, exps)
+    B, S, _, D = xs[0].shape
+    arr = _fp8_tensors(xs, outs, mults, folds)
+    darr = (RopeDesc * max(1, B))(*descs)
+    _check(load().nxattn_rope_quantize_fp8_noalloc(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, _stream(stream)))
     return outs
 
 

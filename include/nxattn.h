@@ -294,6 +294,21 @@ int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors
                              int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nxattn_rope_quantize_fp8 for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments and
+ * results, bit for bit, without the workspace: the running maxima live in a static device
+ * array of the library (256 KiB per GPU, held from the first call on a GPU until the
+ * process ends), so batch * (total heads) must be at most 2048 (NXATTN_ERR_UNSUPPORTED
+ * otherwise). No call allocates. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (several streams, or several host threads) race and
+ * must be ordered by the caller; the array's contents between calls do not matter (each
+ * call clears what it uses with a kernel, no memset). The device is the calling thread's
+ * current one; stream must belong to it.
+ */
+int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
+                                     int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope, hipStream_t stream);
+
+/*
  * Attention of nxattn_fwd with the fp8 score GEMM above (head_dim 128, heads_q % heads_kv
  * == 0, batch <= 8). For branch b, q head h (kv head g = h / (heads_q / heads_kv)):
  *   keys j < P_b: prefix row j (codes prefix_k8[b], exponent prefix_k_exp[b, g]; value

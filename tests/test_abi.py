@@ -302,6 +302,24 @@ def test_rope_quantize_fp8_rejects(lib):
     assert call(t=[tensor(Q, 0, 0, 0)], n=1, r=None) == OK      # no heads at all
 
 
+def test_rope_quantize_fp8_noalloc_rejects(lib):
+    # the variant without a workspace: its static scratch holds 2048 (branch, head) slices;
+    # larger problems are refused on the host, before the scratch is looked up
+    f = lib.nxattn_rope_quantize_fp8_noalloc
+    t = binding.Fp8Tensor()
+    t.x, t.heads, t.codes, t.exps = FAKE, 257, FAKE + GB, FAKE + 2 * GB
+    for i, v in enumerate((257 * 128, 257 * 128, 128)):
+        t.strides[i] = v
+    d = binding.RopeDesc()
+    d.n_axes, d.grid[0], d.pairs[0], d.theta = 1, 1, 64, 10000.0
+    ds = (binding.RopeDesc * 8)(*([d] * 8))
+    assert f(ctypes.byref(t), 1, 1, 8, 1, 128, ds, None) == UNSUPPORTED          # 8 * 257 = 2056 slices
+    assert b"2048" in lib.nxattn_last_error()
+    assert f(None, 1, 1, 8, 1, 128, ds, None) == INVALID
+    assert f(ctypes.byref(t), 0, 1, 8, 1, 128, ds, None) == INVALID
+    assert f(ctypes.byref(t), 1, 1, -1, 1, 128, ds, None) == INVALID
+
+
 def fp8_args(**kw):
     a = binding.FwdFp8Args()
     a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = 2, 64, 8, 2, 128
