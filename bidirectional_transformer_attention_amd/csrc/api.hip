@@ -121,7 +121,11 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
     for (int b = 0; b < a->batch; ++b) {
       const int st = check_rope_desc(a->q_rope[b], a->seq_q, a->head_dim, "nxattn_fwd (q_rope)");
       if (st != NXATTN_OK) return st;
-
+      // the rotation on load holds positions as exact fp32 integers
+      for (int ax = 0; ax < a->q_rope[b].n_axes; ++ax)
+        if ((int64_t)a->q_rope[b].offset[ax] + a->q_rope[b].grid[ax] - 1 >= (1 << 24))
+          return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd (q_rope): positions must stay below 2^24 "
+                      "(rotate q with nxattn_rope_apply instead)");
     }
   // own k and v are not read with prefix_only
   const bool own = !a->prefix_only;
@@ -188,7 +192,7 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
     const nxattn_rope_desc& d = a->q_rope[b];
     RopeQ& r = p.rq[b];
     r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.global_freq = d.global_freq;
-    r.log2_theta = (float)std::log2(d.theta);
+    r.log2_theta = std::log2(d.theta);
     for (int ax = 0; ax < 3; ++ax) {
       r.grid[ax] = ax < d.n_axes ? d.grid[ax] : 1;
       r.pairs[ax] = ax < d.n_axes ? d.pairs[ax] : 0;

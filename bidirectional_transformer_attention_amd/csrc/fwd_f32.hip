@@ -242,16 +242,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
 
 FwdShape fwd_shape_f32(const FwdProblem& p) {
   using namespace f32k;
-  static int per_cu[2] = {-1, -1};   // resident workgroups per CU, D = 64 / 72
-  const int i = p.head_dim == 64 ? 0 : 1;
-  if (per_cu[i] < 0) {
-    int n = 0;
-    const hipError_t e = i == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<64>, 256, 0)
-                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<72>, 256, 0);
-    per_cu[i] = (e != hipSuccess || n < 1) ? 1 : n;
-  }
+  // resident workgroups per CU of the variant that will run (queried on each call: the
+  // library keeps no state)
+  int n = 0;
+  const hipError_t e = p.head_dim == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<64>, 256, 0)
+                                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_f32_kernel<72>, 256, 0);
   const int64_t nqb = (int64_t)(p.heads_q / p.heads_kv) * ((p.seq_q + 31) / 32);
-  return FwdShape{(nqb + WAVES - 1) / WAVES * p.heads_kv, per_cu[i]};
+  return FwdShape{(nqb + WAVES - 1) / WAVES * p.heads_kv, (e != hipSuccess || n < 1) ? 1 : n};
 }
 
 int launch_fwd_f32(const FwdProblem& p, hipStream_t stream) {

@@ -110,7 +110,7 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
 struct RopeQ {
   int32_t n_axes, interleaved, global_freq;
   int32_t grid[3], pairs[3], offset[3];
-  float log2_theta;
+  double log2_theta;
 };
 
 // ---- launchers implemented per kernel file -------------------------------------------

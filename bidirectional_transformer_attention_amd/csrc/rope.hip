@@ -291,6 +291,8 @@ int nx::check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim
   int64_t prod = 1, psum = 0;
   for (int a = 0; a < d.n_axes; ++a) {
     if (d.grid[a] < 1 || d.pairs[a] < 1) return fail(NXATTN_ERR_INVALID, "%s: grid and pairs must be >= 1", who);
+    if (d.offset[a] < 0 || (int64_t)d.offset[a] + d.grid[a] - 1 > INT32_MAX)
+      return fail(NXATTN_ERR_INVALID, "%s: offset[%d] must be >= 0 with offset + grid - 1 in int32", who, a);
     prod *= d.grid[a];
     psum += d.pairs[a];
   }

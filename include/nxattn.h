@@ -5,8 +5,10 @@
  *
  * Conventions shared by every entry point
  *  - Device pointers are owned by the caller; the library allocates no device memory,
- *    keeps no state except a thread-local error message, and never synchronises:
- *    work is enqueued on `stream` (NULL = the default stream) and the call returns.
+ *    keeps no state except a thread-local error message (and, for
+ *    nxattn_rope_quantize_fp8_noalloc alone, its static device scratch and that
+ *    scratch's address per GPU), and never synchronises: work is enqueued on `stream`
+ *    (NULL = the default stream) and the call returns.
  *  - Every argument is validated on the host before anything is enqueued; on error
  *    nothing is launched and the return value is a nonzero nxattn_status. The detail
  *    of the last failing call on this thread is in nxattn_last_error().
@@ -119,9 +121,12 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * q_rope (optional, host memory, `batch` descriptors; NULL: q is used as stored):
  * rotate q on load with the RoPE of nxattn_rope_apply (same descriptor meaning and
  * checks, grid product == seq_q), inside the attention kernel, so that no separate
- * pass over q is needed; the q buffer is not modified. The angle is evaluated in fp32
- * (absolute error about 1e-4 rad at positions near 1000, far below the bf16 rounding
- * of the rotated value). The rotated value is multiplied by scale * log2(e) (the units
+ * pass over q is needed; the q buffer is not modified. Positions (grid coordinate plus
+ * offset) must stay below 2^24 (NXATTN_ERR_UNSUPPORTED otherwise). Each pair's step
+ * theta^(..)/2pi is evaluated in fp64 and carried as two fp32 parts, and position * step
+ * is formed exactly but for the roundings of small terms: the turn is accurate to about
+ * 1e-7 revolutions at every supported position, far below the bf16 rounding of the
+ * rotated value, and the hardware sine and cosine take it. The rotated value is multiplied by scale * log2(e) (the units
  * of the kernel's base-2 softmax) and rounded once to bf16, nearest even: the q used
  * is that rounding divided by scale * log2(e), as close to the rotated q as a stored
  * bf16 q would be, but rounded at a different point.

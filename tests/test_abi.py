@@ -133,6 +133,13 @@ def _with_q_rope(a, descs):
     (dict(), [_bad_global_freq()] * 2, INVALID),
     # a valid q_rope does not skip the other checks (o overlaps q: nothing launches)
     (dict(o=FAKE), [binding.rope_desc((8, 8), (32, 32), (4, 4))] * 2, INVALID),
+    # offsets are non-negative
+    (dict(), [binding.rope_desc((8, 8), (32, 32), (0, -1))] * 2, INVALID),
+    # positions on load stay below 2^24 (the last one here is 2^24)
+    (dict(), [binding.rope_desc((8, 8), (32, 32), (0, 0)), binding.rope_desc((8, 8), (32, 32), (2 ** 24 - 7, 0))],
+     UNSUPPORTED),
+    # offset + grid - 1 must fit int32
+    (dict(), [binding.rope_desc((64,), (64,), (2 ** 31 - 10,))] * 2, INVALID),
 ])
 def test_fwd_q_rope_rejects(lib, kw, descs, code):
     assert call_fwd(lib, _with_q_rope(fwd_args(**kw), descs)) == code

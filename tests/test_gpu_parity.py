@@ -452,6 +452,68 @@ def test_fwd_q_rope_score_jumps(k_mult):
         assert err <= TOL["bf16"], (b, err)
 
 
+@pytest.mark.parametrize("grid,pairs,offsets", [
+    ((8, 8), (32, 32), ((1024, 1024), (16384, 16384))),          # the 2K DiT offset, a long-prefix offset
+    ((4, 4, 4), (22, 21, 21), ((100000, 3, 77), (2 ** 24 - 4, 2 ** 24 - 4, 2 ** 24 - 4))),  # up to the limit
+])
+def test_fwd_q_rope_readout_at_large_positions(grid, pairs, offsets):
+    """The rotated q that the kernel multiplies, read out exactly: with the prefix as the
+    only keys and a single key e_d per kv head, the log-sum-exp is that query's score,
+    ln2 * q~_d, where q~ = bf16(scale * log2(e) * rope(q)) is the kernel's folded rotation.
+    Against the oracle's fp64 rotation (times the same factor, rounded to bf16): at most
+    one bf16 ulp apart, and only where the exact value sits within the fp32 arithmetic's
+    error of a rounding boundary (an angle error of 1e-4 rad would move a few percent of
+    the values)."""
+    D, Hq, B = 128, 16, 2
+    S = int(np.prod(grid))
+    note(f"fwd q_rope readout grid={grid} offsets={offsets}")
+    q = synth.random_tensor((B, S, Hq, D), 4800, torch.bfloat16)
+    qd = q.to(DEV)
+    descs = [nx.rope_desc(grid, pairs, offsets[b]) for b in range(B)]
+    cf = fold_factor(D)
+    got = np.zeros((B, S, Hq, D))
+    v = torch.ones((1, Hq, D), dtype=torch.bfloat16)
+    o = torch.empty_like(qd)
+    read = np.zeros((Hq, D), dtype=bool)
+    for t in range(32):
+        # kv head h holds the single key e_d: head h reads dims 8h .. 8h + 31 (mod 128)
+        k = torch.zeros((1, Hq, D), dtype=torch.bfloat16)
+        dims = [(8 * h + t) % D for h in range(Hq)]
+        for h, d in enumerate(dims):
+            k[0, h, d] = 1.0
+        pre = torch.stack([k, v], 0).contiguous().to(DEV)        # [2, 1, Hkv, D]
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+        nx.nxattn_fwd(qd, None, None, o, [pre, pre], q_rope=descs, lse=lse, prefix_only=True)
+        torch.cuda.synchronize()
+        val = lse.cpu().numpy().astype(np.float64) / np.log(2.0)        # [B, Hq, S]
+        for h, d in enumerate(dims):
+            got[:, :, h, d] = val[:, h, :]
+            read[h, d] = True
+    # the readout is a bf16 value up to the fp32 products of the log-sum-exp
+    gb = torch.from_numpy(got).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.all(np.abs(gb - got) <= 2.0 ** -20 * np.abs(got) + 1e-30)
+    ex = np.stack([oracle.rope(f64(q[b]), grid, pairs, offsets[b]) for b in range(B)]) * cf
+    rb = torch.from_numpy(ex).to(torch.bfloat16).to(torch.float64).numpy()
+    # magnitude of the rotary pair each element belongs to (half-split pairs j, j + 64)
+    qa = f64(q)
+    pair = np.sqrt(qa ** 2 + np.roll(qa, D // 2, axis=-1) ** 2) * cf
+    hd = np.argwhere(read)
+    gb, rb, pair = gb[:, :, read], rb[:, :, read], pair[:, :, read]
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rb), 1e-30))) - 7)
+    miss = gb != rb
+    # one bf16 ulp of the result, plus 2^-13 of the pair's magnitude: the fp32 rotation's
+    # own rounding where the result cancels (an angle error of 1e-3 rad would exceed it)
+    tol = ulp * 1.0001 + 2.0 ** -13 * pair
+    rel = np.abs(gb - rb) / tol
+    w = np.unravel_index(int(np.argmax(rel)), rel.shape)
+    pos = oracle.positions(grid, offsets[w[0]])[w[1]]
+    note(f"  values off the rounded exact rotation: {int(miss.sum())} of {miss.size}; worst error "
+         f"{float(rel[w]):.3f} of its bound at branch {w[0]} token {w[1]} (positions {pos.tolist()}) head, dim "
+         f"{hd[w[2]].tolist()}: {float(gb[w]):.6g} against {float(rb[w]):.6g} (pair {float(pair[w]):.4g})")
+    assert np.all(np.abs(gb - rb) <= tol)
+    assert miss.mean() <= 2e-3
+
+
 # ---------------------------------------------------------------------------- whole workloads
 def step_case(name, rows_per_branch, seed_rows):
     """The whole step (relayout, RoPE, fused attention, CFG) on sampled rows of a full-size
