@@ -1,4 +1,4 @@
-// Fused non-causal attention, fp32 in/out, true fp32 MFMA (v_mfma_f32_32x32x2f32),
+// Fused non-causal attention, fp32 in/out, true fp32 MFMA (v_mfma_f32_16x16x4f32),
 // head_dim 64 or 72 (the vision-encoder shape: KLiteInfer page, "架构": bidirectional
 // attention of the ViT as two strided-batched fp32 GEMMs plus a softmax, TF32 off).
 //
@@ -8,10 +8,18 @@
 // virtual sequence [prefix ++ own] (the concatenation is only index arithmetic), or
 // over one key range of it when the keys are split (each range then writes a normalised
 // fp32 partial and its log-sum-exp for the merge kernel).
-// Each wave keeps S^T = K Q^T in the MFMA accumulator layout (lane = query, registers
-// = keys), so the running max and sum are per lane; the P^T accumulator registers feed
-// the P V MFMA directly as its B operand (no shuffle). K and V tiles are staged through
-// LDS, double-buffered, with the next tile's global loads in flight during compute.
+//
+// 16x16 tiles. A wave's 32 queries are two sub-blocks of 16 (lane l: queries l % 16 and
+// 16 + l % 16). S^T = K Q^T is kept as 4 x 2 blocks of 16 keys x 16 queries (lane l:
+// keys 4(l / 16) .. + 3 of a block), so each K fragment read from LDS feeds both
+// sub-blocks. For P V, register j of key block kb is directly the B operand (P^T) of one
+// 16x16x4 step over keys 16kb + 4k + j (k = 0..3), with the V^T operand read in the same
+// key order: no shuffle of P. The output is O^T in blocks of 16 head dims, so head_dim
+// 72 takes 5 blocks (80 columns, 10 % padding) rather than three of 32 (96 columns).
+// LDS rows are unpadded with 16-byte chunks permuted so that every fragment read hits
+// 64 distinct banks (see kslot / vcol). K and V tiles are double-buffered and loaded
+// straight into LDS, the next tile's loads in flight during compute; two workgroups
+// share a CU, so one wave's softmax overlaps another's MFMAs.
 // MFMA-bound: 4*Sq*Skv*Hq*D flops.
 #include "nx_internal.h"
 
@@ -21,7 +29,6 @@ namespace f32k {
 
 constexpr int WAVES = 4;
 constexpr int BN = KEY_TILE;    // keys per tile (64)
-constexpr int VSTR = 72;        // V row stride in LDS (floats)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_T = 8.0f;   // running max moves only when it grows by > 2^8
@@ -47,17 +54,36 @@ __device__ __forceinline__ int remap_xcd(int i, int n) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// LDS placement. K row r, 16-byte chunk c (floats 4c .. 4c + 3) sits at chunk
+// kslot(r, c) of the row; a score step reads rows 16kb + (l % 16), column 4s + l / 16: for
+// D = 64 (row stride 64 floats, one bank set per row) the chunk is XORed with r & 15, for
+// D = 72 (stride 72 = 8 banks per row) rows with bit 3 set are rotated by one chunk.
 template <int D>
-__global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
-  constexpr int KSTR = D + 1;                 // odd stride: column reads are conflict-free
-  constexpr int NDB = (D + 31) / 32;          // 32-wide output blocks (72 -> 3, last one partial)
+__device__ __forceinline__ int kslot(int r, int c) {
+  if constexpr (D == 64) return c ^ (r & 15);
+  else { const int x = c + ((r >> 3) & 1); return x < D / 4 ? x : x - D / 4; }
+}
+// V row r (a key), column d at float vcol(r, d) of the row; a P V step reads keys
+// 16kb + 4g + j (g = l / 16) at columns 16db + l % 16: the four key groups g must land on
+// four different 16-bank ranges (D = 64: XOR of the 16-column group with g; D = 72: a
+// 16-column rotation of rows with bit 3 set). Columns past D (the padded output block)
+// wrap inside the row.
+template <int D>
+__device__ __forceinline__ int vcol(int r, int d) {
+  if constexpr (D == 64) return d ^ (16 * ((r >> 2) & 3));
+  else { const int x = d + 16 * ((r >> 3) & 1); return x < D ? x : x - D; }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_f32_kernel(Args a) {
   constexpr int CH = D / 4;                   // 16-byte chunks per row
-  constexpr int LD = (BN * CH + 255) / 256;   // chunks per thread per tensor
-  __shared__ float Ks[2][BN * KSTR];
-  __shared__ float Vs[2][BN * VSTR];
+  constexpr int NS = D / 4;                   // k-steps of a score block
+  constexpr int NDB = (D + 15) / 16;          // 16-wide output blocks (72 -> 5, the last partial)
+  __shared__ __attribute__((aligned(1024))) float Ks[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) float Vs[2][BN * D];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 31, hh = lane >> 5;
+  const int a16 = lane & 15, grp4 = lane >> 4;
   const int w = remap_xcd(blockIdx.x, a.total_wg);
   // (branch, kv head, key range) groups of wg_per_group workgroups
   const int grp = w / a.wg_per_group;
@@ -67,8 +93,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   const int qb = rem * WAVES + wave;
   const bool active = qb < a.nqb;
   const int hq = g * a.group + (active ? qb / a.nchunks : 0);
-  const int tok = (active ? qb % a.nchunks : 0) * 32 + n;
-  const int tokc = tok < a.seq ? tok : a.seq - 1;
+  // the lane's two queries: sub-block qs holds token chunk*32 + 16qs + l % 16
+  const int tok0 = (active ? qb % a.nchunks : 0) * 32 + a16;
   // this work item's keys: tiles [t0, t0 + T) of the virtual sequence, keys below kend
   const int P = a.plen[b];
   const int Skv = P + (a.prefix_only ? 0 : a.seq);
@@ -80,162 +106,179 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Args a) {
   const bool partial = a.nsplit > 1 && Tall > a.per;
   const int kend = min((t0 + T) * BN, Skv);
 
-  // Q^T operand: k-step s holds Q[tok][hq][2s + hh]
-  float qv[D / 2];
-  {
-    const float* qrow = a.q + b * a.qs0 + (int64_t)tokc * a.qs1 + (int64_t)hq * a.qs2;
+  // Q^T operand of sub-block qs, k-step s: Q[tok0 + 16qs][4s + l / 16]
+  float qv[2][NS];
 #pragma unroll
-    for (int s = 0; s < D / 2; ++s) qv[s] = qrow[2 * s + hh];
+  for (int qs = 0; qs < 2; ++qs) {
+    const int tk = tok0 + 16 * qs < a.seq ? tok0 + 16 * qs : a.seq - 1;
+    const float* qrow = a.q + b * a.qs0 + (int64_t)tk * a.qs1 + (int64_t)hq * a.qs2;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) qv[qs][st] = qrow[4 * st + grp4];
   }
 
-  // tile loader: thread -> (row, 16-byte chunk) items of K and V
-  auto key_rows = [&](int j, const float*& kr, const float*& vr) {
-    j = j < kend ? j : kend - 1;
-    if (j < P) {
-      const float* base = a.prefix[b] + ((int64_t)j * a.heads_kv + g) * D;
-      kr = base;
-      vr = base + (int64_t)P * a.heads_kv * D;
-    } else {
-      const int64_t off = b * a.ks0 + (int64_t)(j - P) * a.ks1 + (int64_t)g * a.ks2;
-      kr = a.k + off;
-      vr = a.v + off;
-    }
-  };
-  f32x4 stk[LD], stv[LD];
-  auto gload = [&](int t) {
+  // Tile loads go straight to LDS (global_load_lds, 16 bytes a lane, 1 KB an
+  // instruction at consecutive LDS slots): slot x of a tile is row x / CH, chunk position
+  // x % CH, and its lane fetches the global chunk that kslot / vcol place there. The CH
+  // instructions per tensor are dealt round-robin to the 4 waves.
+  const int64_t pstride = (int64_t)a.heads_kv * D;
+  auto tile_dma = [&](int t, int buf) {
+    constexpr int NI = BN * CH / 64;
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int it = threadIdx.x + i * 256;
-      if (it < BN * CH) {
-        const int r = it / CH, c = it % CH;
+    for (int ii = 0; ii < (NI + WAVES - 1) / WAVES; ++ii) {
+      const int ins = ii * WAVES + wave;
+      if (ins < NI) {
+        const int x = ins * 64 + lane;
+        const int r = x / CH, cp = x - r * CH;
+        int jk = t * BN + r;
+        jk = jk < kend ? jk : kend - 1;
         const float *kr, *vr;
-        key_rows(t * BN + r, kr, vr);
-        stk[i] = *reinterpret_cast<const f32x4*>(kr + 4 * c);
-        stv[i] = *reinterpret_cast<const f32x4*>(vr + 4 * c);
+        if (jk < P) {
+          kr = a.prefix[b] + (int64_t)jk * pstride + (int64_t)g * D;
+          vr = kr + (int64_t)P * pstride;
+        } else {
+          const int64_t off = b * a.ks0 + (int64_t)(jk - P) * a.ks1 + (int64_t)g * a.ks2;
+          kr = a.k + off;
+          vr = a.v + off;
+        }
+        // inverse permutations: the global chunk whose LDS position is cp
+        int ck, cv;
+        if constexpr (D == 64) {
+          ck = cp ^ (r & 15);
+          cv = cp ^ (4 * ((r >> 2) & 3));
+        } else {
+          ck = cp - ((r >> 3) & 1);
+          ck = ck < 0 ? ck + CH : ck;
+          cv = cp - 4 * ((r >> 3) & 1);
+          cv = cv < 0 ? cv + CH : cv;
+        }
+        __builtin_amdgcn_global_load_lds(kr + 4 * ck, (__attribute__((address_space(3))) void*)&Ks[buf][ins * 256],
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vr + 4 * cv, (__attribute__((address_space(3))) void*)&Vs[buf][ins * 256],
+                                         16, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const int it = threadIdx.x + i * 256;
-      if (it < BN * CH) {
-        const int r = it / CH, c = it % CH;
-        float* kd = &Ks[buf][r * KSTR + 4 * c];
-        kd[0] = stk[i][0]; kd[1] = stk[i][1]; kd[2] = stk[i][2]; kd[3] = stk[i][3];
-        *reinterpret_cast<f32x4*>(&Vs[buf][r * VSTR + 4 * c]) = stv[i];
-      }
-    }
+  auto wait_tiles = [&]() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
   };
 
-  f32x16 acc_o[NDB];
+  f32x4 acc_o[NDB][2];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-  float m = -__builtin_inff(), l = 0.f;
+  for (int db = 0; db < NDB; ++db) acc_o[db][0] = acc_o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-__builtin_inff(), -__builtin_inff()}, l[2] = {0.f, 0.f};
 
-  gload(t0);
-  lstore(0);
-  __syncthreads();
+  tile_dma(t0, 0);
+  wait_tiles();
 
   for (int t = t0; t < t0 + T; ++t) {
     const int buf = (t - t0) & 1;
-    if (t + 1 < t0 + T) gload(t + 1);
+    if (t + 1 < t0 + T) tile_dma(t + 1, buf ^ 1);
     const float* kb_ = Ks[buf];
     const float* vb_ = Vs[buf];
 
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
+    // S^T = K Q^T: key block kb, query sub-block qs; one K fragment per (kb, step)
+    f32x4 s[4][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const float* krow = kb_ + (kb * 32 + n) * KSTR + hh;
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * kb + a16;
+      const float* krow = kb_ + r * D + grp4;
 #pragma unroll
-      for (int st = 0; st < D / 2; ++st)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * st], qv[st], s[kb], 0, 0, 0);
+      for (int st = 0; st < NS; ++st) {
+        const float kf = krow[4 * kslot<D>(r, st)];
+        s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qv[0][st], s[kb][0], 0, 0, 0);
+        s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qv[1][st], s[kb][1], 0, 0, 0);
+      }
     }
-    // mask keys past the end (only the last tile can have them)
+    // mask keys past the end (only the last tile can have them): register j of block
+    // kb is key 16kb + 4(l / 16) + j
     const int valid = kend - t * BN;
     if (valid < BN) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= valid) s[kb][i] = -__builtin_inff();
-        }
+        for (int j = 0; j < 4; ++j)
+          if (16 * kb + 4 * grp4 + j >= valid) s[kb][0][j] = s[kb][1][j] = -__builtin_inff();
     }
-    // online softmax (base 2, scale folded into one fma per score)
-    float tmax = s[0][0];
+    // online softmax per query (base 2, scale folded into one fma per score); a row's
+    // keys are spread over the four 16-lane groups
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qs = 0; qs < 2; ++qs) {
+      float tmax = s[0][qs][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = __builtin_fmaxf(tmax, s[kb][i]);
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
-      tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
-    }
-    const float cand = tmax * a.c;
-    const bool grow = cand > m + RESCALE_T;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mnew = grow ? cand : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-      m = mnew;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], a.c, -m));
-        s[kb][i] = p;
-        l += p;
+        for (int j = 0; j < 4; ++j) tmax = __builtin_fmaxf(tmax, s[kb][qs][j]);
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(tmax), __float_as_int(tmax), false, false);
+        tmax = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
       }
-    // O^T += V^T P^T: accumulator register i of key block kb is the B operand of one step
+      tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
+      const float cand = tmax * a.c;
+      const bool grow = cand > m[qs] + RESCALE_T;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mnew = grow ? cand : m[qs];
+        const float alpha = __builtin_amdgcn_exp2f(m[qs] - mnew);
+        l[qs] *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + n < D ? db * 32 + n : D - 1;
+        for (int db = 0; db < NDB; ++db) acc_o[db][qs] *= alpha;
+        m[qs] = mnew;
+      }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vb_[key * VSTR + d], s[kb][i], acc_o[db], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qs][j], a.c, -m[qs]));
+          s[kb][qs][j] = p;
+          l[qs] += p;
         }
     }
-    if (t + 1 < t0 + T) lstore(buf ^ 1);
-    __syncthreads();
+    // O^T += V^T P^T: step (kb, j) covers keys 16kb + 4k + j (k = l / 16 in both operands)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * kb + 4 * grp4 + j;
+          const float vf = vb_[r * D + vcol<D>(r, 16 * db + a16)];
+          acc_o[db][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, s[kb][0][j], acc_o[db][0], 0, 0, 0);
+          acc_o[db][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, s[kb][1][j], acc_o[db][1], 0, 0, 0);
+        }
+    wait_tiles();
   }
 
-  // epilogue: combine the two lane halves' partial sums, normalise, store
-  {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l), __float_as_int(l), false, false);
-    l = __int_as_float(sw[0]) + __int_as_float(sw[1]);
-  }
-  if (!active || tok >= a.seq) return;
-  const float inv = 1.0f / l;
-  // log-sum-exp: sum_j exp2(c s_j - m) = l, so lse = ln2 * (m + log2 l)  (l >= 1)
-  const float lse = LN2 * (m + __builtin_amdgcn_logf(l));
-  float* orow;
-  if (partial) {
-    orow = a.part_o + ((((int64_t)split * a.batch + b) * a.seq + tok) * a.heads_q + hq) * D;
-    if (hh == 0) a.part_lse[(((int64_t)split * a.batch + b) * a.heads_q + hq) * a.seq + tok] = lse;
-  } else {
-    orow = a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2;
-    if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = lse;
-  }
+  // epilogue: combine the four lane groups' partial sums, normalise, store (lane l holds
+  // head dims 16db + 4(l / 16) .. + 3 of its two queries)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int qs = 0; qs < 2; ++qs) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l[qs]), __float_as_int(l[qs]), false, false);
+    l[qs] = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+    l[qs] += __shfl_xor(l[qs], 16);
+  }
+  if (!active) return;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = db * 32 + 8 * i4 + 4 * hh;
-      if (d < D)
-        *reinterpret_cast<f32x4*>(orow + d) = f32x4{acc_o[db][4 * i4] * inv, acc_o[db][4 * i4 + 1] * inv,
-                                                    acc_o[db][4 * i4 + 2] * inv, acc_o[db][4 * i4 + 3] * inv};
+  for (int qs = 0; qs < 2; ++qs) {
+    const int tok = tok0 + 16 * qs;
+    if (tok >= a.seq) continue;
+    const float inv = 1.0f / l[qs];
+    // log-sum-exp: sum_j exp2(c s_j - m) = l, so lse = ln2 * (m + log2 l)  (l >= 1)
+    const float lse = LN2 * (m[qs] + __builtin_amdgcn_logf(l[qs]));
+    float* orow;
+    if (partial) {
+      orow = a.part_o + ((((int64_t)split * a.batch + b) * a.seq + tok) * a.heads_q + hq) * D;
+      if (grp4 == 0) a.part_lse[(((int64_t)split * a.batch + b) * a.heads_q + hq) * a.seq + tok] = lse;
+    } else {
+      orow = a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2;
+      if (a.lse && grp4 == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = lse;
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 16 * db + 4 * grp4;
+      if (d < D) *reinterpret_cast<f32x4*>(orow + d) = acc_o[db][qs] * inv;
+    }
+  }
 }
 
 }  // namespace f32k

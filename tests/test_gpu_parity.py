@@ -581,6 +581,27 @@ def test_step_vit_f32_one_layer_sampled():
     step_case("vit_f32", 300, 2)
 
 
+def test_step_vit_f32_all_layers_sampled():
+    # the 27-layer encoder as the benchmark steps it: every layer on its own seeded inputs
+    # (one AttentionStep per layer, all resident), sampled rows of each layer against the
+    # oracle at the fp32 gate
+    wl = synth.WORKLOADS["vit_f32"]
+    note(f"step vit_f32, {wl.layers} layers (sampled rows)")
+    inps = [synth.make_inputs(wl, layer=l) for l in range(wl.layers)]
+    steps = [AttentionStep(wl, inp) for inp in inps]
+    for st in steps:
+        st()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for l, (inp, st) in enumerate(zip(inps, steps)):
+        rows = {0: sample_rows(wl.seq, 40, 900 + l)}
+        ref = oracle_attention(wl, inp, rows)[0]
+        e = attention_err(f64(st.o.cpu()[0][rows[0]]), ref)
+        worst = max(worst, e)
+        assert e <= TOL["f32"], (l, e)
+    note(f"  worst layer error {worst:.3e} (gate {TOL['f32']:.0e})")
+
+
 def test_step_dit1k_bf16_sampled():
     step_case("dit1k_bf16", 96, 3)
 
