@@ -12,12 +12,12 @@
 // 16x16 tiles. A wave's 32 queries are two sub-blocks of 16 (lane l: queries l % 16 and
 // 16 + l % 16). S^T = K Q^T is kept as 4 x 2 blocks of 16 keys x 16 queries (lane l:
 // keys 4(l / 16) .. + 3 of a block), so each K fragment read from LDS feeds both
-// sub-blocks. For P V, register j of key block kb is directly the B operand (P^T) of one
+// sub-blocks, and one 16-byte read feeds four k-steps. For P V, register j of key block kb is directly the B operand (P^T) of one
 // 16x16x4 step over keys 16kb + 4k + j (k = 0..3), with the V^T operand read in the same
 // key order: no shuffle of P. The output is O^T in blocks of 16 head dims, so head_dim
 // 72 takes 5 blocks (80 columns, 10 % padding) rather than three of 32 (96 columns).
-// LDS rows are unpadded with 16-byte chunks permuted so that every fragment read hits
-// 64 distinct banks (see kslot / vcol). K and V tiles are double-buffered and loaded
+// LDS rows are unpadded with 16-byte chunks permuted so that the fragment reads are free
+// of bank conflicts (see kslot / vcol). K and V tiles are double-buffered and loaded
 // straight into LDS, the next tile's loads in flight during compute; two workgroups
 // share a CU, so one wave's softmax overlaps another's MFMAs.
 // MFMA-bound: 4*Sq*Skv*Hq*D flops.
@@ -54,30 +54,35 @@ __device__ __forceinline__ int remap_xcd(int i, int n) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-// LDS placement. K row r, 16-byte chunk c (floats 4c .. 4c + 3) sits at chunk
-// kslot(r, c) of the row; a score step reads rows 16kb + (l % 16), column 4s + l / 16: for
-// D = 64 (row stride 64 floats, one bank set per row) the chunk is XORed with r & 15, for
-// D = 72 (stride 72 = 8 banks per row) rows with bit 3 set are rotated by one chunk.
+// LDS placement (banks: 32 of 4 bytes; a 32-bit read is served per half-wave, a 128-bit
+// read per group of 8 lanes). Tiles arrive by 16-byte chunks, so only whole chunks move.
+// K row r, chunk c sits at chunk kslot(r, c) of the row. A score step group reads chunk
+// 4G + l / 16 of rows 16kb + l % 16 with one ds_read_b128: each 8-lane group reads one
+// chunk column of 8 consecutive rows, which must start on 8 different bank quads (D = 64:
+// chunk XOR r & 7; D = 72, rows 18 chunks = 2 quads apart: rows with bit 2 set move by
+// one chunk).
 template <int D>
 __device__ __forceinline__ int kslot(int r, int c) {
-  if constexpr (D == 64) return c ^ (r & 15);
-  else { const int x = c + ((r >> 3) & 1); return x < D / 4 ? x : x - D / 4; }
+  if constexpr (D == 64) return c ^ (r & 7);
+  else { const int x = c + ((r >> 2) & 1); return x < D / 4 ? x : x - D / 4; }
 }
-// V row r (a key), column d at float vcol(r, d) of the row; a P V step reads keys
-// 16kb + 4g + j (g = l / 16) at columns 16db + l % 16: the four key groups g must land on
-// four different 16-bank ranges (D = 64: XOR of the 16-column group with g; D = 72: a
-// 16-column rotation of rows with bit 3 set). Columns past D (the padded output block)
-// wrap inside the row.
+// V row r (a key), column d at float vcol(r, d) of the row. A P V step reads keys
+// 16kb + 4g + j (g = l / 16) at columns 16db + l % 16; a half-wave holds g = 0, 1 (or 2,
+// 3), whose rows differ in bit 2 and must fall on complementary 16-bank halves (D = 64: a
+// row stride of 64 floats repeats the banks, so the 16-column group is XORed with bit 2
+// of the key; D = 72: rows with bit 2 set are rotated by 16 columns). Columns past D (the
+// padded output block) wrap inside the row.
 template <int D>
 __device__ __forceinline__ int vcol(int r, int d) {
-  if constexpr (D == 64) return d ^ (16 * ((r >> 2) & 3));
-  else { const int x = d + 16 * ((r >> 3) & 1); return x < D ? x : x - D; }
+  if constexpr (D == 64) return d ^ (16 * ((r >> 2) & 1));
+  else { const int x = d + 16 * ((r >> 2) & 1); return x < D ? x : x - D; }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_f32_kernel(Args a) {
   constexpr int CH = D / 4;                   // 16-byte chunks per row
   constexpr int NS = D / 4;                   // k-steps of a score block
+  constexpr int NG = D / 16;                  // groups of four steps read as 16-byte chunks
   constexpr int NDB = (D + 15) / 16;          // 16-wide output blocks (72 -> 5, the last partial)
   __shared__ __attribute__((aligned(1024))) float Ks[2][BN * D];
   __shared__ __attribute__((aligned(1024))) float Vs[2][BN * D];
@@ -106,14 +111,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool partial = a.nsplit > 1 && Tall > a.per;
   const int kend = min((t0 + T) * BN, Skv);
 
-  // Q^T operand of sub-block qs, k-step s: Q[tok0 + 16qs][4s + l / 16]
+  // Q^T operand of sub-block qs. Score steps come in groups G of four: step 4G + w takes
+  // head dims 16G + 4k + w (k = l / 16, the MFMA's k index), so that a lane's K operands
+  // for the group are one 16-byte chunk (one ds_read_b128). With head_dim 72 the last 8
+  // dims form two single steps, 64 + 4t + k (t = 0, 1).
   float qv[2][NS];
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const int tk = tok0 + 16 * qs < a.seq ? tok0 + 16 * qs : a.seq - 1;
     const float* qrow = a.q + b * a.qs0 + (int64_t)tk * a.qs1 + (int64_t)hq * a.qs2;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) qv[qs][st] = qrow[4 * st + grp4];
+    for (int G = 0; G < NG; ++G) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 16 * G + 4 * grp4);
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) qv[qs][4 * G + w4] = x[w4];
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < NS - 4 * NG; ++t2) qv[qs][4 * NG + t2] = qrow[16 * NG + 4 * t2 + grp4];
   }
 
   // Tile loads go straight to LDS (global_load_lds, 16 bytes a lane, 1 KB an
@@ -143,12 +157,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // inverse permutations: the global chunk whose LDS position is cp
         int ck, cv;
         if constexpr (D == 64) {
-          ck = cp ^ (r & 15);
-          cv = cp ^ (4 * ((r >> 2) & 3));
+          ck = cp ^ (r & 7);
+          cv = cp ^ (4 * ((r >> 2) & 1));
         } else {
-          ck = cp - ((r >> 3) & 1);
+          ck = cp - ((r >> 2) & 1);
           ck = ck < 0 ? ck + CH : ck;
-          cv = cp - 4 * ((r >> 3) & 1);
+          cv = cp - 4 * ((r >> 2) & 1);
           cv = cv < 0 ? cv + CH : cv;
         }
         __builtin_amdgcn_global_load_lds(kr + 4 * ck, (__attribute__((address_space(3))) void*)&Ks[buf][ins * 256],
@@ -183,12 +197,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kb = 0; kb < 4; ++kb) {
       s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = 16 * kb + a16;
-      const float* krow = kb_ + r * D + grp4;
+      const float* krow = kb_ + r * D;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const float kf = krow[4 * kslot<D>(r, st)];
-        s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qv[0][st], s[kb][0], 0, 0, 0);
-        s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qv[1][st], s[kb][1], 0, 0, 0);
+      for (int G = 0; G < NG; ++G) {
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(krow + 4 * kslot<D>(r, 4 * G + grp4));
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[w4], qv[0][4 * G + w4], s[kb][0], 0, 0, 0);
+          s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[w4], qv[1][4 * G + w4], s[kb][1], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < NS - 4 * NG; ++t2) {
+        const float kf = krow[4 * kslot<D>(r, 4 * NG + t2) + grp4];
+        s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qv[0][4 * NG + t2], s[kb][0], 0, 0, 0);
+        s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qv[1][4 * NG + t2], s[kb][1], 0, 0, 0);
       }
     }
     // mask keys past the end (only the last tile can have them): register j of block
