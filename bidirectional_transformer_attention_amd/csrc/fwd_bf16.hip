@@ -408,9 +408,10 @@ __device__ __forceinline__ float weights(Wave& w, float c) {
   return l0 + l1;
 }
 
-// FOLD: -m into every register of the next scores' start block. Rebuilt at the end of
-// each softmax rather than kept: its registers are then free while the softmax runs,
-// which is where the kernel's register pressure peaks.
+// FOLD: -m into every register of the score accumulators' start block. The block is
+// kept across tiles and rebuilt only when m moves (the score MFMAs read it, never write
+// it); rebuilding it after every softmax cost 8 moves per half-tile (same-box: 0.5 %
+// at the 1K DiT shape, 0.8 % at 2K).
 template <bool FOLD>
 __device__ __forceinline__ void set_negm(Wave& w) {
   if constexpr (FOLD) {
@@ -454,6 +455,7 @@ __device__ __forceinline__ void full_update(Wave& w, float c) {
         w.s[1][i] -= d;
       }
       w.thr = RESCALE_T;
+      set_negm<FOLD>(w);
     }
   } else {
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -510,7 +512,6 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
     lt = weights<FOLD>(w, c);
   }
   w.l += lt;
-  set_negm<FOLD>(w);
 }
 
 // The per-wave program. Group A (waves 0-3) and group B (waves 4-7) run it half a tile

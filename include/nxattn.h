@@ -126,8 +126,9 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * theta^(..)/2pi is evaluated in fp64 and carried as two fp32 parts, and position * step
  * is formed exactly but for the roundings of small terms: the turn is accurate to about
  * 1e-7 revolutions at every supported position, far below the bf16 rounding of the
- * rotated value, and the hardware sine and cosine take it. The rotated value is multiplied by scale * log2(e) (the units
- * of the kernel's base-2 softmax) and rounded once to bf16, nearest even: the q used
+ * rotated value, and the hardware sine and cosine take it. The rotated value is
+ * multiplied by scale * log2(e) (the units of the kernel's base-2 softmax) and rounded
+ * once to bf16, nearest even: the q used
  * is that rounding divided by scale * log2(e), as close to the rotated q as a stored
  * bf16 q would be, but rounded at a different point.
  * BF16 only: F32 with q_rope returns NXATTN_ERR_UNSUPPORTED (rotate with
