@@ -7,7 +7,9 @@ The pages name fp8 variants of the DiT (NeoPP page, "Run the replay examples": t
 OCP FP8 E4M3 codes with one power-of-two scale per (branch, head); the score GEMM
 multiplies the decoded codes times their scales; everything after the scores (softmax,
 P.V with bf16 V) is the bf16 path. Decoding is exact, so the attention of the fp8 path is
-the attention of the dequantized q and k, which ``reference.attention`` evaluates.
+the attention of the dequantized q and k, which ``reference.attention`` evaluates. A
+second, finer reading (``quantize_fp8_blocks``) gives each run of 32 head_dim elements
+its own power-of-two scale.
 
 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities): exponent field
 e > 0 encodes (1 + m/8) * 2^(e-7), e = 0 encodes (m/8) * 2^-6; the code S.1111.111 is NaN,
@@ -90,3 +92,39 @@ def dequantize_fp8(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
     """codes [B, S, H, D] and exponents [B, H] -> values (float64)."""
     v = e4m3_decode(codes)
     return v * np.exp2(np.asarray(e, dtype=np.float64))[:, None, :, None]
+
+
+# ---- block scaling -------------------------------------------------------------------------
+# A second reading of the recipe, finer than one scale per (branch, head): the scale is
+# shared by each run of BLOCK = 32 consecutive elements of the head_dim axis of one
+# (branch, token, head) row, the block size and the E8M0 scale format of the OCP
+# Microscaling (MX) formats specification. The rule inside a block is the per-slice rule
+# above, so a block is quantized exactly as quantize_fp8 would quantize a slice holding
+# only that block's values. The scale of a block is stored as its E8M0 code e + 127
+# (value 2^(code - 127)), the operand format of the matrix core's scaled fp8 products.
+
+BLOCK = 32
+
+
+def quantize_fp8_blocks(x: np.ndarray, block: int = BLOCK) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantize x [..., D] (D a multiple of block) per run of `block` consecutive elements
+    of the last axis: e = fp8_exponent(max |run|), codes = e4m3_encode(run * 2^-e).
+    Returns (codes uint8 [..., D], scales uint8 [..., D / block]) with each scale held as
+    its E8M0 code e + 127."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if D % block != 0:
+        raise ValueError(f"last axis {D} is not a multiple of {block}")
+    runs = x.reshape(x.shape[:-1] + (D // block, block))
+    amax = np.max(np.abs(runs), axis=-1) if runs.size else np.zeros(runs.shape[:-1])
+    e = np.array([fp8_exponent(a) for a in amax.ravel()], dtype=np.int64).reshape(amax.shape)
+    codes = e4m3_encode(runs * np.exp2(-e.astype(np.float64))[..., None])
+    return codes.reshape(x.shape), (e + 127).astype(np.uint8)
+
+
+def dequantize_fp8_blocks(codes: np.ndarray, scales: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """codes [..., D] and E8M0 scale codes [..., D / block] -> values (float64)."""
+    v = e4m3_decode(codes)
+    runs = v.reshape(v.shape[:-1] + (v.shape[-1] // block, block))
+    s = np.exp2(np.asarray(scales, dtype=np.float64) - 127.0)
+    return (runs * s[..., None]).reshape(v.shape)
