@@ -133,9 +133,14 @@ def _cpu_baseline(wl, rows_per_branch, blas, layers, np, torch, oracle, synth):
                 # prefix K through E4M3 and back
                 from oracle import fp8 as ofp8
                 cf = fold_constant(wl.head_dim)
-                q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None] * cf))[0] / cf
-                k = ofp8.dequantize_fp8(*ofp8.quantize_fp8(k[None]))[0]
-                pk = None if pk is None else ofp8.dequantize_fp8(*ofp8.quantize_fp8(pk[None]))[0]
+                if wl.fp8_blocks:
+                    q = ofp8.dequantize_fp8_blocks(*ofp8.quantize_fp8_blocks(q * cf)) / cf
+                    k = ofp8.dequantize_fp8_blocks(*ofp8.quantize_fp8_blocks(k))
+                    pk = None if pk is None else ofp8.dequantize_fp8_blocks(*ofp8.quantize_fp8_blocks(pk))
+                else:
+                    q = ofp8.dequantize_fp8(*ofp8.quantize_fp8(q[None] * cf))[0] / cf
+                    k = ofp8.dequantize_fp8(*ofp8.quantize_fp8(k[None]))[0]
+                    pk = None if pk is None else ofp8.dequantize_fp8(*ofp8.quantize_fp8(pk[None]))[0]
             oracle.attention(q, k, f64(inp.v[b]), pk, None if pre is None else pre[1])
             flops += 4.0 * len(rows) * (wl.prefix_len[b] + wl.seq) * wl.heads_q * wl.head_dim
         dt += time.perf_counter() - t0
@@ -264,9 +269,11 @@ def main() -> int:
         if wl.prefix_layout == "replay" else 0,
         "rope": 0 if wl.qk_fp8 else 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
         "cfg": 3 * step.q[0].numel() * es if step.use_cfg else 0,
-        # reads q and k twice (rotated inside both passes: maximum, then codes), writes one
-        # byte per element (the prefix K is quantized once, outside the step)
-        "quantize": (2 * es + 1) * (step.q.numel() + step.k.numel()) if wl.qk_fp8 else 0,
+        # per (branch, head): reads q and k twice (rotated inside both passes: maximum, then
+        # codes), writes one byte per element; block scales: one read, the codes and one
+        # scale byte per 32 elements (the prefix K is quantized once, outside the step)
+        "quantize": (((es + 1) * (step.q.numel() + step.k.numel()) + (step.q.numel() + step.k.numel()) // 32)
+                     if wl.fp8_blocks else (2 * es + 1) * (step.q.numel() + step.k.numel())) if wl.qk_fp8 else 0,
     }
     for name, fn in (("relayout", step.relayout), ("rope", step.rope), ("quantize", step.quantize),
                      ("cfg", step.cfg)):
@@ -280,7 +287,8 @@ def main() -> int:
             "frac": round(achieved / peak, 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
                         and not wl.qk_fp8 else None),
-            "kernel": (f"nx::fp8k::fwd_fp8_kernel<{'true' if step.fold_q else 'false'}>" if wl.qk_fp8 else
+            "kernel": (f"nx::fp8k::fwd_fp8_kernel<{'true' if step.fold_q else 'false'}, "
+                       f"{'true' if wl.fp8_blocks else 'false'}>" if wl.qk_fp8 else
                        (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
                        if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),
@@ -326,7 +334,9 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8e4m3 QK / bf16 PV" if wl.qk_fp8 else wl.dtype, "data": "synthetic (seeded N(0,1), shapes of the workload)",
+        "vs_baseline": None,
+        "dtype": ("fp8e4m3 QK (E8M0 scale per 32 elements) / bf16 PV" if wl.fp8_blocks else "fp8e4m3 QK / bf16 PV")
+        if wl.qk_fp8 else wl.dtype, "data": "synthetic (seeded N(0,1), shapes of the workload)",
         "config": {"workload": wl.name, "branches": wl.branches, "seq_q": wl.seq, "grid": list(wl.grid),
                    "prefix_len": list(wl.prefix_len), "heads_q": wl.heads_q, "heads_kv": wl.heads_kv,
                    "head_dim": wl.head_dim, "rope_offsets": [list(o) for o in wl.offsets],

@@ -25,7 +25,7 @@ MAX_SPLITS = 16
 
 SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_fwd_workspace_size",
            "nxattn_attn_merge", "nxattn_quantize_fp8_workspace_size", "nxattn_quantize_fp8",
-           "nxattn_rope_quantize_fp8", "nxattn_rope_quantize_fp8_noalloc", "nxattn_fwd_fp8",
+           "nxattn_quantize_fp8_blocks", "nxattn_rope_quantize_fp8", "nxattn_rope_quantize_fp8_noalloc", "nxattn_fwd_fp8",
            "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error", "nxattn_version")
 
 
@@ -44,7 +44,7 @@ class RopeDesc(ctypes.Structure):
 class Fp8Tensor(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("heads", ctypes.c_int64), ("strides", ctypes.c_int64 * 3),
                 ("codes", ctypes.c_void_p), ("exps", ctypes.c_void_p), ("mult", ctypes.c_float),
-                ("fold_softmax", ctypes.c_int32)]
+                ("fold_softmax", ctypes.c_int32), ("scales", ctypes.c_void_p)]
 
 
 MAX_FP8_TENSORS = 4
@@ -70,7 +70,9 @@ class FwdFp8Args(ctypes.Structure):
                 ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
                 ("prefix_k8", ctypes.c_void_p * MAX_BRANCHES), ("prefix_v", ctypes.c_void_p * MAX_BRANCHES),
                 ("prefix_len", ctypes.c_int32 * MAX_BRANCHES), ("prefix_k_exp", ctypes.c_void_p),
-                ("scale", ctypes.c_float), ("lse", ctypes.c_void_p), ("q_folded", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("lse", ctypes.c_void_p), ("q_folded", ctypes.c_int32),
+                ("q_scales", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("prefix_k_scales", ctypes.c_void_p * MAX_BRANCHES)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -103,6 +105,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nxattn_quantize_fp8.argtypes = [vp, i32, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), vp, vp, vp,
                                         i64, vp]
     lib.nxattn_quantize_fp8.restype = i32
+    lib.nxattn_quantize_fp8_blocks.argtypes = [vp, i32, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), vp, vp,
+                                               vp]
+    lib.nxattn_quantize_fp8_blocks.restype = i32
     lib.nxattn_rope_quantize_fp8.argtypes = [ctypes.POINTER(Fp8Tensor), i32, i32, i64, i64, i64,
                                              ctypes.POINTER(RopeDesc), vp, i64, vp]
     lib.nxattn_rope_quantize_fp8.restype = i32
@@ -395,45 +400,80 @@ def nxattn_quantize_fp8(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e
     return codes, exps
 
 
+def _block_outputs(x, codes, scales):
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise NxattnError(1, "x must be [B, S, H, D] with D contiguous")
+    B, S, H, D = x.shape
+    if D % 32 != 0:
+        raise NxattnError(2, "block scales need head_dim a multiple of 32")
+    if codes is None:
+        codes = torch.empty((B, S, H, D), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, S, H, D // 32), dtype=torch.uint8, device=x.device)
+    if codes.dtype != torch.uint8 or tuple(codes.shape) != (B, S, H, D) or not codes.is_contiguous():
+        raise NxattnError(1, "codes must be a contiguous uint8 [B, S, H, D] tensor")
+    if scales.dtype != torch.uint8 or tuple(scales.shape) != (B, S, H, D // 32) or not scales.is_contiguous():
+        raise NxattnError(1, "scales must be a contiguous uint8 [B, S, H, D / 32] tensor")
+    return codes, scales
+
+
+def nxattn_quantize_fp8_blocks(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                               scales: Optional[torch.Tensor] = None, stream=None):
+    """E4M3 codes (uint8, contiguous [B,S,H,D]) and one E8M0 scale code per 32-element run
+    (uint8 [B,S,H,D/32]) of x [B,S,H,D] (bf16 or f32, strided, D contiguous, D % 32 == 0);
+    outputs allocated with torch when not given. Returns (codes, scales)."""
+    _gpu(x, codes, scales)
+    codes, scales = _block_outputs(x, codes, scales)
+    B, S, H, D = x.shape
+    st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    _check(load().nxattn_quantize_fp8_blocks(x.data_ptr(), _dtype_code(x), B, S, H, D, st, codes.data_ptr(),
+                                             scales.data_ptr(), _stream(stream)))
+    return codes, scales
+
+
 def nxattn_rope_quantize_fp8(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
                              codes: Optional[Sequence[torch.Tensor]] = None,
                              exps: Optional[Sequence[torch.Tensor]] = None,
                              workspace: Optional[torch.Tensor] = None,
                              mults: Optional[Sequence[float]] = None,
-                             folds: Optional[Sequence[bool]] = None, stream=None):
+                             folds: Optional[Sequence[bool]] = None, blocks: bool = False, stream=None):
     """Codes and exponents (as nxattn_quantize_fp8) of each x in xs ([B,S,H_t,D], one
     dtype, shared B, S, D and positions) rotated as nxattn_rope_apply would rotate it and,
     where mults gives a factor other than 0 or 1, multiplied by it in fp32 after the
     rotation's rounding; where folds[t] is true the library multiplies by the softmax
     fold factor instead (the codes nxattn_fwd_fp8 takes with q_folded; mults[t] > 0 then
-    gives the softmax scale). The x are not modified. Returns [(codes, exps)] in the
-    order of xs."""
+    gives the softmax scale). With blocks, each 32-element run gets its own scale (as
+    nxattn_quantize_fp8_blocks; `exps` then holds the uint8 [B,S,H_t,D/32] scale tensors
+    and no workspace is used). The x are not modified. Returns [(codes, exps or scales)]
+    in the order of xs."""
     xs = list(xs)
     if not 1 <= len(xs) <= MAX_FP8_TENSORS:
         raise NxattnError(1, f"need 1 to {MAX_FP8_TENSORS} tensors")
     codes = list(codes) if codes is not None else [None] * len(xs)
     exps = list(exps) if exps is not None else [None] * len(xs)
     _gpu(*xs, *[c for c in codes if c is not None], *[e for e in exps if e is not None], workspace)
-    outs = _rope_quant_outputs(xs, descs, codes, exps)
+    outs = _rope_quant_outputs(xs, descs, codes, exps, blocks)
     B, S, _, D = xs[0].shape
     total = sum(x.shape[2] for x in xs)
-    if workspace is None:
+    if workspace is None and not blocks:
         workspace = torch.empty(max(4, quantize_fp8_workspace_bytes(B, S, total)), dtype=torch.uint8,
                                 device=xs[0].device)
-    arr = _fp8_tensors(xs, outs, mults, folds)
+    arr = _fp8_tensors(xs, outs, mults, folds, blocks)
     darr = (RopeDesc * max(1, B))(*descs)
-    _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, workspace.data_ptr(),
-                                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().nxattn_rope_quantize_fp8(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, wp, wb,
+                                           _stream(stream)))
     return outs
 
 
 def nxattn_rope_quantize_fp8_noalloc(xs: Sequence[torch.Tensor], descs: List[RopeDesc],
                                      codes: Sequence[torch.Tensor], exps: Sequence[torch.Tensor],
                                      mults: Optional[Sequence[float]] = None,
-                                     folds: Optional[Sequence[bool]] = None, stream=None):
-    """nxattn_rope_quantize_fp8 into the given codes and exps without a workspace (the
-    library's static scratch holds the running maxima); nothing is allocated here either.
-    Returns [(codes, exps)] in the order of xs."""
+                                     folds: Optional[Sequence[bool]] = None, blocks: bool = False, stream=None):
+    """nxattn_rope_quantize_fp8 into the given codes and exps (with blocks: the block
+    scales) without a workspace (the library's static scratch holds the running maxima);
+    nothing is allocated here either. Returns [(codes, exps)] in the order of xs."""
     xs = list(xs)
     if not 1 <= len(xs) <= MAX_FP8_TENSORS:
         raise NxattnError(1, f"need 1 to {MAX_FP8_TENSORS} tensors")
@@ -441,51 +481,61 @@ def nxattn_rope_quantize_fp8_noalloc(xs: Sequence[torch.Tensor], descs: List[Rop
     if len(codes) != len(xs) or len(exps) != len(xs) or any(t is None for t in codes + exps):
         raise NxattnError(1, "codes and exps must be given for every tensor")
     _gpu(*xs, *codes, *exps)
-    outs = _rope_quant_outputs(xs, descs, codes, exps)
+    outs = _rope_quant_outputs(xs, descs, codes, exps, blocks)
     B, S, _, D = xs[0].shape
-    arr = _fp8_tensors(xs, outs, mults, folds)
+    arr = _fp8_tensors(xs, outs, mults, folds, blocks)
     darr = (RopeDesc * max(1, B))(*descs)
     _check(load().nxattn_rope_quantize_fp8_noalloc(arr, len(xs), _dtype_code(xs[0]), B, S, D, darr, _stream(stream)))
     return outs
 
 
-def _rope_quant_outputs(xs, descs, codes, exps):
+def _rope_quant_outputs(xs, descs, codes, exps, blocks=False):
     B, S, _, D = xs[0].shape
     outs = []
     for x, c, e in zip(xs, codes, exps):
         if x.dim() != 4 or (x.shape[0], x.shape[1], x.shape[3]) != (B, S, D) or x.dtype != xs[0].dtype:
             raise NxattnError(1, "tensors must share batch, seq, head_dim and dtype")
-        c, e = _quant_outputs(x, c, e)
+        c, e = _block_outputs(x, c, e) if blocks else _quant_outputs(x, c, e)
         outs.append((c, e))
     if len(descs) != B:
         raise NxattnError(1, "one RopeDesc per batch entry is required")
     return outs
 
 
-def _fp8_tensors(xs, outs, mults, folds):
+def _fp8_tensors(xs, outs, mults, folds, blocks=False):
     arr = (Fp8Tensor * len(xs))()
     for i, (x, (c, e)) in enumerate(zip(xs, outs)):
         arr[i].x, arr[i].heads = x.data_ptr(), x.shape[2]
         for k in range(3):
             arr[i].strides[k] = x.stride(k)
-        arr[i].codes, arr[i].exps = c.data_ptr(), e.data_ptr()
+        arr[i].codes = c.data_ptr()
+        if blocks:
+            arr[i].exps, arr[i].scales = None, e.data_ptr()
+        else:
+            arr[i].exps, arr[i].scales = e.data_ptr(), None
         arr[i].mult = float(mults[i]) if mults is not None else 0.0
         arr[i].fold_softmax = 1 if (folds is not None and folds[i]) else 0
     return arr
 
 
-def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_exp: torch.Tensor, v: torch.Tensor,
+def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: Optional[torch.Tensor],
+                   k_exp: Optional[torch.Tensor], v: torch.Tensor,
                    o: torch.Tensor, prefix_k8: Sequence[Optional[torch.Tensor]] = (),
                    prefix_v: Sequence[Optional[torch.Tensor]] = (), prefix_k_exp: Optional[torch.Tensor] = None,
                    scale: float = 0.0, lse: Optional[torch.Tensor] = None, q_folded: bool = False,
-                   stream=None) -> None:
+                   q_scales: Optional[torch.Tensor] = None, k_scales: Optional[torch.Tensor] = None,
+                   prefix_k_scales: Sequence[Optional[torch.Tensor]] = (), stream=None) -> None:
     """Attention with the fp8 score GEMM: q8 [B,S,Hq,128], k8 [B,S,Hkv,128] uint8 codes
     (contiguous), q_exp [B,Hq], k_exp [B,Hkv] int8; v [B,S,Hkv,128] and o [B,S,Hq,128] bf16;
     prefix_k8[b] uint8 [P_b,Hkv,128] and prefix_v[b] bf16 [P_b,Hkv,128] contiguous (or None),
     prefix_k_exp int8 [B,Hkv]. With q_folded, q8 holds the codes of q times
-    softmax_scale*log2(e) (see nxattn_rope_quantize_fp8's folds) and scale is not used."""
-    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, *[t for t in prefix_k8 if t is not None],
-         *[t for t in prefix_v if t is not None])
+    softmax_scale*log2(e) (see nxattn_rope_quantize_fp8's folds) and scale is not used.
+    Block scales: q_scales [B,S,Hq,4], k_scales [B,S,Hkv,4] and prefix_k_scales[b]
+    [P_b,Hkv,4] (uint8 E8M0 codes, contiguous) in place of the exponents (which are then
+    None)."""
+    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, q_scales, k_scales,
+         *[t for t in prefix_k8 if t is not None], *[t for t in prefix_v if t is not None],
+         *[t for t in prefix_k_scales if t is not None])
     B, S, Hq, D = q8.shape
     Hkv = k8.shape[2]
     for t in (q8, k8):
@@ -495,9 +545,19 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_ex
         raise NxattnError(1, "inconsistent q8/k8/v/o shapes")
     if v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 or v.stride(3) != 1 or o.stride(3) != 1:
         raise NxattnError(1, "v and o must be bf16 with head_dim contiguous")
-    for t, shp in ((q_exp, (B, Hq)), (k_exp, (B, Hkv))):
-        if t.dtype != torch.int8 or tuple(t.shape) != shp or not t.is_contiguous():
-            raise NxattnError(1, "exponents must be contiguous int8 [B, H] tensors")
+    block = q_scales is not None
+    if block:
+        if q_exp is not None or k_exp is not None or prefix_k_exp is not None:
+            raise NxattnError(1, "block scales exclude the per-slice exponents")
+        for t, shp in ((q_scales, (B, S, Hq, 4)), (k_scales, (B, S, Hkv, 4))):
+            if t is None or t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous():
+                raise NxattnError(1, "q_scales / k_scales must be contiguous uint8 [B, S, H, 4] tensors")
+    else:
+        if k_scales is not None or any(t is not None for t in prefix_k_scales):
+            raise NxattnError(1, "k_scales / prefix_k_scales need q_scales")
+        for t, shp in ((q_exp, (B, Hq)), (k_exp, (B, Hkv))):
+            if t is None or t.dtype != torch.int8 or tuple(t.shape) != shp or not t.is_contiguous():
+                raise NxattnError(1, "exponents must be contiguous int8 [B, H] tensors")
     if len(prefix_k8) not in (0, B) or len(prefix_v) != len(prefix_k8):
         raise NxattnError(1, "prefix_k8 and prefix_v need one entry per batch entry")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, S)):
@@ -505,7 +565,11 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_ex
     a = FwdFp8Args()
     a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, Hkv, D
     a.q_folded = 1 if q_folded else 0
-    a.q8, a.k8, a.q_exp, a.k_exp = q8.data_ptr(), k8.data_ptr(), q_exp.data_ptr(), k_exp.data_ptr()
+    a.q8, a.k8 = q8.data_ptr(), k8.data_ptr()
+    a.q_exp = q_exp.data_ptr() if q_exp is not None else None
+    a.k_exp = k_exp.data_ptr() if k_exp is not None else None
+    a.q_scales = q_scales.data_ptr() if block else None
+    a.k_scales = k_scales.data_ptr() if block else None
     a.v, a.o = v.data_ptr(), o.data_ptr()
     for i in range(3):
         a.v_strides[i] = v.stride(i)
@@ -516,6 +580,7 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_ex
         if pk is None or pk.numel() == 0:
             a.prefix_k8[b] = None
             a.prefix_v[b] = None
+            a.prefix_k_scales[b] = None
             a.prefix_len[b] = 0
             continue
         if (pk.dtype != torch.uint8 or not pk.is_contiguous() or pv is None or pv.dtype != torch.bfloat16
@@ -524,6 +589,14 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: torch.Tensor, k_ex
         a.prefix_k8[b] = pk.data_ptr()
         a.prefix_v[b] = pv.data_ptr()
         a.prefix_len[b] = pk.shape[0]
+        if block:
+            ps = prefix_k_scales[b] if b < len(prefix_k_scales) else None
+            if (ps is None or ps.dtype != torch.uint8 or not ps.is_contiguous()
+                    or tuple(ps.shape) != (pk.shape[0], Hkv, 4)):
+                raise NxattnError(1, "prefix_k_scales entries must be contiguous uint8 [P, Hkv, 4] tensors")
+            a.prefix_k_scales[b] = ps.data_ptr()
+        else:
+            a.prefix_k_scales[b] = None
     a.prefix_k_exp = prefix_k_exp.data_ptr() if prefix_k_exp is not None else None
     a.scale = float(scale)
     a.lse = lse.data_ptr() if lse is not None else None

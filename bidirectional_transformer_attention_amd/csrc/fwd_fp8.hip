@@ -1,9 +1,12 @@
 // Fused non-causal GQA attention with an FP8 score GEMM: q and k are OCP E4M3 codes with
-// one power-of-two scale per (branch, head), v and the output are bf16, head_dim 128.
-// The scores come from v_mfma_scale_f32_32x32x64_f8f6f4, whose per-lane E8M0 scale
-// operands apply the (power-of-two) dequantisation exactly inside the matrix core: the
-// key rows take the scale of the tensor they come from (prefix or own keys), the query
-// columns the scale of their head. Softmax, P (bf16) and O^T += V^T P^T are the bf16
+// one power-of-two scale per (branch, head) or, with BLOCK, one per run of 32 head_dim
+// elements of a row; v and the output are bf16, head_dim 128. The scores come from
+// v_mfma_scale_f32_32x32x64_f8f6f4, whose per-lane E8M0 scale operands apply the
+// (power-of-two) dequantisation exactly inside the matrix core: for row (or column) r,
+// lane r's scale covers bytes 0-15 of lanes r and r + 32 and lane r + 32's scale bytes
+// 16-31 of both. Per slice, the key rows take the scale of the tensor they come from
+// (prefix or own keys) and the query columns that of their head; with BLOCK each lane
+// takes the scale of the run whose codes that placement puts under it. Softmax, P (bf16) and O^T += V^T P^T are the bf16
 // kernel's. KLiteInfer page, "架构": scores GEMM, softmax, output GEMM; NeoPP page: the
 // DiT attends to [conditioning prefix ++ own tokens], and it names fp8 DiT variants
 // without a recipe (the recipe here is the quantisation of q and k in quant.hip).
@@ -15,6 +18,7 @@
 // chunk ^ (row & 7)); a score step is one 32x32x64 MFMA, so a tile needs 4 score MFMAs
 // next to its 16 P V MFMAs; q stays in registers as 16 VGPRs of codes.
 // MFMA-bound: 4*Sq*Skv*Hq*D flops per launch, half on the fp8 and half on the bf16 unit.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -44,6 +48,8 @@ constexpr int BUF_FLAGS = 0x00020000;
 struct Args {
   const uint8_t* q8; const uint8_t* k8; const uint16_t* v; uint16_t* o;
   const int8_t* q_exp; const int8_t* k_exp; const int8_t* pk_exp;
+  const uint8_t* q_sc; const uint8_t* k_sc;     // BLOCK: E8M0 codes [.., heads, 4] per row
+  const uint8_t* pk_sc[NXATTN_MAX_BRANCHES];
   int64_t vs0, vs1, vs2, os0, os1, os2;
   const uint8_t* pk8[NXATTN_MAX_BRANCHES];
   const uint16_t* pv[NXATTN_MAX_BRANCHES];
@@ -70,9 +76,14 @@ __device__ __forceinline__ void barrier_only() {
 // not the matrix core, sets the pace, and same-box runs were 1.7 % faster at the 1K DiT
 // shape (0.2 % slower at 2K) without them. The iteration's one barrier is the one after
 // the tile loads land (the second slot reads only buffers no load of the iteration writes).
+// The wait is the builtin (every counter to zero), not inline asm: the compiler's own wait
+// insertion sees it and knows that the tile loads and the block-scale loads issued before
+// it have landed, so it adds no waits for them after the barrier (behind an asm wait it
+// assumed them outstanding and waited on the next iteration's fresh scale loads).
 __device__ __forceinline__ void wait_dma_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -85,6 +96,10 @@ __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[VTILEB];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[VTILEB];
 template <int PAR> __device__ __forceinline__ uint8_t* kbuf() { return PAR ? lds_k1 : lds_k0; }
 template <int PAR> __device__ __forceinline__ uint8_t* vbuf() { return PAR ? lds_v1 : lds_v0; }
+// BLOCK: the four run scales (E8M0 codes) of each key row of a K tile, beside the tile
+__shared__ __attribute__((aligned(256))) uint8_t lds_s0[BN * 4];
+__shared__ __attribute__((aligned(256))) uint8_t lds_s1[BN * 4];
+template <int PAR> __device__ __forceinline__ uint8_t* sbuf() { return PAR ? lds_s1 : lds_s0; }
 
 // Steady-state tile loads of one wave (rows 16ws .. 16ws+15 of a tile): K in 2
 // instructions of 8 rows (lane -> row rl8 = lane/8, slot lane%8), V in 4 of 4 rows
@@ -98,7 +113,7 @@ struct DmaPlan {
 };
 
 struct Wave {
-  v8i q8[2];          // Q^T operand, k-step ks: codes Q[row][64ks + 32hh .. +31]
+  v8i q8[2];          // Q^T operand, k-step ks: codes Q[row][64ks + 16hh + 32e .. +15], e = 0, 1
   f32x16 o[4];        // O^T accumulators, d-block db
   f32x16 s[2];        // S^T accumulators of the tile being scored (2 key blocks of 32)
   bf16x8 p[4];        // P^T operand of the tile being accumulated
@@ -107,10 +122,17 @@ struct Wave {
   float thr;          // FOLD: row max of the shifted scores above which m moves (-inf before
                       // the first tile); else (m + RESCALE_T) / c on raw scores
   f32x16 negm;        // FOLD: -m in every register, the score accumulators' start value
-  int kbase, kxh;     // K fragment (kb, ks, half e): kbase + kb*32*KROWB + ((64ks + 16e) ^ kxh)
+  int kbase, kxh;     // K fragment (kb, ks, half e): kbase + kb*32*KROWB + ((64ks + 32e) ^ kxh)
   int vbase, vy;      // V^T fragment of d-block db at vbase + (64db ^ vy)
-  int qsc;            // E8M0 scale of the wave's q head (B operand)
+  int qsc;            // E8M0 scale of the B operand: the q head's, or (BLOCK) the row's run
+                      // scales shifted so that k-step ks finds its own in byte 2ks
 };
+
+// Byte of the scale operands that k-step ks uses: per slice the value itself (byte 0);
+// with BLOCK byte 2ks of a row's four run scales shifted right by 8 * (lane half), i.e.
+// run 2ks + half, the run whose codes the lane's scale covers in that step
+template <bool BLOCK, int KS>
+constexpr int scale_byte() { return BLOCK ? 2 * KS : 0; }
 
 __device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* smem, int byte) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((const lds_u8*)smem + byte);
@@ -121,12 +143,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* smem, int byte) {
 __device__ __forceinline__ v8i kfrag(const uint8_t* ksm, const Wave& w, int kb, int ks) {
   const int base = w.kbase + kb * 32 * KROWB;
   const u32x4 a = lds_read_b128(ksm, base + ((64 * ks) ^ w.kxh));
-  const u32x4 b = lds_read_b128(ksm, base + ((64 * ks + 16) ^ w.kxh));
+  const u32x4 b = lds_read_b128(ksm, base + ((64 * ks + 32) ^ w.kxh));
   return __builtin_bit_cast(v8i, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+// formats 0 / 0: E4M3 for both operands; the E8M0 scales are byte SEL of ksc / qsc (op_sel
+// picks the byte: measured)
+template <int SEL>
 __device__ __forceinline__ f32x16 mfma_s(v8i k, v8i q, f32x16 acc, int ksc, int qsc) {
-  // formats 0 / 0: E4M3 for both operands; E8M0 scales from the low byte of ksc / qsc
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k, q, acc, 0, 0, 0, ksc, 0, qsc);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k, q, acc, 0, 0, SEL, ksc, SEL, qsc);
 }
 
 // One GEMM phase: O^T += V_t^T P_t^T (16 bf16 MFMAs), then S^T = K_{t+1} Q^T (4 fp8
@@ -152,7 +176,7 @@ __device__ __forceinline__ void sched8_steps() {
   }
 }
 
-template <int VPAR, int KPAR, bool FOLD, bool DMA = false>
+template <int VPAR, int KPAR, bool FOLD, bool BLOCK, bool DMA = false>
 __device__ __forceinline__ void gemm_phase(Wave& w, int ksc0, int ksc1, const DmaPlan* plan = nullptr) {
   const uint8_t* vsm = vbuf<VPAR>();
   const uint8_t* ksm = kbuf<KPAR>();
@@ -198,7 +222,10 @@ __device__ __forceinline__ void gemm_phase(Wave& w, int ksc0, int ksc1, const Dm
       w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (DIST + 1)], w.p[kbhs], w.o[db], 0, 0, 0);
     } else {
       const int j = i - 16, ks = j >> 1, kb = j & 1;
-      w.s[kb] = mfma_s(kf[j], w.q8[ks], ks == 0 ? (FOLD ? w.negm : f32x16{}) : w.s[kb], kb ? ksc1 : ksc0, w.qsc);
+      if (ks == 0)
+        w.s[kb] = mfma_s<scale_byte<BLOCK, 0>()>(kf[j], w.q8[0], FOLD ? w.negm : f32x16{}, kb ? ksc1 : ksc0, w.qsc);
+      else
+        w.s[kb] = mfma_s<scale_byte<BLOCK, 1>()>(kf[j], w.q8[1], w.s[kb], kb ? ksc1 : ksc0, w.qsc);
     }
   }
   sched8_reads<0, DIST>();
@@ -206,15 +233,16 @@ __device__ __forceinline__ void gemm_phase(Wave& w, int ksc0, int ksc1, const Dm
 }
 
 // S^T only (prologue).
-template <int KPAR, bool FOLD>
+template <int KPAR, bool FOLD, bool BLOCK>
 __device__ __forceinline__ void gemm_s_only(Wave& w, int ksc0, int ksc1) {
   const uint8_t* ksm = kbuf<KPAR>();
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int kb = 0; kb < 2; ++kb)
+    w.s[kb] = mfma_s<scale_byte<BLOCK, 0>()>(kfrag(ksm, w, kb, 0), w.q8[0], FOLD ? w.negm : f32x16{},
+                                             kb ? ksc1 : ksc0, w.qsc);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      w.s[kb] = mfma_s(kfrag(ksm, w, kb, ks), w.q8[ks], ks == 0 ? (FOLD ? w.negm : f32x16{}) : w.s[kb],
-                       kb ? ksc1 : ksc0, w.qsc);
+  for (int kb = 0; kb < 2; ++kb)
+    w.s[kb] = mfma_s<scale_byte<BLOCK, 1>()>(kfrag(ksm, w, kb, 1), w.q8[1], w.s[kb], kb ? ksc1 : ksc0, w.qsc);
 }
 
 // Row max of the tile; rows whose max exceeds their threshold move m (rescaling l, O).
@@ -249,6 +277,9 @@ __device__ __forceinline__ void max_update(Wave& w, float c) {
         w.s[1][i] -= d;
       }
       w.thr = RESCALE_T;
+      // the score accumulators' start block follows m; kept between rescales
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.negm[i] = -w.m;
     }
   } else {
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -321,15 +352,13 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
       if (pass == 1 || !__builtin_amdgcn_ballot_w64(!(lt <= RESCALE_LIM))) break;
     }
     w.l += lt;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w.negm[i] = -w.m;
   } else {
     max_update<FOLD>(w, c);
     w.l += weights<FOLD>(w, c);
   }
 }
 
-template <bool GROUP_A, bool FOLD>
+template <bool GROUP_A, bool FOLD, bool BLOCK>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
@@ -344,21 +373,26 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   const int Skv = P + a.seq;
   const int T = (Skv + BN - 1) / BN;
   const float c = a.c;
-  // E8M0 scales: key rows of the prefix / own keys, and this wave's q head
-  const int sc_own = 127 + (int)a.k_exp[b * a.heads_kv + g];
-  const int sc_pre = P > 0 ? 127 + (int)a.pk_exp[b * a.heads_kv + g] : sc_own;
+  // E8M0 scales, per slice: key rows of the prefix / own keys, and this wave's q head
+  const int sc_own = BLOCK ? 0 : 127 + (int)a.k_exp[b * a.heads_kv + g];
+  const int sc_pre = BLOCK ? 0 : (P > 0 ? 127 + (int)a.pk_exp[b * a.heads_kv + g] : sc_own);
 
   Wave w;
   {
     const uint8_t* qrow = a.q8 + (((int64_t)b * a.seq + tokc) * a.heads_q + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * hh);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * hh + 16);
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 16 * hh);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 16 * hh + 32);
       w.q8[ks] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
-  w.qsc = 127 + (int)a.q_exp[b * a.heads_q + hq];
+  if constexpr (BLOCK) {
+    const uint32_t qs = *reinterpret_cast<const uint32_t*>(a.q_sc + (((int64_t)b * a.seq + tokc) * a.heads_q + hq) * 4);
+    w.qsc = (int)(qs >> (8 * hh));
+  } else {
+    w.qsc = 127 + (int)a.q_exp[b * a.heads_q + hq];
+  }
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
   // FOLD: m starts at 0 (the accumulators start at -m = 0) and the first tile always
@@ -370,9 +404,13 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
 #pragma unroll
   for (int i = 0; i < 16; ++i) w.negm[i] = 0.f;
   // K fragment of key block kb, k-step ks, half e: row kb*32 + n, 16-byte chunk
-  // 4ks + 2hh + e at slot chunk ^ (n & 7): byte n*KROWB + ((64ks + 16e) ^ (32hh ^ 16(n&7)))
+  // 4ks + 2e + hh at slot chunk ^ (n & 7): byte n*KROWB + ((64ks + 32e) ^ (16hh ^ 16(n&7))).
+  // The matrix core scales bytes 0-15 of lanes r and r + 32 (one 32-wide k block) by lane
+  // r's scale and bytes 16-31 of both by lane r + 32's (measured), so half e of k-step ks
+  // holds 16 codes of run 2ks + e: lane half hh its elements 16hh .. 16hh + 15, and the
+  // lane's scale is that of run 2ks + hh. q's fragments are placed the same way.
   w.kbase = n * KROWB;
-  w.kxh = (32 * hh) ^ (16 * (n & 7));
+  w.kxh = (16 * hh) ^ (16 * (n & 7));
   {
     const int q = lane >> 4, j = lane & 15;
     const int rsub = j >> 2, csub = 4 * (j & 3);
@@ -430,8 +468,54 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   auto valid_at = [&](int pos) { const int r = Skv - tile_at(pos) * BN; return r < BN ? r : BN; };
   const bool last_whole = T * BN <= Skv && ((T - 1) * BN >= P || T * BN <= P);
   const int nwhole = T - (sb >= 0 ? 1 : 0) - (last_whole ? 0 : 1);
-  // E8M0 scale of this lane's key row in key block kb of tile t
+  // E8M0 scale of this lane's key row in key block kb of tile t (per slice)
   auto ksc = [&](int t, int kb) { return t * BN + kb * 32 + n < P ? sc_pre : sc_own; };
+  // BLOCK: the four run scales of the 64 key rows of a tile travel into LDS with the K
+  // tile (sbuf<p> beside kbuf<p>): one 4-byte direct-to-LDS load per lane (lane = row)
+  // from wave 0, instead of every wave gathering its rows from memory (which cost 9 % at
+  // the 1K DiT shape). A whole tile lies inside the prefix or inside the own keys, so its
+  // rows are one buffer (uniform), a uniform row offset and the lane's row; the
+  // straddling and the ragged tile take per-lane addresses (rows past the keys read the
+  // last key's: their scores are masked).
+  const uint8_t* ksc_pre = BLOCK && P > 0 ? a.pk_sc[b] + (int64_t)g * 4 : nullptr;
+  const uint8_t* ksc_own = BLOCK ? a.k_sc + ((int64_t)b * a.seq * a.heads_kv + g) * 4 : nullptr;
+  const uint32_t ksc_row = (uint32_t)a.heads_kv * 4;               // bytes between key rows
+  const uint32_t ksc_lane = (uint32_t)lane * ksc_row;
+  const __amdgpu_buffer_rsrc_t ksr_own =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ksc_own), 0, BUF_RECORDS, BUF_FLAGS);
+  const __amdgpu_buffer_rsrc_t ksr_pre =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(P > 0 ? ksc_pre : ksc_own), 0, BUF_RECORDS, BUF_FLAGS);
+  // the scales of the tile at position pos into dst (wave 0 only; WHOLE: pos < nwhole)
+  auto dma_s = [&](int pos, uint8_t* dst, auto whole) {
+    if constexpr (BLOCK) {
+      if (wave != 0) return;
+      const int t = tile_at(pos);
+      if (decltype(whole)::value || pos < nwhole) {
+        const int j0 = t * BN;
+        const bool pre = j0 < P;
+        const uint32_t soff = (uint32_t)(pre ? j0 : j0 - P) * ksc_row;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pre ? ksr_pre : ksr_own,
+                                                 (__attribute__((address_space(3))) void*)(lds_u8*)dst, 4, ksc_lane,
+                                                 soff, 0, 0);
+      } else {
+        int j = t * BN + lane;
+        j = j < Skv ? j : Skv - 1;
+        const uint8_t* src = j < P ? ksc_pre + (int64_t)j * ksc_row : ksc_own + (int64_t)(j - P) * ksc_row;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_u8*)dst, 4, 0, 0);
+      }
+    }
+  };
+  // scale operands of key block kb for the tile in sbuf<PAR> (BLOCK: this lane's row's
+  // four run scales, shifted right by 8 * (lane half)) or of tile t (per slice)
+  auto kop = [&](auto par, int t, int kb) -> int {
+    if constexpr (BLOCK) {
+      const uint32_t v = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+          (const lds_u8*)sbuf<decltype(par)::value>() + (32 * kb + n) * 4);
+      return (int)(v >> (8 * hh));
+    } else {
+      return ksc(t, kb);
+    }
+  };
 
   const int rl8 = lane >> 3, rl4 = lane >> 4;
   const uint32_t koff = (uint32_t)(rl8 * krow) + 16u * (uint32_t)((lane & 7) ^ rl8);
@@ -453,12 +537,19 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     return pl;
   };
 
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using Whole = std::true_type;
+  using AnyTile = std::false_type;
+
   // ---- prologue (as in the bf16 kernel)
+  dma_s(0, sbuf<0>(), AnyTile{});
+  if (T > 1) dma_s(1, sbuf<1>(), AnyTile{});
   dma_k(tile_at(0), kbuf<0>(), wave, All{});
   dma_v(tile_at(0), vbuf<0>(), wave, All{});
   if (T > 1) dma_k(tile_at(1), kbuf<1>(), wave, All{});
   wait_dma_barrier();
-  gemm_s_only<0, FOLD>(w, ksc(tile_at(0), 0), ksc(tile_at(0), 1));
+  gemm_s_only<0, FOLD, BLOCK>(w, kop(P0{}, tile_at(0), 0), kop(P0{}, tile_at(0), 1));
   if (GROUP_A) softmax<true, FOLD>(w, c, valid_at(0), hh);
   barrier_only();
 
@@ -467,11 +558,16 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     constexpr bool FAST = decltype(fast)::value;
     asm volatile("" : "+v"(w.kbase), "+v"(w.kxh), "+v"(w.vbase), "+v"(w.vy));
     const int ts = t + 1 < T ? tile_at(t + 1) : 0;
+    // tile t+1 (scored now) sits in kbuf / sbuf PAR ^ 1; tile t+2 goes to PAR
+    using KP = std::integral_constant<int, PAR ^ 1>;
+    const int s0 = kop(KP{}, ts, 0), s1 = kop(KP{}, ts, 1);
     if constexpr (FAST) {
+      dma_s(t + 2, sbuf<PAR>(), Whole{});
       const DmaPlan pl = plan_of(t);
-      gemm_phase<PAR, PAR ^ 1, FOLD, true>(w, ksc(ts, 0), ksc(ts, 1), &pl);
+      gemm_phase<PAR, PAR ^ 1, FOLD, BLOCK, true>(w, s0, s1, &pl);
     } else {
-      gemm_phase<PAR, PAR ^ 1, FOLD>(w, ksc(ts, 0), ksc(ts, 1));
+      if (t + 2 < T) dma_s(t + 2, sbuf<PAR>(), AnyTile{});
+      gemm_phase<PAR, PAR ^ 1, FOLD, BLOCK>(w, s0, s1);
       if (t + 2 < T) dma_k(tile_at(t + 2), kbuf<PAR>(), wave, Half{});
       if (t + 1 < T) dma_v(tile_at(t + 1), vbuf<PAR ^ 1>(), wave, Half{});
     }
@@ -485,11 +581,10 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     softmax<decltype(mask)::value, FOLD>(w, c, valid_at(t), hh);
     __builtin_amdgcn_sched_barrier(0);
     const int ts = t + 1 < T ? tile_at(t + 1) : 0;
-    gemm_phase<PAR, PAR ^ 1, FOLD>(w, ksc(ts, 0), ksc(ts, 1));
+    using KP = std::integral_constant<int, PAR ^ 1>;
+    gemm_phase<PAR, PAR ^ 1, FOLD, BLOCK>(w, kop(KP{}, ts, 0), kop(KP{}, ts, 1));
     wait_dma_barrier();
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
   using Fast = std::true_type;
   using Slow = std::false_type;
   using Mask = std::true_type;
@@ -537,12 +632,12 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
 }
 
-template <bool FOLD>
+template <bool FOLD, bool BLOCK>
 __global__ __launch_bounds__(THREADS) void fwd_fp8_kernel(Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true, FOLD>(a, lane, wave);
-  else wave_program<false, FOLD>(a, lane, wave);
+  if (wave < 4) wave_program<true, FOLD, BLOCK>(a, lane, wave);
+  else wave_program<false, FOLD, BLOCK>(a, lane, wave);
 }
 
 }  // namespace fp8k
@@ -563,19 +658,41 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   if (p->heads_q % p->heads_kv != 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: heads_q %% heads_kv != 0");
   if (p->heads_q > 4096) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: heads_q > 4096");
   if (!(p->scale == p->scale) || std::isinf(p->scale)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: scale is not finite");
+  // block scales (q_scales set: k_scales and each prefix's scales, no exponents) or one
+  // exponent per slice (no scales)
+  const bool block = p->q_scales != nullptr;
+  if (block && (p->q_exp || p->k_exp || p->prefix_k_exp))
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: block scales (q_scales) exclude q_exp, k_exp and prefix_k_exp");
+  if (!block && p->k_scales) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: k_scales given without q_scales");
   bool any_prefix = false;
   for (int b = 0; b < p->batch; ++b) {
     if (p->prefix_len[b] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: prefix_len[%d] < 0", b);
     const bool has = p->prefix_len[b] > 0;
     if (has != (p->prefix_k8[b] != nullptr) || has != (p->prefix_v[b] != nullptr))
       return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: prefix_k8[%d] / prefix_v[%d] must be non-NULL iff prefix_len > 0", b, b);
+    if ((block && has) != (p->prefix_k_scales[b] != nullptr))
+      return fail(NXATTN_ERR_INVALID,
+                  "nxattn_fwd_fp8: prefix_k_scales[%d] must be non-NULL iff block scales and prefix_len > 0", b);
     if ((int64_t)p->prefix_len[b] + p->seq_q > INT32_MAX)
       return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: prefix_len[%d] + seq_q overflows int32", b);
     any_prefix |= has;
   }
   if (p->batch == 0 || p->seq_q == 0) return NXATTN_OK;
-  if (!p->q8 || !p->k8 || !p->v || !p->o || !p->q_exp || !p->k_exp || (any_prefix && !p->prefix_k_exp))
+  if (!p->q8 || !p->k8 || !p->v || !p->o)
     return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: NULL pointer");
+  if (block ? !p->k_scales : (!p->q_exp || !p->k_exp || (any_prefix && !p->prefix_k_exp)))
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: NULL pointer (exponents or scales)");
+  if (block) {
+    // the key-scale rows of a whole tile are read with 32-bit buffer offsets
+    int64_t rows = p->seq_q;
+    for (int b = 0; b < p->batch; ++b) rows = std::max<int64_t>(rows, p->prefix_len[b]);
+    if (rows * p->heads_kv * 4 > INT32_MAX)
+      return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: block scales of one branch exceed 2 GiB");
+    auto al4 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; };
+    bool ok = al4(p->q_scales) && al4(p->k_scales);
+    for (int b = 0; b < p->batch; ++b) ok = ok && al4(p->prefix_k_scales[b]);
+    if (!ok) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: scales must be 4-byte aligned");
+  }
   for (int i = 0; i < 3; ++i) {
     if (p->v_strides[i] < 0 || p->o_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative stride");
     if ((p->v_strides[i] * 2) % 16 != 0 || (p->o_strides[i] * 2) % 16 != 0)
@@ -593,13 +710,15 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   const int64_t vb = ((B - 1) * p->v_strides[0] + (S - 1) * p->v_strides[1] + (Hkv - 1) * p->v_strides[2] + D) * 2;
   const int64_t lb = p->lse ? B * Hq * S * 4 : 0;
   struct Span { const void* ptr; int64_t n; };
-  Span ins[6 + 2 * NXATTN_MAX_BRANCHES] = {{p->q8, B * S * Hq * D}, {p->k8, B * S * Hkv * D}, {p->v, vb},
+  Span ins[8 + 3 * NXATTN_MAX_BRANCHES] = {{p->q8, B * S * Hq * D}, {p->k8, B * S * Hkv * D}, {p->v, vb},
                                            {p->q_exp, B * Hq}, {p->k_exp, B * Hkv},
-                                           {p->prefix_k_exp, any_prefix ? B * Hkv : 0}};
-  int nin = 6;
+                                           {p->prefix_k_exp, any_prefix ? B * Hkv : 0},
+                                           {p->q_scales, B * S * Hq * 4}, {p->k_scales, B * S * Hkv * 4}};
+  int nin = 8;
   for (int b = 0; b < p->batch; ++b) {
     ins[nin++] = Span{p->prefix_k8[b], (int64_t)p->prefix_len[b] * Hkv * D};
     ins[nin++] = Span{p->prefix_v[b], (int64_t)p->prefix_len[b] * Hkv * D * 2};
+    ins[nin++] = Span{p->prefix_k_scales[b], (int64_t)p->prefix_len[b] * Hkv * 4};
   }
   for (int i = 0; i < nin; ++i)
     if (ins[i].ptr && (overlaps(p->o, ob, ins[i].ptr, ins[i].n) || (p->lse && overlaps(p->lse, lb, ins[i].ptr, ins[i].n))))
@@ -609,6 +728,7 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   Args a;
   a.q8 = p->q8; a.k8 = p->k8; a.v = static_cast<const uint16_t*>(p->v); a.o = static_cast<uint16_t*>(p->o);
   a.q_exp = p->q_exp; a.k_exp = p->k_exp; a.pk_exp = p->prefix_k_exp ? p->prefix_k_exp : p->k_exp;
+  a.q_sc = p->q_scales; a.k_sc = p->k_scales;
   a.vs0 = p->v_strides[0]; a.vs1 = p->v_strides[1]; a.vs2 = p->v_strides[2];
   a.os0 = p->o_strides[0]; a.os1 = p->o_strides[1]; a.os2 = p->o_strides[2];
   for (int b = 0; b < NXATTN_MAX_BRANCHES; ++b) {
@@ -616,6 +736,7 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     a.pk8[b] = in ? p->prefix_k8[b] : nullptr;
     a.pv[b] = in ? static_cast<const uint16_t*>(p->prefix_v[b]) : nullptr;
     a.plen[b] = in ? p->prefix_len[b] : 0;
+    a.pk_sc[b] = in ? p->prefix_k_scales[b] : nullptr;
   }
   a.batch = p->batch; a.seq = p->seq_q; a.heads_q = p->heads_q; a.heads_kv = p->heads_kv;
   a.group = p->heads_q / p->heads_kv;
@@ -628,9 +749,16 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   const float scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)D);
   a.c = scale * LOG2E;
   a.lse = p->lse;
-  if (p->q_folded)
-    fwd_fp8_kernel<true><<<a.total_wg, THREADS, 0, stream>>>(a);
-  else
-    fwd_fp8_kernel<false><<<a.total_wg, THREADS, 0, stream>>>(a);
+  if (block) {
+    if (p->q_folded)
+      fwd_fp8_kernel<true, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+    else
+      fwd_fp8_kernel<false, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+  } else {
+    if (p->q_folded)
+      fwd_fp8_kernel<true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
+    else
+      fwd_fp8_kernel<false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
+  }
   return check_launch("nxattn_fwd_fp8");
 }

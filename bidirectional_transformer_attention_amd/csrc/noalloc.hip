@@ -57,6 +57,13 @@ extern "C" int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors
     if (tensors[t].heads < 0) return fail(NXATTN_ERR_INVALID, "%s: negative heads", who);
     total += tensors[t].heads;
   }
+  // block scaling keeps no running maxima: the scratch is not used (rope_quantize checks
+  // that every tensor with heads has the same kind of scale)
+  bool blocks = false;
+  for (int t = 0; t < n_tensors; ++t)
+    if (tensors[t].heads > 0) { blocks = tensors[t].scales != nullptr; break; }
+  if (blocks)
+    return rope_quantize(who, tensors, n_tensors, dtype, batch, seq, head_dim, rope, nullptr, 0, stream);
   if (batch * total > NOALLOC_SLICES)
     return fail(NXATTN_ERR_UNSUPPORTED,
                 "%s: batch * total heads = %lld exceeds the %lld (branch, head) slices of the static scratch; "

@@ -70,32 +70,38 @@ __device__ __forceinline__ int fp8_exponent(float amax) {
   const int e = E - 9 + (m > 0.875f ? 1 : 0);
   return e < -127 ? -127 : e;
 }
+// 2^-e exactly, for e in [-127, 126]
+__device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 
 // The tensors of one RoPE launch: they share batch, seq, head_dim, dtype and positions, and
 // their heads are laid end to end (tensor t owns heads hoff[t] .. hoff[t+1]-1 of the
 // launch; hoff[t] = total heads for t >= n). Rotation in place uses x[0] only; the fp8
 // passes read every x and write codes[t] (contiguous [batch, seq, heads_t, head_dim]) and
-// exps[t] ([batch, heads_t]), with the running maxima in amax (AMAX_SLOTS copies of
-// [batch * total heads], copy stride astride).
+// either exps[t] ([batch, heads_t]), with the running maxima in amax (AMAX_SLOTS copies of
+// [batch * total heads], copy stride astride), or, with blocks set, scales[t] (E8M0
+// codes, contiguous [batch, seq, heads_t, head_dim / 32]) in a single pass.
 constexpr int ROPE_MAX_TENSORS = NXATTN_MAX_FP8_TENSORS;
 struct RopeTensors {
   void* x[ROPE_MAX_TENSORS];
   int64_t sb[ROPE_MAX_TENSORS], ss[ROPE_MAX_TENSORS], sh[ROPE_MAX_TENSORS];
   uint8_t* codes[ROPE_MAX_TENSORS];
   int8_t* exps[ROPE_MAX_TENSORS];
+  uint8_t* scales[ROPE_MAX_TENSORS];
   float mult[ROPE_MAX_TENSORS];   // fp8 passes: multiplier of the stored rotated values (1: none)
   int32_t hoff[ROPE_MAX_TENSORS + 1];
   int32_t n;
   uint32_t* amax;
   int64_t astride;
+  int32_t blocks;                 // fp8: one scale per 32-element run (head_dim % 64 == 0)
 };
-enum class RopeMode { Rotate, Max, Codes };
+enum class RopeMode { Rotate, Max, Codes, Blocks };
 
 // Validates the RoPE arguments (errors name `who`; rope and the x pointers and strides of
 // every tensor) and launches: with fp8 == false, the in-place rotation of x[0]; with
 // fp8 == true (total heads <= 4096), the clear of the maxima, the pass that takes them
-// from the rotated values and the pass that writes exponents and codes. The caller checks
-// codes, exps and amax.
+// from the rotated values and the pass that writes exponents and codes, or with
+// tt.blocks the one pass that writes codes and block scales. The caller checks codes,
+// exps, scales and amax.
 int rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64_t seq, int64_t head_dim, int dtype,
                 const nxattn_rope_desc* rope, bool fp8, hipStream_t stream);
 

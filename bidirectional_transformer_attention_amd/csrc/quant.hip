@@ -1,5 +1,5 @@
 // FP8 (OCP E4M3) quantization of q or k for the fp8 score GEMM: one power-of-two scale
-// per (branch, head). The pages name fp8 DiT variants (NeoPP page, "Run the replay
+// per (branch, head), or (nxattn_quantize_fp8_blocks) one per run of 32 elements of a row. The pages name fp8 DiT variants (NeoPP page, "Run the replay
 // examples") without a recipe; this one keeps every step exact except the final rounding:
 // e = smallest integer with max|x| <= 448 * 2^e over the (branch, head) slice, then each
 // element x * 2^-e (an exact power-of-two scaling) is rounded to the nearest E4M3 value,
@@ -210,6 +210,44 @@ __global__ __launch_bounds__(THREADS) void quant_kernel(Args a) {
   }
 }
 
+// Block scaling: one thread per run of 32 consecutive elements of a row (branch, token,
+// head): the run's maximum gives its exponent e (the per-slice rule applied to the run),
+// then its 32 codes of x * 2^-e and its E8M0 scale e + 127. Rows are read in order, the
+// codes (and scales) written contiguously.
+struct BlockArgs {
+  const void* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t sb, ss, sh;            // input strides (elements)
+  int64_t runs;                  // batch * seq * heads * runs per row
+  int32_t seq, heads, rpr;       // rpr: runs per row, head_dim / 32
+};
+
+template <typename T>
+__global__ __launch_bounds__(THREADS) void block_kernel(BlockArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+  if (i >= a.runs) return;
+  const int64_t r = i / a.rpr;
+  const int k = (int)(i - r * a.rpr);
+  const int64_t bs = r / a.heads, h = r - bs * a.heads;
+  const int64_t b = bs / a.seq, s = bs - b * a.seq;
+  const T* src = static_cast<const T*>(a.x) + b * a.sb + s * a.ss + h * a.sh + 32 * k;
+  float v[4][8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) load8<T>(src + 8 * g, v[g]);
+  float m = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[g][e]));
+  const int e = fp8_exponent(m);
+  const float inv = exp2_neg(e);
+  u32x2* out = reinterpret_cast<u32x2*>(a.codes + i * 32);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) out[g] = codes8(v[g], inv);
+  a.scales[i] = (uint8_t)(e + 127);
+}
+
 }  // namespace quantk
 
 void launch_fp8_exponents(const uint32_t* amax, int8_t* exps, int64_t n, hipStream_t stream) {
@@ -317,6 +355,47 @@ extern "C" int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int6
   return check_launch("nxattn_quantize_fp8");
 }
 
+extern "C" int nxattn_quantize_fp8_blocks(const void* x, int dtype, int64_t batch, int64_t seq, int64_t heads,
+                                          int64_t head_dim, const int64_t strides[3], uint8_t* codes,
+                                          uint8_t* scales, hipStream_t stream) {
+  using namespace quantk;
+  static const char* who = "nxattn_quantize_fp8_blocks";
+  clear_error();
+  if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
+  if (batch < 0 || seq < 0 || heads < 0 || head_dim < 0 || !strides) return fail(NXATTN_ERR_INVALID, "%s: bad sizes", who);
+  if (head_dim % 32 != 0 || head_dim > 1024)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 32 up to 1024", who);
+  if (seq > INT32_MAX / 2 || heads > INT32_MAX / 2 || batch > INT32_MAX / 2)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: size out of range", who);
+  if (batch == 0 || seq == 0 || heads == 0 || head_dim == 0) return NXATTN_OK;
+  if (!x || !codes || !scales) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
+  const int64_t es = esize(dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+    if ((strides[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
+  }
+  if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "%s: x is not 16-byte aligned", who);
+  if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
+  const int64_t runs = batch * seq * heads * (head_dim / 32);
+  const int64_t grid = (runs + THREADS - 1) / THREADS;
+  if (grid > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: problem too large", who);
+  const int64_t xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
+  const int64_t cb = batch * seq * heads * head_dim;
+  if (overlaps(x, xb, codes, cb) || overlaps(x, xb, scales, runs) || overlaps(codes, cb, scales, runs))
+    return fail(NXATTN_ERR_INVALID, "%s: x, codes and scales must not overlap", who);
+  BlockArgs a;
+  a.x = x; a.codes = codes; a.scales = scales;
+  a.sb = strides[0]; a.ss = strides[1]; a.sh = strides[2];
+  a.runs = runs;
+  a.seq = (int32_t)seq; a.heads = (int32_t)heads; a.rpr = (int32_t)(head_dim / 32);
+  if (dtype == NXATTN_BF16)
+    block_kernel<uint16_t><<<(unsigned)grid, THREADS, 0, stream>>>(a);
+  else
+    block_kernel<float><<<(unsigned)grid, THREADS, 0, stream>>>(a);
+  return check_launch(who);
+}
+
 namespace nx {
 
 // Validation and launches of nxattn_rope_quantize_fp8 with the running maxima in
@@ -335,12 +414,26 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
     total += tensors[t].heads;
     if (total > quantk::MAX_HEADS) return fail(NXATTN_ERR_UNSUPPORTED, "%s: more than %d heads in total", who, quantk::MAX_HEADS);
   }
+  // block scales (every tensor with heads has scales, none exps) or one exponent per
+  // slice (every one exps, none scales)
+  bool blocks = false;
+  for (int t = 0; t < n_tensors; ++t)
+    if (tensors[t].heads > 0) { blocks = tensors[t].scales != nullptr; break; }
+  for (int t = 0; t < n_tensors; ++t)
+    if (tensors[t].heads > 0 && ((tensors[t].scales != nullptr) != blocks || (tensors[t].exps != nullptr) == blocks))
+      return fail(NXATTN_ERR_INVALID, "%s: every tensor needs scales (block scaling) or every tensor exps, not both",
+                  who);
+  if (blocks && head_dim % 64 != 0)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: block scales need head_dim a multiple of 64", who);
   if (batch == 0 || seq == 0 || total == 0) return NXATTN_OK;
-  if (!workspace) return fail(NXATTN_ERR_INVALID, "%s: NULL workspace", who);
-  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(NXATTN_ERR_ALIGN, "%s: workspace not 4-byte aligned", who);
-  const int64_t need = amax_words(batch * total) * 4;
-  if (workspace_bytes < need)
-    return fail(NXATTN_ERR_INVALID, "%s: workspace_bytes %lld < %lld", who, (long long)workspace_bytes, (long long)need);
+  // the running maxima of the per-slice exponents; block scaling needs none
+  const int64_t need = blocks ? 0 : amax_words(batch * total) * 4;
+  if (!blocks) {
+    if (!workspace) return fail(NXATTN_ERR_INVALID, "%s: NULL workspace", who);
+    if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(NXATTN_ERR_ALIGN, "%s: workspace not 4-byte aligned", who);
+    if (workspace_bytes < need)
+      return fail(NXATTN_ERR_INVALID, "%s: workspace_bytes %lld < %lld", who, (long long)workspace_bytes, (long long)need);
+  }
   // the tensors with heads, heads laid end to end
   const int64_t es = esize(dtype);
   RopeTensors tt;
@@ -348,11 +441,11 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
   struct Span { const void* p; int64_t n; };
   Span xs[NXATTN_MAX_FP8_TENSORS], outs[2 * NXATTN_MAX_FP8_TENSORS + 1];
   int nout = 0;
-  outs[nout++] = {workspace, need};
+  if (!blocks) outs[nout++] = {workspace, need};
   for (int t = 0; t < n_tensors; ++t) {
     const nxattn_fp8_tensor& z = tensors[t];
     if (z.heads == 0) continue;
-    if (!z.x || !z.codes || !z.exps) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer in tensor %d", who, t);
+    if (!z.x || !z.codes) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer in tensor %d", who, t);
     if (reinterpret_cast<uintptr_t>(z.codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
     for (int i = 0; i < 3; ++i)
       if (z.strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
@@ -374,11 +467,16 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
     tt.sb[k] = z.strides[0]; tt.ss[k] = z.strides[1]; tt.sh[k] = z.strides[2];
     tt.codes[k] = z.codes;
     tt.exps[k] = z.exps;
+    tt.scales[k] = z.scales;
     tt.hoff[k + 1] = tt.hoff[k] + (int32_t)z.heads;
     xs[k] = {z.x, ((batch - 1) * z.strides[0] + (seq - 1) * z.strides[1] + (z.heads - 1) * z.strides[2] + head_dim) * es};
     outs[nout++] = {z.codes, batch * seq * z.heads * head_dim};
-    outs[nout++] = {z.exps, batch * z.heads};
+    if (blocks)
+      outs[nout++] = {z.scales, batch * seq * z.heads * (head_dim / 32)};
+    else
+      outs[nout++] = {z.exps, batch * z.heads};
   }
+  tt.blocks = blocks ? 1 : 0;
   for (int i = tt.n + 1; i <= ROPE_MAX_TENSORS; ++i) tt.hoff[i] = tt.hoff[tt.n];
   // outputs must not overlap one another, an input or the workspace; inputs may overlap
   // one another but not the workspace
@@ -390,7 +488,7 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
       if (overlaps(outs[i].p, outs[i].n, xs[k].p, xs[k].n))
         return fail(NXATTN_ERR_INVALID, "%s: an output or the workspace overlaps an input", who);
   }
-  tt.amax = static_cast<uint32_t*>(workspace);
+  tt.amax = blocks ? nullptr : static_cast<uint32_t*>(workspace);
   tt.astride = amax_stride(batch * total);
   // validates the RoPE arguments and the inputs (head_dim 8..256 among them) before the
   // first launch

@@ -84,14 +84,17 @@ __device__ __forceinline__ V pick(const V (&a)[ROPE_MAX_TENSORS], int t) {
 // into copy blockIdx % AMAX_SLOTS of tt.amax (cleared beforehand). MODE Codes: x is read
 // only; each workgroup first turns the copies of its branch's maxima into the exponents e
 // (the branch's first workgroup also stores them), then writes the E4M3 codes of the
-// rotated, rounded values times 2^-e.
+// rotated, rounded values times 2^-e. MODE Blocks: x is read only; each run of 32
+// elements of a row takes its exponent from its own maximum, reduced over the lanes that
+// hold the run, and the codes and the run's E8M0 scale are written in the same pass.
 template <typename T, RopeMode MODE>
 __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, int32_t heads, int32_t D,
                                                    RopeArgs args) {
   constexpr bool FP8 = MODE != RopeMode::Rotate;
+  constexpr bool SLICE = MODE == RopeMode::Max || MODE == RopeMode::Codes;
   __shared__ float cs[ROPE_TOK][ROPE_MAX_HALF];
   __shared__ float sn[ROPE_TOK][ROPE_MAX_HALF];
-  __shared__ uint32_t hw[FP8 ? ROPE_MAX_HEADS : 1];   // Max: running maxima; Codes: bits of 2^-e
+  __shared__ uint32_t hw[SLICE ? ROPE_MAX_HEADS : 1];   // Max: running maxima; Codes: bits of 2^-e
   const int half = D / 2;
   const int blocks_per_branch = (seq + ROPE_TOK - 1) / ROPE_TOK;
   const int b = (int)blockIdx.x / blocks_per_branch;
@@ -157,7 +160,11 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
   // with (token, head) advanced without divisions, issuing the loads of ROPE_UNROLL rows
   // before it uses them (lanes past the end load row 0 and drop it). The trip count is the
   // same for every thread, so with a power-of-two row width (<= 32 lanes, inside one
-  // wave) the lanes of a row combine their maxima with swaps.
+  // wave) the lanes of a row combine their maxima with swaps. In MODE Blocks a 32-element
+  // run is held by 8 aligned lanes (half-split pairs: the lo groups of quads 8i .. 8i+7
+  // form run i, their hi groups run i + half/32) or by 4 (adjacent pairs: quad q holds
+  // elements 8q .. 8q+7 of run q/4); head_dim % 64 == 0 keeps runs inside rows and the
+  // lane groups aligned, and all lanes of a group share one `in`.
   const int quads = half / 4;
   const bool pow2 = (quads & (quads - 1)) == 0;
   const int rstep = 256 / quads;
@@ -174,6 +181,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
     T* const xt = static_cast<T*>(tt.x[t]) + b * tt.sb[t] + (int64_t)s0 * tt.ss[t];
     const int64_t sst = tt.ss[t], sht = tt.sh[t];
     uint8_t* const ct = FP8 ? tt.codes[t] + ((int64_t)b * seq + s0) * ht * D : nullptr;
+    uint8_t* const st = MODE == RopeMode::Blocks ? tt.scales[t] + ((int64_t)b * seq + s0) * ht * (D / 32) : nullptr;
     const float mu = FP8 ? tt.mult[t] : 1.f;
     const int rows = ntok * ht;
     const int hstep = rstep % ht, tstep = rstep / ht;
@@ -249,6 +257,42 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
             if (in[u]) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(wl[e]), __builtin_fabsf(wh[e])));
+            }
+          } else if constexpr (MODE == RopeMode::Blocks) {
+            float ml = 0.f, mh = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ml = __builtin_fmaxf(ml, __builtin_fabsf(wl[e]));
+              mh = __builtin_fmaxf(mh, __builtin_fabsf(wh[e]));
+            }
+            if constexpr (!il) {
+#pragma unroll
+              for (int d = 1; d < 8; d <<= 1) {
+                ml = __builtin_fmaxf(ml, __shfl_xor(ml, d));
+                mh = __builtin_fmaxf(mh, __shfl_xor(mh, d));
+              }
+            } else {
+              ml = __builtin_fmaxf(ml, mh);
+#pragma unroll
+              for (int d = 1; d < 4; d <<= 1) ml = __builtin_fmaxf(ml, __shfl_xor(ml, d));
+              mh = ml;
+            }
+            const int el = fp8_exponent(ml), eh = fp8_exponent(mh);
+            if (in[u]) {
+              const float il2 = exp2_neg(el), ih2 = exp2_neg(eh);
+              const int64_t row = (int64_t)tku[u] * ht + hu[u];
+              uint8_t* crow = ct + row * D;   // contiguous
+              *reinterpret_cast<uint32_t*>(crow + o1) = fp8x4(wl[0] * il2, wl[1] * il2, wl[2] * il2, wl[3] * il2);
+              *reinterpret_cast<uint32_t*>(crow + o2) = fp8x4(wh[0] * ih2, wh[1] * ih2, wh[2] * ih2, wh[3] * ih2);
+              uint8_t* srow = st + row * (D / 32);
+              if constexpr (!il) {
+                if ((q4 & 7) == 0) {
+                  srow[j0 / 32] = (uint8_t)(el + 127);
+                  srow[(j0 + half) / 32] = (uint8_t)(eh + 127);
+                }
+              } else {
+                if ((q4 & 3) == 0) srow[q4 / 4] = (uint8_t)(el + 127);
+              }
             }
           } else if (in[u]) {
             const float inv = __uint_as_float(hw[h0 + hu[u]]);
@@ -356,6 +400,13 @@ int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64
   const bool bf = dtype == NXATTN_BF16;
   if (!fp8) {
     if (bf) launch((uint16_t*)nullptr, Rot{}); else launch((float*)nullptr, Rot{});
+    return check_launch(who);
+  }
+  if (tt.blocks) {
+    if (head_dim % 64 != 0)
+      return fail(NXATTN_ERR_UNSUPPORTED, "%s: block scales need head_dim a multiple of 64", who);
+    using Blk = std::integral_constant<RopeMode, RopeMode::Blocks>;
+    if (bf) launch((uint16_t*)nullptr, Blk{}); else launch((float*)nullptr, Blk{});
     return check_launch(who);
   }
   // maxima of the rotated values, then exponents and codes

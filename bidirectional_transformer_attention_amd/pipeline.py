@@ -7,9 +7,11 @@
        key splits, one launch over key ranges plus one merge launch)
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
 With the fp8 score GEMM (``qk_fp8`` workloads) q and own k are rotated and quantized to
-E4M3 in one call before the attention call. Each prefix K is quantized once, when the
-step is set up: the injected conditioning cache is the same for every denoising step
-(NeoPP page, intro), so its codes are too.
+E4M3 in one call before the attention call, with one scale per (branch, head) or, for
+``fp8_blocks`` workloads, one per run of 32 head_dim elements (then in a single pass and
+without a workspace). Each prefix K is quantized once, when the step is set up: the
+injected conditioning cache is the same for every denoising step (NeoPP page, intro), so
+its codes are too.
 
 Only tensor allocation and argument marshalling happen here; every step runs in the HIP
 library. The prefix of branch b is passed as one layer slice [2, P_b, Hkv, D] of the
@@ -66,19 +68,28 @@ class AttentionStep:
         if self.splits > 1:
             n = nx.fwd_workspace_bytes(self.B, self.S, self.Hq, self.D, self.splits)
             self.workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.blocks = wl.qk_fp8 and wl.fp8_blocks
         if wl.qk_fp8:
-            # E4M3 codes, exponents and the quantizer's workspace, allocated once
+            # E4M3 codes, their exponents (per (branch, head)) or block scales (per run of
+            # 32 elements, E8M0 codes) and the quantizer's workspace, allocated once
             self.q8 = torch.empty(self.q.shape, dtype=torch.uint8, device=dev)
             self.k8 = torch.empty(self.k.shape, dtype=torch.uint8, device=dev)
-            self.qe = torch.empty((self.B, self.Hq), dtype=torch.int8, device=dev)
-            self.ke = torch.empty((self.B, self.Hkv), dtype=torch.int8, device=dev)
-            self.pke = torch.zeros((self.B, self.Hkv), dtype=torch.int8, device=dev)
             self.pk8 = [None if p is None else torch.empty((1, p.shape[1], self.Hkv, self.D), dtype=torch.uint8,
                                                            device=dev) for p in self.prefix_online]
-            plen = max([p.shape[1] for p in self.prefix_online if p is not None] + [1])
-            n = max(nx.quantize_fp8_workspace_bytes(self.B, self.S, self.Hq + self.Hkv),
-                    nx.quantize_fp8_workspace_bytes(1, plen, self.Hkv))
-            self.qws = torch.empty(max(4, n), dtype=torch.uint8, device=dev)
+            if self.blocks:
+                nb = self.D // 32
+                self.qs = torch.empty((self.B, self.S, self.Hq, nb), dtype=torch.uint8, device=dev)
+                self.ks = torch.empty((self.B, self.S, self.Hkv, nb), dtype=torch.uint8, device=dev)
+                self.pks = [None if p is None else torch.empty((1, p.shape[1], self.Hkv, nb), dtype=torch.uint8,
+                                                               device=dev) for p in self.prefix_online]
+            else:
+                self.qe = torch.empty((self.B, self.Hq), dtype=torch.int8, device=dev)
+                self.ke = torch.empty((self.B, self.Hkv), dtype=torch.int8, device=dev)
+                self.pke = torch.zeros((self.B, self.Hkv), dtype=torch.int8, device=dev)
+                plen = max([p.shape[1] for p in self.prefix_online if p is not None] + [1])
+                n = max(nx.quantize_fp8_workspace_bytes(self.B, self.S, self.Hq + self.Hkv),
+                        nx.quantize_fp8_workspace_bytes(1, plen, self.Hkv))
+                self.qws = torch.empty(max(4, n), dtype=torch.uint8, device=dev)
         self.use_cfg = self.B == 2 and wl.guidance > 1.0
         self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
         if wl.qk_fp8:
@@ -88,7 +99,11 @@ class AttentionStep:
     def quantize_prefix(self) -> None:
         """E4M3 codes of each prefix K (fp8 workloads), once per conditioning cache."""
         for b, p in enumerate(self.prefix_online):
-            if p is not None:
+            if p is None:
+                continue
+            if self.blocks:
+                nx.nxattn_quantize_fp8_blocks(p[0].unsqueeze(0), self.pk8[b], self.pks[b])
+            else:
                 nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)
 
     def relayout(self) -> None:
@@ -109,10 +124,21 @@ class AttentionStep:
         codes carry the softmax fold factor, which the library forms."""
         if not self.wl.qk_fp8:
             return
+        if self.blocks:
+            nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qs, self.ks],
+                                        folds=[self.fold_q, False], blocks=True)
+            return
         nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qe, self.ke], self.qws,
                                     folds=[self.fold_q, False])
 
     def attention(self) -> None:
+        if self.blocks:
+            nx.nxattn_fwd_fp8(self.q8, self.k8, None, None, self.v, self.o,
+                              [None if p is None else p[0] for p in self.pk8],
+                              [None if p is None else p[1] for p in self.prefix_online],
+                              q_folded=self.fold_q, q_scales=self.qs, k_scales=self.ks,
+                              prefix_k_scales=[None if p is None else p[0] for p in self.pks])
+            return
         if self.wl.qk_fp8:
             nx.nxattn_fwd_fp8(self.q8, self.k8, self.qe, self.ke, self.v, self.o,
                               [None if p is None else p[0] for p in self.pk8],

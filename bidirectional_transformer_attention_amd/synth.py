@@ -31,7 +31,10 @@ checkpoints):
                  the keys into 2 ranges.
 * ``dit1k_fp8qk``, ``dit2k_fp8qk`` the 1K and 2K DiT steps (same shapes and seeds) with
                  q and k quantized each step to FP8 E4M3 for the score GEMM (the pages
-                 name fp8 DiT variants, NeoPP "Run the replay examples").
+                 name fp8 DiT variants, NeoPP "Run the replay examples"), one scale per
+                 (branch, head).
+* ``dit1k_fp8blk``, ``dit2k_fp8blk`` the same with one scale per run of 32 head_dim
+                 elements of each row.
 
 Seeds: ``1_000_000*c + 1000*layer + 10*branch + t`` with t = 0 q, 1 own k, 2 own v,
 3 prefix k, 4 prefix v; values drawn in fp32 on the CPU with ``torch.Generator`` and
@@ -67,6 +70,7 @@ class Workload:
     theta: float = 10000.0
     splits: int = 0               # key ranges per branch in the attention call (0: one pass)
     qk_fp8: bool = False          # q and k quantized to E4M3 for the score GEMM (bf16 tensors in)
+    fp8_blocks: bool = False      # qk_fp8 with one scale per 32-element run instead of per head
 
     @property
     def seq(self) -> int:
@@ -100,9 +104,12 @@ WORKLOADS: Dict[str, Workload] = {
                              (16384, 256), 32, 8, 128, guidance=4.0, splits=2),
 }
 # the DiT steps with the fp8 score GEMM: same shapes and seeds, q and k quantized each step
+# with one scale per (branch, head) (fp8qk) or per run of 32 head_dim elements (fp8blk)
 for _n in ("dit1k_bf16", "dit2k_bf16"):
     _w = WORKLOADS[_n]
     WORKLOADS[_n.replace("bf16", "fp8qk")] = dataclasses.replace(_w, name=_n.replace("bf16", "fp8qk"), qk_fp8=True)
+    WORKLOADS[_n.replace("bf16", "fp8blk")] = dataclasses.replace(_w, name=_n.replace("bf16", "fp8blk"), qk_fp8=True,
+                                                                  fp8_blocks=True)
 
 
 def bench_workload(name: str) -> Workload:

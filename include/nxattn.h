@@ -255,6 +255,24 @@ int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, in
                         int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Block scaling, a finer reading of the same recipe: the scale is shared by each run of 32
+ * consecutive head_dim elements of one (branch, token, head) row, the block size and scale
+ * format of the OCP Microscaling (MX) formats. Inside a run the rule is the one above (e =
+ * the smallest integer with max|run| <= 448 * 2^e, 0 for an all-zero run, at least -127;
+ * codes of x * 2^-e, nearest even), and the scale is stored as its E8M0 code e + 127
+ * (value 2^(code - 127)), the form the fp8 matrix core takes. One scale per run needs no
+ * reduction across the tensor, so one pass writes codes and scales.
+ *
+ * nxattn_quantize_fp8_blocks: x as in nxattn_quantize_fp8 with head_dim a multiple of 32 up
+ * to 1024 -> codes uint8 [batch, seq, heads, head_dim] contiguous (8-byte aligned) and
+ * scales uint8 [batch, seq, heads, head_dim / 32] contiguous. x, codes and scales must not
+ * overlap (NXATTN_ERR_INVALID). One launch on `stream`, no workspace.
+ */
+int nxattn_quantize_fp8_blocks(const void* x, int dtype, int64_t batch, int64_t seq, int64_t heads,
+                               int64_t head_dim, const int64_t strides[3], uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream);
+
+/*
  * RoPE and FP8 quantization together, for tensors that share positions (the q and k of
  * the own tokens): for each tensor t, codes_t and exps_t are exactly what
  * nxattn_quantize_fp8 gives for x_t after nxattn_rope_apply(x_t, rope), bit for bit, but
@@ -268,7 +286,12 @@ int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, in
  *           of 16 bytes; head_dim contiguous), 16-byte aligned; read only (tensors may
  *           share or overlap their x);
  *   codes   out, uint8 [batch, seq, heads, head_dim] contiguous, 8-byte aligned;
- *   exps    out, int8 [batch, heads];
+ *   exps    out, int8 [batch, heads] (one exponent per slice), or NULL with scales;
+ *   scales  out, uint8 [batch, seq, heads, head_dim / 32] E8M0 codes (block scaling, as
+ *           nxattn_quantize_fp8_blocks gives for the rotated values), or NULL with exps.
+ *           Either every tensor of a call has exps or every one has scales
+ *           (NXATTN_ERR_INVALID otherwise); block scaling needs head_dim % 64 == 0, takes
+ *           one launch and no workspace (workspace may be NULL, workspace_bytes 0);
  *   mult    with fold_softmax == 0: 0 or 1: none; else a finite multiplier > 0 applied
  *           (fp32 multiply) to each rotated value as stored in dtype before quantization,
  *           so that the codes are those of mult * rope(x).
@@ -279,10 +302,11 @@ int nxattn_quantize_fp8(const void* x, int dtype, int64_t batch, int64_t seq, in
  *           scores then arrive in base-2 units), so a caller never forms c itself.
  * Shared: dtype F32 or BF16; head_dim a multiple of 8 in [8, 256]; batch <=
  * NXATTN_MAX_BRANCHES; rope as in nxattn_rope_apply (grid product == seq); the total of
- * the heads at most 4096. workspace: nxattn_quantize_fp8_workspace_size(batch, seq, total
- * heads) bytes, 4-byte aligned, contents on entry irrelevant. No output may overlap an x,
- * another output or the workspace, and no x the workspace (NXATTN_ERR_INVALID). The
- * rotated values must be finite. Three launches on `stream`.
+ * the heads at most 4096. workspace (per-slice exponents only):
+ * nxattn_quantize_fp8_workspace_size(batch, seq, total heads) bytes, 4-byte aligned,
+ * contents on entry irrelevant. No output may overlap an x, another output or the
+ * workspace, and no x the workspace (NXATTN_ERR_INVALID). The rotated values must be
+ * finite. Three launches on `stream` (one with block scaling).
  */
 #define NXATTN_MAX_FP8_TENSORS 4
 typedef struct {
@@ -293,6 +317,7 @@ typedef struct {
   int8_t* exps;
   float mult;
   int32_t fold_softmax;
+  uint8_t* scales;
 } nxattn_fp8_tensor;
 
 int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
@@ -309,7 +334,8 @@ int nxattn_rope_quantize_fp8(const nxattn_fp8_tensor* tensors, int32_t n_tensors
  * that overlap in time on one GPU (several streams, or several host threads) race and
  * must be ordered by the caller; the array's contents between calls do not matter (each
  * call clears what it uses with a kernel, no memset). The device is the calling thread's
- * current one; stream must belong to it.
+ * current one; stream must belong to it. Block scaling (tensors with scales) needs no
+ * maxima: such a call does not touch the array and has no slice limit.
  */
 int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors, int32_t n_tensors, int dtype, int64_t batch,
                                      int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope, hipStream_t stream);
@@ -332,6 +358,15 @@ int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors, int32_t n
  * in base-2 units, s_j * log2(e) = 2^(q_exp + e_j) <dec(q8), dec(k8_j)>, `scale` is not
  * used, and the kernel's softmax takes one exp2 per score with no multiply in front
  * (its score accumulators start at minus the running max), the bf16 kernel's q_rope fold.
+ *
+ * Block scales (q_scales != NULL): q8, k8 and the prefix codes carry one E8M0 scale per run
+ * of 32 head_dim elements of each row, as nxattn_quantize_fp8_blocks and the block mode of
+ * nxattn_rope_quantize_fp8 write them, and the dot products sum the runs' products each
+ * times its two scales: s_j = scale * sum_r 2^(eq_r + ek_jr) <dec(q8_r), dec(k8_jr)>.
+ * q_scales uint8 [batch, seq_q, heads_q, 4], k_scales uint8 [batch, seq_q, heads_kv, 4] and
+ * prefix_k_scales[b] uint8 [P_b, heads_kv, 4] (non-NULL iff prefix_len[b] > 0), contiguous
+ * and 4-byte aligned; q_exp, k_exp and prefix_k_exp must then be NULL. Without q_scales,
+ * k_scales and every prefix_k_scales[b] must be NULL.
  */
 typedef struct {
   int32_t batch;
@@ -354,6 +389,9 @@ typedef struct {
   float scale;
   float* lse;                                         /* NULL, or [batch, heads_q, seq_q] fp32 */
   int32_t q_folded;                                   /* see above */
+  const uint8_t* q_scales;                            /* block scales, see above */
+  const uint8_t* k_scales;
+  const uint8_t* prefix_k_scales[NXATTN_MAX_BRANCHES];
 } nxattn_fwd_fp8_args;
 
 int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* args, hipStream_t stream);

@@ -307,6 +307,22 @@ def test_rope_quantize_fp8_rejects(lib):
     assert call(t=[good[0], tensor(K, 2, CK, EK)], w=K + 128) == INVALID   # workspace overlaps k
     assert call(S=0, r=None) == OK
     assert call(t=[tensor(Q, 0, 0, 0)], n=1, r=None) == OK      # no heads at all
+    # block scaling: every tensor with heads has scales and no exps, head_dim % 64 == 0,
+    # no workspace
+    SQ, SK = FAKE + 8 * GB, FAKE + 9 * GB
+
+    def btensor(x, heads, codes, scales):
+        t = tensor(x, heads, codes, 0)
+        t.scales = scales
+        return t
+    bgood = [btensor(Q, 8, CQ, SQ), btensor(K, 2, CK, SK)]
+    assert call(t=[bgood[0], good[1]]) == INVALID                # mixed kinds of scale
+    both = btensor(K, 2, CK, SK)
+    both.exps = EK
+    assert call(t=[bgood[0], both]) == INVALID                   # exps and scales on one tensor
+    assert call(t=bgood, D=96, r=[desc(pairs=48), desc(pairs=48)]) == UNSUPPORTED   # head_dim % 64
+    assert call(t=[bgood[0], btensor(K, 2, CK, CQ + 64)]) == INVALID   # scales overlap codes of q
+    assert call(t=bgood, S=0, r=None, w=None, wb=0) == OK        # no workspace needed
 
 
 def test_rope_quantize_fp8_noalloc_rejects(lib):
@@ -327,6 +343,28 @@ def test_rope_quantize_fp8_noalloc_rejects(lib):
     assert f(ctypes.byref(t), 1, 1, -1, 1, 128, ds, None) == INVALID
 
 
+def test_quantize_fp8_blocks_rejects(lib):
+    f = lib.nxattn_quantize_fp8_blocks
+    X, C, S_ = FAKE, FAKE + GB, FAKE + 2 * GB
+    st = (ctypes.c_int64 * 3)(64 * 4 * 128, 4 * 128, 128)
+
+    def call(x=X, dtype=1, B=2, S=64, H=4, D=128, strides=st, c=C, s=S_):
+        return f(x, dtype, B, S, H, D, strides, c, s, None)
+    assert call(dtype=5) == UNSUPPORTED
+    assert call(D=48) == UNSUPPORTED                             # runs of 32
+    assert call(D=2048) == UNSUPPORTED
+    assert call(B=-1) == INVALID
+    assert call(strides=None) == INVALID
+    assert call(c=None) == INVALID and call(s=None) == INVALID
+    assert call(x=X + 8) == ALIGN
+    assert call(c=C + 4) == ALIGN
+    assert call(strides=(ctypes.c_int64 * 3)(64 * 4 * 128, 4 * 128, 132)) == ALIGN   # 264-byte head stride
+    assert call(s=C + 100) == INVALID                            # scales overlap codes
+    assert call(c=X + 64) == INVALID                             # codes overlap x
+    assert call(S=0) == OK
+    assert b"nxattn_quantize_fp8_blocks" in lib.nxattn_last_error() or lib.nxattn_last_error() == b""
+
+
 def fp8_args(**kw):
     a = binding.FwdFp8Args()
     a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = 2, 64, 8, 2, 128
@@ -338,7 +376,7 @@ def fp8_args(**kw):
     for i, s in enumerate((64 * 8 * 128, 8 * 128, 128)):
         a.o_strides[i] = s
     for key, val in kw.items():
-        if key in ("prefix_len", "prefix_k8", "prefix_v", "v_strides", "o_strides"):
+        if key in ("prefix_len", "prefix_k8", "prefix_v", "v_strides", "o_strides", "prefix_k_scales"):
             for i, x in enumerate(val):
                 getattr(a, key)[i] = x
         else:
@@ -359,6 +397,15 @@ def fp8_args(**kw):
     (dict(prefix_len=(5, 0), prefix_k8=(FAKE + 5 * GB, None), prefix_v=(FAKE + 6 * GB, None)), INVALID),  # exps
     (dict(o=FAKE + GB), INVALID),                                         # o overlaps k8
     (dict(scale=float("inf")), INVALID),
+    # block scales: q_scales and k_scales instead of every exponent
+    (dict(q_scales=FAKE + 7 * GB, k_scales=FAKE + 8 * GB), INVALID),      # exponents still set
+    (dict(q_exp=None, k_exp=None, q_scales=FAKE + 7 * GB), INVALID),      # k_scales missing
+    (dict(k_scales=FAKE + 8 * GB), INVALID),                              # k_scales without q_scales
+    (dict(q_exp=None, k_exp=None, q_scales=FAKE + 7 * GB + 2, k_scales=FAKE + 8 * GB), ALIGN),
+    (dict(q_exp=None, k_exp=None, q_scales=FAKE + 7 * GB, k_scales=FAKE + 8 * GB, prefix_len=(5, 0),
+          prefix_k8=(FAKE + 5 * GB, None), prefix_v=(FAKE + 6 * GB, None)), INVALID),  # prefix scales missing
+    (dict(prefix_k_scales=(FAKE + 9 * GB, None)), INVALID),               # prefix scales without a prefix
+    (dict(q_exp=None, k_exp=None, q_scales=FAKE + 7 * GB, k_scales=FAKE + 8 * GB, o=FAKE + 8 * GB), INVALID),
 ])
 def test_fwd_fp8_rejects(lib, kw, code):
     assert lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(**kw)), None) == code

@@ -606,9 +606,10 @@ def test_step_dit1k_bf16_sampled():
     step_case("dit1k_bf16", 96, 3)
 
 
-@pytest.mark.parametrize("name", ["dit1k_fp8qk+replay", "dit2k_fp8qk"])
+@pytest.mark.parametrize("name", ["dit1k_fp8qk+replay", "dit2k_fp8qk", "dit1k_fp8blk+replay", "dit2k_fp8blk"])
 def test_step_fp8qk_sampled(name):
-    """The bench configuration of the fp8 score GEMM at full size.
+    """The bench configuration of the fp8 score GEMM at full size, with one scale per
+    (branch, head) (fp8qk) or per run of 32 head_dim elements (fp8blk).
 
     1. Isolation: the codes of the step's q and k as nxattn_rope_apply rotates them (q
        times the softmax fold factor), and of each prefix K, bit for bit against the
@@ -634,39 +635,46 @@ def test_step_fp8qk_sampled(name):
     assert torch.equal(step.k.cpu().view(torch.int16), inp.k.view(torch.int16))
     assert step.fold_q
     cf = fold_factor(wl.head_dim)
-    q8, qe, k8, ke = (t.cpu().numpy() for t in (step.q8, step.qe, step.k8, step.ke))
+    if wl.fp8_blocks:
+        quant, deq = ofp8.quantize_fp8_blocks, ofp8.dequantize_fp8_blocks
+        q8, qe, k8, ke = (t.cpu().numpy() for t in (step.q8, step.qs, step.k8, step.ks))
+    else:
+        quant, deq = ofp8.quantize_fp8, ofp8.dequantize_fp8
+        q8, qe, k8, ke = (t.cpu().numpy() for t in (step.q8, step.qe, step.k8, step.ke))
     o = step.o.cpu()
     # 1. isolation
     qr, kr = step.q.clone(), step.k.clone()
     nx.nxattn_rope_apply(qr, step.descs)
     nx.nxattn_rope_apply(kr, step.descs)
     torch.cuda.synchronize()
-    rq, rqe = ofp8.quantize_fp8(f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32)))
-    rk, rke = ofp8.quantize_fp8(f64(kr.cpu()))
+    rq, rqe = quant(f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32)))
+    rk, rke = quant(f64(kr.cpu()))
     del qr, kr
     assert np.array_equal(q8, rq) and np.array_equal(qe, rqe)
     assert np.array_equal(k8, rk) and np.array_equal(ke, rke)
-    dq_iso, dk_iso = ofp8.dequantize_fp8(rq, rqe) / cf, ofp8.dequantize_fp8(rk, rke)
+    dq_iso, dk_iso = deq(rq, rqe) / cf, deq(rk, rke)
     del rq, rk
     # 2. the oracle chain
     bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
     q_chain = torch.stack([bf(oracle_rope(wl, inp.q, b)) for b in range(wl.branches)])
     k_chain = torch.stack([bf(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)])
-    cq, cqe = ofp8.quantize_fp8(f64(q_chain.float() * torch.tensor(cf, dtype=torch.float32)))
-    ck, cke = ofp8.quantize_fp8(f64(k_chain))
+    cq, cqe = quant(f64(q_chain.float() * torch.tensor(cf, dtype=torch.float32)))
+    ck, cke = quant(f64(k_chain))
     del q_chain, k_chain
     nq, nk = int(np.count_nonzero(q8 != cq)), int(np.count_nonzero(k8 != ck))
     note(f"  codes that differ from the oracle chain's: q {nq} of {q8.size}, k {nk} of {k8.size}; "
          f"exponents differing: q {int(np.count_nonzero(qe != cqe))}, k {int(np.count_nonzero(ke != cke))}")
-    dq_ch, dk_ch = ofp8.dequantize_fp8(cq, cqe) / cf, ofp8.dequantize_fp8(ck, cke)
+    dq_ch, dk_ch = deq(cq, cqe) / cf, deq(ck, cke)
     del cq, ck
     for b in range(wl.branches):
         pre = step.prefix_online[b]
         dpk = pv = pk_ex = None
         if pre is not None:
-            pc, pe = ofp8.quantize_fp8(f64(pre[0].cpu())[None])
-            assert np.array_equal(step.pk8[b].cpu().numpy(), pc) and np.array_equal(step.pke[b].cpu().numpy(), pe[0])
-            dpk, pv, pk_ex = ofp8.dequantize_fp8(pc, pe)[0], f64(pre[1].cpu()), f64(pre[0].cpu())
+            pc, pe = quant(f64(pre[0].cpu())[None])
+            got_e = step.pks[b].cpu().numpy() if wl.fp8_blocks else step.pke[b].cpu().numpy()
+            assert np.array_equal(step.pk8[b].cpu().numpy(), pc)
+            assert np.array_equal(got_e, pe if wl.fp8_blocks else pe[0])
+            dpk, pv, pk_ex = deq(pc, pe)[0], f64(pre[1].cpu()), f64(pre[0].cpu())
         rows = sample_rows(wl.seq, 48, 700 + b)
         ar = np.arange(len(rows))
         g = f64(o[b][torch.from_numpy(rows)])
