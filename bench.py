@@ -13,7 +13,9 @@ branches, divided by the step time). ``roofline`` is measured on the fused atten
 kernel with HIP events recorded on the stream it runs on; ``cpu_baseline`` times the
 CPU fp64 oracle on a bounded sample of the same workload. ``gate_16k_tokens`` times the
 16K-token 2K DiT step (both CFG branches) beside the headline workload, with its kernel's
-fraction of the bf16 MFMA peak.
+fraction of the bf16 MFMA peak. ``fp8_step`` times the same step with the fp8 score GEMM
+(q and k as E4M3 codes with one scale per 32-element run) beside it, with its speedup over
+the bf16 step of the same run.
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ PEAK = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}   # TFLOP/s, dense MFMA, MI
 PEAK_FP8QK = 2.0 / (1.0 / PEAK["fp8"] + 1.0 / PEAK["bf16"])
 HBM_PEAK = 8000.0                               # GB/s
 GATE_WORKLOAD = "dit2k_bf16"   # its prefix is given in the replay layout
+FP8_WORKLOAD = "dit1k_fp8blk"  # the headline step with the block-scaled fp8 score GEMM
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_dit1k_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "bidirectional_transformer_attention_amd", "csrc", "fwd_bf16.hip")
 
@@ -200,6 +203,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gate-steps", type=int, default=10,
                     help="timed steps of the 16K-token gate workload (2K DiT, both branches); 0: skip")
+    ap.add_argument("--fp8-steps", type=int, default=50,
+                    help="timed steps of the headline step with the fp8 score GEMM (dit1k workloads); 0: skip")
     ap.add_argument("--cpu-layers", type=int, default=1,
                     help="layers of a multi-layer workload that the CPU oracle timing covers")
     ap.add_argument("--cpu-1thread-rows", type=int, default=-1,
@@ -233,6 +238,23 @@ def main() -> int:
     flops_step = wl.flops() * layers
     ms_step, fwd_avg, fwd_min = time_step(steps_all if layers > 1 else step, args.steps, args.warmup, torch)
     value = flops_step / (ms_step * 1e-3) / 1e12
+
+    # the same step with the fp8 score GEMM (block scales), timed right after the bf16 step
+    # with the same warmup, against it
+    fp8 = None
+    if args.fp8_steps > 0 and wl.name.split("+")[0] == "dit1k_bf16":
+        fwl = synth.bench_workload(FP8_WORKLOAD)
+        fstep = AttentionStep(fwl, synth.make_inputs(fwl), "cuda:0")
+        f_ms, f_fwd, f_min = time_step(fstep, args.fp8_steps, args.warmup, torch)
+        ffl = fwl.flops()
+        fp8 = {"workload": fwl.name, "steps": args.fp8_steps,
+               "dtype": "fp8e4m3 QK (E8M0 scale per 32 elements) / bf16 PV",
+               "ms_per_step": round(f_ms, 4), "step_tflops": round(ffl / f_ms / 1e9, 1),
+               "speedup_vs_bf16_step": round(ms_step / f_ms, 4),
+               "kernel": "nx::fp8k::fwd_fp8_kernel<true, true>", "kernel_ms_avg": round(f_fwd, 4),
+               "kernel_ms_min": round(f_min, 4), "kernel_tflops": round(ffl / f_fwd / 1e9, 1),
+               "kernel_frac_of_fp8qk_peak": round(ffl / f_fwd / 1e9 / PEAK_FP8QK, 4)}
+        del fstep
 
     # the headline shape alone: the cond branch, 4096 x (4096 + 512), as a batch-1 launch
     headline = None
@@ -356,6 +378,7 @@ def main() -> int:
         "side_calls": side,
         "headline_cond_branch": headline,
         "gate_16k_tokens": gate,
+        "fp8_step": fp8,
     }
     print(json.dumps(out))
     return 0
