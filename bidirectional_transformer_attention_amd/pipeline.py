@@ -161,3 +161,30 @@ class AttentionStep:
         self.attention()
         self.cfg()
         return self.out if self.use_cfg else self.o
+
+    def capture(self, warmup: int = 2) -> "torch.cuda.CUDAGraph":
+        """Record one step (the same launches as a call, on the same buffers) into a HIP
+        graph; see ``capture_steps``."""
+        return capture_steps([self], warmup)
+
+
+def capture_steps(steps: List[AttentionStep], warmup: int = 2) -> "torch.cuda.CUDAGraph":
+    """Record the given steps, one after another (the layers of a multi-layer step), into
+    one HIP graph; ``graph.replay()`` then runs them with one submission, for callers
+    that drive the step from a captured loop. A step allocates nothing and clears nothing with memset,
+    so it can be captured. Like a call, a replay rotates k in place (bf16 path) and
+    overwrites the outputs."""
+    side = torch.cuda.Stream()                      # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            for st in steps:
+                st()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for st in steps:
+            st()
+    torch.cuda.synchronize()
+    return graph
