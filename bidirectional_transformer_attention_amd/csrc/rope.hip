@@ -30,18 +30,26 @@ struct RopeArgs {
   RopeBranch br[NXATTN_MAX_BRANCHES];
 };
 
-// codes of 4 values times inv (an exact power of two); the scaled values of finite inputs
-// lie in [-448, 448], where v_cvt_pk_fp8_f32 rounds to nearest even E4M3; NaN -> 0x7F
+// codes of 4 scaled values; the scaled values of finite inputs lie in [-448, 448], where
+// v_cvt_pk_fp8_f32 rounds to nearest even E4M3 (the rotated values of the fused calls are
+// finite by contract, so no NaN case)
 __device__ __forceinline__ uint32_t fp8x4(float y0, float y1, float y2, float y3) {
   int c = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
   c = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, c, true);
-  uint32_t u = (uint32_t)c;
-  if (y0 != y0) u = (u & 0xffffff00u) | 0x7Fu;
-  if (y1 != y1) u = (u & 0xffff00ffu) | 0x7F00u;
-  if (y2 != y2) u = (u & 0xff00ffffu) | 0x7F0000u;
-  if (y3 != y3) u = (u & 0x00ffffffu) | 0x7F000000u;
-  return u;
+  return (uint32_t)c;
 }
+
+// maximum over aligned groups of 4 (quad permutations) or 8 lanes (then the mirror of each
+// 8-lane half row) through DPP moves, without the LDS crossbar
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float m) {
+  return __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), CTRL, 0xF, 0xF, true)));
+}
+__device__ __forceinline__ float max4_lanes(float m) {
+  m = dpp_max<0xB1>(m);      // quad_perm [1,0,3,2]
+  return dpp_max<0x4E>(m);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float max8_lanes(float m) { return dpp_max<0x141>(max4_lanes(m)); }  // row_half_mirror
 
 // 4 consecutive elements as loaded and stored (bf16: two words; fp32: one 16-byte vector)
 template <typename T>
@@ -266,15 +274,10 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
               mh = __builtin_fmaxf(mh, __builtin_fabsf(wh[e]));
             }
             if constexpr (!il) {
-#pragma unroll
-              for (int d = 1; d < 8; d <<= 1) {
-                ml = __builtin_fmaxf(ml, __shfl_xor(ml, d));
-                mh = __builtin_fmaxf(mh, __shfl_xor(mh, d));
-              }
+              ml = max8_lanes(ml);
+              mh = max8_lanes(mh);
             } else {
-              ml = __builtin_fmaxf(ml, mh);
-#pragma unroll
-              for (int d = 1; d < 4; d <<= 1) ml = __builtin_fmaxf(ml, __shfl_xor(ml, d));
+              ml = max4_lanes(__builtin_fmaxf(ml, mh));
               mh = ml;
             }
             const int el = fp8_exponent(ml), eh = fp8_exponent(mh);
