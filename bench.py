@@ -37,6 +37,7 @@ PEAK_FP8QK = 2.0 / (1.0 / PEAK["fp8"] + 1.0 / PEAK["bf16"])
 HBM_PEAK = 8000.0                               # GB/s
 GATE_WORKLOAD = "dit2k_bf16"   # its prefix is given in the replay layout
 FP8_WORKLOAD = "dit1k_fp8blk"  # the headline step with the block-scaled fp8 score GEMM
+GATE_WARMUP = 5                # untimed 16K-token steps (about 35 ms) before its timed ones
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_dit1k_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "bidirectional_transformer_attention_amd", "csrc", "fwd_bf16.hip")
 
@@ -262,15 +263,17 @@ def main() -> int:
             return None
         fwl = synth.bench_workload(FP8_WORKLOAD)
         fstep = AttentionStep(fwl, synth.make_inputs(fwl), "cuda:0")
-        f_ms, f_fwd, f_min = time_step(fstep, args.fp8_steps, args.warmup, torch)
+        # its own buffers are fresh: at least 30 untimed steps before timing
+        fw = max(args.warmup, 30)
+        f_ms, f_fwd, f_min = time_step(fstep, args.fp8_steps, fw, torch)
         if args.graph:
-            f_ms = time_graph(capture_steps([fstep]), args.fp8_steps, args.warmup, torch)
+            f_ms = time_graph(capture_steps([fstep]), args.fp8_steps, fw, torch)
         ffl = fwl.flops()
-        return {"workload": fwl.name, "steps": args.fp8_steps,
+        return {"workload": fwl.name, "steps": args.fp8_steps, "warmup": fw,
                 "dtype": "fp8e4m3 QK (E8M0 scale per 32 elements) / bf16 PV",
                 "ms_per_step": round(f_ms, 4), "step_tflops": round(ffl / f_ms / 1e9, 1),
                 "speedup_vs_bf16_step": None,
-                "kernel": "nx::fp8k::fwd_fp8_kernel<true, true>", "kernel_ms_avg": round(f_fwd, 4),
+                "kernel": "nx::fp8k::fwd_fp8_kernel<true, true, false>", "kernel_ms_avg": round(f_fwd, 4),
                 "kernel_ms_min": round(f_min, 4), "kernel_tflops": round(ffl / f_fwd / 1e9, 1),
                 "kernel_frac_of_fp8qk_peak": round(ffl / f_fwd / 1e9 / PEAK_FP8QK, 4)}
 
@@ -281,11 +284,12 @@ def main() -> int:
             return None
         gwl = synth.bench_workload(GATE_WORKLOAD)
         gstep = AttentionStep(gwl, synth.make_inputs(gwl), "cuda:0")
-        g_ms, g_fwd, g_min = time_step(gstep, args.gate_steps, 2, torch)
+        g_ms, g_fwd, g_min = time_step(gstep, args.gate_steps, GATE_WARMUP, torch)
         if args.graph:
-            g_ms = time_graph(capture_steps([gstep]), args.gate_steps, 2, torch)
+            g_ms = time_graph(capture_steps([gstep]), args.gate_steps, GATE_WARMUP, torch)
         gfl = gwl.flops()
-        return {"workload": gwl.name, "steps": args.gate_steps, "gflop_per_step": round(gfl / 1e9, 1),
+        return {"workload": gwl.name, "steps": args.gate_steps, "warmup": GATE_WARMUP,
+                "gflop_per_step": round(gfl / 1e9, 1),
                 "ms_per_step": round(g_ms, 4), "step_tflops": round(gfl / g_ms / 1e9, 1),
                 "step_frac": round(gfl / g_ms / 1e9 / PEAK["bf16"], 4),
                 "kernel": "nx::bf16k::fwd_bf16_kernel<true>", "kernel_ms_avg": round(g_fwd, 4),
@@ -366,7 +370,7 @@ def main() -> int:
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
                         and not wl.qk_fp8 else None),
             "kernel": (f"nx::fp8k::fwd_fp8_kernel<{'true' if step.fold_q else 'false'}, "
-                       f"{'true' if wl.fp8_blocks else 'false'}>" if wl.qk_fp8 else
+                       f"{'true' if wl.fp8_blocks else 'false'}, false>" if wl.qk_fp8 else
                        (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
                        if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),

@@ -72,7 +72,9 @@ class FwdFp8Args(ctypes.Structure):
                 ("prefix_len", ctypes.c_int32 * MAX_BRANCHES), ("prefix_k_exp", ctypes.c_void_p),
                 ("scale", ctypes.c_float), ("lse", ctypes.c_void_p), ("q_folded", ctypes.c_int32),
                 ("q_scales", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
-                ("prefix_k_scales", ctypes.c_void_p * MAX_BRANCHES)]
+                ("prefix_k_scales", ctypes.c_void_p * MAX_BRANCHES),
+                ("q", ctypes.c_void_p), ("q_strides", ctypes.c_int64 * 3), ("q_rope", ctypes.POINTER(RopeDesc)),
+                ("q8_out", ctypes.c_void_p), ("q_scales_out", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -518,13 +520,15 @@ def _fp8_tensors(xs, outs, mults, folds, blocks=False):
     return arr
 
 
-def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: Optional[torch.Tensor],
+def nxattn_fwd_fp8(q8: Optional[torch.Tensor], k8: torch.Tensor, q_exp: Optional[torch.Tensor],
                    k_exp: Optional[torch.Tensor], v: torch.Tensor,
                    o: torch.Tensor, prefix_k8: Sequence[Optional[torch.Tensor]] = (),
                    prefix_v: Sequence[Optional[torch.Tensor]] = (), prefix_k_exp: Optional[torch.Tensor] = None,
                    scale: float = 0.0, lse: Optional[torch.Tensor] = None, q_folded: bool = False,
                    q_scales: Optional[torch.Tensor] = None, k_scales: Optional[torch.Tensor] = None,
-                   prefix_k_scales: Sequence[Optional[torch.Tensor]] = (), stream=None) -> None:
+                   prefix_k_scales: Sequence[Optional[torch.Tensor]] = (), q: Optional[torch.Tensor] = None,
+                   q_rope: Optional[Sequence[RopeDesc]] = None, q8_out: Optional[torch.Tensor] = None,
+                   q_scales_out: Optional[torch.Tensor] = None, stream=None) -> None:
     """Attention with the fp8 score GEMM: q8 [B,S,Hq,128], k8 [B,S,Hkv,128] uint8 codes
     (contiguous), q_exp [B,Hq], k_exp [B,Hkv] int8; v [B,S,Hkv,128] and o [B,S,Hq,128] bf16;
     prefix_k8[b] uint8 [P_b,Hkv,128] and prefix_v[b] bf16 [P_b,Hkv,128] contiguous (or None),
@@ -532,24 +536,40 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: Optional[torch.Ten
     softmax_scale*log2(e) (see nxattn_rope_quantize_fp8's folds) and scale is not used.
     Block scales: q_scales [B,S,Hq,4], k_scales [B,S,Hkv,4] and prefix_k_scales[b]
     [P_b,Hkv,4] (uint8 E8M0 codes, contiguous) in place of the exponents (which are then
-    None)."""
-    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, q_scales, k_scales,
+    None). With q_rope (one RopeDesc per batch entry), q8 is None and q (bf16
+    [B,S,Hq,128], head_dim contiguous) is rotated, folded and block-quantized on load; the
+    keys take block scales; q8_out [B,S,Hq,128] and q_scales_out [B,S,Hq,4] (uint8,
+    contiguous, optional) receive the codes and run scales formed on load."""
+    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, q_scales, k_scales, q, q8_out, q_scales_out,
          *[t for t in prefix_k8 if t is not None], *[t for t in prefix_v if t is not None],
          *[t for t in prefix_k_scales if t is not None])
-    B, S, Hq, D = q8.shape
+    qrope = q_rope is not None
+    if qrope:
+        if q8 is not None or q is None or q.dtype != torch.bfloat16 or q.dim() != 4 or q.stride(3) != 1:
+            raise NxattnError(1, "q_rope takes q (bf16 [B, S, Hq, 128], head_dim contiguous) and no q8")
+        B, S, Hq, D = q.shape
+        if len(q_rope) != B:
+            raise NxattnError(1, "one RopeDesc per batch entry is required")
+    else:
+        if q is not None or q8 is None:
+            raise NxattnError(1, "q8 is required (q only with q_rope)")
+        B, S, Hq, D = q8.shape
     Hkv = k8.shape[2]
-    for t in (q8, k8):
+    for t in ((k8,) if qrope else (q8, k8)):
         if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 4:
             raise NxattnError(1, "q8 and k8 must be contiguous uint8 [B, S, H, D] tensors")
     if tuple(k8.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D) or tuple(o.shape) != (B, S, Hq, D):
         raise NxattnError(1, "inconsistent q8/k8/v/o shapes")
     if v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 or v.stride(3) != 1 or o.stride(3) != 1:
         raise NxattnError(1, "v and o must be bf16 with head_dim contiguous")
-    block = q_scales is not None
+    block = q_scales is not None or qrope
     if block:
         if q_exp is not None or k_exp is not None or prefix_k_exp is not None:
             raise NxattnError(1, "block scales exclude the per-slice exponents")
-        for t, shp in ((q_scales, (B, S, Hq, 4)), (k_scales, (B, S, Hkv, 4))):
+        checks = ((k_scales, (B, S, Hkv, 4)),) if qrope else ((q_scales, (B, S, Hq, 4)), (k_scales, (B, S, Hkv, 4)))
+        if qrope and q_scales is not None:
+            raise NxattnError(1, "q_rope forms q's scales itself: q_scales must be None")
+        for t, shp in checks:
             if t is None or t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous():
                 raise NxattnError(1, "q_scales / k_scales must be contiguous uint8 [B, S, H, 4] tensors")
     else:
@@ -565,11 +585,26 @@ def nxattn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, q_exp: Optional[torch.Ten
     a = FwdFp8Args()
     a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, Hkv, D
     a.q_folded = 1 if q_folded else 0
-    a.q8, a.k8 = q8.data_ptr(), k8.data_ptr()
+    a.q8 = q8.data_ptr() if q8 is not None else None
+    a.k8 = k8.data_ptr()
     a.q_exp = q_exp.data_ptr() if q_exp is not None else None
     a.k_exp = k_exp.data_ptr() if k_exp is not None else None
-    a.q_scales = q_scales.data_ptr() if block else None
+    a.q_scales = q_scales.data_ptr() if q_scales is not None else None
     a.k_scales = k_scales.data_ptr() if block else None
+    if qrope:
+        a.q = q.data_ptr()
+        for i in range(3):
+            a.q_strides[i] = q.stride(i)
+        arr = (RopeDesc * len(q_rope))(*q_rope)
+        a._q_rope_keep = arr
+        a.q_rope = ctypes.cast(arr, ctypes.POINTER(RopeDesc))
+        if (q8_out is None) != (q_scales_out is None):
+            raise NxattnError(1, "q8_out and q_scales_out go together")
+        if q8_out is not None:
+            for t, shp in ((q8_out, (B, S, Hq, D)), (q_scales_out, (B, S, Hq, 4))):
+                if t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous():
+                    raise NxattnError(1, "q8_out / q_scales_out must be contiguous uint8 [B, S, Hq, 128 / 4] tensors")
+            a.q8_out, a.q_scales_out = q8_out.data_ptr(), q_scales_out.data_ptr()
     a.v, a.o = v.data_ptr(), o.data_ptr()
     for i in range(3):
         a.v_strides[i] = v.stride(i)

@@ -117,16 +117,12 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   if (a->q_rope && a->dtype != NXATTN_BF16)
     return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: q_rope is supported for BF16 only");
   if (a->batch == 0 || a->seq_q == 0) return NXATTN_OK;
-  if (a->q_rope)
-    for (int b = 0; b < a->batch; ++b) {
-      const int st = check_rope_desc(a->q_rope[b], a->seq_q, a->head_dim, "nxattn_fwd (q_rope)");
-      if (st != NXATTN_OK) return st;
-      // the rotation on load holds positions as exact fp32 integers
-      for (int ax = 0; ax < a->q_rope[b].n_axes; ++ax)
-        if ((int64_t)a->q_rope[b].offset[ax] + a->q_rope[b].grid[ax] - 1 >= (1 << 24))
-          return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd (q_rope): positions must stay below 2^24 "
-                      "(rotate q with nxattn_rope_apply instead)");
-    }
+  RopeQ rq[NXATTN_MAX_BRANCHES];
+  std::memset(rq, 0, sizeof(rq));
+  if (a->q_rope) {
+    const int st = rope_q_setup(a->q_rope, a->batch, a->seq_q, a->head_dim, "nxattn_fwd (q_rope)", rq);
+    if (st != NXATTN_OK) return st;
+  }
   // own k and v are not read with prefix_only
   const bool own = !a->prefix_only;
   if (!a->q || !a->o || (own && (!a->k || !a->v))) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
@@ -187,18 +183,7 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   }
   p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
   p.rope_q = a->q_rope != nullptr;
-  std::memset(p.rq, 0, sizeof(p.rq));
-  for (int b = 0; p.rope_q && b < a->batch; ++b) {
-    const nxattn_rope_desc& d = a->q_rope[b];
-    RopeQ& r = p.rq[b];
-    r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.global_freq = d.global_freq;
-    r.log2_theta = std::log2(d.theta);
-    for (int ax = 0; ax < 3; ++ax) {
-      r.grid[ax] = ax < d.n_axes ? d.grid[ax] : 1;
-      r.pairs[ax] = ax < d.n_axes ? d.pairs[ax] : 0;
-      r.offset[ax] = ax < d.n_axes ? d.offset[ax] : 0;
-    }
-  }
+  std::memcpy(p.rq, rq, sizeof(p.rq));
   // Key ranges of `per` whole tiles. The range length is at least ceil(max tiles /
   // num_splits) and at least the tile work per resident workgroup slot of the GPU
   // (sum over branches of tiles * workgroups per range, over the workgroups the GPU
@@ -250,4 +235,25 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   for (int i = 0; i < 3; ++i) m.os[i] = a->o_strides[i];
   m.o = a->o; m.lse = a->lse;
   return launch_merge(m, stream);
+}
+
+int nx::rope_q_setup(const nxattn_rope_desc* d, int batch, int64_t seq, int64_t head_dim, const char* who,
+                     RopeQ* out) {
+  for (int b = 0; b < batch; ++b) {
+    const int st = check_rope_desc(d[b], seq, head_dim, who);
+    if (st != NXATTN_OK) return st;
+    for (int ax = 0; ax < d[b].n_axes; ++ax)
+      if ((int64_t)d[b].offset[ax] + d[b].grid[ax] - 1 >= (1 << 24))
+        return fail(NXATTN_ERR_UNSUPPORTED, "%s: positions must stay below 2^24 (rotate q with nxattn_rope_apply "
+                    "instead)", who);
+    RopeQ& r = out[b];
+    r.n_axes = d[b].n_axes; r.interleaved = d[b].interleaved; r.global_freq = d[b].global_freq;
+    r.log2_theta = std::log2(d[b].theta);
+    for (int ax = 0; ax < 3; ++ax) {
+      r.grid[ax] = ax < d[b].n_axes ? d[b].grid[ax] : 1;
+      r.pairs[ax] = ax < d[b].n_axes ? d[b].pairs[ax] : 0;
+      r.offset[ax] = ax < d[b].n_axes ? d[b].offset[ax] : 0;
+    }
+  }
+  return NXATTN_OK;
 }

@@ -20,9 +20,11 @@
 // MFMA-bound: 4*Sq*Skv*Hq*D flops per launch, half on the fp8 and half on the bf16 unit.
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <type_traits>
 
 #include "nx_internal.h"
+#include "rope_turn.h"
 
 namespace nx {
 
@@ -57,6 +59,12 @@ struct Args {
   int32_t batch, seq, heads_q, heads_kv, group, nchunks, nqb, wg_per_group, total_wg;
   float c;  // scale * log2(e)
   float* lse;
+  // QROPE: q as bf16 (element strides), rotated, folded and block-quantized on load
+  const uint16_t* q;
+  int64_t qs0, qs1, qs2;
+  RopeQ rq[NXATTN_MAX_BRANCHES];
+  uint8_t* q8_out;      // QROPE, optional: the codes [B, S, Hq, 128] and run scales [B, S, Hq, 4]
+  uint8_t* qsc_out;     // formed on load
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -126,6 +134,7 @@ struct Wave {
   int vbase, vy;      // V^T fragment of d-block db at vbase + (64db ^ vy)
   int qsc;            // E8M0 scale of the B operand: the q head's, or (BLOCK) the row's run
                       // scales shifted so that k-step ks finds its own in byte 2ks
+  uint32_t qrun;      // QROPE: the row's four run scales in run order (for q_scales_out)
 };
 
 // Byte of the scale operands that k-step ks uses: per slice the value itself (byte 0);
@@ -358,7 +367,107 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
   }
 }
 
-template <bool GROUP_A, bool FOLD, bool BLOCK>
+// QROPE: this lane's q codes and run scales formed in registers. The lane holds dims
+// 64ks + 32e + 16hh + i (k-step ks, half e, i < 16) of its query row, as bf16. They are
+// rotated with the branch's RoPE (RopeTurns; half-split pairs (j, j + 64) are ks 0 and 1
+// at the same (e, i), adjacent pairs neighbouring i) and multiplied by c, both in fp32
+// (no bf16 rounding in between). Run 2ks + e (32 dims) is half e of k-step ks in both lane
+// halves, so its maximum is the larger of this lane's and its partner's (lane ^ 32), and
+// both form the same exponent (smallest e with max <= 448 * 2^e, at least -127); the codes
+// are the values times 2^-e rounded to nearest even E4M3. The lane's scale for k-step ks is
+// that of run 2ks + hh, in byte 2ks of w.qsc (the layout the score MFMAs' op_sel reads).
+// The lane's bf16 q values (loaded at the start of the work item, before the first tiles'
+// DMA, so that waiting for them never waits for the DMA): raw[ks][e][h] holds dims
+// 64ks + 32e + 16hh + 8h .. +7.
+struct QRaw {
+  u32x4 raw[2][2][2];
+};
+__device__ __forceinline__ QRaw q_rope_load(const Args& a, int b, int tokc, int hq, int hh) {
+  const uint16_t* qrow = a.q + b * a.qs0 + (int64_t)tokc * a.qs1 + (int64_t)hq * a.qs2;
+  QRaw r;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8)
+        r.raw[ks][e][h8] = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * e + 16 * hh + 8 * h8);
+  return r;
+}
+
+__device__ __forceinline__ void q_rope_quantize(Wave& w, const Args& a, const QRaw& qr, int b, int tokc,
+                                                int lane) {
+  const int hh = lane >> 5;
+  float x[2][2][16];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const u32x4 v = qr.raw[ks][e][h8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[ks][e][8 * h8 + 2 * k] = __uint_as_float(v[k] << 16);
+          x[ks][e][8 * h8 + 2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+        }
+      }
+  const RopeQ& r = a.rq[b];
+  const RopeTurns rt(r, tokc, lane);
+  const float c = a.c;
+  if (!r.interleaved) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float sn, cs;
+        rt.turn(32 * e + 16 * hh + i, sn, cs);
+        const float xa = x[0][e][i], xb = x[1][e][i];
+        x[0][e][i] = (xa * cs - xb * sn) * c;
+        x[1][e][i] = (xa * sn + xb * cs) * c;
+      }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float sn, cs;
+          rt.turn((64 * ks + 32 * e + 16 * hh + i) >> 1, sn, cs);
+          const float xa = x[ks][e][i], xb = x[ks][e][i + 1];
+          x[ks][e][i] = (xa * cs - xb * sn) * c;
+          x[ks][e][i + 1] = (xa * sn + xb * cs) * c;
+        }
+  }
+  int sc[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 cw[2];        // half e of the k-step's operand: bytes 16e .. 16e + 15
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(x[ks][e][i]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+      m = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+      const int ex = fp8_exponent(m);
+      sc[ks][e] = ex + 127;
+      const float inv = exp2_neg(ex);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int cc = __builtin_amdgcn_cvt_pk_fp8_f32(x[ks][e][4 * k] * inv, x[ks][e][4 * k + 1] * inv, 0, false);
+        cc = __builtin_amdgcn_cvt_pk_fp8_f32(x[ks][e][4 * k + 2] * inv, x[ks][e][4 * k + 3] * inv, cc, true);
+        cw[e][k] = (uint32_t)cc;
+      }
+    }
+    w.q8[ks] = __builtin_bit_cast(v8i, __builtin_shufflevector(cw[0], cw[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  w.qsc = (hh ? sc[0][1] : sc[0][0]) | ((hh ? sc[1][1] : sc[1][0]) << 16);
+  w.qrun = (uint32_t)sc[0][0] | ((uint32_t)sc[0][1] << 8) | ((uint32_t)sc[1][0] << 16) | ((uint32_t)sc[1][1] << 24);
+}
+
+template <bool GROUP_A, bool FOLD, bool BLOCK, bool QROPE>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
@@ -378,7 +487,10 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   const int sc_pre = BLOCK ? 0 : (P > 0 ? 127 + (int)a.pk_exp[b * a.heads_kv + g] : sc_own);
 
   Wave w;
-  {
+  QRaw qraw;
+  if constexpr (QROPE) {
+    qraw = q_rope_load(a, b, tokc, hq, hh);
+  } else {
     const uint8_t* qrow = a.q8 + (((int64_t)b * a.seq + tokc) * a.heads_q + hq) * D;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -387,7 +499,26 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
       w.q8[ks] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
-  if constexpr (BLOCK) {
+  // QROPE: the codes formed from q (after the first tiles' DMA is issued) and, if asked
+  // for, copied out
+  auto q_rope_codes = [&]() {
+    q_rope_quantize(w, a, qraw, b, tokc, lane);
+    if (a.q8_out && active && tok < a.seq) {
+      // the codes and run scales formed here, for callers that check or reuse them
+      const int64_t row = ((int64_t)b * a.seq + tok) * a.heads_q + hq;
+      uint8_t* orow = a.q8_out + row * D;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const v8i v = w.q8[ks];
+        *reinterpret_cast<u32x4*>(orow + 64 * ks + 16 * hh) = u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+        *reinterpret_cast<u32x4*>(orow + 64 * ks + 32 + 16 * hh) =
+            u32x4{(uint32_t)v[4], (uint32_t)v[5], (uint32_t)v[6], (uint32_t)v[7]};
+      }
+      if (hh == 0) *reinterpret_cast<uint32_t*>(a.qsc_out + row * 4) = w.qrun;
+    }
+  };
+  if constexpr (QROPE) {
+  } else if constexpr (BLOCK) {
     const uint32_t qs = *reinterpret_cast<const uint32_t*>(a.q_sc + (((int64_t)b * a.seq + tokc) * a.heads_q + hq) * 4);
     w.qsc = (int)(qs >> (8 * hh));
   } else {
@@ -548,6 +679,7 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   dma_k(tile_at(0), kbuf<0>(), wave, All{});
   dma_v(tile_at(0), vbuf<0>(), wave, All{});
   if (T > 1) dma_k(tile_at(1), kbuf<1>(), wave, All{});
+  if constexpr (QROPE) q_rope_codes();    // while the first tiles are in flight
   wait_dma_barrier();
   gemm_s_only<0, FOLD, BLOCK>(w, kop(P0{}, tile_at(0), 0), kop(P0{}, tile_at(0), 1));
   if (GROUP_A) softmax<true, FOLD>(w, c, valid_at(0), hh);
@@ -632,12 +764,12 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
 }
 
-template <bool FOLD, bool BLOCK>
+template <bool FOLD, bool BLOCK, bool QROPE>
 __global__ __launch_bounds__(THREADS) void fwd_fp8_kernel(Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true, FOLD, BLOCK>(a, lane, wave);
-  else wave_program<false, FOLD, BLOCK>(a, lane, wave);
+  if (wave < 4) wave_program<true, FOLD, BLOCK, QROPE>(a, lane, wave);
+  else wave_program<false, FOLD, BLOCK, QROPE>(a, lane, wave);
 }
 
 }  // namespace fp8k
@@ -658,11 +790,22 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   if (p->heads_q % p->heads_kv != 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: heads_q %% heads_kv != 0");
   if (p->heads_q > 4096) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: heads_q > 4096");
   if (!(p->scale == p->scale) || std::isinf(p->scale)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: scale is not finite");
-  // block scales (q_scales set: k_scales and each prefix's scales, no exponents) or one
-  // exponent per slice (no scales)
-  const bool block = p->q_scales != nullptr;
+  // q: codes (q8 with q_exp, or with q_scales) or, with q_rope, bf16 q rotated, folded and
+  // block-quantized on load; keys: block scales (k_scales and each prefix's scales) with
+  // q_scales or q_rope, one exponent per slice otherwise
+  const bool qrope = p->q_rope != nullptr;
+  const bool block = p->q_scales != nullptr || qrope;
+  if (qrope && (p->q8 || p->q_scales || p->q_exp))
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: q_rope takes bf16 q: q8, q_scales and q_exp must be NULL");
+  if (qrope && p->q_folded)
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: q_rope folds the softmax scale itself: q_folded must be 0");
+  if (!qrope && p->q) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: q given without q_rope");
+  if ((p->q8_out != nullptr) != (p->q_scales_out != nullptr) || (!qrope && p->q8_out))
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: q8_out and q_scales_out go together, with q_rope only");
+  if (p->q8_out && (!aligned16(p->q8_out) || (reinterpret_cast<uintptr_t>(p->q_scales_out) & 3u)))
+    return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: q8_out must be 16-byte and q_scales_out 4-byte aligned");
   if (block && (p->q_exp || p->k_exp || p->prefix_k_exp))
-    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: block scales (q_scales) exclude q_exp, k_exp and prefix_k_exp");
+    return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: block scales exclude q_exp, k_exp and prefix_k_exp");
   if (!block && p->k_scales) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: k_scales given without q_scales");
   bool any_prefix = false;
   for (int b = 0; b < p->batch; ++b) {
@@ -678,7 +821,7 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     any_prefix |= has;
   }
   if (p->batch == 0 || p->seq_q == 0) return NXATTN_OK;
-  if (!p->q8 || !p->k8 || !p->v || !p->o)
+  if (!(qrope ? p->q : p->q8) || !p->k8 || !p->v || !p->o)
     return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: NULL pointer");
   if (block ? !p->k_scales : (!p->q_exp || !p->k_exp || (any_prefix && !p->prefix_k_exp)))
     return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: NULL pointer (exponents or scales)");
@@ -698,8 +841,13 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     if ((p->v_strides[i] * 2) % 16 != 0 || (p->o_strides[i] * 2) % 16 != 0)
       return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
   }
-  if (!aligned16(p->q8) || !aligned16(p->k8) || !aligned16(p->v) || !aligned16(p->o))
-    return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: q8/k8/v/o must be 16-byte aligned");
+  if (!aligned16(qrope ? p->q : p->q8) || !aligned16(p->k8) || !aligned16(p->v) || !aligned16(p->o))
+    return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: q8 (or q)/k8/v/o must be 16-byte aligned");
+  if (qrope)
+    for (int i = 0; i < 3; ++i) {
+      if (p->q_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative stride");
+      if ((p->q_strides[i] * 2) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
+    }
   for (int b = 0; b < p->batch; ++b)
     if ((p->prefix_k8[b] && !aligned16(p->prefix_k8[b])) || (p->prefix_v[b] && !aligned16(p->prefix_v[b])))
       return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: prefix_k8[%d] / prefix_v[%d] misaligned", b, b);
@@ -709,8 +857,10 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   const int64_t ob = ((B - 1) * p->o_strides[0] + (S - 1) * p->o_strides[1] + (Hq - 1) * p->o_strides[2] + D) * 2;
   const int64_t vb = ((B - 1) * p->v_strides[0] + (S - 1) * p->v_strides[1] + (Hkv - 1) * p->v_strides[2] + D) * 2;
   const int64_t lb = p->lse ? B * Hq * S * 4 : 0;
+  const int64_t qb = qrope ? ((B - 1) * p->q_strides[0] + (S - 1) * p->q_strides[1] + (Hq - 1) * p->q_strides[2] + D) * 2
+                           : B * S * Hq * D;
   struct Span { const void* ptr; int64_t n; };
-  Span ins[8 + 3 * NXATTN_MAX_BRANCHES] = {{p->q8, B * S * Hq * D}, {p->k8, B * S * Hkv * D}, {p->v, vb},
+  Span ins[8 + 3 * NXATTN_MAX_BRANCHES] = {{qrope ? p->q : p->q8, qb}, {p->k8, B * S * Hkv * D}, {p->v, vb},
                                            {p->q_exp, B * Hq}, {p->k_exp, B * Hkv},
                                            {p->prefix_k_exp, any_prefix ? B * Hkv : 0},
                                            {p->q_scales, B * S * Hq * 4}, {p->k_scales, B * S * Hkv * 4}};
@@ -720,15 +870,31 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     ins[nin++] = Span{p->prefix_v[b], (int64_t)p->prefix_len[b] * Hkv * D * 2};
     ins[nin++] = Span{p->prefix_k_scales[b], (int64_t)p->prefix_len[b] * Hkv * 4};
   }
-  for (int i = 0; i < nin; ++i)
-    if (ins[i].ptr && (overlaps(p->o, ob, ins[i].ptr, ins[i].n) || (p->lse && overlaps(p->lse, lb, ins[i].ptr, ins[i].n))))
-      return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: o or lse overlaps an input");
-  if (p->lse && overlaps(p->lse, lb, p->o, ob)) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: lse overlaps o");
+  // outputs: o, lse and (with q_rope) the codes and scales formed on load
+  const Span outs[4] = {{p->o, ob}, {p->lse, lb}, {p->q8_out, p->q8_out ? B * S * Hq * D : 0},
+                        {p->q_scales_out, p->q_scales_out ? B * S * Hq * 4 : 0}};
+  for (int j = 0; j < 4; ++j) {
+    if (!outs[j].ptr) continue;
+    for (int i = 0; i < nin; ++i)
+      if (ins[i].ptr && overlaps(outs[j].ptr, outs[j].n, ins[i].ptr, ins[i].n))
+        return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: an output overlaps an input");
+    for (int i = j + 1; i < 4; ++i)
+      if (outs[i].ptr && overlaps(outs[j].ptr, outs[j].n, outs[i].ptr, outs[i].n))
+        return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: outputs overlap");
+  }
 
   Args a;
   a.q8 = p->q8; a.k8 = p->k8; a.v = static_cast<const uint16_t*>(p->v); a.o = static_cast<uint16_t*>(p->o);
   a.q_exp = p->q_exp; a.k_exp = p->k_exp; a.pk_exp = p->prefix_k_exp ? p->prefix_k_exp : p->k_exp;
   a.q_sc = p->q_scales; a.k_sc = p->k_scales;
+  a.q8_out = p->q8_out; a.qsc_out = p->q_scales_out;
+  a.q = static_cast<const uint16_t*>(p->q);
+  a.qs0 = p->q_strides[0]; a.qs1 = p->q_strides[1]; a.qs2 = p->q_strides[2];
+  std::memset(a.rq, 0, sizeof(a.rq));
+  if (qrope) {
+    const int st = rope_q_setup(p->q_rope, p->batch, p->seq_q, D, "nxattn_fwd_fp8 (q_rope)", a.rq);
+    if (st != NXATTN_OK) return st;
+  }
   a.vs0 = p->v_strides[0]; a.vs1 = p->v_strides[1]; a.vs2 = p->v_strides[2];
   a.os0 = p->o_strides[0]; a.os1 = p->o_strides[1]; a.os2 = p->o_strides[2];
   for (int b = 0; b < NXATTN_MAX_BRANCHES; ++b) {
@@ -749,16 +915,18 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   const float scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)D);
   a.c = scale * LOG2E;
   a.lse = p->lse;
-  if (block) {
+  if (qrope) {
+    fwd_fp8_kernel<true, true, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+  } else if (block) {
     if (p->q_folded)
-      fwd_fp8_kernel<true, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+      fwd_fp8_kernel<true, true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
     else
-      fwd_fp8_kernel<false, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+      fwd_fp8_kernel<false, true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
   } else {
     if (p->q_folded)
-      fwd_fp8_kernel<true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
+      fwd_fp8_kernel<true, false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
     else
-      fwd_fp8_kernel<false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
+      fwd_fp8_kernel<false, false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
   }
   return check_launch("nxattn_fwd_fp8");
 }

@@ -111,13 +111,17 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
                   int64_t seq, int64_t head_dim, const nxattn_rope_desc* rope, void* workspace,
                   int64_t workspace_bytes, hipStream_t stream);
 
-// RoPE of q applied on load by the fused attention kernel (axes beyond n_axes have grid
+// RoPE of q applied on load by the fused attention kernels (axes beyond n_axes have grid
 // 1, pairs 0, offset 0)
 struct RopeQ {
   int32_t n_axes, interleaved, global_freq;
   int32_t grid[3], pairs[3], offset[3];
   double log2_theta;
 };
+// Checks `batch` q_rope descriptors (check_rope_desc, and every position below 2^24: the
+// rotation on load holds positions as exact fp32 integers) and converts them into out[];
+// errors name `who`.
+int rope_q_setup(const nxattn_rope_desc* d, int batch, int64_t seq, int64_t head_dim, const char* who, RopeQ* out);
 
 // ---- launchers implemented per kernel file -------------------------------------------
 struct FwdProblem {

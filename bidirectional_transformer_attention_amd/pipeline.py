@@ -8,8 +8,9 @@
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
 With the fp8 score GEMM (``qk_fp8`` workloads) q and own k are rotated and quantized to
 E4M3 in one call before the attention call, with one scale per (branch, head) or, for
-``fp8_blocks`` workloads, one per run of 32 head_dim elements (then in a single pass and
-without a workspace). Each prefix K is quantized once, when the step is set up: the
+``fp8_blocks`` workloads, one per run of 32 head_dim elements (a single pass without a
+workspace). With ``q_on_load`` (block scales only) that call quantizes only k and the
+attention kernel rotates, folds and quantizes q as it loads it. Each prefix K is quantized once, when the step is set up: the
 injected conditioning cache is the same for every denoising step (NeoPP page, intro), so
 its codes are too.
 
@@ -29,7 +30,7 @@ from .synth import Inputs, Workload
 
 class AttentionStep:
     def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None,
-                 splits: Optional[int] = None, fold_q: bool = True):
+                 splits: Optional[int] = None, fold_q: bool = True, q_on_load: bool = False):
         self.wl = wl
         # fp8: q's codes carry softmax_scale*log2(e), so the attention's softmax takes one
         # exp2 per score with no multiply in front
@@ -69,16 +70,20 @@ class AttentionStep:
             n = nx.fwd_workspace_bytes(self.B, self.S, self.Hq, self.D, self.splits)
             self.workspace = torch.empty(n, dtype=torch.uint8, device=dev)
         self.blocks = wl.qk_fp8 and wl.fp8_blocks
+        # block scaling only: q rotated, folded and quantized by the attention kernel as it
+        # loads it (no q codes in memory) instead of by the quantize call
+        self.q_on_load = bool(q_on_load) and self.blocks
         if wl.qk_fp8:
             # E4M3 codes, their exponents (per (branch, head)) or block scales (per run of
             # 32 elements, E8M0 codes) and the quantizer's workspace, allocated once
-            self.q8 = torch.empty(self.q.shape, dtype=torch.uint8, device=dev)
+            self.q8 = None if self.q_on_load else torch.empty(self.q.shape, dtype=torch.uint8, device=dev)
             self.k8 = torch.empty(self.k.shape, dtype=torch.uint8, device=dev)
             self.pk8 = [None if p is None else torch.empty((1, p.shape[1], self.Hkv, self.D), dtype=torch.uint8,
                                                            device=dev) for p in self.prefix_online]
             if self.blocks:
                 nb = self.D // 32
-                self.qs = torch.empty((self.B, self.S, self.Hq, nb), dtype=torch.uint8, device=dev)
+                self.qs = None if self.q_on_load else torch.empty((self.B, self.S, self.Hq, nb), dtype=torch.uint8,
+                                                                  device=dev)
                 self.ks = torch.empty((self.B, self.S, self.Hkv, nb), dtype=torch.uint8, device=dev)
                 self.pks = [None if p is None else torch.empty((1, p.shape[1], self.Hkv, nb), dtype=torch.uint8,
                                                                device=dev) for p in self.prefix_online]
@@ -124,6 +129,9 @@ class AttentionStep:
         codes carry the softmax fold factor, which the library forms."""
         if not self.wl.qk_fp8:
             return
+        if self.q_on_load:
+            nx.nxattn_rope_quantize_fp8([self.k], self.descs, [self.k8], [self.ks], blocks=True)
+            return
         if self.blocks:
             nx.nxattn_rope_quantize_fp8([self.q, self.k], self.descs, [self.q8, self.k8], [self.qs, self.ks],
                                         folds=[self.fold_q, False], blocks=True)
@@ -132,6 +140,13 @@ class AttentionStep:
                                     folds=[self.fold_q, False])
 
     def attention(self) -> None:
+        if self.q_on_load:
+            nx.nxattn_fwd_fp8(None, self.k8, None, None, self.v, self.o,
+                              [None if p is None else p[0] for p in self.pk8],
+                              [None if p is None else p[1] for p in self.prefix_online],
+                              k_scales=self.ks, prefix_k_scales=[None if p is None else p[0] for p in self.pks],
+                              q=self.q, q_rope=self.descs)
+            return
         if self.blocks:
             nx.nxattn_fwd_fp8(self.q8, self.k8, None, None, self.v, self.o,
                               [None if p is None else p[0] for p in self.pk8],

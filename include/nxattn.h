@@ -365,8 +365,22 @@ int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors, int32_t n
  * times its two scales: s_j = scale * sum_r 2^(eq_r + ek_jr) <dec(q8_r), dec(k8_jr)>.
  * q_scales uint8 [batch, seq_q, heads_q, 4], k_scales uint8 [batch, seq_q, heads_kv, 4] and
  * prefix_k_scales[b] uint8 [P_b, heads_kv, 4] (non-NULL iff prefix_len[b] > 0), contiguous
- * and 4-byte aligned; q_exp, k_exp and prefix_k_exp must then be NULL. Without q_scales,
- * k_scales and every prefix_k_scales[b] must be NULL.
+ * and 4-byte aligned; q_exp, k_exp and prefix_k_exp must then be NULL. Without q_scales
+ * (or q_rope), k_scales and every prefix_k_scales[b] must be NULL.
+ *
+ * q rotated and quantized on load (q_rope != NULL, `batch` descriptors in host memory, as
+ * nxattn_fwd's q_rope, positions below 2^24): q is bf16 [batch, seq_q, heads_q, 128] with
+ * element strides q_strides {b, s, h} (multiples of 16 bytes, 16-byte aligned) and is only
+ * read. The kernel rotates each row with the turns of nxattn_fwd's q_rope, multiplies it
+ * by c = scale * log2(e) (both in fp32, with no bf16 rounding in between) and forms the
+ * codes and run scales of block scaling from those values in registers; the keys take
+ * block scales (k_scales, prefix_k_scales). q8, q_scales and q_exp must be NULL and
+ * q_folded 0 (the fold is implied). Without q_rope, q must be NULL. Optionally (both
+ * non-NULL or both NULL, with q_rope only) the kernel also writes the codes it formed to
+ * q8_out (uint8 [batch, seq_q, heads_q, 128] contiguous, 16-byte aligned) and the run
+ * scales to q_scales_out (uint8 E8M0 [batch, seq_q, heads_q, 4], 4-byte aligned), as
+ * nxattn_fwd_fp8 with q_scales would take them. No output may overlap an input or another
+ * output.
  */
 typedef struct {
   int32_t batch;
@@ -392,6 +406,11 @@ typedef struct {
   const uint8_t* q_scales;                            /* block scales, see above */
   const uint8_t* k_scales;
   const uint8_t* prefix_k_scales[NXATTN_MAX_BRANCHES];
+  const void* q;                                      /* q_rope: bf16 q, see above */
+  int64_t q_strides[3];
+  const nxattn_rope_desc* q_rope;
+  uint8_t* q8_out;                                    /* q_rope, optional: codes formed on load */
+  uint8_t* q_scales_out;
 } nxattn_fwd_fp8_args;
 
 int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* args, hipStream_t stream);

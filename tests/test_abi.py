@@ -412,6 +412,47 @@ def test_fwd_fp8_rejects(lib, kw, code):
     assert nx.last_error() != ""
 
 
+def test_fwd_fp8_q_on_load_rejects(lib):
+    # q rotated, folded and block-quantized on load: bf16 q + q_rope instead of q8 and its
+    # exponents; the keys take block scales
+    descs = (binding.RopeDesc * 2)(*[nx.rope_desc((64,), (64,), (b,)) for b in range(2)])
+    Q = FAKE + 9 * GB
+
+    def call(**kw):
+        base = dict(q8=None, q_exp=None, k_exp=None, k_scales=FAKE + 8 * GB, q=Q)
+        base.update(kw)
+        a = fp8_args(**{k: v for k, v in base.items() if k not in ("q_strides", "rope")})
+        for i, st in enumerate(base.get("q_strides", (64 * 8 * 128, 8 * 128, 128))):
+            a.q_strides[i] = st
+        a.q_rope = ctypes.cast(base.get("rope", descs), ctypes.POINTER(binding.RopeDesc))
+        return lib.nxattn_fwd_fp8(ctypes.byref(a), None)
+    assert call(q8=FAKE) == INVALID                                   # q8 as well
+    assert call(q_scales=FAKE + 7 * GB) == INVALID                    # q's scales are formed in the kernel
+    assert call(q_folded=1) == INVALID                                # the fold is implied
+    assert call(k_scales=None, k_exp=FAKE + 3 * GB + 4096) == INVALID  # keys need block scales
+    assert call(q=None) == INVALID
+    assert call(q=Q + 8) == ALIGN
+    assert call(q_strides=(64 * 8 * 128, 8 * 128 + 4, 128)) == ALIGN
+    far = (binding.RopeDesc * 2)(*[nx.rope_desc((64,), (64,), ((1 << 24) - 10,)) for _ in range(2)])
+    assert call(rope=far) == UNSUPPORTED                              # positions reach 2^24
+    assert b"2^24" in lib.nxattn_last_error()
+    bad = (binding.RopeDesc * 2)(*[nx.rope_desc((63,), (64,), (0,)) for _ in range(2)])
+    assert call(rope=bad) == INVALID                                  # grid product != seq_q
+    assert call(o=Q) == INVALID                                       # o overlaps q
+    # the optional copies of the codes and scales formed on load: both or neither, with
+    # q_rope only, aligned, overlapping nothing
+    assert call(q8_out=FAKE + 10 * GB) == INVALID
+    assert call(q8_out=FAKE + 10 * GB + 8, q_scales_out=FAKE + 11 * GB) == ALIGN
+    assert call(q8_out=FAKE + 10 * GB, q_scales_out=FAKE + 11 * GB + 2) == ALIGN
+    assert call(q8_out=Q, q_scales_out=FAKE + 11 * GB) == INVALID      # overlaps q
+    assert call(q8_out=FAKE + 10 * GB, q_scales_out=FAKE + 10 * GB + 64) == INVALID   # overlap each other
+    # q without q_rope; codes out without q_rope
+    a = fp8_args(q=Q)
+    assert lib.nxattn_fwd_fp8(ctypes.byref(a), None) == INVALID
+    a = fp8_args(q8_out=FAKE + 10 * GB, q_scales_out=FAKE + 11 * GB)
+    assert lib.nxattn_fwd_fp8(ctypes.byref(a), None) == INVALID
+
+
 def test_fwd_null_args(lib):
     assert lib.nxattn_fwd(None, None) == INVALID
 

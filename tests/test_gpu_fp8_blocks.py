@@ -228,3 +228,122 @@ def test_fwd_fp8_blocks_deterministic():
         torch.cuda.synchronize()
         outs.append((o.cpu(), ls.cpu()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def qload_case(B, S, Hq, Hkv, P, seed, grid=None, pairs=(64,), offsets=None, inter=False, gf=False, span=2,
+               q_view=False):
+    """nxattn_fwd_fp8 with q rotated, folded and block-quantized on load (keys
+    block-quantized without RoPE), checked two ways:
+    - isolated: the codes and run scales the kernel formed (q8_out, q_scales_out) are
+      dequantized by the oracle, and the output and lse are held to the oracle's attention
+      of them (output at the bf16 gate, lse at its own tolerance);
+    - the oracle chain: fp64 RoPE of q times the fold factor, block quantization; the
+      kernel's codes are compared with the chain's (the kernel rotates in fp32, so a value
+      within a few fp32 ulps of a rounding boundary may take the neighbouring code: counted,
+      and held to a handful), and the output is held to the bf16 gate against the attention
+      of the chain's codes."""
+    D = 128
+    grid = grid or (S,)
+    offsets = offsets or [tuple(5 * b + a for a in range(len(grid))) for b in range(B)]
+    note(f"fwd fp8 q on load B={B} S={S} Hq={Hq} Hkv={Hkv} P={P} grid={grid} pairs={pairs} inter={inter} "
+         f"gf={gf} offsets={offsets[0]} seed={seed}")
+    if q_view:
+        qfull = graded((B, S, Hq + 2, D), seed, span)
+        q = qfull[:, :, 1:Hq + 1, :]
+    else:
+        q = graded((B, S, Hq, D), seed, span)
+    k = graded((B, S, Hkv, D), seed + 1, span)
+    v = synth.random_tensor((B, S, Hkv, D), seed + 2, torch.bfloat16)
+    pk = [graded((p, Hkv, D), seed + 3 + b, span) if p else None for b, p in enumerate(P)]
+    pv = [synth.random_tensor((p, Hkv, D), seed + 13 + b, torch.bfloat16) if p else None for b, p in enumerate(P)]
+    descs = [nx.rope_desc(grid, pairs, offsets[b], 10000.0, inter, gf) for b in range(B)]
+    qd = (qfull.to(DEV)[:, :, 1:Hq + 1, :] if q_view else q.to(DEV))
+    q_before = qd.clone()
+    k8, ks = nx.nxattn_quantize_fp8_blocks(k.to(DEV))
+    pk8, pks = [], []
+    for b in range(B):
+        if pk[b] is None:
+            pk8.append(None)
+            pks.append(None)
+            continue
+        c, s_ = nx.nxattn_quantize_fp8_blocks(pk[b].to(DEV)[None])
+        pk8.append(c[0])
+        pks.append(s_[0])
+    o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+    ls = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    q8o = torch.full((B, S, Hq, D), 0x7F, dtype=torch.uint8, device=DEV)
+    qso = torch.full((B, S, Hq, D // 32), 0xFF, dtype=torch.uint8, device=DEV)
+    nx.nxattn_fwd_fp8(None, k8, None, None, v.to(DEV), o, pk8, [t.to(DEV) if t is not None else None for t in pv],
+                      lse=ls, k_scales=ks, prefix_k_scales=pks, q=qd, q_rope=descs, q8_out=q8o, q_scales_out=qso)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.view(torch.int16).cpu(), q_before.view(torch.int16).cpu())   # q is only read
+    cf = float(fold_factor(D))
+    dk = ofp8.dequantize_fp8_blocks(*ofp8.quantize_fp8_blocks(f64(k)))
+    kc, kcs = q8o.cpu().numpy(), qso.cpu().numpy()
+    worst_iso = worst_ch = 0.0
+    n_code = n_scale = 0
+    for b in range(B):
+        qr = oracle.rope(f64(q[b]), grid, pairs, offsets[b], 10000.0, interleaved=inter, global_freq=gf) * cf
+        cc, cs = ofp8.quantize_fp8_blocks(qr)
+        n_code += int(np.count_nonzero(cc != kc[b]))
+        n_scale += int(np.count_nonzero(cs != kcs[b]))
+        dpk = None
+        if pk[b] is not None:
+            dpk = ofp8.dequantize_fp8_blocks(*ofp8.quantize_fp8_blocks(f64(pk[b])))
+        rest = (dk[b], f64(v[b]), dpk, f64(pv[b]) if pv[b] is not None else None)
+        g = f64(o.cpu()[b])
+        iso = (ofp8.dequantize_fp8_blocks(kc[b], kcs[b]) / cf,) + rest
+        err_iso = attention_err(g, oracle.attention(*iso))
+        err_ch = attention_err(g, oracle.attention(ofp8.dequantize_fp8_blocks(cc, cs) / cf, *rest))
+        worst_iso, worst_ch = max(worst_iso, err_iso), max(worst_ch, err_ch)
+        assert err_iso <= TOL["bf16"], (b, err_iso)
+        assert err_ch <= TOL["bf16"], (b, err_ch)
+        rl = oracle.attention_lse(*iso)
+        assert lse_err_ok(f64(ls.cpu()[b]), rl), (b, float(np.max(np.abs(f64(ls.cpu()[b]) - rl))))
+    total = B * S * Hq * D
+    note(f"  worst branch error {worst_iso:.3e} against the kernel's own codes, {worst_ch:.3e} against the oracle "
+         f"chain (gate {TOL['bf16']:.0e}); codes differing from the chain's: {n_code} of {total}, run scales "
+         f"{n_scale} of {total // 32}")
+    assert n_code <= max(8, total // 10000) and n_scale <= max(2, total // 320000)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,P", [
+    (2, 300, 8, 2, (37, 0)),
+    (1, 1, 8, 1, (200,)),
+    (2, 200, 4, 2, (300, 7)),
+    (1, 129, 4, 4, (0,)),
+])
+def test_fwd_fp8_q_on_load_reduced(B, S, Hq, Hkv, P):
+    qload_case(B, S, Hq, Hkv, P, 5800 + S)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(grid=(12, 25), pairs=(32, 32)),                         # 2-D, two sections
+    dict(grid=(3, 10, 10), pairs=(16, 24, 24), inter=True),      # 3-D, adjacent pairs
+    dict(grid=(10, 30), pairs=(32, 32), gf=True),                # one global ladder over both axes
+    dict(grid=(300,), pairs=(64,), offsets=[((1 << 24) - 300,), ((1 << 23) + 7,)]),   # positions near 2^24
+    dict(grid=(300,), pairs=(64,), q_view=True),                 # q as a strided view
+])
+def test_fwd_fp8_q_on_load_rope_forms(kw):
+    qload_case(2, 300, 8, 2, (40, 0), 5900, **kw)
+
+
+def test_fwd_fp8_q_on_load_deterministic():
+    note("fwd fp8 q on load determinism")
+    B, S, Hq, Hkv, D, P = 2, 300, 8, 2, 128, 99
+    q = graded((B, S, Hq, D), 6000, 2).to(DEV)
+    k = graded((B, S, Hkv, D), 6001, 2).to(DEV)
+    v = synth.random_tensor((B, S, Hkv, D), 6002, torch.bfloat16).to(DEV)
+    pk = graded((1, P, Hkv, D), 6003, 2).to(DEV)
+    pv = synth.random_tensor((P, Hkv, D), 6004, torch.bfloat16).to(DEV)
+    descs = [nx.rope_desc((S,), (64,), (7 * b,)) for b in range(B)]
+    [(k8, ks)] = nx.nxattn_rope_quantize_fp8([k], descs, blocks=True)
+    pk8, pks = nx.nxattn_quantize_fp8_blocks(pk)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+        nx.nxattn_fwd_fp8(None, k8, None, None, v, o, [pk8[0], None], [pv, None], k_scales=ks,
+                          prefix_k_scales=[pks[0], None], q=q, q_rope=descs)
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.equal(outs[0], outs[1])

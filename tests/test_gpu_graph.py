@@ -29,11 +29,12 @@ def bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-@pytest.mark.parametrize("name", ["dit1k_bf16", "dit1k_fp8qk", "dit1k_fp8blk", "longctx_bf16"])
-def test_step_graph_replays_match_eager(name):
+@pytest.mark.parametrize("name,q_on_load", [("dit1k_bf16", False), ("dit1k_fp8qk", False), ("dit1k_fp8blk", False),
+                                             ("dit1k_fp8blk", True), ("longctx_bf16", False)])
+def test_step_graph_replays_match_eager(name, q_on_load):
     wl = synth.bench_workload(name)
-    note(f"step graph {wl.name}: replays against the eager step")
-    step = AttentionStep(wl, synth.make_inputs(wl))
+    note(f"step graph {wl.name}{' (q quantized on load)' if q_on_load else ''}: replays against the eager step")
+    step = AttentionStep(wl, synth.make_inputs(wl), q_on_load=q_on_load)
     q0, k0 = step.q.clone(), step.k.clone()
     out = step()                                   # eager
     torch.cuda.synchronize()

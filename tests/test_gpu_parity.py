@@ -606,66 +606,89 @@ def test_step_dit1k_bf16_sampled():
     step_case("dit1k_bf16", 96, 3)
 
 
-@pytest.mark.parametrize("name", ["dit1k_fp8qk+replay", "dit2k_fp8qk", "dit1k_fp8blk+replay", "dit2k_fp8blk"])
-def test_step_fp8qk_sampled(name):
+@pytest.mark.parametrize("name,q_on_load", [("dit1k_fp8qk+replay", False), ("dit2k_fp8qk", False),
+                                             ("dit1k_fp8blk+replay", False), ("dit2k_fp8blk", False),
+                                             ("dit1k_fp8blk+replay", True)])
+def test_step_fp8qk_sampled(name, q_on_load):
     """The bench configuration of the fp8 score GEMM at full size, with one scale per
-    (branch, head) (fp8qk) or per run of 32 head_dim elements (fp8blk).
+    (branch, head) (fp8qk) or per run of 32 head_dim elements (fp8blk; with q_on_load the
+    attention kernel rotates, folds and quantizes q itself as it loads it, so q has no
+    stored codes).
 
-    1. Isolation: the codes of the step's q and k as nxattn_rope_apply rotates them (q
-       times the softmax fold factor), and of each prefix K, bit for bit against the
-       oracle's quantization; sampled rows of the attention against the oracle's
-       attention of those dequantized codes.
-    2. The oracle chain alone: the oracle's fp64 RoPE rounded to bf16 (as a stored
-       rotation), q times the fold factor in fp32, the oracle's quantization; the GPU
-       attention against the oracle's attention of that chain's dequantized codes, at the
-       bf16 gate. Codes that differ from the chain's (a bf16 rounding of the rotation
+    1. Isolation: the codes of the step's k (and, fp8qk, q) as nxattn_rope_apply rotates
+       them (q times the softmax fold factor), and of each prefix K, bit for bit against
+       the oracle's quantization; sampled rows of the attention against the oracle's
+       attention of those dequantized codes (fp8blk: with the chain's q below).
+    2. The oracle chain alone: the oracle's fp64 RoPE, rounded to bf16 where the path
+       stores a rotation (k; q of fp8qk), q times the fold factor, the oracle's
+       quantization; the GPU attention against the oracle's attention of that chain's
+       dequantized codes, at the bf16 gate. Codes that differ from the chain's (a rounding
        that falls the other way) are counted and printed.
     3. The recipe's own error, printed and not gated: the GPU attention against the
        exact oracle attention of the unquantized inputs.
     """
     from oracle import fp8 as ofp8
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else synth.bench_workload(name.split("+")[0])
-    note(f"step {name} (fp8 score GEMM, sampled rows)")
+    note(f"step {name} (fp8 score GEMM{', q quantized on load' if q_on_load else ''}, sampled rows)")
     inp = synth.make_inputs(wl)
-    step = AttentionStep(wl, inp)
+    step = AttentionStep(wl, inp, q_on_load=q_on_load)
     step()
     torch.cuda.synchronize()
-    # the step rotates inside the quantizer and leaves q and k as given
+    # the step rotates inside the quantizer (and the attention kernel) and leaves q and k as given
     assert torch.equal(step.q.cpu().view(torch.int16), inp.q.view(torch.int16))
     assert torch.equal(step.k.cpu().view(torch.int16), inp.k.view(torch.int16))
     assert step.fold_q
     cf = fold_factor(wl.head_dim)
-    if wl.fp8_blocks:
+    qload = step.q_on_load
+    if qload:
+        quant, deq = ofp8.quantize_fp8_blocks, ofp8.dequantize_fp8_blocks
+        k8, ke = (t.cpu().numpy() for t in (step.k8, step.ks))
+    elif wl.fp8_blocks:
         quant, deq = ofp8.quantize_fp8_blocks, ofp8.dequantize_fp8_blocks
         q8, qe, k8, ke = (t.cpu().numpy() for t in (step.q8, step.qs, step.k8, step.ks))
     else:
         quant, deq = ofp8.quantize_fp8, ofp8.dequantize_fp8
         q8, qe, k8, ke = (t.cpu().numpy() for t in (step.q8, step.qe, step.k8, step.ke))
     o = step.o.cpu()
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    # 2. the oracle chain (q first: fp8blk's isolated reference takes the chain's q)
+    if qload:
+        q_chain = np.stack([oracle_rope(wl, inp.q, b) for b in range(wl.branches)]) * float(cf)
+        cq, cqe = quant(q_chain)
+    else:
+        q_chain = torch.stack([bf(oracle_rope(wl, inp.q, b)) for b in range(wl.branches)])
+        cq, cqe = quant(f64(q_chain.float() * torch.tensor(cf, dtype=torch.float32)))
+    del q_chain
+    dq_ch = deq(cq, cqe) / cf
+    k_chain = torch.stack([bf(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)])
+    ck, cke = quant(f64(k_chain))
+    del k_chain
+    dk_ch = deq(ck, cke)
     # 1. isolation
-    qr, kr = step.q.clone(), step.k.clone()
-    nx.nxattn_rope_apply(qr, step.descs)
+    kr = step.k.clone()
     nx.nxattn_rope_apply(kr, step.descs)
     torch.cuda.synchronize()
-    rq, rqe = quant(f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32)))
     rk, rke = quant(f64(kr.cpu()))
-    del qr, kr
-    assert np.array_equal(q8, rq) and np.array_equal(qe, rqe)
+    del kr
     assert np.array_equal(k8, rk) and np.array_equal(ke, rke)
-    dq_iso, dk_iso = deq(rq, rqe) / cf, deq(rk, rke)
-    del rq, rk
-    # 2. the oracle chain
-    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
-    q_chain = torch.stack([bf(oracle_rope(wl, inp.q, b)) for b in range(wl.branches)])
-    k_chain = torch.stack([bf(oracle_rope(wl, inp.k, b)) for b in range(wl.branches)])
-    cq, cqe = quant(f64(q_chain.float() * torch.tensor(cf, dtype=torch.float32)))
-    ck, cke = quant(f64(k_chain))
-    del q_chain, k_chain
-    nq, nk = int(np.count_nonzero(q8 != cq)), int(np.count_nonzero(k8 != ck))
-    note(f"  codes that differ from the oracle chain's: q {nq} of {q8.size}, k {nk} of {k8.size}; "
-         f"exponents differing: q {int(np.count_nonzero(qe != cqe))}, k {int(np.count_nonzero(ke != cke))}")
-    dq_ch, dk_ch = deq(cq, cqe) / cf, deq(ck, cke)
-    del cq, ck
+    dk_iso = deq(rk, rke)
+    if qload:
+        dq_iso = dq_ch
+        msg_q = "q formed in the kernel"
+    else:
+        qr = step.q.clone()
+        nx.nxattn_rope_apply(qr, step.descs)
+        torch.cuda.synchronize()
+        rq, rqe = quant(f64(qr.cpu().float() * torch.tensor(cf, dtype=torch.float32)))
+        del qr
+        assert np.array_equal(q8, rq) and np.array_equal(qe, rqe)
+        dq_iso = deq(rq, rqe) / cf
+        msg_q = (f"q {int(np.count_nonzero(q8 != cq))} of {q8.size} (exponents "
+                 f"{int(np.count_nonzero(qe != cqe))})")
+        del rq
+    note(f"  codes that differ from the oracle chain's: {msg_q}, k {int(np.count_nonzero(k8 != ck))} of {k8.size} "
+         f"(exponents {int(np.count_nonzero(ke != cke))})")
+    del cq, ck, rk
     for b in range(wl.branches):
         pre = step.prefix_online[b]
         dpk = pv = pk_ex = None
