@@ -60,6 +60,21 @@ def traffic_record():
     return rec
 
 
+def bf16_kernel_name(step) -> str:
+    """The bf16 attention kernel a step launches: q rotated on load, and both CFG branches
+    per workgroup (guidance combination in the epilogue)."""
+    return (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}, "
+            f"{'true' if step.fuse_cfg else 'false'}>")
+
+
+def fp8_kernel_name(step) -> str:
+    """The fp8 attention kernel a step launches (softmax fold, block scales, q quantized on
+    load, both CFG branches per workgroup)."""
+    t = lambda x: "true" if x else "false"  # noqa: E731
+    return (f"nx::fp8k::fwd_fp8_kernel<{t(step.fold_q or step.q_on_load)}, {t(step.blocks)}, {t(step.q_on_load)}, "
+            f"{t(step.fuse_cfg)}>")
+
+
 def time_call(fn, stream, reps: int = 20) -> float:
     """Average GPU milliseconds of fn() (which enqueues work on `stream`): HIP events around
     reps calls that were all enqueued behind a spin kernel, so the GPU runs them back to back
@@ -252,8 +267,10 @@ def main() -> int:
     # a step of a multi-layer workload (the 27-layer ViT encoder) runs every layer, each
     # on its own seeded inputs
     layers = wl.layers
-    steps_all = [AttentionStep(wl, synth.make_inputs(wl, layer=l), "cuda:0", splits=args.splits)
-                 for l in range(layers)]
+    # the production step: with CFG on the bf16 path the attention call writes the guided
+    # output itself and the two branch outputs are not stored
+    steps_all = [AttentionStep(wl, synth.make_inputs(wl, layer=l), "cuda:0", splits=args.splits,
+                               keep_branches=False) for l in range(layers)]
     step = steps_all[0]
     flops_step = wl.flops() * layers
     def fp8_block():
@@ -262,7 +279,7 @@ def main() -> int:
         if args.fp8_steps <= 0 or wl.name.split("+")[0] != "dit1k_bf16":
             return None
         fwl = synth.bench_workload(FP8_WORKLOAD)
-        fstep = AttentionStep(fwl, synth.make_inputs(fwl), "cuda:0")
+        fstep = AttentionStep(fwl, synth.make_inputs(fwl), "cuda:0", keep_branches=False)
         # its own buffers are fresh: at least 30 untimed steps before timing
         fw = max(args.warmup, 30)
         f_ms, f_fwd, f_min = time_step(fstep, args.fp8_steps, fw, torch)
@@ -273,7 +290,7 @@ def main() -> int:
                 "dtype": "fp8e4m3 QK (E8M0 scale per 32 elements) / bf16 PV",
                 "ms_per_step": round(f_ms, 4), "step_tflops": round(ffl / f_ms / 1e9, 1),
                 "speedup_vs_bf16_step": None,
-                "kernel": "nx::fp8k::fwd_fp8_kernel<true, true, false>", "kernel_ms_avg": round(f_fwd, 4),
+                "kernel": fp8_kernel_name(fstep), "kernel_ms_avg": round(f_fwd, 4),
                 "kernel_ms_min": round(f_min, 4), "kernel_tflops": round(ffl / f_fwd / 1e9, 1),
                 "kernel_frac_of_fp8qk_peak": round(ffl / f_fwd / 1e9 / PEAK_FP8QK, 4)}
 
@@ -283,7 +300,7 @@ def main() -> int:
         if args.gate_steps <= 0 or wl.name == GATE_WORKLOAD:
             return None
         gwl = synth.bench_workload(GATE_WORKLOAD)
-        gstep = AttentionStep(gwl, synth.make_inputs(gwl), "cuda:0")
+        gstep = AttentionStep(gwl, synth.make_inputs(gwl), "cuda:0", keep_branches=False)
         g_ms, g_fwd, g_min = time_step(gstep, args.gate_steps, GATE_WARMUP, torch)
         if args.graph:
             g_ms = time_graph(capture_steps([gstep]), args.gate_steps, GATE_WARMUP, torch)
@@ -292,7 +309,7 @@ def main() -> int:
                 "gflop_per_step": round(gfl / 1e9, 1),
                 "ms_per_step": round(g_ms, 4), "step_tflops": round(gfl / g_ms / 1e9, 1),
                 "step_frac": round(gfl / g_ms / 1e9 / PEAK["bf16"], 4),
-                "kernel": "nx::bf16k::fwd_bf16_kernel<true>", "kernel_ms_avg": round(g_fwd, 4),
+                "kernel": bf16_kernel_name(gstep), "kernel_ms_avg": round(g_fwd, 4),
                 "kernel_ms_min": round(g_min, 4), "kernel_tflops": round(gfl / g_fwd / 1e9, 1),
                 "kernel_frac": round(gfl / g_fwd / 1e9 / PEAK["bf16"], 4), "gate_frac": 0.5,
                 "gate_ms": round(gfl / (0.5 * PEAK["bf16"]) / 1e9, 4)}
@@ -350,7 +367,7 @@ def main() -> int:
         "relayout": sum(2 * 2 * p * wl.heads_kv * wl.head_dim * es for p in wl.prefix_len)
         if wl.prefix_layout == "replay" else 0,
         "rope": 0 if wl.qk_fp8 else 2 * step.k.numel() * es + (0 if step.fuse_q_rope else 2 * step.q.numel() * es),
-        "cfg": 3 * step.q[0].numel() * es if step.use_cfg else 0,
+        "cfg": 3 * step.q[0].numel() * es if step.use_cfg and not step.fuse_cfg else 0,
         # per (branch, head): reads q and k twice (rotated inside both passes: maximum, then
         # codes), writes one byte per element; block scales: one read, the codes and one
         # scale byte per 32 elements (the prefix K is quantized once, outside the step)
@@ -365,14 +382,14 @@ def main() -> int:
         gbs = nbytes[name] / (ms * 1e-3) / 1e9
         side[name] = {"us": round(1000 * ms, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
                       "frac_of_hbm": round(gbs / HBM_PEAK, 4)}
+    if step.fuse_cfg:
+        side["cfg"] = "inside the attention call"
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
                         and not wl.qk_fp8 else None),
-            "kernel": (f"nx::fp8k::fwd_fp8_kernel<{'true' if step.fold_q else 'false'}, "
-                       f"{'true' if wl.fp8_blocks else 'false'}, false>" if wl.qk_fp8 else
-                       (f"nx::bf16k::fwd_bf16_kernel<{'true' if step.fuse_q_rope else 'false'}>")
-                       if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
+            "kernel": (fp8_kernel_name(step) if wl.qk_fp8 else
+                       bf16_kernel_name(step) if wl.dtype == "bf16" else f"nx::f32k::fwd_f32_kernel<{wl.head_dim}>")
             + (" + nx::mergek::merge_kernel" if step.splits > 1 else ""),
             "kernel_ms_avg": round(fwd_avg, 4), "kernel_ms_min": round(fwd_min, 4)}
     if layers > 1:
@@ -421,7 +438,8 @@ def main() -> int:
                                  "(prefix K codes made once per conditioning cache)"
                             if wl.qk_fp8 else "relayout + rope(q,k) + fused attention")
                    + (f" over {step.splits} key ranges + merge" if step.splits > 1 else "")
-                   + (" + cfg" if step.use_cfg else "") + (f", x {layers} layers" if layers > 1 else ""),
+                   + ((" with the cfg combine in its epilogue (branch outputs not stored)" if step.fuse_cfg
+                       else " + cfg") if step.use_cfg else "") + (f", x {layers} layers" if layers > 1 else ""),
                    "pct_of_bf16_peak_step": round(100 * value / PEAK[wl.dtype], 2)},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -59,7 +59,8 @@ class FwdArgs(ctypes.Structure):
                 ("prefix_kv", ctypes.c_void_p * MAX_BRANCHES), ("prefix_len", ctypes.c_int32 * MAX_BRANCHES),
                 ("scale", ctypes.c_float), ("q_rope", ctypes.POINTER(RopeDesc)),
                 ("lse", ctypes.c_void_p), ("prefix_only", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+                ("cfg_out", ctypes.c_void_p), ("cfg_strides", ctypes.c_int64 * 2), ("guidance", ctypes.c_float)]
 
 
 class FwdFp8Args(ctypes.Structure):
@@ -74,7 +75,8 @@ class FwdFp8Args(ctypes.Structure):
                 ("q_scales", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
                 ("prefix_k_scales", ctypes.c_void_p * MAX_BRANCHES),
                 ("q", ctypes.c_void_p), ("q_strides", ctypes.c_int64 * 3), ("q_rope", ctypes.POINTER(RopeDesc)),
-                ("q8_out", ctypes.c_void_p), ("q_scales_out", ctypes.c_void_p)]
+                ("q8_out", ctypes.c_void_p), ("q_scales_out", ctypes.c_void_p),
+                ("cfg_out", ctypes.c_void_p), ("cfg_strides", ctypes.c_int64 * 2), ("guidance", ctypes.c_float)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -214,26 +216,28 @@ def nxattn_rope_apply(x: torch.Tensor, descs: List[RopeDesc], stream=None) -> No
     _check(load().nxattn_rope_apply(x.data_ptr(), B, S, H, D, st, _dtype_code(x), arr, _stream(stream)))
 
 
-def make_fwd_args(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: torch.Tensor,
+def make_fwd_args(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: Optional[torch.Tensor],
                   prefix: Sequence[Optional[torch.Tensor]], scale: float = 0.0,
                   q_rope: Optional[Sequence[RopeDesc]] = None, lse: Optional[torch.Tensor] = None,
                   prefix_only: bool = False, num_splits: int = 0,
-                  workspace: Optional[torch.Tensor] = None) -> FwdArgs:
+                  workspace: Optional[torch.Tensor] = None, cfg_out: Optional[torch.Tensor] = None,
+                  guidance: float = 0.0) -> FwdArgs:
     """FwdArgs for the tensors; q_rope (one RopeDesc per batch entry) is kept alive on
     the returned object for as long as it is in use. k and v may be None with
-    prefix_only (heads_kv then comes from the first prefix)."""
+    prefix_only (heads_kv then comes from the first prefix); o may be None with cfg_out."""
     B, S, Hq, D = q.shape
     a = FwdArgs()
     a.dtype = _dtype_code(q)
     hkv = k.shape[2] if k is not None else next(p.shape[2] for p in prefix if p is not None)
     a.batch, a.seq_q, a.heads_q, a.heads_kv, a.head_dim = B, S, Hq, hkv, D
-    a.q, a.o = q.data_ptr(), o.data_ptr()
+    a.q = q.data_ptr()
+    a.o = o.data_ptr() if o is not None else None
     a.k = k.data_ptr() if k is not None else None
     a.v = v.data_ptr() if v is not None else None
     for i in range(3):
         a.q_strides[i] = q.stride(i)
         a.kv_strides[i] = k.stride(i) if k is not None else 0
-        a.o_strides[i] = o.stride(i)
+        a.o_strides[i] = o.stride(i) if o is not None else 0
     for b in range(MAX_BRANCHES):
         p = prefix[b] if b < len(prefix) else None
         if p is None or p.numel() == 0:
@@ -253,6 +257,10 @@ def make_fwd_args(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if cfg_out is not None:
+        a.cfg_out = cfg_out.data_ptr()
+        a.cfg_strides[0], a.cfg_strides[1] = cfg_out.stride(0), cfg_out.stride(1)
+        a.guidance = float(guidance)
     return a
 
 
@@ -265,11 +273,12 @@ def fwd_workspace_bytes(batch: int, seq_q: int, heads_q: int, head_dim: int, num
     return int(n.value)
 
 
-def nxattn_fwd(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: torch.Tensor,
+def nxattn_fwd(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: Optional[torch.Tensor],
                prefix: Sequence[Optional[torch.Tensor]] = (), scale: float = 0.0, stream=None,
                q_rope: Optional[Sequence[RopeDesc]] = None, lse: Optional[torch.Tensor] = None,
                prefix_only: bool = False, num_splits: int = 0,
-               workspace: Optional[torch.Tensor] = None) -> None:
+               workspace: Optional[torch.Tensor] = None, cfg_out: Optional[torch.Tensor] = None,
+               guidance: float = 0.0) -> None:
     """o = attention(q, [prefix_k ++ k], [prefix_v ++ v]) for every branch.
 
     q, o [B,S,Hq,D]; k, v [B,S,Hkv,D] (same strides); prefix[b] contiguous [2,P_b,Hkv,D] or None.
@@ -280,19 +289,27 @@ def nxattn_fwd(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Ten
     num_splits > 1: split every branch's keys into that many ranges merged by a second
     kernel; workspace is a device tensor of at least fwd_workspace_bytes() bytes (one is
     allocated with torch when None).
+    cfg_out: None, or a [S, Hq, D] tensor of q's dtype (last dim contiguous) that receives
+    the guidance combination of the two branches (batch 2: branch 0 cond, 1 uncond),
+    computed by the attention kernel; o may then be None (branch outputs not stored).
     """
     own = [t for t in (k, v) if t is not None]
-    _gpu(q, o, *own, lse, workspace, *[p for p in prefix if p is not None])
+    _gpu(q, o, *own, lse, workspace, cfg_out, *[p for p in prefix if p is not None])
+    if o is None and cfg_out is None:
+        raise NxattnError(1, "o is required unless cfg_out is given")
+    if cfg_out is not None and (cfg_out.dim() != 3 or tuple(cfg_out.shape) != (q.shape[1], q.shape[2], q.shape[3])
+                                or cfg_out.stride(2) != 1 or cfg_out.dtype != q.dtype):
+        raise NxattnError(1, "cfg_out must be [S, Hq, D] of q's dtype with a contiguous last dim")
     if not prefix_only and len(own) != 2:
         raise NxattnError(1, "k and v are required unless prefix_only")
-    if q.dim() != 4 or o.dim() != 4 or any(t.dim() != 4 for t in own):
+    if q.dim() != 4 or (o is not None and o.dim() != 4) or any(t.dim() != 4 for t in own):
         raise NxattnError(1, "q, k, v, o must be 4-D [B, S, H, D]")
     if len(own) == 2 and (k.shape != v.shape or k.stride() != v.stride()):
         raise NxattnError(1, "k and v must have the same shape and strides")
     if len(own) == 1:
         raise NxattnError(1, "give both k and v, or neither")
-    if o.shape != q.shape or any(q.shape[0] != t.shape[0] or q.shape[1] != t.shape[1] or q.shape[3] != t.shape[3]
-                                 for t in own):
+    if (o is not None and o.shape != q.shape) or any(q.shape[0] != t.shape[0] or q.shape[1] != t.shape[1]
+                                                     or q.shape[3] != t.shape[3] for t in own):
         raise NxattnError(1, "inconsistent q/k/v/o shapes")
     if prefix_only and (len(prefix) != q.shape[0] or any(p is None for p in prefix)):
         raise NxattnError(1, "prefix_only needs one prefix per batch entry")
@@ -307,7 +324,7 @@ def nxattn_fwd(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Ten
         if (not p.is_contiguous() or p.dim() != 4 or p.shape[0] != 2
                 or p.shape[2] != hkv or p.shape[3] != q.shape[3] or p.dtype != q.dtype):
             raise NxattnError(1, "prefix entries must be contiguous [2, P, Hkv, D] of q's dtype")
-    for t in (*own, o):
+    for t in (*own, *([o] if o is not None else [])):
         if t.dtype != q.dtype:
             raise NxattnError(1, "q, k, v, o dtypes differ")
     if q_rope is not None and len(q_rope) != q.shape[0]:
@@ -315,7 +332,7 @@ def nxattn_fwd(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Ten
     if num_splits > 1 and workspace is None:
         n = fwd_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], q.shape[3], num_splits)
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    a = make_fwd_args(q, k, v, o, prefix, scale, q_rope, lse, prefix_only, num_splits, workspace)
+    a = make_fwd_args(q, k, v, o, prefix, scale, q_rope, lse, prefix_only, num_splits, workspace, cfg_out, guidance)
     _check(load().nxattn_fwd(ctypes.byref(a), _stream(stream)))
 
 
@@ -522,13 +539,14 @@ def _fp8_tensors(xs, outs, mults, folds, blocks=False):
 
 def nxattn_fwd_fp8(q8: Optional[torch.Tensor], k8: torch.Tensor, q_exp: Optional[torch.Tensor],
                    k_exp: Optional[torch.Tensor], v: torch.Tensor,
-                   o: torch.Tensor, prefix_k8: Sequence[Optional[torch.Tensor]] = (),
+                   o: Optional[torch.Tensor], prefix_k8: Sequence[Optional[torch.Tensor]] = (),
                    prefix_v: Sequence[Optional[torch.Tensor]] = (), prefix_k_exp: Optional[torch.Tensor] = None,
                    scale: float = 0.0, lse: Optional[torch.Tensor] = None, q_folded: bool = False,
                    q_scales: Optional[torch.Tensor] = None, k_scales: Optional[torch.Tensor] = None,
                    prefix_k_scales: Sequence[Optional[torch.Tensor]] = (), q: Optional[torch.Tensor] = None,
                    q_rope: Optional[Sequence[RopeDesc]] = None, q8_out: Optional[torch.Tensor] = None,
-                   q_scales_out: Optional[torch.Tensor] = None, stream=None) -> None:
+                   q_scales_out: Optional[torch.Tensor] = None, stream=None,
+                   cfg_out: Optional[torch.Tensor] = None, guidance: float = 0.0) -> None:
     """Attention with the fp8 score GEMM: q8 [B,S,Hq,128], k8 [B,S,Hkv,128] uint8 codes
     (contiguous), q_exp [B,Hq], k_exp [B,Hkv] int8; v [B,S,Hkv,128] and o [B,S,Hq,128] bf16;
     prefix_k8[b] uint8 [P_b,Hkv,128] and prefix_v[b] bf16 [P_b,Hkv,128] contiguous (or None),
@@ -539,8 +557,11 @@ def nxattn_fwd_fp8(q8: Optional[torch.Tensor], k8: torch.Tensor, q_exp: Optional
     None). With q_rope (one RopeDesc per batch entry), q8 is None and q (bf16
     [B,S,Hq,128], head_dim contiguous) is rotated, folded and block-quantized on load; the
     keys take block scales; q8_out [B,S,Hq,128] and q_scales_out [B,S,Hq,4] (uint8,
-    contiguous, optional) receive the codes and run scales formed on load."""
-    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, q_scales, k_scales, q, q8_out, q_scales_out,
+    contiguous, optional) receive the codes and run scales formed on load.
+    cfg_out: None, or a bf16 [S, Hq, 128] tensor (last dim contiguous) that receives the
+    guidance combination of the two branches (batch 2), as with nxattn_fwd; o may then
+    be None."""
+    _gpu(q8, k8, q_exp, k_exp, v, o, prefix_k_exp, lse, q_scales, k_scales, q, q8_out, q_scales_out, cfg_out,
          *[t for t in prefix_k8 if t is not None], *[t for t in prefix_v if t is not None],
          *[t for t in prefix_k_scales if t is not None])
     qrope = q_rope is not None
@@ -558,10 +579,17 @@ def nxattn_fwd_fp8(q8: Optional[torch.Tensor], k8: torch.Tensor, q_exp: Optional
     for t in ((k8,) if qrope else (q8, k8)):
         if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 4:
             raise NxattnError(1, "q8 and k8 must be contiguous uint8 [B, S, H, D] tensors")
-    if tuple(k8.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D) or tuple(o.shape) != (B, S, Hq, D):
+    if o is None and cfg_out is None:
+        raise NxattnError(1, "o is required unless cfg_out is given")
+    if (tuple(k8.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D)
+            or (o is not None and tuple(o.shape) != (B, S, Hq, D))):
         raise NxattnError(1, "inconsistent q8/k8/v/o shapes")
-    if v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 or v.stride(3) != 1 or o.stride(3) != 1:
+    if v.dtype != torch.bfloat16 or v.stride(3) != 1 or (o is not None and (o.dtype != torch.bfloat16
+                                                                             or o.stride(3) != 1)):
         raise NxattnError(1, "v and o must be bf16 with head_dim contiguous")
+    if cfg_out is not None and (cfg_out.dim() != 3 or tuple(cfg_out.shape) != (S, Hq, D) or cfg_out.stride(2) != 1
+                                or cfg_out.dtype != torch.bfloat16):
+        raise NxattnError(1, "cfg_out must be bf16 [S, Hq, 128] with a contiguous last dim")
     block = q_scales is not None or qrope
     if block:
         if q_exp is not None or k_exp is not None or prefix_k_exp is not None:
@@ -605,10 +633,15 @@ def nxattn_fwd_fp8(q8: Optional[torch.Tensor], k8: torch.Tensor, q_exp: Optional
                 if t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous():
                     raise NxattnError(1, "q8_out / q_scales_out must be contiguous uint8 [B, S, Hq, 128 / 4] tensors")
             a.q8_out, a.q_scales_out = q8_out.data_ptr(), q_scales_out.data_ptr()
-    a.v, a.o = v.data_ptr(), o.data_ptr()
+    a.v = v.data_ptr()
+    a.o = o.data_ptr() if o is not None else None
     for i in range(3):
         a.v_strides[i] = v.stride(i)
-        a.o_strides[i] = o.stride(i)
+        a.o_strides[i] = o.stride(i) if o is not None else 0
+    if cfg_out is not None:
+        a.cfg_out = cfg_out.data_ptr()
+        a.cfg_strides[0], a.cfg_strides[1] = cfg_out.stride(0), cfg_out.stride(1)
+        a.guidance = float(guidance)
     for b in range(MAX_BRANCHES):
         pk = prefix_k8[b] if b < len(prefix_k8) else None
         pv = prefix_v[b] if b < len(prefix_v) else None

@@ -116,6 +116,21 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   }
   if (a->q_rope && a->dtype != NXATTN_BF16)
     return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: q_rope is supported for BF16 only");
+  // branch pairs: the guidance combination written by the attention kernel itself
+  const bool pair = a->cfg_out != nullptr;
+  if (pair) {
+    if (a->dtype != NXATTN_BF16) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: cfg_out is supported for BF16 only");
+    if (a->batch != 2) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: cfg_out needs batch 2 (cond, uncond), got %d", a->batch);
+    if (a->num_splits > 1) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: cfg_out with num_splits > 1");
+    if (!(a->guidance == a->guidance) || std::isinf(a->guidance))
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd: guidance is not finite");
+    for (int i = 0; i < 2; ++i) {
+      if (a->cfg_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: negative cfg stride");
+      if ((a->cfg_strides[i] * 2) % 16 != 0)
+        return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: cfg stride %lld is not a multiple of 16 bytes", (long long)a->cfg_strides[i]);
+    }
+    if (!aligned16(a->cfg_out)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: cfg_out must be 16-byte aligned");
+  }
   if (a->batch == 0 || a->seq_q == 0) return NXATTN_OK;
   RopeQ rq[NXATTN_MAX_BRANCHES];
   std::memset(rq, 0, sizeof(rq));
@@ -125,16 +140,16 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   }
   // own k and v are not read with prefix_only
   const bool own = !a->prefix_only;
-  if (!a->q || !a->o || (own && (!a->k || !a->v))) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
+  if (!a->q || (!a->o && !pair) || (own && (!a->k || !a->v))) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: NULL q/k/v/o");
   const int64_t es = esize(a->dtype);
   const int64_t* sts[3] = {a->q_strides, a->kv_strides, a->o_strides};
   for (int t = 0; t < 3; ++t)
     for (int i = 0; i < 3; ++i) {
-      if (t == 1 && !own) continue;
+      if ((t == 1 && !own) || (t == 2 && !a->o)) continue;
       if (sts[t][i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: negative stride");
       if ((sts[t][i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: stride %lld is not a multiple of 16 bytes", (long long)sts[t][i]);
     }
-  if (!aligned16(a->q) || !aligned16(a->o) || (own && (!aligned16(a->k) || !aligned16(a->v))))
+  if (!aligned16(a->q) || (a->o && !aligned16(a->o)) || (own && (!aligned16(a->k) || !aligned16(a->v))))
     return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: q/k/v/o must be 16-byte aligned");
   for (int b = 0; b < a->batch; ++b)
     if (a->prefix_kv[b] && !aligned16(a->prefix_kv[b])) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: prefix_kv[%d] misaligned", b);
@@ -157,9 +172,11 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
                   (long long)a->workspace_bytes, (long long)L.total, ns);
   }
   const int64_t wb = ns > 1 ? L.total : 0;
+  const int64_t cst[3] = {0, a->cfg_strides[0], a->cfg_strides[1]};
+  const int64_t cb = pair ? extent_bytes(cst, 1, a->seq_q, a->heads_q, D, es) : 0;
   struct Span { const void* p; int64_t n; const char* name; };
-  const Span outs[3] = {{a->o, ob, "o"}, {a->lse, lb, "lse"}, {a->workspace, wb, "workspace"}};
-  for (int i = 0; i < 3; ++i) {
+  const Span outs[4] = {{a->o, ob, "o"}, {a->lse, lb, "lse"}, {a->workspace, wb, "workspace"}, {a->cfg_out, cb, "cfg_out"}};
+  for (int i = 0; i < 4; ++i) {
     const Span& x = outs[i];
     if (!x.p || x.n == 0) continue;
     if (overlaps(x.p, x.n, a->q, qb) || overlaps(x.p, x.n, a->k, kb) || overlaps(x.p, x.n, a->v, kb))
@@ -184,6 +201,10 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   p.scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
   p.rope_q = a->q_rope != nullptr;
   std::memcpy(p.rq, rq, sizeof(p.rq));
+  p.cfg = a->cfg_out;
+  p.cs[0] = pair ? a->cfg_strides[0] : 0;
+  p.cs[1] = pair ? a->cfg_strides[1] : 0;
+  p.guidance = pair ? a->guidance : 0.f;
   // Key ranges of `per` whole tiles. The range length is at least ceil(max tiles /
   // num_splits) and at least the tile work per resident workgroup slot of the GPU
   // (sum over branches of tiles * workgroups per range, over the workgroups the GPU

@@ -83,6 +83,11 @@ struct Args {
   float* part_o;
   float* part_lse;
   int32_t nsplit, per, prefix_only;
+  // branch pairs: out[i, h] = bf16(fma(guidance, c - u, u)) with c, u the bf16 outputs of
+  // branches 0 and 1 (o may then be NULL: branch outputs not stored)
+  uint16_t* cfg;
+  int64_t cs0, cs1;
+  float guidance;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -150,6 +155,11 @@ __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[TILEB];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[TILEB];
 template <int PAR> __device__ __forceinline__ uint8_t* kbuf() { return PAR ? lds_k1 : lds_k0; }
 template <int PAR> __device__ __forceinline__ uint8_t* vbuf() { return PAR ? lds_v1 : lds_v0; }
+// Branch pairs: the first branch's rounded output, held until the second branch's epilogue
+// (entry (wave, j, lane): 16 words-pairs per lane). Only the pair kernels use it; one
+// workgroup per CU runs at a time (two waves per SIMD at these register counts), so
+// 64 KB more fit beside the tiles.
+__shared__ __attribute__((aligned(16))) u32x2 lds_keep[WAVES * 16 * 64];
 
 // Direct-to-LDS tile load plan of a wave for one iteration: K tile t+2 and V tile t+1,
 // each wholly inside the prefix or wholly inside the own keys. Instruction i (0-3: K,
@@ -458,28 +468,35 @@ __device__ __forceinline__ void softmax(Wave& w, float c, int valid, int hh) {
 }
 
 // The per-wave program. Group A (waves 0-3) and group B (waves 4-7) run it half a tile
-// apart; both execute the same sequence of workgroup barriers.
-template <bool GROUP_A, bool FOLD>
+// apart; both execute the same sequence of workgroup barriers. PAIR: the workgroup runs
+// branch 0 and then branch 1 of its query blocks, keeps branch 0's rounded output in
+// registers and writes the guidance combination of the two.
+template <bool GROUP_A, bool FOLD, bool PAIR>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
   // (kv head, branch, key range) groups in kv-head-major order: each XCD's contiguous
-  // share mixes the CFG branches, whose key counts differ
+  // share mixes the CFG branches, whose key counts differ (PAIR: (kv head) groups)
   const int grp = wg / a.wg_per_group;
   const int split = grp % a.nsplit, gb = grp / a.nsplit;
-  const int g = gb / a.batch, b = gb % a.batch;
+  const int g = PAIR ? gb : gb / a.batch, b0 = PAIR ? 0 : gb % a.batch;
   const int qb = (wg % a.wg_per_group) * WAVES + wave;
   const bool active = qb < a.nqb;
   const int hq = g * a.group + (active ? qb / a.nchunks : 0);
   const int tok = (active ? qb % a.nchunks : 0) * 32 + n;
   const int tokc = tok < a.seq ? tok : a.seq - 1;
+  // one branch (PAIR: branch bi of the pair, the two passes inlined one after the other)
+  auto pass = [&](auto bic) {
+  constexpr int bi = decltype(bic)::value;
+  const int b = PAIR ? bi : b0;
   // this work item's keys: tiles [t0, t0 + T) of the virtual sequence, keys below kend
   const int P = a.plen[b];
   const int Skv = P + (a.prefix_only ? 0 : a.seq);
   const int t0 = split * a.per;
   const int Tall = (Skv + BN - 1) / BN;
   const int T = min(a.per, Tall - t0);
-  if (T <= 0) return;   // empty key range (uniform over the workgroup, before any barrier)
+  if (T <= 0) return;   // empty key range (uniform over the workgroup, before any barrier;
+                        // PAIR launches have one range per branch and T >= 1)
   // a branch whose keys fit in one range writes its result directly, without a merge
   const bool partial = a.nsplit > 1 && Tall > a.per;
   const int kend = min((t0 + T) * BN, Skv);
@@ -680,6 +697,43 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(w.l), __float_as_int(w.l), false, false);
     w.l = __int_as_float(sw[0]) + __int_as_float(sw[1]);
   }
+  if (PAIR) {
+    // no early exit: every wave takes part in the second branch's barriers
+    if (active && tok < a.seq) {
+      const float inv = 1.0f / w.l;
+      if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
+      uint16_t* orow = a.o ? a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2 : nullptr;
+      uint16_t* crow = a.cfg + (int64_t)tok * a.cs0 + (int64_t)hq * a.cs1;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = 32 * db + 8 * i4 + 4 * hh;
+          const u32x2 r = u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
+                                pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
+          if (orow) *reinterpret_cast<u32x2*>(orow + d) = r;
+          __attribute__((address_space(3))) u32x2* kp =
+              (__attribute__((address_space(3))) u32x2*)&lds_keep[(wave * 16 + 4 * db + i4) * 64 + lane];
+          if constexpr (bi == 0) {
+            *kp = r;
+          } else {
+            const u32x2 cv = *kp;
+            // the arithmetic of the combine pass on the two rounded outputs: c = branch 0,
+            // u = branch 1, fma(guidance, c - u, u) in fp32, rounded to nearest even
+            u32x2 o2;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const uint32_t cw = cv[e], uw = r[e];
+              const float c0 = __uint_as_float(cw << 16), c1 = __uint_as_float(cw & 0xffff0000u);
+              const float u0 = __uint_as_float(uw << 16), u1 = __uint_as_float(uw & 0xffff0000u);
+              o2[e] = pack_bf16x2(__builtin_fmaf(a.guidance, c0 - u0, u0), __builtin_fmaf(a.guidance, c1 - u1, u1));
+            }
+            *reinterpret_cast<u32x2*>(crow + d) = o2;
+          }
+        }
+    }
+    return;
+  }
   if (!active || tok >= a.seq) return;
   const float inv = 1.0f / w.l;
   // log-sum-exp of the scaled scores: sum_j exp2(c s_j - m) = l, so in natural log
@@ -711,14 +765,24 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
                 pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
     }
   if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = lse;
+  };
+  if constexpr (PAIR) {
+    pass(std::integral_constant<int, 0>{});
+    // the second branch's first loads refill buffers that group B may still be reading
+    // for the first branch's last tile
+    barrier_only();
+    pass(std::integral_constant<int, 1>{});
+  } else {
+    pass(std::integral_constant<int, 0>{});
+  }
 }
 
-template <bool FOLD>
+template <bool FOLD, bool PAIR>
 __global__ __launch_bounds__(THREADS) void fwd_bf16_kernel(Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true, FOLD>(a, lane, wave);
-  else wave_program<false, FOLD>(a, lane, wave);
+  if (wave < 4) wave_program<true, FOLD, PAIR>(a, lane, wave);
+  else wave_program<false, FOLD, PAIR>(a, lane, wave);
 }
 
 }  // namespace bf16k
@@ -728,8 +792,8 @@ FwdShape fwd_shape_bf16(const FwdProblem& p) {
   // resident workgroups per CU (registers and LDS bound it) of the variant that will run,
   // queried on each call: the library keeps no state
   int n = 0;
-  const hipError_t e = p.rope_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<true>, THREADS, 0)
-                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<false>, THREADS, 0);
+  const hipError_t e = p.rope_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<true, false>, THREADS, 0)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_bf16_kernel<false, false>, THREADS, 0);
   const int64_t nqb = (int64_t)(p.heads_q / p.heads_kv) * ((p.seq_q + 31) / 32);
   return FwdShape{(nqb + WAVES - 1) / WAVES * p.heads_kv, (e != hipSuccess || n < 1) ? 1 : n};
 }
@@ -748,7 +812,8 @@ int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
   a.nchunks = (p.seq_q + 31) / 32;
   const int64_t nqb = (int64_t)a.group * a.nchunks;
   const int64_t wpg = (nqb + WAVES - 1) / WAVES;
-  const int64_t total = wpg * p.heads_kv * p.batch * p.nsplit;
+  const bool pair = p.cfg != nullptr;   // one workgroup per (kv head, query blocks), both branches
+  const int64_t total = wpg * p.heads_kv * (pair ? 1 : p.batch * p.nsplit);
   if (total > INT32_MAX / 2) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: problem too large");
   a.nqb = (int)nqb; a.wg_per_group = (int)wpg; a.total_wg = (int)total;
   a.c = p.scale * LOG2E;
@@ -760,8 +825,16 @@ int launch_fwd_bf16(const FwdProblem& p, hipStream_t stream) {
     a.k = a.q; a.v = a.q;
     a.ks0 = a.ks1 = a.ks2 = 0;
   }
-  if (a.rope_q) fwd_bf16_kernel<true><<<a.total_wg, THREADS, 0, stream>>>(a);
-  else fwd_bf16_kernel<false><<<a.total_wg, THREADS, 0, stream>>>(a);
+  a.cfg = static_cast<uint16_t*>(p.cfg);
+  a.cs0 = p.cs[0]; a.cs1 = p.cs[1];
+  a.guidance = p.guidance;
+  if (pair) {
+    if (a.rope_q) fwd_bf16_kernel<true, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+    else fwd_bf16_kernel<false, true><<<a.total_wg, THREADS, 0, stream>>>(a);
+  } else {
+    if (a.rope_q) fwd_bf16_kernel<true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
+    else fwd_bf16_kernel<false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
+  }
   return check_launch("nxattn_fwd(bf16)");
 }
 

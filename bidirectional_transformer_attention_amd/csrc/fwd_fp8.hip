@@ -65,6 +65,11 @@ struct Args {
   RopeQ rq[NXATTN_MAX_BRANCHES];
   uint8_t* q8_out;      // QROPE, optional: the codes [B, S, Hq, 128] and run scales [B, S, Hq, 4]
   uint8_t* qsc_out;     // formed on load
+  // branch pairs: out[i, h] = bf16(fma(guidance, c - u, u)) with c, u the bf16 outputs of
+  // branches 0 and 1 (o may then be NULL: branch outputs not stored)
+  uint16_t* cfg;
+  int64_t cs0, cs1;
+  float guidance;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -97,6 +102,18 @@ __device__ __forceinline__ void wait_dma_barrier() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// A wave-uniform pointer stated as such (read back from the first lane), so that the buffer
+// descriptors built from it stay in scalar registers: under the register pressure of the
+// branch-pair kernels the compiler otherwise computed some in vector registers and
+// wrapped every tile load in a loop over the distinct values.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // LDS: K (fp8) and V (bf16) tiles, double-buffered, as four distinct objects
 __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[KTILEB];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[KTILEB];
@@ -107,6 +124,10 @@ template <int PAR> __device__ __forceinline__ uint8_t* vbuf() { return PAR ? lds
 // BLOCK: the four run scales (E8M0 codes) of each key row of a K tile, beside the tile
 __shared__ __attribute__((aligned(256))) uint8_t lds_s0[BN * 4];
 __shared__ __attribute__((aligned(256))) uint8_t lds_s1[BN * 4];
+// Branch pairs: the first branch's rounded output, held until the second branch's epilogue
+// (entry (wave, j, lane)); only the pair kernels use it. 16-byte aligned so that it is
+// placed after the tile buffers, whose LDS offsets then fit the reads' immediate field.
+__shared__ __attribute__((aligned(16))) u32x2 lds_keep[WAVES * 16 * 64];
 template <int PAR> __device__ __forceinline__ uint8_t* sbuf() { return PAR ? lds_s1 : lds_s0; }
 
 // Steady-state tile loads of one wave (rows 16ws .. 16ws+15 of a tile): K in 2
@@ -467,17 +488,22 @@ __device__ __forceinline__ void q_rope_quantize(Wave& w, const Args& a, const QR
   w.qrun = (uint32_t)sc[0][0] | ((uint32_t)sc[0][1] << 8) | ((uint32_t)sc[1][0] << 16) | ((uint32_t)sc[1][1] << 24);
 }
 
-template <bool GROUP_A, bool FOLD, bool BLOCK, bool QROPE>
+// PAIR: the workgroup runs branch 0 and then branch 1 of its query blocks (two inlined
+// passes), keeps branch 0's rounded output in LDS and writes the guidance combination.
+template <bool GROUP_A, bool FOLD, bool BLOCK, bool QROPE, bool PAIR>
 __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) {
   const int n = lane & 31, hh = lane >> 5;
   const int wg = remap_xcd(blockIdx.x, a.total_wg);
   const int grp = wg / a.wg_per_group;
-  const int g = grp / a.batch, b = grp % a.batch;
+  const int g = PAIR ? grp : grp / a.batch, b0 = PAIR ? 0 : grp % a.batch;
   const int qb = (wg % a.wg_per_group) * WAVES + wave;
   const bool active = qb < a.nqb;
   const int hq = g * a.group + (active ? qb / a.nchunks : 0);
   const int tok = (active ? qb % a.nchunks : 0) * 32 + n;
   const int tokc = tok < a.seq ? tok : a.seq - 1;
+  auto pass = [&](auto bic) {
+  constexpr int bi = decltype(bic)::value;
+  const int b = PAIR ? bi : b0;
   const int P = a.plen[b];
   const int Skv = P + a.seq;
   const int T = (Skv + BN - 1) / BN;
@@ -613,9 +639,10 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   const uint32_t ksc_row = (uint32_t)a.heads_kv * 4;               // bytes between key rows
   const uint32_t ksc_lane = (uint32_t)lane * ksc_row;
   const __amdgpu_buffer_rsrc_t ksr_own =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ksc_own), 0, BUF_RECORDS, BUF_FLAGS);
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint8_t*>(ksc_own)), 0, BUF_RECORDS, BUF_FLAGS);
   const __amdgpu_buffer_rsrc_t ksr_pre =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(P > 0 ? ksc_pre : ksc_own), 0, BUF_RECORDS, BUF_FLAGS);
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint8_t*>(P > 0 ? ksc_pre : ksc_own)), 0, BUF_RECORDS,
+                                        BUF_FLAGS);
   // the scales of the tile at position pos into dst (wave 0 only; WHOLE: pos < nwhole)
   auto dma_s = [&](int pos, uint8_t* dst, auto whole) {
     if constexpr (BLOCK) {
@@ -658,8 +685,8 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
     const bool kp = jk < P, vp = jv < P;
     const uint8_t* kb_ = kp ? kpre + (int64_t)jk * krow : kown + (int64_t)(jk - P) * krow;
     const uint16_t* vb_ = vp ? vpre + (int64_t)jv * pvrow : vown + (int64_t)(jv - P) * vs1;
-    pl.krsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb_), 0, BUF_RECORDS, BUF_FLAGS);
-    pl.vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb_), 0, BUF_RECORDS, BUF_FLAGS);
+    pl.krsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint8_t*>(kb_)), 0, BUF_RECORDS, BUF_FLAGS);
+    pl.vrsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint16_t*>(vb_)), 0, BUF_RECORDS, BUF_FLAGS);
     pl.krs = (uint32_t)(8 * krow);
     pl.vrs = (uint32_t)(8 * (vp ? pvrow : vs1));
     pl.koff = koff;
@@ -751,25 +778,74 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   }
   if (!active || tok >= a.seq) return;
   const float inv = 1.0f / w.l;
-  uint16_t* orow = a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2;
+  uint16_t* orow = a.o ? a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2 : nullptr;
+  uint16_t* crow = PAIR ? a.cfg + (int64_t)tok * a.cs0 + (int64_t)hq * a.cs1 : nullptr;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d = 32 * db + 8 * i4 + 4 * hh;
-      *reinterpret_cast<u32x2*>(orow + d) =
-          u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
-                pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
+      const u32x2 r = u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
+                            pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
+      if (!PAIR || orow) *reinterpret_cast<u32x2*>(orow + d) = r;
+      if constexpr (PAIR) {
+        __attribute__((address_space(3))) u32x2* kp =
+            (__attribute__((address_space(3))) u32x2*)&lds_keep[(wave * 16 + 4 * db + i4) * 64 + lane];
+        if constexpr (bi == 0) {
+          *kp = r;
+        } else {
+          // the arithmetic of the combine pass on the two rounded outputs: c = branch 0,
+          // u = branch 1, fma(guidance, c - u, u) in fp32, rounded to nearest even
+          const u32x2 cv = *kp;
+          u32x2 o2;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t cw = cv[e], uw = r[e];
+            const float c0 = __uint_as_float(cw << 16), c1 = __uint_as_float(cw & 0xffff0000u);
+            const float u0 = __uint_as_float(uw << 16), u1 = __uint_as_float(uw & 0xffff0000u);
+            o2[e] = pack_bf16x2(__builtin_fmaf(a.guidance, c0 - u0, u0), __builtin_fmaf(a.guidance, c1 - u1, u1));
+          }
+          *reinterpret_cast<u32x2*>(crow + d) = o2;
+        }
+      }
     }
   if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
+  };
+  if constexpr (PAIR) {
+    pass(std::integral_constant<int, 0>{});
+    // the second branch's first loads refill buffers that group B may still be reading
+    // for the first branch's last tile
+    barrier_only();
+    pass(std::integral_constant<int, 1>{});
+  } else {
+    pass(std::integral_constant<int, 0>{});
+  }
 }
 
-template <bool FOLD, bool BLOCK, bool QROPE>
+template <bool FOLD, bool BLOCK, bool QROPE, bool PAIR>
 __global__ __launch_bounds__(THREADS) void fwd_fp8_kernel(Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave < 4) wave_program<true, FOLD, BLOCK, QROPE>(a, lane, wave);
-  else wave_program<false, FOLD, BLOCK, QROPE>(a, lane, wave);
+  if (wave < 4) wave_program<true, FOLD, BLOCK, QROPE, PAIR>(a, lane, wave);
+  else wave_program<false, FOLD, BLOCK, QROPE, PAIR>(a, lane, wave);
+}
+
+// launch of the instantiation that matches the call
+template <bool PAIR>
+static void launch_fp8(const Args& a, bool qrope, bool block, bool folded, hipStream_t stream) {
+  if (qrope) {
+    fwd_fp8_kernel<true, true, true, PAIR><<<a.total_wg, THREADS, 0, stream>>>(a);
+  } else if (block) {
+    if (folded)
+      fwd_fp8_kernel<true, true, false, PAIR><<<a.total_wg, THREADS, 0, stream>>>(a);
+    else
+      fwd_fp8_kernel<false, true, false, PAIR><<<a.total_wg, THREADS, 0, stream>>>(a);
+  } else {
+    if (folded)
+      fwd_fp8_kernel<true, false, false, PAIR><<<a.total_wg, THREADS, 0, stream>>>(a);
+    else
+      fwd_fp8_kernel<false, false, false, PAIR><<<a.total_wg, THREADS, 0, stream>>>(a);
+  }
 }
 
 }  // namespace fp8k
@@ -820,8 +896,21 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
       return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: prefix_len[%d] + seq_q overflows int32", b);
     any_prefix |= has;
   }
+  // branch pairs: the guidance combination written by the attention kernel itself
+  const bool pair = p->cfg_out != nullptr;
+  if (pair) {
+    if (p->batch != 2) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: cfg_out needs batch 2 (cond, uncond), got %d", p->batch);
+    if (!(p->guidance == p->guidance) || std::isinf(p->guidance))
+      return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: guidance is not finite");
+    for (int i = 0; i < 2; ++i) {
+      if (p->cfg_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative cfg stride");
+      if ((p->cfg_strides[i] * 2) % 16 != 0)
+        return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: cfg stride %lld is not a multiple of 16 bytes", (long long)p->cfg_strides[i]);
+    }
+    if (!aligned16(p->cfg_out)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: cfg_out must be 16-byte aligned");
+  }
   if (p->batch == 0 || p->seq_q == 0) return NXATTN_OK;
-  if (!(qrope ? p->q : p->q8) || !p->k8 || !p->v || !p->o)
+  if (!(qrope ? p->q : p->q8) || !p->k8 || !p->v || (!p->o && !pair))
     return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: NULL pointer");
   if (block ? !p->k_scales : (!p->q_exp || !p->k_exp || (any_prefix && !p->prefix_k_exp)))
     return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: NULL pointer (exponents or scales)");
@@ -837,11 +926,12 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     if (!ok) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: scales must be 4-byte aligned");
   }
   for (int i = 0; i < 3; ++i) {
-    if (p->v_strides[i] < 0 || p->o_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative stride");
-    if ((p->v_strides[i] * 2) % 16 != 0 || (p->o_strides[i] * 2) % 16 != 0)
+    const int64_t os = p->o ? p->o_strides[i] : 0;
+    if (p->v_strides[i] < 0 || os < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative stride");
+    if ((p->v_strides[i] * 2) % 16 != 0 || (os * 2) % 16 != 0)
       return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
   }
-  if (!aligned16(qrope ? p->q : p->q8) || !aligned16(p->k8) || !aligned16(p->v) || !aligned16(p->o))
+  if (!aligned16(qrope ? p->q : p->q8) || !aligned16(p->k8) || !aligned16(p->v) || (p->o && !aligned16(p->o)))
     return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: q8 (or q)/k8/v/o must be 16-byte aligned");
   if (qrope)
     for (int i = 0; i < 3; ++i) {
@@ -854,7 +944,8 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   if (p->lse && (reinterpret_cast<uintptr_t>(p->lse) & 3u)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: lse misaligned");
   // outputs must not overlap any input
   const int64_t B = p->batch, S = p->seq_q, Hq = p->heads_q, Hkv = p->heads_kv;
-  const int64_t ob = ((B - 1) * p->o_strides[0] + (S - 1) * p->o_strides[1] + (Hq - 1) * p->o_strides[2] + D) * 2;
+  const int64_t ob = p->o ? ((B - 1) * p->o_strides[0] + (S - 1) * p->o_strides[1] + (Hq - 1) * p->o_strides[2] + D) * 2 : 0;
+  const int64_t cb = pair ? ((S - 1) * p->cfg_strides[0] + (Hq - 1) * p->cfg_strides[1] + D) * 2 : 0;
   const int64_t vb = ((B - 1) * p->v_strides[0] + (S - 1) * p->v_strides[1] + (Hkv - 1) * p->v_strides[2] + D) * 2;
   const int64_t lb = p->lse ? B * Hq * S * 4 : 0;
   const int64_t qb = qrope ? ((B - 1) * p->q_strides[0] + (S - 1) * p->q_strides[1] + (Hq - 1) * p->q_strides[2] + D) * 2
@@ -870,15 +961,15 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     ins[nin++] = Span{p->prefix_v[b], (int64_t)p->prefix_len[b] * Hkv * D * 2};
     ins[nin++] = Span{p->prefix_k_scales[b], (int64_t)p->prefix_len[b] * Hkv * 4};
   }
-  // outputs: o, lse and (with q_rope) the codes and scales formed on load
-  const Span outs[4] = {{p->o, ob}, {p->lse, lb}, {p->q8_out, p->q8_out ? B * S * Hq * D : 0},
-                        {p->q_scales_out, p->q_scales_out ? B * S * Hq * 4 : 0}};
-  for (int j = 0; j < 4; ++j) {
+  // outputs: o, lse, (with q_rope) the codes and scales formed on load, the guided output
+  const Span outs[5] = {{p->o, ob}, {p->lse, lb}, {p->q8_out, p->q8_out ? B * S * Hq * D : 0},
+                        {p->q_scales_out, p->q_scales_out ? B * S * Hq * 4 : 0}, {p->cfg_out, cb}};
+  for (int j = 0; j < 5; ++j) {
     if (!outs[j].ptr) continue;
     for (int i = 0; i < nin; ++i)
       if (ins[i].ptr && overlaps(outs[j].ptr, outs[j].n, ins[i].ptr, ins[i].n))
         return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: an output overlaps an input");
-    for (int i = j + 1; i < 4; ++i)
+    for (int i = j + 1; i < 5; ++i)
       if (outs[i].ptr && overlaps(outs[j].ptr, outs[j].n, outs[i].ptr, outs[i].n))
         return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: outputs overlap");
   }
@@ -909,24 +1000,18 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   a.nchunks = (p->seq_q + 31) / 32;
   const int64_t nqb = (int64_t)a.group * a.nchunks;
   const int64_t wpg = (nqb + WAVES - 1) / WAVES;
-  const int64_t total = wpg * p->heads_kv * p->batch;
+  // branch pairs: one workgroup per (kv head, query blocks) serves both branches
+  const int64_t total = wpg * p->heads_kv * (pair ? 1 : p->batch);
   if (total > INT32_MAX / 2) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: problem too large");
   a.nqb = (int)nqb; a.wg_per_group = (int)wpg; a.total_wg = (int)total;
   const float scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)D);
   a.c = scale * LOG2E;
   a.lse = p->lse;
-  if (qrope) {
-    fwd_fp8_kernel<true, true, true><<<a.total_wg, THREADS, 0, stream>>>(a);
-  } else if (block) {
-    if (p->q_folded)
-      fwd_fp8_kernel<true, true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
-    else
-      fwd_fp8_kernel<false, true, false><<<a.total_wg, THREADS, 0, stream>>>(a);
-  } else {
-    if (p->q_folded)
-      fwd_fp8_kernel<true, false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
-    else
-      fwd_fp8_kernel<false, false, false><<<a.total_wg, THREADS, 0, stream>>>(a);
-  }
+  a.cfg = static_cast<uint16_t*>(p->cfg_out);
+  a.cs0 = pair ? p->cfg_strides[0] : 0;
+  a.cs1 = pair ? p->cfg_strides[1] : 0;
+  a.guidance = pair ? p->guidance : 0.f;
+  if (pair) launch_fp8<true>(a, qrope, block, p->q_folded != 0, stream);
+  else launch_fp8<false>(a, qrope, block, p->q_folded != 0, stream);
   return check_launch("nxattn_fwd_fp8");
 }

@@ -144,6 +144,12 @@ struct FwdProblem {
   int32_t nsplit, per;
   float* part_o;
   float* part_lse;
+  // branch pairs (bf16, batch 2, one key range): cfg [seq_q, heads_q, D] with strides cs
+  // {s, h} receives the guidance combination of the two branches' rounded outputs, and o
+  // may be NULL
+  void* cfg;
+  int64_t cs[2];
+  float guidance;
 };
 constexpr int KEY_TILE = 64;            // keys per tile in both attention kernels
 // Launch shape of an attention kernel for a problem: workgroups per key range of one

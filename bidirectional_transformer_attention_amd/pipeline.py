@@ -5,7 +5,10 @@
        (the bf16 path; every branch with its own offsets)
     -> fused attention over [prefix ++ own] for all branches in one launch (or, with
        key splits, one launch over key ranges plus one merge launch)
-    -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies.
+    -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies: with
+       one key range (bf16 or fp8 score GEMM), inside the attention call (each workgroup runs
+       both branches of its query rows and writes the combination; ``keep_branches``
+       also stores the branch outputs), else as a separate pass.
 With the fp8 score GEMM (``qk_fp8`` workloads) q and own k are rotated and quantized to
 E4M3 in one call before the attention call, with one scale per (branch, head) or, for
 ``fp8_blocks`` workloads, one per run of 32 head_dim elements (a single pass without a
@@ -30,7 +33,8 @@ from .synth import Inputs, Workload
 
 class AttentionStep:
     def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None,
-                 splits: Optional[int] = None, fold_q: bool = True, q_on_load: bool = False):
+                 splits: Optional[int] = None, fold_q: bool = True, q_on_load: bool = False,
+                 fuse_cfg: Optional[bool] = None, keep_branches: bool = True):
         self.wl = wl
         # fp8: q's codes carry softmax_scale*log2(e), so the attention's softmax takes one
         # exp2 per score with no multiply in front
@@ -97,6 +101,15 @@ class AttentionStep:
                 self.qws = torch.empty(max(4, n), dtype=torch.uint8, device=dev)
         self.use_cfg = self.B == 2 and wl.guidance > 1.0
         self.out = torch.empty_like(self.q[0]) if self.use_cfg else None
+        # bf16 with one key range: the attention kernel serves both branches of its query
+        # rows and writes the guidance combination itself (no combine pass); with
+        # keep_branches it also stores the two branch outputs in o
+        can_fuse = self.use_cfg and wl.dtype == "bf16" and self.splits <= 1
+        self.fuse_cfg = can_fuse if fuse_cfg is None else bool(fuse_cfg)
+        if self.fuse_cfg and not can_fuse:
+            raise ValueError("the guidance combination folds into the bf16 / fp8 attention call with one key "
+                             "range only")
+        self.keep_branches = bool(keep_branches) or not self.fuse_cfg
         if wl.qk_fp8:
             self.relayout()
             self.quantize_prefix()
@@ -140,33 +153,41 @@ class AttentionStep:
                                     folds=[self.fold_q, False])
 
     def attention(self) -> None:
+        # with the guidance combination inside the call: the guided output, and the branch
+        # outputs only if kept
+        o = self.o if self.keep_branches else None
+        g = dict(cfg_out=self.out, guidance=self.wl.guidance) if self.fuse_cfg else {}
         if self.q_on_load:
-            nx.nxattn_fwd_fp8(None, self.k8, None, None, self.v, self.o,
+            nx.nxattn_fwd_fp8(None, self.k8, None, None, self.v, o,
                               [None if p is None else p[0] for p in self.pk8],
                               [None if p is None else p[1] for p in self.prefix_online],
                               k_scales=self.ks, prefix_k_scales=[None if p is None else p[0] for p in self.pks],
-                              q=self.q, q_rope=self.descs)
+                              q=self.q, q_rope=self.descs, **g)
             return
         if self.blocks:
-            nx.nxattn_fwd_fp8(self.q8, self.k8, None, None, self.v, self.o,
+            nx.nxattn_fwd_fp8(self.q8, self.k8, None, None, self.v, o,
                               [None if p is None else p[0] for p in self.pk8],
                               [None if p is None else p[1] for p in self.prefix_online],
                               q_folded=self.fold_q, q_scales=self.qs, k_scales=self.ks,
-                              prefix_k_scales=[None if p is None else p[0] for p in self.pks])
+                              prefix_k_scales=[None if p is None else p[0] for p in self.pks], **g)
             return
         if self.wl.qk_fp8:
-            nx.nxattn_fwd_fp8(self.q8, self.k8, self.qe, self.ke, self.v, self.o,
+            nx.nxattn_fwd_fp8(self.q8, self.k8, self.qe, self.ke, self.v, o,
                               [None if p is None else p[0] for p in self.pk8],
                               [None if p is None else p[1] for p in self.prefix_online],
                               self.pke if any(p is not None for p in self.prefix_online) else None,
-                              q_folded=self.fold_q)
+                              q_folded=self.fold_q, **g)
+            return
+        if self.fuse_cfg:
+            nx.nxattn_fwd(self.q, self.k, self.v, o, self.prefix_online,
+                          q_rope=self.descs if self.fuse_q_rope else None, **g)
             return
         nx.nxattn_fwd(self.q, self.k, self.v, self.o, self.prefix_online,
                       q_rope=self.descs if self.fuse_q_rope else None,
                       num_splits=self.splits, workspace=self.workspace)
 
     def cfg(self) -> None:
-        if self.use_cfg:
+        if self.use_cfg and not self.fuse_cfg:
             nx.nxattn_cfg_combine(self.o[0], self.o[1], self.out, self.wl.guidance)
 
     def __call__(self) -> torch.Tensor:

@@ -162,6 +162,19 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
  * workspace, workspace_bytes: with num_splits > 1, 16-byte aligned device memory of at
  *   least nxattn_fwd_workspace_size() bytes, overlapping nothing else; its contents on
  *   entry do not matter and it is busy until the merge kernel has run on `stream`.
+ *
+ * cfg_out (optional, device; off when NULL): classifier-free guidance folded into the
+ * attention call (LingBot-Video page, "Key Parameters": guidance_scale; NeoPP page: the
+ * cond and uncond KV branches). BF16, batch 2 (branch 0 cond, branch 1 uncond), and one
+ * key range (num_splits 0 or 1) only; NXATTN_ERR_UNSUPPORTED / _INVALID otherwise.
+ *   cfg_out[i, h, :] = nxattn_cfg_combine of the two branches' outputs, bit for bit:
+ *   fma(guidance, c - u, u) in fp32 on c = o[0, i, h, :] and u = o[1, i, h, :] as rounded
+ *   to bf16, rounded to nearest even. Layout [seq_q, heads_q, head_dim], element strides
+ *   cfg_strides {s, h} (multiples of 8, head_dim contiguous), 16-byte aligned; it must
+ *   not overlap the inputs, o, lse or the workspace. guidance must be finite.
+ *   One workgroup serves both branches of its query rows, so no combine pass and no
+ *   second reading of the branch outputs is needed. o may be NULL: the branch outputs
+ *   are then not stored (lse, if given, is still written for both branches).
  */
 typedef struct {
   int32_t dtype;
@@ -186,6 +199,9 @@ typedef struct {
   int32_t num_splits;               /* 0/1: one pass; 2..NXATTN_MAX_SPLITS key ranges */
   void* workspace;                  /* num_splits > 1: caller's device scratch        */
   int64_t workspace_bytes;
+  void* cfg_out;                    /* NULL, or the guidance combination (see above)  */
+  int64_t cfg_strides[2];           /* cfg_out element strides {s, h}                 */
+  float guidance;
 } nxattn_fwd_args;
 
 int nxattn_fwd(const nxattn_fwd_args* args, hipStream_t stream);
@@ -381,6 +397,11 @@ int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors, int32_t n
  * scales to q_scales_out (uint8 E8M0 [batch, seq_q, heads_q, 4], 4-byte aligned), as
  * nxattn_fwd_fp8 with q_scales would take them. No output may overlap an input or another
  * output.
+ *
+ * cfg_out, cfg_strides, guidance (off when cfg_out is NULL): the guidance combination of
+ * the two branches written by this call, exactly as in nxattn_fwd (batch 2, branch 0
+ * cond; bit for bit nxattn_cfg_combine of the two branches' rounded outputs); o may then
+ * be NULL.
  */
 typedef struct {
   int32_t batch;
@@ -411,6 +432,9 @@ typedef struct {
   const nxattn_rope_desc* q_rope;
   uint8_t* q8_out;                                    /* q_rope, optional: codes formed on load */
   uint8_t* q_scales_out;
+  void* cfg_out;                                      /* NULL, or the guidance combination      */
+  int64_t cfg_strides[2];                             /* (as in nxattn_fwd_args)                */
+  float guidance;
 } nxattn_fwd_fp8_args;
 
 int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* args, hipStream_t stream);

@@ -70,7 +70,7 @@ def fwd_args(**kw):
         a.prefix_len[b] = 0
     a.scale = 0.0
     for key, val in kw.items():
-        if key in ("prefix_kv", "prefix_len", "q_strides", "kv_strides", "o_strides"):
+        if key in ("prefix_kv", "prefix_len", "q_strides", "kv_strides", "o_strides", "cfg_strides"):
             for i, x in enumerate(val):
                 getattr(a, key)[i] = x
         else:
@@ -167,6 +167,28 @@ WS = FAKE + 8 * GB          # a workspace / lse address clear of q, k, v and o
     (dict(num_splits=4, workspace=WS, workspace_bytes=1 << 30, lse=WS + 4096), INVALID, "overlaps lse"),
 ])
 def test_fwd_lse_split_rejects(lib, kw, code, msg):
+    assert call_fwd(lib, fwd_args(**kw)) == code
+    assert msg in nx.last_error()
+
+
+CFG = dict(cfg_out=WS, cfg_strides=(8 * 128, 128), guidance=4.0)   # a valid guidance output
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(CFG, dtype=0, head_dim=64), UNSUPPORTED, "BF16 only"),
+    (dict(CFG, batch=1), INVALID, "batch 2"),
+    (dict(CFG, batch=3), INVALID, "batch 2"),
+    (dict(CFG, num_splits=2), UNSUPPORTED, "num_splits"),
+    (dict(CFG, guidance=float("inf")), INVALID, "guidance"),
+    (dict(CFG, cfg_out=WS + 8), ALIGN, "cfg_out must be 16-byte aligned"),
+    (dict(CFG, cfg_strides=(8 * 128, 132)), ALIGN, "cfg stride"),
+    (dict(CFG, cfg_strides=(-8, 128)), INVALID, "negative cfg stride"),
+    (dict(CFG, cfg_out=FAKE), INVALID, "cfg_out overlaps q"),
+    (dict(CFG, cfg_out=FAKE + (1 << 32) + 4096), INVALID, "cfg_out overlaps o"),
+    (dict(o=None), INVALID, "NULL q/k/v/o"),                              # o is needed without cfg_out
+    (dict(CFG, o=None, lse=WS + 64), INVALID, "cfg_out overlaps lse"),   # o NULL accepted, next check fires
+])
+def test_fwd_cfg_out_rejects(lib, kw, code, msg):
     assert call_fwd(lib, fwd_args(**kw)) == code
     assert msg in nx.last_error()
 
@@ -376,7 +398,7 @@ def fp8_args(**kw):
     for i, s in enumerate((64 * 8 * 128, 8 * 128, 128)):
         a.o_strides[i] = s
     for key, val in kw.items():
-        if key in ("prefix_len", "prefix_k8", "prefix_v", "v_strides", "o_strides", "prefix_k_scales"):
+        if key in ("prefix_len", "prefix_k8", "prefix_v", "v_strides", "o_strides", "prefix_k_scales", "cfg_strides"):
             for i, x in enumerate(val):
                 getattr(a, key)[i] = x
         else:
@@ -410,6 +432,23 @@ def fp8_args(**kw):
 def test_fwd_fp8_rejects(lib, kw, code):
     assert lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(**kw)), None) == code
     assert nx.last_error() != ""
+
+
+CFG8 = dict(cfg_out=FAKE + 10 * GB, cfg_strides=(8 * 128, 128), guidance=4.0)   # a valid guidance output
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(CFG8, batch=1), INVALID, "batch 2"),
+    (dict(CFG8, guidance=float("nan")), INVALID, "guidance"),
+    (dict(CFG8, cfg_out=FAKE + 10 * GB + 8), ALIGN, "cfg_out must be 16-byte aligned"),
+    (dict(CFG8, cfg_strides=(8 * 128, 132)), ALIGN, "cfg stride"),      # 264 bytes
+    (dict(CFG8, cfg_out=FAKE + 4 * GB), INVALID, "outputs overlap"),                  # cfg_out overlaps o
+    (dict(o=None), INVALID, "NULL pointer"),                                         # o needed without cfg_out
+    (dict(CFG8, o=None, cfg_out=FAKE + GB), INVALID, "an output overlaps an input"),  # o NULL accepted
+])
+def test_fwd_fp8_cfg_out_rejects(lib, kw, code, msg):
+    assert lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(**kw)), None) == code
+    assert msg in nx.last_error()
 
 
 def test_fwd_fp8_q_on_load_rejects(lib):
