@@ -374,6 +374,10 @@ def main() -> int:
         "quantize": (((es + 1) * (step.q.numel() + step.k.numel()) + (step.q.numel() + step.k.numel()) // 32)
                      if wl.fp8_blocks else (2 * es + 1) * (step.q.numel() + step.k.numel())) if wl.qk_fp8 else 0,
     }
+    if step.fuse_prep:
+        # one launch: the rotation of k and the relayouts of the prefixes
+        nbytes["rope"] += nbytes["relayout"]
+        nbytes["relayout"] = 0
     for name, fn in (("relayout", step.relayout), ("rope", step.rope), ("quantize", step.quantize),
                      ("cfg", step.cfg)):
         if nbytes[name] == 0:
@@ -384,6 +388,8 @@ def main() -> int:
                       "frac_of_hbm": round(gbs / HBM_PEAK, 4)}
     if step.fuse_cfg:
         side["cfg"] = "inside the attention call"
+    if step.fuse_prep:
+        side["relayout"] = "in the launch that rotates k (its bytes are in rope's)"
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": (rec["bytes_per_launch"] if rec and rec.get("workload") == wl.name and step.splits <= 1
@@ -433,7 +439,8 @@ def main() -> int:
                    "guidance": wl.guidance, "prefix_layout_in": "replay [2,H,P,D] relaid each step"
                    if wl.prefix_layout == "replay" else "online [2,P,H,D]",
                    "splits": step.splits, "layers_per_step": layers,
-                   "step": ("relayout + rope(k) + fused attention (q rotated on load)" if step.fuse_q_rope
+                   "step": (("relayout and rope(k) in one launch" if step.fuse_prep else "relayout + rope(k)")
+                            + " + fused attention (q rotated on load)" if step.fuse_q_rope
                             else "relayout + fp8 quantize(rope(q), rope(k)) + fused attention with fp8 QK "
                                  "(prefix K codes made once per conditioning cache)"
                             if wl.qk_fp8 else "relayout + rope(q,k) + fused attention")

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     quantize_fp8_workspace_bytes,
     nxattn_kv_relayout,
     nxattn_rope_apply,
+    nxattn_rope_apply_relayout,
     rope_desc,
     status_string,
     last_error,

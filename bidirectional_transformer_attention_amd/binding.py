@@ -23,7 +23,7 @@ NXATTN_BF16 = 1
 MAX_BRANCHES = 8
 MAX_SPLITS = 16
 
-SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_fwd", "nxattn_fwd_workspace_size",
+SYMBOLS = ("nxattn_kv_relayout", "nxattn_rope_apply", "nxattn_rope_apply_relayout", "nxattn_fwd", "nxattn_fwd_workspace_size",
            "nxattn_attn_merge", "nxattn_quantize_fp8_workspace_size", "nxattn_quantize_fp8",
            "nxattn_quantize_fp8_blocks", "nxattn_rope_quantize_fp8", "nxattn_rope_quantize_fp8_noalloc", "nxattn_fwd_fp8",
            "nxattn_cfg_combine", "nxattn_status_string", "nxattn_last_error", "nxattn_version")
@@ -39,6 +39,12 @@ class RopeDesc(ctypes.Structure):
     _fields_ = [("n_axes", ctypes.c_int32), ("grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int32 * 3),
                 ("offset", ctypes.c_int32 * 3), ("theta", ctypes.c_double), ("interleaved", ctypes.c_int32),
                 ("global_freq", ctypes.c_int32)]
+
+
+class RelayoutJob(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("layers", ctypes.c_int64),
+                ("kv_heads", ctypes.c_int64), ("seq", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("dir", ctypes.c_int32)]
 
 
 class Fp8Tensor(ctypes.Structure):
@@ -96,6 +102,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nxattn_rope_apply.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), i32,
                                       ctypes.POINTER(RopeDesc), vp]
     lib.nxattn_rope_apply.restype = i32
+    lib.nxattn_rope_apply_relayout.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64), i32,
+                                               ctypes.POINTER(RopeDesc), ctypes.POINTER(RelayoutJob), ctypes.c_int32, vp]
+    lib.nxattn_rope_apply_relayout.restype = i32
     lib.nxattn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp]
     lib.nxattn_fwd.restype = i32
     lib.nxattn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_int64)]
@@ -184,8 +193,8 @@ def rope_desc(grid: Sequence[int], pairs: Sequence[int], offset: Sequence[int], 
 
 
 # ---------------------------------------------------------------------------------------
-def nxattn_kv_relayout(src: torch.Tensor, dst: torch.Tensor, direction: int, stream=None) -> None:
-    """dir 0: src replay [L,2,H,S,D] -> dst online [L,2,S,H,D]; dir 1: the inverse."""
+def _relayout_sizes(src: torch.Tensor, dst: torch.Tensor, direction: int):
+    """(L, H, S, D) of a relayout of src into dst (checked as nxattn_kv_relayout takes them)."""
     _gpu(src, dst)
     if src.dim() != 5 or dst.dim() != 5 or src.shape[1] != 2:
         raise NxattnError(1, "relayout expects 5-D [L, 2, ., ., D] tensors")
@@ -197,6 +206,12 @@ def nxattn_kv_relayout(src: torch.Tensor, dst: torch.Tensor, direction: int, str
     H, S = (A, B) if direction == 0 else (B, A)
     if tuple(dst.shape) != (L, 2, B, A, D):
         raise NxattnError(1, f"dst shape {tuple(dst.shape)} does not match {(L, 2, B, A, D)}")
+    return L, H, S, D
+
+
+def nxattn_kv_relayout(src: torch.Tensor, dst: torch.Tensor, direction: int, stream=None) -> None:
+    """dir 0: src replay [L,2,H,S,D] -> dst online [L,2,S,H,D]; dir 1: the inverse."""
+    L, H, S, D = _relayout_sizes(src, dst, direction)
     _check(load().nxattn_kv_relayout(src.data_ptr(), dst.data_ptr(), L, H, S, D, _dtype_code(src),
                                      int(direction), _stream(stream)))
 
@@ -214,6 +229,34 @@ def nxattn_rope_apply(x: torch.Tensor, descs: List[RopeDesc], stream=None) -> No
     st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
     arr = (RopeDesc * max(1, B))(*descs)
     _check(load().nxattn_rope_apply(x.data_ptr(), B, S, H, D, st, _dtype_code(x), arr, _stream(stream)))
+
+
+def nxattn_rope_apply_relayout(x: torch.Tensor, descs: List[RopeDesc],
+                               jobs: Sequence[tuple] = (), stream=None) -> None:
+    """nxattn_rope_apply(x, descs) and, in the same launch, nxattn_kv_relayout(src, dst,
+    direction) for each (src, dst, direction) in jobs (tensors of x's dtype)."""
+    _gpu(x)
+    if x.dim() != 4:
+        raise NxattnError(1, "x must be [B, S, H, D]")
+    B, S, H, D = x.shape
+    if x.stride(3) != 1:
+        raise NxattnError(1, "the head_dim dimension must be contiguous")
+    if len(descs) != B:
+        raise NxattnError(1, "one RopeDesc per batch entry is required")
+    if len(jobs) > MAX_BRANCHES:
+        raise NxattnError(1, f"at most {MAX_BRANCHES} relayout jobs")
+    arr_j = (RelayoutJob * max(1, len(jobs)))()
+    for i, (src, dst, direction) in enumerate(jobs):
+        if src.dtype != x.dtype:
+            raise NxattnError(1, "relayout jobs must have x's dtype")
+        L, Hk, Sk, Dk = _relayout_sizes(src, dst, direction)
+        j = arr_j[i]
+        j.src, j.dst, j.layers, j.kv_heads, j.seq, j.head_dim, j.dir = (src.data_ptr(), dst.data_ptr(), L, Hk, Sk,
+                                                                         Dk, int(direction))
+    st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    arr = (RopeDesc * max(1, B))(*descs)
+    _check(load().nxattn_rope_apply_relayout(x.data_ptr(), B, S, H, D, st, _dtype_code(x), arr, arr_j, len(jobs),
+                                             _stream(stream)))
 
 
 def make_fwd_args(q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], o: Optional[torch.Tensor],

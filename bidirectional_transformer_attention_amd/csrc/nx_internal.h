@@ -96,14 +96,46 @@ struct RopeTensors {
 };
 enum class RopeMode { Rotate, Max, Codes, Blocks };
 
+// ---- KV relayout ----------------------------------------------------------------------
+// Rows of vpr vectors: src viewed as [LC][A][B][vpr], dst as [LC][B][A][vpr] (replay <->
+// online, dims 2 and 3 exchanged); this thread moves vectors i0, i0 + step, ... of dst.
+template <typename V>
+__device__ __forceinline__ void relayout_rows(const V* __restrict__ src, V* __restrict__ dst, int64_t A, int64_t B,
+                                              int64_t vpr, int64_t total, int64_t i0, int64_t step) {
+  for (int64_t i = i0; i < total; i += step) {
+    const int64_t c = i % vpr;
+    const int64_t r = i / vpr;        // destination row (lc, b, a)
+    const int64_t a = r % A;
+    const int64_t t = r / A;
+    const int64_t b = t % B;
+    const int64_t lc = t / B;
+    dst[i] = src[((lc * A + a) * B + b) * vpr + c];
+  }
+}
+// Relayout jobs appended to a RoPE launch (16-byte vectors): job j moves `total` vectors
+// with the workgroups blk0[j] .. blk0[j + 1] - 1 after the RoPE workgroups.
+struct RelayoutJobs {
+  const u32x4* src[NXATTN_MAX_BRANCHES];
+  u32x4* dst[NXATTN_MAX_BRANCHES];
+  int64_t A[NXATTN_MAX_BRANCHES], B[NXATTN_MAX_BRANCHES], vpr[NXATTN_MAX_BRANCHES], total[NXATTN_MAX_BRANCHES];
+  int32_t blk0[NXATTN_MAX_BRANCHES + 1];
+  int32_t n;
+};
+// workgroups a relayout of `total` vectors takes (as its own launch would)
+inline int32_t relayout_blocks(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int32_t)(blocks < 256 * 64 ? blocks : 256 * 64);
+}
+
 // Validates the RoPE arguments (errors name `who`; rope and the x pointers and strides of
 // every tensor) and launches: with fp8 == false, the in-place rotation of x[0]; with
 // fp8 == true (total heads <= 4096), the clear of the maxima, the pass that takes them
 // from the rotated values and the pass that writes exponents and codes, or with
 // tt.blocks the one pass that writes codes and block scales. The caller checks codes,
-// exps, scales and amax.
+// exps, scales and amax. With jobs (rotation only; checked by the caller), the jobs' rows
+// move in the same launch.
 int rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64_t seq, int64_t head_dim, int dtype,
-                const nxattn_rope_desc* rope, bool fp8, hipStream_t stream);
+                const nxattn_rope_desc* rope, bool fp8, hipStream_t stream, const RelayoutJobs* jobs = nullptr);
 
 // nxattn_rope_quantize_fp8 (validation and launches; errors name `who`) with the running
 // maxima in `workspace`.

@@ -13,17 +13,8 @@ namespace nx {
 template <typename V>
 __global__ __launch_bounds__(256) void relayout_kernel(const V* __restrict__ src, V* __restrict__ dst,
                                                        int64_t A, int64_t B, int64_t vpr, int64_t total) {
-  // src viewed as [LC][A][B][vpr], dst as [LC][B][A][vpr]
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
-    const int64_t c = i % vpr;
-    const int64_t r = i / vpr;        // destination row (lc, b, a)
-    const int64_t a = r % A;
-    const int64_t t = r / A;
-    const int64_t b = t % B;
-    const int64_t lc = t / B;
-    dst[i] = src[((lc * A + a) * B + b) * vpr + c];
-  }
+  relayout_rows(src, dst, A, B, vpr, total, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                (int64_t)gridDim.x * blockDim.x);
 }
 
 template <typename V>
@@ -31,8 +22,7 @@ static int launch(const void* src, void* dst, int64_t A, int64_t B, int64_t row_
                   hipStream_t stream) {
   const int64_t vpr = row_bytes / (int64_t)sizeof(V);
   const int64_t total = vpr * rows_total;
-  const int64_t blocks = (total + 255) / 256;
-  const int grid = (int)(blocks < 256 * 64 ? blocks : 256 * 64);
+  const int grid = relayout_blocks(total);
   relayout_kernel<V><<<grid, 256, 0, stream>>>(static_cast<const V*>(src), static_cast<V*>(dst), A, B, vpr, total);
   return check_launch("nxattn_kv_relayout");
 }

@@ -95,9 +95,10 @@ __device__ __forceinline__ V pick(const V (&a)[ROPE_MAX_TENSORS], int t) {
 // rotated, rounded values times 2^-e. MODE Blocks: x is read only; each run of 32
 // elements of a row takes its exponent from its own maximum, reduced over the lanes that
 // hold the run, and the codes and the run's E8M0 scale are written in the same pass.
+// The work of one workgroup (block index blk) of the RoPE launch.
 template <typename T, RopeMode MODE>
-__global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, int32_t heads, int32_t D,
-                                                   RopeArgs args) {
+__device__ __forceinline__ void rope_block(const RopeTensors& tt, int32_t seq, int32_t heads, int32_t D,
+                                           const RopeArgs& args, int blk) {
   constexpr bool FP8 = MODE != RopeMode::Rotate;
   constexpr bool SLICE = MODE == RopeMode::Max || MODE == RopeMode::Codes;
   __shared__ float cs[ROPE_TOK][ROPE_MAX_HALF];
@@ -105,8 +106,8 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
   __shared__ uint32_t hw[SLICE ? ROPE_MAX_HEADS : 1];   // Max: running maxima; Codes: bits of 2^-e
   const int half = D / 2;
   const int blocks_per_branch = (seq + ROPE_TOK - 1) / ROPE_TOK;
-  const int b = (int)blockIdx.x / blocks_per_branch;
-  const int s0 = ((int)blockIdx.x - b * blocks_per_branch) * ROPE_TOK;
+  const int b = blk / blocks_per_branch;
+  const int s0 = (blk - b * blocks_per_branch) * ROPE_TOK;
   const RopeBranch& br = args.br[b];
   // tensor of launch head v: the number of tensor starts at or below v
   auto tensor_of = [&](int v) {
@@ -323,10 +324,34 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, 
     walk(std::false_type{});
   if constexpr (MODE == RopeMode::Max) {
     __syncthreads();
-    uint32_t* am = tt.amax + (blockIdx.x % AMAX_SLOTS) * tt.astride + (int64_t)b * heads;
+    uint32_t* am = tt.amax + (blk % AMAX_SLOTS) * tt.astride + (int64_t)b * heads;
     for (int w = threadIdx.x; w < heads; w += blockDim.x)
       if (hw[w] != 0u) atomicMax(&am[w], hw[w]);
   }
+}
+
+template <typename T, RopeMode MODE>
+__global__ __launch_bounds__(256) void rope_kernel(RopeTensors tt, int32_t seq, int32_t heads, int32_t D,
+                                                   RopeArgs args) {
+  rope_block<T, MODE>(tt, seq, heads, D, args, (int)blockIdx.x);
+}
+
+// The RoPE launch with relayout jobs appended: workgroups [0, nrope) rotate, the rest move
+// the jobs' rows (job j owns workgroups nrope + blk0[j] .. nrope + blk0[j + 1] - 1).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_relayout_kernel(RopeTensors tt, int32_t seq, int32_t heads, int32_t D,
+                                                            RopeArgs args, int32_t nrope, RelayoutJobs jobs) {
+  const int blk = (int)blockIdx.x;
+  if (blk < nrope) {
+    rope_block<T, RopeMode::Rotate>(tt, seq, heads, D, args, blk);
+    return;
+  }
+  const int r = blk - nrope;
+  int j = 0;
+  while (j + 1 < jobs.n && r >= jobs.blk0[j + 1]) ++j;
+  const int64_t nthreads = (int64_t)(jobs.blk0[j + 1] - jobs.blk0[j]) * 256;
+  relayout_rows(jobs.src[j], jobs.dst[j], jobs.A[j], jobs.B[j], jobs.vpr[j], jobs.total[j],
+                (int64_t)(r - jobs.blk0[j]) * 256 + threadIdx.x, nthreads);
 }
 
 }  // namespace nx
@@ -352,7 +377,7 @@ int nx::check_rope_desc(const nxattn_rope_desc& d, int64_t seq, int64_t head_dim
 }
 
 int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64_t seq, int64_t head_dim,
-                    int dtype, const nxattn_rope_desc* rope, bool fp8, hipStream_t stream) {
+                    int dtype, const nxattn_rope_desc* rope, bool fp8, hipStream_t stream, const RelayoutJobs* jobs) {
   if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
     return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
   const int64_t heads = tt.hoff[tt.n];
@@ -362,7 +387,18 @@ int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64
     return fail(NXATTN_ERR_UNSUPPORTED, "%s: head_dim %lld must be a multiple of 8 in [8, 256]", who, (long long)head_dim);
   if (seq > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: size out of range", who);
   if (fp8 && heads > ROPE_MAX_HEADS) return fail(NXATTN_ERR_UNSUPPORTED, "%s: heads > %d in total", who, ROPE_MAX_HEADS);
-  if (batch == 0 || seq == 0 || heads == 0) return NXATTN_OK;
+  const bool with_jobs = jobs && jobs->n > 0;
+  if (batch == 0 || seq == 0 || heads == 0) {
+    if (!with_jobs) return NXATTN_OK;
+    // relayout jobs alone
+    RopeArgs none;
+    memset(&none, 0, sizeof(none));
+    if (dtype == NXATTN_BF16)
+      rope_relayout_kernel<uint16_t><<<jobs->blk0[jobs->n], 256, 0, stream>>>(tt, 1, 1, 8, none, 0, *jobs);
+    else
+      rope_relayout_kernel<float><<<jobs->blk0[jobs->n], 256, 0, stream>>>(tt, 1, 1, 8, none, 0, *jobs);
+    return check_launch(who);
+  }
   if (!rope) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
   RopeArgs args;
   memset(&args, 0, sizeof(args));
@@ -390,8 +426,19 @@ int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64
     }
   }
   const int64_t blocks = batch * ((seq + ROPE_TOK - 1) / ROPE_TOK);
-  if (blocks > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: too many tokens", who);
+  if (blocks + (with_jobs ? jobs->blk0[jobs->n] : 0) > INT32_MAX)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: too many tokens", who);
   const unsigned grid = (unsigned)blocks;
+  if (with_jobs) {
+    const unsigned g2 = grid + (unsigned)jobs->blk0[jobs->n];
+    if (dtype == NXATTN_BF16)
+      rope_relayout_kernel<uint16_t><<<g2, 256, 0, stream>>>(tt, (int32_t)seq, (int32_t)heads, (int32_t)head_dim, args,
+                                                              (int32_t)blocks, *jobs);
+    else
+      rope_relayout_kernel<float><<<g2, 256, 0, stream>>>(tt, (int32_t)seq, (int32_t)heads, (int32_t)head_dim, args,
+                                                           (int32_t)blocks, *jobs);
+    return check_launch(who);
+  }
   auto launch = [&](auto* tp, auto mode_tag) {
     using T = std::remove_pointer_t<decltype(tp)>;
     constexpr RopeMode M = decltype(mode_tag)::value;
@@ -433,4 +480,72 @@ extern "C" int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t he
   if (strides) { tt.sb[0] = strides[0]; tt.ss[0] = strides[1]; tt.sh[0] = strides[2]; }
   for (int i = 1; i <= ROPE_MAX_TENSORS; ++i) tt.hoff[i] = (int32_t)heads;
   return rope_launch("nxattn_rope_apply", tt, batch, seq, head_dim, dtype, rope, false, stream);
+}
+
+extern "C" int nxattn_rope_apply_relayout(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                                          const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
+                                          const nxattn_relayout_job* jobs, int32_t n_jobs, hipStream_t stream) {
+  static const char* who = "nxattn_rope_apply_relayout";
+  clear_error();
+  if (heads < 0 || heads > (1 << 28))
+    return fail(heads < 0 ? NXATTN_ERR_INVALID : NXATTN_ERR_UNSUPPORTED, "%s: heads out of range", who);
+  if (batch > 0 && seq > 0 && heads > 0 && !strides) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
+  if (n_jobs < 0 || n_jobs > NXATTN_MAX_BRANCHES)
+    return fail(NXATTN_ERR_INVALID, "%s: n_jobs %d not in [0, %d]", who, n_jobs, NXATTN_MAX_BRANCHES);
+  if (n_jobs > 0 && !jobs) return fail(NXATTN_ERR_INVALID, "%s: NULL jobs", who);
+  if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
+  const int64_t es = esize(dtype);
+  // the rotated tensor's byte extent (for the overlap checks)
+  int64_t xb = 0;
+  if (batch > 0 && seq > 0 && heads > 0 && head_dim > 0 && strides)
+    xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
+  RelayoutJobs rj;
+  memset(&rj, 0, sizeof(rj));
+  int64_t jbytes[NXATTN_MAX_BRANCHES] = {0};
+  for (int32_t i = 0; i < n_jobs; ++i) {
+    const nxattn_relayout_job& j = jobs[i];
+    if (j.dir != 0 && j.dir != 1) return fail(NXATTN_ERR_INVALID, "%s: job %d: dir must be 0 or 1", who, i);
+    if (j.layers < 0 || j.kv_heads < 0 || j.seq < 0 || j.head_dim < 0)
+      return fail(NXATTN_ERR_INVALID, "%s: job %d: negative size", who, i);
+    if (j.layers == 0 || j.kv_heads == 0 || j.seq == 0 || j.head_dim == 0) continue;
+    if (!j.src || !j.dst) return fail(NXATTN_ERR_INVALID, "%s: job %d: NULL pointer", who, i);
+    if (j.head_dim > (INT64_C(1) << 20) || j.kv_heads > (INT64_C(1) << 20) || j.seq > (INT64_C(1) << 31) ||
+        j.layers > (INT64_C(1) << 20))
+      return fail(NXATTN_ERR_UNSUPPORTED, "%s: job %d: size out of range", who, i);
+    const int64_t row_bytes = j.head_dim * es;
+    if (row_bytes % 16 != 0 || !aligned16(j.src) || !aligned16(j.dst))
+      return fail(NXATTN_ERR_UNSUPPORTED, "%s: job %d: rows and pointers must be 16-byte multiples "
+                  "(nxattn_kv_relayout takes the others)", who, i);
+    const int64_t rows = j.layers * 2 * j.kv_heads * j.seq;
+    jbytes[i] = rows * row_bytes;
+    const int n = rj.n;
+    rj.src[n] = static_cast<const u32x4*>(j.src);
+    rj.dst[n] = static_cast<u32x4*>(j.dst);
+    rj.A[n] = j.dir == 0 ? j.kv_heads : j.seq;
+    rj.B[n] = j.dir == 0 ? j.seq : j.kv_heads;
+    rj.vpr[n] = row_bytes / 16;
+    rj.total[n] = rj.vpr[n] * rows;
+    rj.blk0[n + 1] = rj.blk0[n] + relayout_blocks(rj.total[n]);
+    ++rj.n;
+  }
+  // every job's destination must overlap nothing it or the rotation reads or writes
+  for (int32_t i = 0; i < n_jobs; ++i) {
+    if (!jbytes[i]) continue;
+    if (overlaps(jobs[i].dst, jbytes[i], x, xb) || overlaps(jobs[i].src, jbytes[i], x, xb))
+      return fail(NXATTN_ERR_INVALID, "%s: job %d overlaps x", who, i);
+    for (int32_t k = 0; k < n_jobs; ++k)
+      if (jbytes[k] && overlaps(jobs[i].dst, jbytes[i], jobs[k].src, jbytes[k]))
+        return fail(NXATTN_ERR_INVALID, "%s: job %d's dst overlaps job %d's src", who, i, k);
+    for (int32_t k = 0; k < i; ++k)
+      if (jbytes[k] && overlaps(jobs[i].dst, jbytes[i], jobs[k].dst, jbytes[k]))
+        return fail(NXATTN_ERR_INVALID, "%s: the dst of jobs %d and %d overlap", who, k, i);
+  }
+  RopeTensors tt;
+  memset(&tt, 0, sizeof(tt));
+  tt.n = 1;
+  tt.x[0] = x;
+  if (strides) { tt.sb[0] = strides[0]; tt.ss[0] = strides[1]; tt.sh[0] = strides[2]; }
+  for (int i = 1; i <= ROPE_MAX_TENSORS; ++i) tt.hoff[i] = (int32_t)heads;
+  return rope_launch(who, tt, batch, seq, head_dim, dtype, rope, false, stream, &rj);
 }

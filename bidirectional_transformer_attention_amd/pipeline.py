@@ -2,7 +2,8 @@
 
     relayout (replay -> online, when the prefix arrives in the replay layout)
     -> RoPE on own k, and on own q unless the attention kernel rotates q as it loads it
-       (the bf16 path; every branch with its own offsets)
+       (the bf16 path; every branch with its own offsets); the relayouts run as extra
+       workgroups of the launch that rotates k (``fuse_prep``)
     -> fused attention over [prefix ++ own] for all branches in one launch (or, with
        key splits, one launch over key ranges plus one merge launch)
     -> CFG combine of branch 0 (cond) and branch 1 (uncond) when guidance applies: with
@@ -34,7 +35,7 @@ from .synth import Inputs, Workload
 class AttentionStep:
     def __init__(self, wl: Workload, inp: Inputs, device: str = "cuda", fuse_q_rope: Optional[bool] = None,
                  splits: Optional[int] = None, fold_q: bool = True, q_on_load: bool = False,
-                 fuse_cfg: Optional[bool] = None, keep_branches: bool = True):
+                 fuse_cfg: Optional[bool] = None, keep_branches: bool = True, fuse_prep: Optional[bool] = None):
         self.wl = wl
         # fp8: q's codes carry softmax_scale*log2(e), so the attention's softmax takes one
         # exp2 per score with no multiply in front
@@ -110,8 +111,12 @@ class AttentionStep:
             raise ValueError("the guidance combination folds into the bf16 / fp8 attention call with one key "
                              "range only")
         self.keep_branches = bool(keep_branches) or not self.fuse_cfg
+        # the prefix relayouts ride in the launch that rotates k (fp8 workloads rotate
+        # inside their quantizer instead, and relay once when set up)
+        self.fuse_prep = (not wl.qk_fp8 and any(p is not None for p in self.prefix_src)) if fuse_prep is None \
+            else bool(fuse_prep) and not wl.qk_fp8
         if wl.qk_fp8:
-            self.relayout()
+            self.relayout(always=True)
             self.quantize_prefix()
 
     def quantize_prefix(self) -> None:
@@ -124,17 +129,24 @@ class AttentionStep:
             else:
                 nx.nxattn_quantize_fp8(p[0].unsqueeze(0), self.pk8[b], self.pke[b:b + 1], self.qws)
 
-    def relayout(self) -> None:
-        for src, dst in zip(self.prefix_src, self.prefix_online):
-            if src is not None:
-                nx.nxattn_kv_relayout(src, dst.unsqueeze(0), 0)
+    def relayout_jobs(self) -> list:
+        return [(src, dst.unsqueeze(0), 0) for src, dst in zip(self.prefix_src, self.prefix_online) if src is not None]
+
+    def relayout(self, always: bool = False) -> None:
+        if self.fuse_prep and not always:
+            return                      # done in rope()
+        for src, dst, d in self.relayout_jobs():
+            nx.nxattn_kv_relayout(src, dst, d)
 
     def rope(self) -> None:
         if self.wl.qk_fp8:
             return                      # rotated inside quantize(): only the codes are needed
         if not self.fuse_q_rope:
             nx.nxattn_rope_apply(self.q, self.descs)
-        nx.nxattn_rope_apply(self.k, self.descs)
+        if self.fuse_prep:
+            nx.nxattn_rope_apply_relayout(self.k, self.descs, self.relayout_jobs())
+        else:
+            nx.nxattn_rope_apply(self.k, self.descs)
 
     def quantize(self) -> None:
         """E4M3 codes of the rotated q and k (one call for both: the rotation evaluated

@@ -98,6 +98,32 @@ int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_
                       hipStream_t stream);
 
 /*
+ * The RoPE of x (exactly nxattn_rope_apply, same arguments and checks) and n_jobs KV
+ * relayouts (each exactly nxattn_kv_relayout of its job: replay <-> online layout, NeoPP
+ * page, "KV file layout") in one launch: a DiT step's rotation of k and the relayout of
+ * each branch's prefix then cost one kernel boundary instead of 1 + n_jobs. The jobs run
+ * in workgroups appended after the rotation's; the results are bit for bit those of the
+ * separate calls.
+ *   jobs: host array of n_jobs (0 .. NXATTN_MAX_BRANCHES) descriptors, read during the
+ *   call; each job's src and dst hold layers*2*kv_heads*seq rows of head_dim elements of
+ *   x's dtype. Rows and pointers must be 16-byte multiples (NXATTN_ERR_UNSUPPORTED
+ *   otherwise: nxattn_kv_relayout takes the rest). No job's src or dst may overlap x, a
+ *   job's dst may not overlap any job's src or another job's dst (NXATTN_ERR_INVALID).
+ *   Jobs with a zero size are skipped; with no rotation work (batch, seq or heads zero;
+ *   head_dim is still checked), the jobs alone run.
+ */
+typedef struct {
+  const void* src;
+  void* dst;
+  int64_t layers, kv_heads, seq, head_dim;
+  int32_t dir;                       /* 0: replay -> online, 1: online -> replay */
+} nxattn_relayout_job;
+
+int nxattn_rope_apply_relayout(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                               const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
+                               const nxattn_relayout_job* jobs, int32_t n_jobs, hipStream_t stream);
+
+/*
  * Fused non-causal attention over [prefix ++ own] for every branch of a CFG batch.
  * KLiteInfer page, section "架构": bidirectional attention is scores GEMM, softmax,
  * output GEMM (here fused, the score matrix never leaves the chip); NeoPP page:

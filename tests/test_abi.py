@@ -537,6 +537,44 @@ def test_rope_rejects(lib):
     assert rope_call(lib, [good], S=0) == OK
 
 
+def rope_relayout_call(lib, jobs, n=None, descs=None, S=64, D=64, ptr=FAKE):
+    descs = descs or [nx.rope_desc((S,), (D // 2,), (0,))] if S else [nx.rope_desc((64,), (32,), (0,))]
+    st = (ctypes.c_int64 * 3)(S * 2 * D, 2 * D, D)
+    arr = (binding.RopeDesc * 1)(*descs)
+    arr_j = (binding.RelayoutJob * max(1, len(jobs)))()
+    for i, kw in enumerate(jobs):
+        j = arr_j[i]
+        j.src, j.dst = kw.get("src", FAKE + GB), kw.get("dst", FAKE + 2 * GB)
+        j.layers, j.kv_heads, j.seq, j.head_dim = kw.get("L", 1), kw.get("H", 2), kw.get("S", 16), kw.get("D", 64)
+        j.dir = kw.get("dir", 0)
+    return lib.nxattn_rope_apply_relayout(ptr, 1, S, 2, D, st, 0, arr, arr_j if jobs else None,
+                                          len(jobs) if n is None else n, None)
+
+
+@pytest.mark.parametrize("jobs,n,kw,code,msg", [
+    ([], 9, {}, INVALID, "n_jobs"),
+    ([], 1, {}, INVALID, "NULL jobs"),
+    ([dict(dir=2)], None, {}, INVALID, "dir"),
+    ([dict(S=-1)], None, {}, INVALID, "negative size"),
+    ([dict(src=None)], None, {}, INVALID, "NULL pointer"),
+    ([dict(D=62)], None, {}, UNSUPPORTED, "16-byte"),                     # 248-byte rows (f32)
+    ([dict(dst=FAKE + 2 * GB + 8)], None, {}, UNSUPPORTED, "16-byte"),
+    ([dict(dst=FAKE + 1024)], None, {}, INVALID, "overlaps x"),            # x is 32 KiB at FAKE
+    ([dict(src=FAKE + 4096)], None, {}, INVALID, "overlaps x"),
+    ([dict(), dict(src=FAKE + 3 * GB, dst=FAKE + 2 * GB + 64)], None, {}, INVALID, "dst of jobs 0 and 1 overlap"),
+    ([dict(), dict(src=FAKE + 2 * GB + 64, dst=FAKE + 3 * GB)], None, {}, INVALID, "dst overlaps job 1's src"),
+    ([dict()], None, dict(D=60), UNSUPPORTED, "head_dim"),                # the rotation's own checks still apply
+])
+def test_rope_relayout_rejects(lib, jobs, n, kw, code, msg):
+    assert rope_relayout_call(lib, jobs, n, **kw) == code
+    assert msg in nx.last_error()
+
+
+def test_rope_relayout_empty_is_a_noop(lib):
+    assert rope_relayout_call(lib, [], S=0) == OK
+    assert rope_relayout_call(lib, [dict(L=0)], S=0) == OK              # zero-size job skipped
+
+
 # ----------------------------------------------------------------------------- cfg
 def test_cfg_rejects(lib):
     f = lib.nxattn_cfg_combine

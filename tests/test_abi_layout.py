@@ -24,6 +24,7 @@ STRUCTS = {
     "nxattn_fp8_tensor": binding.Fp8Tensor,
     "nxattn_fwd_args": binding.FwdArgs,
     "nxattn_fwd_fp8_args": binding.FwdFp8Args,
+    "nxattn_relayout_job": binding.RelayoutJob,
 }
 
 
