@@ -4,15 +4,22 @@
 //
 // One workgroup handles TOK consecutive tokens of one branch. The angle of each
 // (token, pair) depends only on the position and the pair, not on the head, so the
-// workgroup first evaluates cos/sin once per (token, pair) in fp64 into LDS, then all
-// threads rotate every head of those tokens. A thread owns four consecutive rotary
-// pairs of one (token, head) and moves them with one or two vector loads. HBM-bound:
+// workgroup first evaluates cos/sin once per (token, pair) into LDS, then all threads
+// rotate every head of those tokens. fp32 data: the angle in fp64 and the library's fp64
+// sine and cosine. bf16 data with every position below 2^24: each pair's step in
+// revolutions per position is evaluated once in fp64 and split into two fp32 parts,
+// and the turn pos * step is formed exactly but for the roundings of small terms
+// (below 1e-7 revolutions) and taken by the hardware sine and cosine, far below the bf16
+// rounding of the result. A thread owns four consecutive rotary pairs of one
+// (token, head) and moves them with one or two vector loads. HBM-bound:
 // 2 * B*S*H*D*esize bytes per call.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <type_traits>
 
 #include "nx_internal.h"
+#include "rope_turn.h"
 
 namespace nx {
 
@@ -28,6 +35,7 @@ struct RopeBranch {
 };
 struct RopeArgs {
   RopeBranch br[NXATTN_MAX_BRANCHES];
+  int32_t turns;      // bf16 data, every position below 2^24: turns in fp32 revolutions
 };
 
 // codes of 4 scaled values; the scaled values of finite inputs lie in [-448, 448], where
@@ -140,6 +148,36 @@ __device__ __forceinline__ void rope_block(const RopeTensors& tt, int32_t seq, i
   const int g1 = br.grid[1], g2 = br.grid[2];
   const int p0 = br.pairs[0], p1 = br.pairs[1], p2 = br.pairs[2];
   const int f0 = br.offset[0], f1 = br.offset[1], f2 = br.offset[2];
+  if (sizeof(T) == 2 && args.turns) {
+    // each pair's step in revolutions per position (fp64, once), as hi + lo in fp32
+    __shared__ float st_hi[ROPE_MAX_HALF], st_lo[ROPE_MAX_HALF];
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+      const bool ax1 = j >= p0, ax2 = j >= p0 + p1;
+      const int u = j - (ax1 ? p0 : 0) - (ax2 ? p1 : 0);
+      const int pk = ax2 ? p2 : ax1 ? p1 : p0;
+      const double e = br.global_freq ? -2.0 * (double)j / (double)D : -2.0 * (double)u / (2.0 * (double)pk);
+      const double step = exp2_taylor(br.log2_theta * e) * 0.15915494309189535;
+      const float hi = (float)step;
+      st_hi[j] = hi;
+      st_lo[j] = (float)(step - (double)hi);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ROPE_TOK * half; idx += blockDim.x) {
+      const int tk = idx / half, j = idx - tk * half;
+      const int s = s0 + tk;
+      if (s >= seq) continue;
+      const int s12 = s / g2, c2 = s - s12 * g2;
+      const int c0 = s12 / g1, c1 = s12 - c0 * g1;
+      const bool ax1 = j >= p0, ax2 = j >= p0 + p1;
+      const float pos = (float)(ax2 ? c2 + f2 : ax1 ? c1 + f1 : c0 + f0);   // exact below 2^24
+      const float hi = st_hi[j];
+      const float rev = pos * hi;
+      const float err = __builtin_fmaf(pos, hi, -rev);
+      const float f = __builtin_amdgcn_fractf(rev) + __builtin_fmaf(pos, st_lo[j], err);
+      cs[tk][j] = __builtin_amdgcn_cosf(f);
+      sn[tk][j] = __builtin_amdgcn_sinf(f);
+    }
+  } else
   for (int idx = threadIdx.x; idx < ROPE_TOK * half; idx += blockDim.x) {
     const int tk = idx / half, j = idx - tk * half;
     const int s = s0 + tk;
@@ -402,10 +440,13 @@ int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64
   if (!rope) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);
   RopeArgs args;
   memset(&args, 0, sizeof(args));
+  // bf16 data: angles as exact fp32 turns when every position is below 2^24 (fp32 integers)
+  int64_t max_pos = 0;
   for (int64_t b = 0; b < batch; ++b) {
     const nxattn_rope_desc& d = rope[b];
     const int st = check_rope_desc(d, seq, head_dim, who);
     if (st != NXATTN_OK) return st;
+    for (int a = 0; a < d.n_axes; ++a) max_pos = std::max<int64_t>(max_pos, (int64_t)d.offset[a] + d.grid[a] - 1);
     RopeBranch& r = args.br[b];
     r.n_axes = d.n_axes; r.interleaved = d.interleaved; r.global_freq = d.global_freq;
     r.log2_theta = std::log2(d.theta);
@@ -415,6 +456,7 @@ int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64
       r.offset[a] = a < d.n_axes ? d.offset[a] : 0;
     }
   }
+  args.turns = dtype == NXATTN_BF16 && max_pos < (INT64_C(1) << 24);
   const int64_t es = esize(dtype);
   for (int t = 0; t < tt.n; ++t) {
     if (!tt.x[t]) return fail(NXATTN_ERR_INVALID, "%s: NULL pointer", who);

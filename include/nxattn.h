@@ -90,8 +90,12 @@ typedef struct {
  * strides = {stride_b, stride_s, stride_h} in elements; the head_dim elements of a
  * row are contiguous. rope points to `batch` host descriptors (one per branch, so the
  * two CFG branches may use different offsets); batch <= NXATTN_MAX_BRANCHES.
- * The rotation is computed in fp32 from an fp64 angle; bf16 results are rounded to
- * nearest even. Supported: head_dim even, 8 <= head_dim <= 256, dtype F32 or BF16.
+ * The rotation is computed in fp32. F32 data: from an fp64 angle and fp64 sine and
+ * cosine. BF16 data (every position below 2^24): each pair's step in revolutions is
+ * evaluated in fp64 and the turn position * step formed exactly in fp32 but for the
+ * roundings of small terms (below 1e-7 revolutions), then taken by the hardware sine and
+ * cosine, as q_rope in nxattn_fwd does; bf16 results are rounded to nearest even.
+ * Supported: head_dim a multiple of 8, 8 <= head_dim <= 256, dtype F32 or BF16.
  */
 int nxattn_rope_apply(void* x, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                       const int64_t strides[3], int dtype, const nxattn_rope_desc* rope,
