@@ -699,38 +699,68 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   }
   if (PAIR) {
     // no early exit: every wave takes part in the second branch's barriers
-    if (active && tok < a.seq) {
+    if constexpr (bi == 0) {
+      if (active && tok < a.seq) {
+        const float inv = 1.0f / w.l;
+        if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
+        uint16_t* orow = a.o ? a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2 : nullptr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = 32 * db + 8 * i4 + 4 * hh;
+            const u32x2 r = u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
+                                  pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
+            if (orow) *reinterpret_cast<u32x2*>(orow + d) = r;
+            *(__attribute__((address_space(3))) u32x2*)&lds_keep[(wave * 16 + 4 * db + i4) * 64 + lane] = r;
+          }
+      }
+    } else if (active) {
+      // The wave's 32 rows: this lane's row half of branch 0 (kept in LDS) in registers
+      // first; then the guided values go back into the same 8 KB, row-major with the 16-byte
+      // chunk c of row n at chunk c ^ (n & 15), and leave as whole 256-byte rows (16 lanes
+      // per row) instead of 8-byte pieces of 32 rows per store.
+      const bool valid = tok < a.seq;
       const float inv = 1.0f / w.l;
-      if (a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
-      uint16_t* orow = a.o ? a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2 : nullptr;
-      uint16_t* crow = a.cfg + (int64_t)tok * a.cs0 + (int64_t)hq * a.cs1;
+      if (valid && a.lse && hh == 0) a.lse[((int64_t)b * a.heads_q + hq) * a.seq + tok] = LN2 * (w.m + __builtin_amdgcn_logf(w.l));
+      uint16_t* orow = (valid && a.o) ? a.o + b * a.os0 + (int64_t)tok * a.os1 + (int64_t)hq * a.os2 : nullptr;
+      typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+      lds_u32x2* keep = (lds_u32x2*)&lds_keep[wave * 16 * 64];
+      u32x2 cv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) cv[j] = keep[j * 64 + lane];
+      lds_u8* stage = (lds_u8*)&lds_keep[wave * 16 * 64];
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = 32 * db + 8 * i4 + 4 * hh;
+          const int d = 32 * db + 8 * i4 + 4 * hh, ch = 4 * db + i4;
           const u32x2 r = u32x2{pack_bf16x2(w.o[db][4 * i4] * inv, w.o[db][4 * i4 + 1] * inv),
                                 pack_bf16x2(w.o[db][4 * i4 + 2] * inv, w.o[db][4 * i4 + 3] * inv)};
           if (orow) *reinterpret_cast<u32x2*>(orow + d) = r;
-          __attribute__((address_space(3))) u32x2* kp =
-              (__attribute__((address_space(3))) u32x2*)&lds_keep[(wave * 16 + 4 * db + i4) * 64 + lane];
-          if constexpr (bi == 0) {
-            *kp = r;
-          } else {
-            const u32x2 cv = *kp;
-            // the arithmetic of the combine pass on the two rounded outputs: c = branch 0,
-            // u = branch 1, fma(guidance, c - u, u) in fp32, rounded to nearest even
-            u32x2 o2;
+          // the arithmetic of the combine pass on the two rounded outputs: c = branch 0,
+          // u = branch 1, fma(guidance, c - u, u) in fp32, rounded to nearest even
+          u32x2 o2;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const uint32_t cw = cv[e], uw = r[e];
-              const float c0 = __uint_as_float(cw << 16), c1 = __uint_as_float(cw & 0xffff0000u);
-              const float u0 = __uint_as_float(uw << 16), u1 = __uint_as_float(uw & 0xffff0000u);
-              o2[e] = pack_bf16x2(__builtin_fmaf(a.guidance, c0 - u0, u0), __builtin_fmaf(a.guidance, c1 - u1, u1));
-            }
-            *reinterpret_cast<u32x2*>(crow + d) = o2;
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t cw = cv[ch][e], uw = r[e];
+            const float c0 = __uint_as_float(cw << 16), c1 = __uint_as_float(cw & 0xffff0000u);
+            const float u0 = __uint_as_float(uw << 16), u1 = __uint_as_float(uw & 0xffff0000u);
+            o2[e] = pack_bf16x2(__builtin_fmaf(a.guidance, c0 - u0, u0), __builtin_fmaf(a.guidance, c1 - u1, u1));
           }
+          *(lds_u32x2*)(stage + n * ROWB + 16 * (ch ^ (n & 15)) + 8 * hh) = o2;
         }
+      // lane L writes chunk L % 16 of rows L / 16 + 4k (the wave's own LDS writes above
+      // are ordered before these reads)
+      const int ch = lane & 15, tok0 = tok - n;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int nr = (lane >> 4) + 4 * k;
+        const u32x4 v = *(lds_u32x4*)(stage + nr * ROWB + 16 * (ch ^ (nr & 15)));
+        if (tok0 + nr < a.seq)
+          *reinterpret_cast<u32x4*>(a.cfg + (int64_t)(tok0 + nr) * a.cs0 + (int64_t)hq * a.cs1 + 8 * ch) = v;
+      }
     }
     return;
   }
