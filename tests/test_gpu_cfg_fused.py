@@ -16,6 +16,7 @@ from bidirectional_transformer_attention_amd.pipeline import AttentionStep
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+D_FP8 = 128
 
 
 def note(msg):
@@ -185,3 +186,37 @@ def test_step_fp8_fused_cfg_equals_separate_pass(name, q_on_load):
     assert same(keep.o, o_sep), "branch outputs differ"
     assert same(out_keep, out_sep), "combination differs (branch outputs stored)"
     assert same(out_lean, out_sep), "combination differs (no branch outputs)"
+
+
+@pytest.mark.parametrize("blocks", [True, False])
+def test_fwd_fp8_cfg_out_deterministic(blocks):
+    S, Hq, Hkv = 300, 8, 2
+    note(f"fwd_fp8 cfg_out determinism (blocks={blocks})")
+    q = synth.random_tensor((2, S, Hq, D_FP8), 331, torch.bfloat16).to(DEV)
+    k = synth.random_tensor((2, S, Hkv, D_FP8), 332, torch.bfloat16).to(DEV)
+    v = synth.random_tensor((2, S, Hkv, D_FP8), 333, torch.bfloat16).to(DEV)
+    pk = synth.random_tensor((1, 40, Hkv, D_FP8), 334, torch.bfloat16).to(DEV)
+    pv = synth.random_tensor((40, Hkv, D_FP8), 335, torch.bfloat16).to(DEV)
+    if blocks:
+        q8, qs = nx.nxattn_quantize_fp8_blocks(q)
+        k8, ks = nx.nxattn_quantize_fp8_blocks(k)
+        pk8, pks = nx.nxattn_quantize_fp8_blocks(pk)
+        args = (q8, k8, None, None, v)
+        kw = dict(q_scales=qs, k_scales=ks, prefix_k_scales=[pks[0], None])
+        pke = None
+    else:
+        q8, qe = nx.nxattn_quantize_fp8(q)
+        k8, ke = nx.nxattn_quantize_fp8(k)
+        pk8, pe = nx.nxattn_quantize_fp8(pk)
+        args = (q8, k8, qe, ke, v)
+        kw = {}
+        pke = torch.zeros((2, Hkv), dtype=torch.int8, device=DEV)
+        pke[0] = pe[0]
+    outs = []
+    for _ in range(3):
+        out = torch.full((S, Hq, D_FP8), float("nan"), dtype=torch.bfloat16, device=DEV)
+        nx.nxattn_fwd_fp8(*args, None, [pk8[0], None], [pv, None], pke, cfg_out=out, guidance=4.0, **kw)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0].float()).any()
+    assert all(same(outs[0], o) for o in outs[1:])
