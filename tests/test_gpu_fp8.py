@@ -191,6 +191,7 @@ def fp8_case(B, S, Hq, Hkv, P, seed, pre_mult=1.0, lse=True, fold=False):
     (3, 70, 2, 1, (5, 0, 64)),
     (2, 200, 4, 2, (300, 7)),     # prefix longer than the own tokens; ragged last tile
     (1, 129, 4, 4, (0,)),         # G = 1, no prefix
+    (8, 70, 4, 2, (0, 1, 63, 64, 65, 130, 7, 300)),   # the most branches a call takes
 ])
 def test_fwd_fp8_reduced(B, S, Hq, Hkv, P):
     fp8_case(B, S, Hq, Hkv, P, 4200 + S)

@@ -123,6 +123,9 @@ SPLIT_CASES = [
     (torch.bfloat16, 3, 70, 2, 1, 128, (5, 0, 64), 5),
     (torch.float32, 2, 97, 3, 3, 72, (13, 640), 4),
     (torch.float32, 1, 64, 2, 2, 64, (32,), 2),
+    # the most branches and the most key ranges a call takes
+    (torch.bfloat16, 8, 60, 4, 1, 128, (0, 300, 64, 1, 129, 700, 5, 40), 16),
+    (torch.float32, 8, 33, 2, 2, 64, (900, 0, 3, 64, 65, 2, 31, 200), 16),
 ]
 
 

@@ -97,6 +97,24 @@ def test_rope_strided_interleaved_and_per_branch_offsets():
         assert np.max(np.abs(f64(out[b, :, 1:5]) - ref)) <= 2e-6 * max(1.0, np.max(np.abs(ref)))
 
 
+def test_rope_most_branches():
+    # eight descriptors (the most a call takes), each with its own offsets and pair split
+    note("rope, 8 branches")
+    grid, D = (5, 7), 128
+    S = int(np.prod(grid))
+    x = synth.random_tensor((8, S, 3, D), 24, torch.bfloat16)
+    d = x.to(DEV)
+    splits = [(32, 32), (16, 48), (48, 16), (1, 63), (63, 1), (32, 32), (20, 44), (40, 24)]
+    offs = [(0, 0), (1, 2), (512, 512), (7, 0), (0, 9), (1000, 3), (65, 66), (2 ** 20, 5)]
+    nx.nxattn_rope_apply(d, [nx.rope_desc(grid, splits[b], offs[b]) for b in range(8)])
+    torch.cuda.synchronize()
+    out = d.cpu()
+    for b in range(8):
+        ref = oracle.rope(f64(x[b]), grid, splits[b], offs[b])
+        err = float(np.max(np.abs(f64(out[b]) - ref) / np.maximum(1.0, np.abs(ref))))
+        assert err <= 2.0 ** -8, (b, err)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_rope_global_frequency_ladder(dtype):
     # one theta ladder over all pairs, the sections choose the axis (3-D MRoPE)
@@ -201,6 +219,7 @@ def fwd_case(dtype, B, S, Hq, Hkv, D, plens, seed, scale_v=1.0):
     (3, 70, 2, 1, (5, 0, 64)),
     (2, 640, 8, 2, (128, 200)),   # whole prefix tiles, then a straddling one (processed last)
     (2, 200, 4, 2, (300, 7)),     # prefix longer than the own tokens; ragged last tile
+    (8, 97, 4, 2, (0, 1, 31, 64, 65, 127, 200, 3)),   # the most branches a call takes
 ])
 def test_fwd_bf16_reduced(B, S, Hq, Hkv, P):
     fwd_case(torch.bfloat16, B, S, Hq, Hkv, 128, P, 1000 + S)
@@ -212,6 +231,7 @@ def test_fwd_bf16_reduced(B, S, Hq, Hkv, P):
     (2, 97, 3, 3, 72, (13, 64)),
     (1, 1, 2, 1, 64, (0,)),
     (1, 5, 4, 4, 72, (70,)),
+    (8, 40, 2, 1, 72, (0, 5, 16, 17, 33, 64, 100, 2)),  # the most branches a call takes
 ])
 def test_fwd_f32_reduced(B, S, Hq, Hkv, D, P):
     fwd_case(torch.float32, B, S, Hq, Hkv, D, P, 2000 + S)
