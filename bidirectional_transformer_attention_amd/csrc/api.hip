@@ -149,6 +149,10 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
       if (sts[t][i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: negative stride");
       if ((sts[t][i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: stride %lld is not a multiple of 16 bytes", (long long)sts[t][i]);
     }
+  // key tiles (64 rows) are fetched through raw buffers with 32-bit byte offsets
+  if (own && a->kv_strides[1] > INT32_MAX / (es * KEY_TILE))
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: kv token stride %lld elements spans 2 GiB or more per %d rows",
+                (long long)a->kv_strides[1], KEY_TILE);
   if (!aligned16(a->q) || (a->o && !aligned16(a->o)) || (own && (!aligned16(a->k) || !aligned16(a->v))))
     return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: q/k/v/o must be 16-byte aligned");
   for (int b = 0; b < a->batch; ++b)

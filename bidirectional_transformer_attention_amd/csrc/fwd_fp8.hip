@@ -931,6 +931,10 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
     if ((p->v_strides[i] * 2) % 16 != 0 || (os * 2) % 16 != 0)
       return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
   }
+  // V tiles (64 rows) are fetched through raw buffers with 32-bit byte offsets
+  if (p->v_strides[1] > INT32_MAX / (2 * KEY_TILE))
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: v token stride %lld elements spans 2 GiB or more per %d rows",
+                (long long)p->v_strides[1], KEY_TILE);
   if (!aligned16(qrope ? p->q : p->q8) || !aligned16(p->k8) || !aligned16(p->v) || (p->o && !aligned16(p->o)))
     return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: q8 (or q)/k8/v/o must be 16-byte aligned");
   if (qrope)

@@ -146,7 +146,9 @@ int nxattn_rope_apply_relayout(void* x, int64_t batch, int64_t seq, int64_t head
  * scale <= 0 selects 1/sqrt(head_dim). Accumulation is fp32; P is rounded to bf16
  * before the P*V product on the bf16 path; the output is rounded to nearest even.
  * Supported: BF16 with head_dim 128; F32 with head_dim 64 or 72 (true fp32 MFMA, no
- * reduced-precision inputs); heads_q % heads_kv == 0; batch <= 8; seq_q >= 1.
+ * reduced-precision inputs); heads_q % heads_kv == 0; batch <= 8; seq_q >= 1; a token
+ * stride kv_strides[1] under 2^31 bytes per 64 rows (key tiles are fetched through
+ * 32-bit offsets), NXATTN_ERR_UNSUPPORTED otherwise.
  *
  * q_rope (optional, host memory, `batch` descriptors; NULL: q is used as stored):
  * rotate q on load with the RoPE of nxattn_rope_apply (same descriptor meaning and
@@ -397,7 +399,8 @@ int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors, int32_t n
  * prefix_k8[b] E4M3 [P_b, heads_kv, 128] contiguous; prefix_v[b] bf16 [P_b, heads_kv, 128]
  * contiguous (the V half of one layer slice of the online cache); exponents int8 in
  * device memory. lse as in nxattn_fwd. Outputs must not overlap inputs. scale <= 0 selects
- * 1/sqrt(128).
+ * 1/sqrt(128). v's token stride v_strides[1] must span under 2^31 bytes per 64 rows
+ * (NXATTN_ERR_UNSUPPORTED otherwise).
  *
  * q_folded != 0: q8 holds the codes of c * q with c = scale * log2(e), as
  * nxattn_rope_quantize_fp8 writes them with fold_softmax = 1. The products then are the scores

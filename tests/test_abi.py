@@ -101,6 +101,10 @@ def call_fwd(lib, a):
     (dict(prefix_len=(-1, 0)), INVALID),
     (dict(o=FAKE), INVALID),                           # o overlaps q
     (dict(scale=float("nan")), INVALID),
+    # a 64-row key tile must span under 2 GiB (32-bit buffer offsets); the bound itself passes
+    # validation up to the overlap check
+    (dict(kv_strides=(64 * 2 ** 24, 2 ** 24, 128)), UNSUPPORTED),
+    (dict(dtype=0, head_dim=64, kv_strides=(64 * 2 ** 23, 2 ** 23, 64)), UNSUPPORTED),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert call_fwd(lib, fwd_args(**kw)) == code
@@ -428,6 +432,7 @@ def fp8_args(**kw):
           prefix_k8=(FAKE + 5 * GB, None), prefix_v=(FAKE + 6 * GB, None)), INVALID),  # prefix scales missing
     (dict(prefix_k_scales=(FAKE + 9 * GB, None)), INVALID),               # prefix scales without a prefix
     (dict(q_exp=None, k_exp=None, q_scales=FAKE + 7 * GB, k_scales=FAKE + 8 * GB, o=FAKE + 8 * GB), INVALID),
+    (dict(v_strides=(64 * 2 ** 24, 2 ** 24, 128)), UNSUPPORTED),          # 64 V rows span 2 GiB
 ])
 def test_fwd_fp8_rejects(lib, kw, code):
     assert lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(**kw)), None) == code
