@@ -30,12 +30,6 @@ int check_launch(const char* what) {
   return NXATTN_OK;
 }
 
-// Byte extent of a strided [n0, n1, n2, inner] view (0 if empty).
-static int64_t extent_bytes(const int64_t st[3], int64_t n0, int64_t n1, int64_t n2, int64_t inner, int64_t es) {
-  if (n0 <= 0 || n1 <= 0 || n2 <= 0 || inner <= 0) return 0;
-  return ((n0 - 1) * st[0] + (n1 - 1) * st[1] + (n2 - 1) * st[2] + inner) * es;
-}
-
 // Workspace of a split-key nxattn_fwd: fp32 partial outputs, then (256-byte aligned)
 // their log-sum-exp. Returns false if the sizes are out of range.
 struct SplitLayout { int64_t o_bytes, lse_offset, total; };
@@ -147,7 +141,7 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
     for (int i = 0; i < 3; ++i) {
       if ((t == 1 && !own) || (t == 2 && !a->o)) continue;
       if (sts[t][i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd: negative stride");
-      if ((sts[t][i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: stride %lld is not a multiple of 16 bytes", (long long)sts[t][i]);
+      if (!stride16(sts[t][i], es)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: stride %lld is not a multiple of 16 bytes", (long long)sts[t][i]);
     }
   // key tiles (64 rows) are fetched through raw buffers with 32-bit byte offsets
   if (own && a->kv_strides[1] > INT32_MAX / (es * KEY_TILE))
@@ -161,9 +155,9 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
     return fail(NXATTN_ERR_ALIGN, "nxattn_fwd: lse is not 4-byte aligned");
   // outputs (o, lse, workspace) must not overlap any input or each other
   const int64_t D = a->head_dim;
-  const int64_t ob = extent_bytes(a->o_strides, a->batch, a->seq_q, a->heads_q, D, es);
-  const int64_t qb = extent_bytes(a->q_strides, a->batch, a->seq_q, a->heads_q, D, es);
-  const int64_t kb = own ? extent_bytes(a->kv_strides, a->batch, a->seq_q, a->heads_kv, D, es) : 0;
+  const int64_t ob = a->o ? span_bytes(a->o_strides, a->batch, a->seq_q, a->heads_q, D, es) : 0;
+  const int64_t qb = span_bytes(a->q_strides, a->batch, a->seq_q, a->heads_q, D, es);
+  const int64_t kb = own ? span_bytes(a->kv_strides, a->batch, a->seq_q, a->heads_kv, D, es) : 0;
   const int64_t lb = a->lse ? (int64_t)a->batch * a->heads_q * a->seq_q * 4 : 0;
   int ns = a->num_splits > 1 ? a->num_splits : 1;
   SplitLayout L;
@@ -177,7 +171,9 @@ extern "C" int nxattn_fwd(const nxattn_fwd_args* a, hipStream_t stream) {
   }
   const int64_t wb = ns > 1 ? L.total : 0;
   const int64_t cst[3] = {0, a->cfg_strides[0], a->cfg_strides[1]};
-  const int64_t cb = pair ? extent_bytes(cst, 1, a->seq_q, a->heads_q, D, es) : 0;
+  const int64_t cb = pair ? span_bytes(cst, 1, a->seq_q, a->heads_q, D, es) : 0;
+  if (ob < 0 || qb < 0 || kb < 0 || cb < 0)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd: q, k, v, o or cfg_out strides span more than 2^50 bytes");
   struct Span { const void* p; int64_t n; const char* name; };
   const Span outs[4] = {{a->o, ob, "o"}, {a->lse, lb, "lse"}, {a->workspace, wb, "workspace"}, {a->cfg_out, cb, "cfg_out"}};
   for (int i = 0; i < 4; ++i) {

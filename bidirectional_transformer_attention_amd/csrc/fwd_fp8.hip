@@ -904,7 +904,7 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
       return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: guidance is not finite");
     for (int i = 0; i < 2; ++i) {
       if (p->cfg_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative cfg stride");
-      if ((p->cfg_strides[i] * 2) % 16 != 0)
+      if (!stride16(p->cfg_strides[i], 2))
         return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: cfg stride %lld is not a multiple of 16 bytes", (long long)p->cfg_strides[i]);
     }
     if (!aligned16(p->cfg_out)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: cfg_out must be 16-byte aligned");
@@ -928,7 +928,7 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   for (int i = 0; i < 3; ++i) {
     const int64_t os = p->o ? p->o_strides[i] : 0;
     if (p->v_strides[i] < 0 || os < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative stride");
-    if ((p->v_strides[i] * 2) % 16 != 0 || (os * 2) % 16 != 0)
+    if (!stride16(p->v_strides[i], 2) || !stride16(os, 2))
       return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
   }
   // V tiles (64 rows) are fetched through raw buffers with 32-bit byte offsets
@@ -940,7 +940,7 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   if (qrope)
     for (int i = 0; i < 3; ++i) {
       if (p->q_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_fwd_fp8: negative stride");
-      if ((p->q_strides[i] * 2) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
+      if (!stride16(p->q_strides[i], 2)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: strides must be multiples of 16 bytes");
     }
   for (int b = 0; b < p->batch; ++b)
     if ((p->prefix_k8[b] && !aligned16(p->prefix_k8[b])) || (p->prefix_v[b] && !aligned16(p->prefix_v[b])))
@@ -948,12 +948,14 @@ extern "C" int nxattn_fwd_fp8(const nxattn_fwd_fp8_args* p, hipStream_t stream) 
   if (p->lse && (reinterpret_cast<uintptr_t>(p->lse) & 3u)) return fail(NXATTN_ERR_ALIGN, "nxattn_fwd_fp8: lse misaligned");
   // outputs must not overlap any input
   const int64_t B = p->batch, S = p->seq_q, Hq = p->heads_q, Hkv = p->heads_kv;
-  const int64_t ob = p->o ? ((B - 1) * p->o_strides[0] + (S - 1) * p->o_strides[1] + (Hq - 1) * p->o_strides[2] + D) * 2 : 0;
-  const int64_t cb = pair ? ((S - 1) * p->cfg_strides[0] + (Hq - 1) * p->cfg_strides[1] + D) * 2 : 0;
-  const int64_t vb = ((B - 1) * p->v_strides[0] + (S - 1) * p->v_strides[1] + (Hkv - 1) * p->v_strides[2] + D) * 2;
+  const int64_t cst[3] = {0, p->cfg_strides[0], p->cfg_strides[1]};
+  const int64_t ob = p->o ? span_bytes(p->o_strides, B, S, Hq, D, 2) : 0;
+  const int64_t cb = pair ? span_bytes(cst, 1, S, Hq, D, 2) : 0;
+  const int64_t vb = span_bytes(p->v_strides, B, S, Hkv, D, 2);
   const int64_t lb = p->lse ? B * Hq * S * 4 : 0;
-  const int64_t qb = qrope ? ((B - 1) * p->q_strides[0] + (S - 1) * p->q_strides[1] + (Hq - 1) * p->q_strides[2] + D) * 2
-                           : B * S * Hq * D;
+  const int64_t qb = qrope ? span_bytes(p->q_strides, B, S, Hq, D, 2) : B * S * Hq * D;
+  if (ob < 0 || cb < 0 || vb < 0 || qb < 0)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_fwd_fp8: q, v, o or cfg_out strides span more than 2^50 bytes");
   struct Span { const void* ptr; int64_t n; };
   Span ins[8 + 3 * NXATTN_MAX_BRANCHES] = {{qrope ? p->q : p->q8, qb}, {p->k8, B * S * Hkv * D}, {p->v, vb},
                                            {p->q_exp, B * Hq}, {p->k_exp, B * Hkv},

@@ -159,17 +159,17 @@ extern "C" int nxattn_attn_merge(const void* const* part_o, const float* const* 
   const int64_t es = esize(dtype);
   for (int i = 0; i < 3; ++i) {
     if (part_strides[i] < 0 || o_strides[i] < 0) return fail(NXATTN_ERR_INVALID, "nxattn_attn_merge: negative stride");
-    if ((part_strides[i] * es) % 16 != 0 || (o_strides[i] * es) % 16 != 0)
+    if (!stride16(part_strides[i], es) || !stride16(o_strides[i], es))
       return fail(NXATTN_ERR_ALIGN, "nxattn_attn_merge: strides must be multiples of 16 bytes");
   }
   if (!aligned16(o)) return fail(NXATTN_ERR_ALIGN, "nxattn_attn_merge: o is not 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(NXATTN_ERR_ALIGN, "nxattn_attn_merge: lse is not 4-byte aligned");
-  auto extent = [&](const int64_t st[3]) {
-    return ((batch - 1) * st[0] + (seq - 1) * st[1] + (heads - 1) * st[2] + head_dim) * es;
-  };
-  const int64_t ob = extent(o_strides), pb = extent(part_strides);
-  const int64_t lb = batch * heads * seq * 4;
+  const int64_t ob = span_bytes(o_strides, batch, seq, heads, head_dim, es);
+  const int64_t pb = span_bytes(part_strides, batch, seq, heads, head_dim, es);
+  const int64_t lb = dense_bytes(batch, heads, seq, 1, 4);
+  if (ob < 0 || pb < 0 || lb < 0)
+    return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_attn_merge: sizes or strides span more than 2^50 bytes");
   const bool same_strides = part_strides[0] == o_strides[0] && part_strides[1] == o_strides[1] &&
                             part_strides[2] == o_strides[2];
   for (int p = 0; p < n_parts; ++p) {

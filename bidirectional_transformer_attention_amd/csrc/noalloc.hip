@@ -52,6 +52,7 @@ extern "C" int nxattn_rope_quantize_fp8_noalloc(const nxattn_fp8_tensor* tensors
   if (!tensors || n_tensors < 1 || n_tensors > NXATTN_MAX_FP8_TENSORS)
     return fail(NXATTN_ERR_INVALID, "%s: need 1 to %d tensors", who, NXATTN_MAX_FP8_TENSORS);
   if (batch < 0) return fail(NXATTN_ERR_INVALID, "%s: negative size", who);
+  if (batch > NXATTN_MAX_BRANCHES) return fail(NXATTN_ERR_UNSUPPORTED, "%s: batch > %d", who, NXATTN_MAX_BRANCHES);
   int64_t total = 0;
   for (int t = 0; t < n_tensors; ++t) {
     if (tensors[t].heads < 0) return fail(NXATTN_ERR_INVALID, "%s: negative heads", who);

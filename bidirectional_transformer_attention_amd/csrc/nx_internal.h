@@ -24,6 +24,35 @@ inline bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
+// Largest byte extent a tensor argument may span (2^50 bytes, far beyond any device's
+// memory). The extents for the overlap checks are formed with overflow checks against
+// it, so caller-supplied sizes and strides of any value keep the host arithmetic exact.
+constexpr int64_t MAX_SPAN = INT64_C(1) << 50;
+
+// Byte extent of a strided [n0, n1, n2, inner] view of es-byte elements: 0 when a size is
+// 0 or less, -1 when a stride is negative or the extent exceeds MAX_SPAN.
+inline int64_t span_bytes(const int64_t st[3], int64_t n0, int64_t n1, int64_t n2, int64_t inner, int64_t es) {
+  if (n0 <= 0 || n1 <= 0 || n2 <= 0 || inner <= 0) return 0;
+  const int64_t n[3] = {n0, n1, n2};
+  int64_t e = inner, t = 0;
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || __builtin_mul_overflow(n[i] - 1, st[i], &t) || __builtin_add_overflow(e, t, &e)) return -1;
+  return (__builtin_mul_overflow(e, es, &e) || e > MAX_SPAN) ? -1 : e;
+}
+
+// Bytes of n0 * n1 * n2 * n3 dense es-byte elements (sizes >= 0), -1 beyond MAX_SPAN.
+inline int64_t dense_bytes(int64_t n0, int64_t n1, int64_t n2, int64_t n3, int64_t es) {
+  const int64_t n[4] = {n0, n1, n2, n3};
+  int64_t e = es;
+  for (int i = 0; i < 4; ++i)
+    if (n[i] < 0 || __builtin_mul_overflow(e, n[i], &e)) return -1;
+  return e > MAX_SPAN ? -1 : e;
+}
+
+// A stride of s es-byte elements is a whole number of 16-byte units (the unsigned product
+// is exact modulo 16 for any s).
+inline bool stride16(int64_t s, int64_t es) { return ((uint64_t)s * (uint64_t)es) % 16u == 0; }
+
 // ---- device-side element types ------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -296,7 +296,7 @@ int quant_setup(const char* who, const void* x, int dtype, int64_t batch, int64_
   const int64_t es = esize(dtype);
   for (int i = 0; i < 3; ++i) {
     if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
-    if ((strides[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
+    if (!stride16(strides[i], es)) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
   }
   if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "%s: x is not 16-byte aligned", who);
   if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
@@ -308,8 +308,9 @@ int quant_setup(const char* who, const void* x, int dtype, int64_t batch, int64_
   if (workspace_bytes < need)
     return fail(NXATTN_ERR_INVALID, "%s: workspace_bytes %lld < %lld", who, (long long)workspace_bytes, (long long)need);
   if (batch * nchunks > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: problem too large", who);
-  const int64_t xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
-  const int64_t cb = batch * seq * heads * head_dim;
+  const int64_t xb = span_bytes(strides, batch, seq, heads, head_dim, es);
+  const int64_t cb = dense_bytes(batch, seq, heads, head_dim, 1);
+  if (xb < 0 || cb < 0) return fail(NXATTN_ERR_UNSUPPORTED, "%s: sizes or strides span more than 2^50 bytes", who);
   if (overlaps(x, xb, codes, cb) || overlaps(x, xb, exps, batch * heads) || overlaps(x, xb, workspace, need) ||
       overlaps(codes, cb, exps, batch * heads) || overlaps(codes, cb, workspace, need) ||
       overlaps(exps, batch * heads, workspace, need))
@@ -373,15 +374,17 @@ extern "C" int nxattn_quantize_fp8_blocks(const void* x, int dtype, int64_t batc
   const int64_t es = esize(dtype);
   for (int i = 0; i < 3; ++i) {
     if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
-    if ((strides[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
+    if (!stride16(strides[i], es)) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
   }
   if (!aligned16(x)) return fail(NXATTN_ERR_ALIGN, "%s: x is not 16-byte aligned", who);
   if (reinterpret_cast<uintptr_t>(codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
-  const int64_t runs = batch * seq * heads * (head_dim / 32);
+  const int64_t runs = dense_bytes(batch, seq, heads, head_dim / 32, 1);
+  const int64_t xb = span_bytes(strides, batch, seq, heads, head_dim, es);
+  const int64_t cb = dense_bytes(batch, seq, heads, head_dim, 1);
+  if (runs < 0 || xb < 0 || cb < 0)
+    return fail(NXATTN_ERR_UNSUPPORTED, "%s: sizes or strides span more than 2^50 bytes", who);
   const int64_t grid = (runs + THREADS - 1) / THREADS;
   if (grid > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: problem too large", who);
-  const int64_t xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
-  const int64_t cb = batch * seq * heads * head_dim;
   if (overlaps(x, xb, codes, cb) || overlaps(x, xb, scales, runs) || overlaps(codes, cb, scales, runs))
     return fail(NXATTN_ERR_INVALID, "%s: x, codes and scales must not overlap", who);
   BlockArgs a;
@@ -408,6 +411,8 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
   if (dtype != NXATTN_F32 && dtype != NXATTN_BF16)
     return fail(NXATTN_ERR_UNSUPPORTED, "%s: dtype %d is not F32 or BF16", who, dtype);
   if (batch < 0 || seq < 0 || head_dim < 0) return fail(NXATTN_ERR_INVALID, "%s: negative size", who);
+  if (batch > NXATTN_MAX_BRANCHES) return fail(NXATTN_ERR_UNSUPPORTED, "%s: batch > %d", who, NXATTN_MAX_BRANCHES);
+  if (seq > INT32_MAX) return fail(NXATTN_ERR_UNSUPPORTED, "%s: size out of range", who);
   int64_t total = 0;
   for (int t = 0; t < n_tensors; ++t) {
     if (tensors[t].heads < 0) return fail(NXATTN_ERR_INVALID, "%s: negative heads", who);
@@ -449,6 +454,10 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
     if (reinterpret_cast<uintptr_t>(z.codes) & 7u) return fail(NXATTN_ERR_ALIGN, "%s: codes not 8-byte aligned", who);
     for (int i = 0; i < 3; ++i)
       if (z.strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+    const int64_t zxb = span_bytes(z.strides, batch, seq, z.heads, head_dim, es);
+    const int64_t zcb = dense_bytes(batch, seq, z.heads, head_dim, 1);
+    if (zxb < 0 || zcb < 0)
+      return fail(NXATTN_ERR_UNSUPPORTED, "%s: tensor %d's sizes or strides span more than 2^50 bytes", who, t);
     if (!(z.mult >= 0.f) || std::isinf(z.mult))
       return fail(NXATTN_ERR_INVALID, "%s: mult of tensor %d must be finite and >= 0", who, t);
     if (z.fold_softmax != 0 && z.fold_softmax != 1)
@@ -469,8 +478,8 @@ int rope_quantize(const char* who, const nxattn_fp8_tensor* tensors, int32_t n_t
     tt.exps[k] = z.exps;
     tt.scales[k] = z.scales;
     tt.hoff[k + 1] = tt.hoff[k] + (int32_t)z.heads;
-    xs[k] = {z.x, ((batch - 1) * z.strides[0] + (seq - 1) * z.strides[1] + (z.heads - 1) * z.strides[2] + head_dim) * es};
-    outs[nout++] = {z.codes, batch * seq * z.heads * head_dim};
+    xs[k] = {z.x, zxb};
+    outs[nout++] = {z.codes, zcb};
     if (blocks)
       outs[nout++] = {z.scales, batch * seq * z.heads * (head_dim / 32)};
     else

@@ -45,9 +45,11 @@ extern "C" int nxattn_kv_relayout(const void* src, void* dst, int64_t layers, in
   if (head_dim > (INT64_C(1) << 20) || kv_heads > (INT64_C(1) << 20) || seq > (INT64_C(1) << 31) ||
       layers > (INT64_C(1) << 20))
     return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_kv_relayout: size out of range");
+  const int64_t bytes = dense_bytes(layers * 2, kv_heads, seq, head_dim, es);
+  if (bytes < 0) return fail(NXATTN_ERR_UNSUPPORTED, "nxattn_kv_relayout: the tensor spans more than 2^50 bytes");
   const int64_t rows = layers * 2 * kv_heads * seq;
   const int64_t row_bytes = head_dim * es;
-  if (overlaps(src, rows * row_bytes, dst, rows * row_bytes))
+  if (overlaps(src, bytes, dst, bytes))
     return fail(NXATTN_ERR_INVALID, "nxattn_kv_relayout: src and dst overlap");
   // dir 0: src [LC][H][S] -> dst [LC][S][H]; dir 1: src [LC][S][H] -> dst [LC][H][S]
   const int64_t A = dir == 0 ? kv_heads : seq;

@@ -464,8 +464,10 @@ int nx::rope_launch(const char* who, const RopeTensors& tt, int64_t batch, int64
     const int64_t st[3] = {tt.sb[t], tt.ss[t], tt.sh[t]};
     for (int i = 0; i < 3; ++i) {
       if (st[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
-      if ((st[i] * es) % 16 != 0) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
+      if (!stride16(st[i], es)) return fail(NXATTN_ERR_ALIGN, "%s: strides must be multiples of 16 bytes", who);
     }
+    if (span_bytes(st, batch, seq, tt.hoff[t + 1] - tt.hoff[t], head_dim, es) < 0)
+      return fail(NXATTN_ERR_UNSUPPORTED, "%s: sizes or strides span more than 2^50 bytes", who);
   }
   const int64_t blocks = batch * ((seq + ROPE_TOK - 1) / ROPE_TOK);
   if (blocks + (with_jobs ? jobs->blk0[jobs->n] : 0) > INT32_MAX)
@@ -540,8 +542,12 @@ extern "C" int nxattn_rope_apply_relayout(void* x, int64_t batch, int64_t seq, i
   const int64_t es = esize(dtype);
   // the rotated tensor's byte extent (for the overlap checks)
   int64_t xb = 0;
-  if (batch > 0 && seq > 0 && heads > 0 && head_dim > 0 && strides)
-    xb = ((batch - 1) * strides[0] + (seq - 1) * strides[1] + (heads - 1) * strides[2] + head_dim) * es;
+  if (batch > 0 && seq > 0 && heads > 0 && head_dim > 0 && strides) {
+    for (int i = 0; i < 3; ++i)
+      if (strides[i] < 0) return fail(NXATTN_ERR_INVALID, "%s: negative stride", who);
+    xb = span_bytes(strides, batch, seq, heads, head_dim, es);
+    if (xb < 0) return fail(NXATTN_ERR_UNSUPPORTED, "%s: sizes or strides of x span more than 2^50 bytes", who);
+  }
   RelayoutJobs rj;
   memset(&rj, 0, sizeof(rj));
   int64_t jbytes[NXATTN_MAX_BRANCHES] = {0};
@@ -559,8 +565,9 @@ extern "C" int nxattn_rope_apply_relayout(void* x, int64_t batch, int64_t seq, i
     if (row_bytes % 16 != 0 || !aligned16(j.src) || !aligned16(j.dst))
       return fail(NXATTN_ERR_UNSUPPORTED, "%s: job %d: rows and pointers must be 16-byte multiples "
                   "(nxattn_kv_relayout takes the others)", who, i);
+    jbytes[i] = dense_bytes(j.layers * 2, j.kv_heads, j.seq, j.head_dim, es);
+    if (jbytes[i] < 0) return fail(NXATTN_ERR_UNSUPPORTED, "%s: job %d spans more than 2^50 bytes", who, i);
     const int64_t rows = j.layers * 2 * j.kv_heads * j.seq;
-    jbytes[i] = rows * row_bytes;
     const int n = rj.n;
     rj.src[n] = static_cast<const u32x4*>(j.src);
     rj.dst[n] = static_cast<u32x4*>(j.dst);

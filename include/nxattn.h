@@ -18,6 +18,9 @@
  *  - Strides are in elements; the innermost (head_dim) dimension is contiguous.
  *  - Base pointers must be 16-byte aligned and every stride must keep rows 16-byte
  *    aligned (NXATTN_ERR_ALIGN otherwise).
+ *  - No tensor argument's sizes and strides may span more than 2^50 bytes (far beyond
+ *    any device's memory): such calls return NXATTN_ERR_UNSUPPORTED, whatever values
+ *    the sizes and strides take (the host arithmetic that checks them cannot overflow).
  */
 #ifndef NXATTN_H
 #define NXATTN_H

@@ -580,6 +580,37 @@ def test_rope_relayout_empty_is_a_noop(lib):
     assert rope_relayout_call(lib, [dict(L=0)], S=0) == OK              # zero-size job skipped
 
 
+# ----------------------------------------------------------------------------- extents
+BIG = 2 ** 60   # a stride (elements) whose products leave int64 at these sizes
+
+
+def test_huge_sizes_and_strides_are_rejected(lib):
+    """Sizes and strides far beyond any device's memory are refused as unsupported, with
+    the extents formed without signed overflow (the UBSan run of this file checks that)."""
+    def refused(code):
+        return code == UNSUPPORTED and "2^50" in nx.last_error()
+    # attention: a q, o or batch stride whose view spans more than 2^50 bytes
+    assert refused(call_fwd(lib, fwd_args(q_strides=(BIG, 8 * 128, 128))))
+    assert refused(call_fwd(lib, fwd_args(o_strides=(64 * 8 * 128, BIG, 128))))
+    assert refused(call_fwd(lib, fwd_args(q_strides=(2 ** 62, 8 * 128, 128))))
+    assert refused(lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(v_strides=(BIG, 2 * 128, 128))), None))
+    assert refused(lib.nxattn_fwd_fp8(ctypes.byref(fp8_args(o_strides=(64 * 8 * 128, 8 * 128, BIG))), None))
+    # merge: strides, and a row count whose lse bytes leave int64
+    po, pl = [FAKE, FAKE + GB], [FAKE + 2 * GB, FAKE + 3 * GB]
+    assert refused(merge_call(lib, po, pl, pst=(BIG, 8 * 128, 128)))
+    assert refused(merge_call(lib, po, pl, B=2 ** 40, S=2 ** 40))
+    # relayout: sizes inside the per-dimension limits whose product leaves int64
+    assert refused(lib.nxattn_kv_relayout(FAKE, FAKE + (1 << 30), 2 ** 20, 2 ** 20, 2 ** 31, 2 ** 20, 1, 0, None))
+    # RoPE: a token stride, and a relayout job of absurd size
+    assert refused(rope_call(lib, [nx.rope_desc((64,), (32,), (0,))], strides=(64 * 2 * 64, BIG, 64)))
+    assert refused(rope_relayout_call(lib, [dict(L=2 ** 20, H=2 ** 20, S=2 ** 31)]))
+    # quantizers
+    X, C, E, W = FAKE, FAKE + GB, FAKE + 2 * GB, FAKE + 3 * GB
+    st = (ctypes.c_int64 * 3)(BIG, 4 * 128, 128)
+    assert refused(lib.nxattn_quantize_fp8(X, 1, 2, 64, 4, 128, st, C, E, W, 1 << 20, None))
+    assert refused(lib.nxattn_quantize_fp8_blocks(X, 1, 2, 64, 4, 128, st, C, E, None))
+
+
 # ----------------------------------------------------------------------------- cfg
 def test_cfg_rejects(lib):
     f = lib.nxattn_cfg_combine
