@@ -340,6 +340,8 @@ __device__ __forceinline__ void rotate_q(bf16x8* qf, const RopeQ& r, int tok, in
 template <bool FOLD>
 __device__ __forceinline__ float weights(Wave& w, float c) {
   const float nm = -w.m;
+  // the two partial sums start from the first weights (the same values as 0 + p, since a
+  // weight is never -0, without the two adds)
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -352,8 +354,8 @@ __device__ __forceinline__ float weights(Wave& w, float c) {
                               : __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e], c, nm));
         const float p1 = FOLD ? __builtin_amdgcn_exp2f(w.s[kb][8 * hs + 2 * e + 1])
                               : __builtin_amdgcn_exp2f(__builtin_fmaf(w.s[kb][8 * hs + 2 * e + 1], c, nm));
-        l0 += p0;
-        l1 += p1;
+        l0 = (kb | hs | e) ? l0 + p0 : p0;
+        l1 = (kb | hs | e) ? l1 + p1 : p1;
         pk[e] = pack_bf16x2(p0, p1);
       }
       w.p[2 * kb + hs] = as_bf16x8(pk);
@@ -523,6 +525,9 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   // V (transposing read): row r = 4*(q>>1) + rsub, column col = 32db + 16(q&1) + csub,
   // chunk col>>3 = 4db + e at slot (4db + e) ^ 4rsub, i.e. byte
   // r*ROWB + 16e + 2*(csub&7) + (64db ^ 64rsub).
+  // The fragment addresses these give are the same for every tile: the compiler keeps
+  // them in registers (20 more VGPRs, 234 in the branch-pair kernel, no spills), so the
+  // main loop does no address arithmetic for its LDS reads.
   w.kbase = n * ROWB + 16 * (hh ^ (n & 1));
   w.kx = 16 * (n & 14);
   {
@@ -634,9 +639,6 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   auto iter_a = [&](int t, auto par, auto fast) {
     constexpr int PAR = decltype(par)::value;        // t & 1
     constexpr bool FAST = decltype(fast)::value;
-    // opaque per iteration: keeps the compiler from hoisting the per-fragment address
-    // arithmetic out of the loop (which would pin a dozen more registers)
-    asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
     if constexpr (FAST) {
       const DmaPlan pl = plan_of(t);
       gemm_phase<PAR, PAR ^ 1, true, FOLD, true>(w, &pl);
@@ -653,7 +655,6 @@ __device__ __forceinline__ void wave_program(const Args& a, int lane, int wave) 
   // MASK: the position may be the range's last, possibly ragged, tile
   auto iter_b = [&](int t, auto par, auto mask) {
     constexpr int PAR = decltype(par)::value;
-    asm volatile("" : "+v"(w.kbase), "+v"(w.kx), "+v"(w.vbase), "+v"(w.vy));
     softmax<decltype(mask)::value, FOLD>(w, c, valid_at(t), hh);
     prio_only<2>();
     gemm_phase<PAR, PAR ^ 1, true, FOLD>(w);

@@ -331,6 +331,8 @@ __device__ __forceinline__ void max_update(Wave& w, float c) {
 template <bool FOLD>
 __device__ __forceinline__ float weights(Wave& w, float c) {
   const float nm = -w.m;
+  // the two partial sums start from the first weights (the same values as 0 + p, since a
+  // weight is never -0, without the two adds)
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -342,8 +344,8 @@ __device__ __forceinline__ float weights(Wave& w, float c) {
         const float x0 = w.s[kb][8 * hs + 2 * e], x1 = w.s[kb][8 * hs + 2 * e + 1];
         const float p0 = __builtin_amdgcn_exp2f(FOLD ? x0 : __builtin_fmaf(x0, c, nm));
         const float p1 = __builtin_amdgcn_exp2f(FOLD ? x1 : __builtin_fmaf(x1, c, nm));
-        l0 += p0;
-        l1 += p1;
+        l0 = (kb | hs | e) ? l0 + p0 : p0;
+        l1 = (kb | hs | e) ? l1 + p1 : p1;
         pk[e] = pack_bf16x2(p0, p1);
       }
       w.p[2 * kb + hs] = as_bf16x8(pk);
